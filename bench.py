@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Benchmark of BATQuant's online W4A4 linear-layer hot path on one MI355X.
+
+One step is one pass of the whole online path over one batch of synthetic input: the fused
+transform + clip + MXFP4 quantiser (K1) on the bf16 activations, then the MXFP4 x MXFP4
+scaled-MFMA GEMM (K2) against weights prepared offline.  Default workload: the
+q_proj-shaped layer S=2048 tokens, N=4096 in-features, out=4096 (Qwen3-8B shape), seeded
+synthetic data.
+
+Inputs are resident in HBM before timing starts.  Every step uses the next of R buffer sets
+(activations, codes, scales, prepared weights, output), with R chosen so the sets together
+exceed the 256 MB Infinity Cache several times over; the measured rates are therefore HBM
+rates, not cache rates.  Kernel durations come from HIP events recorded on the stream the
+kernels are launched on; the step time is wall clock around the timed steps.
+
+Prints one JSON line.  --gpus above 1 is refused: this path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fused BAT+clip+MXFP4 quantize GB/s; W4A4 MXFP4 GEMM TFLOPS (% of peak)"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+FP4_PEAK_TFLOPS = 10100.0        # MI355X dense MXFP4 MFMA
+
+
+def k1_bytes(S, N):
+    """Algorithmic bytes of one quantiser launch: bf16 in (2 B/elem), codes out (0.5 B/elem),
+    scales out (1 B per 32 elem), plus the parameters (A, B_i, two ratios per block)."""
+    k = N // 32
+    return S * N * 2 + S * N // 2 + S * k + 256 + 64 * k + 8 * k
+
+
+def k2_flops(S, N, out):
+    return 2 * S * N * out
+
+
+def k2_bytes(S, N, out):
+    """Compulsory bytes of one GEMM launch: both MXFP4 operands once, fp32 output once."""
+    return (S + out) * (N // 2 + N // 32) + 4 * S * out
+
+
+def cpu_baseline(L, seconds):
+    """The oracle as it stands, on a bounded sample of token rows of the same layer:
+    quantise the sampled rows and compute every output of those rows."""
+    import numpy as np
+    from oracle import oracle
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+    S, N, out = L.cfg.S, L.cfg.N, L.cfg.out
+    r1, r2 = oracle.clip_ratio(L.alpha_min), oracle.clip_ratio(L.alpha_max)
+    wq, we = oracle.prepare_weight(L.W, L.A, L.B, nthreads=threads)   # offline, untimed
+
+    def run(rows):
+        idx = np.linspace(0, S - 1, rows).astype(np.int64)
+        t0 = time.perf_counter()
+        xq, xe = oracle.quantize_act(L.x_bits[idx], L.A, L.B, r1, r2, nthreads=threads)
+        t1 = time.perf_counter()
+        oracle.gemm(xq, xe, wq, we, nthreads=threads)
+        t2 = time.perf_counter()
+        return t1 - t0, t2 - t1
+
+    probe = min(S, threads)
+    tq, tg = run(probe)
+    rows = int(min(S, max(probe, probe * seconds / max(tq + tg, 1e-6))))
+    tq, tg = run(rows)
+    return {
+        "value": round(k1_bytes(rows, N) / tq / 1e9, 4),
+        "unit": "GB/s",
+        "gemm_value": round(k2_flops(rows, N, out) / tg / 1e12, 6),
+        "gemm_unit": "TFLOP/s",
+        "seconds": round(tq + tg, 2),
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{rows} of {S} token rows: quantise them and compute all {out} outputs "
+                  f"of each (plain C oracle, OpenMP over rows)",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="q_proj")
+    ap.add_argument("--rotate-bytes", type=float, default=2.0e9,
+                    help="total bytes of the rotated buffer sets")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain device copy of known size (for counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs the path on one GPU only; --gpus must be 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import w4a4_batq_quantize_amd as bq
+    import workloads as wl
+
+    L = wl.make_layer(args.config)
+    S, N, out = L.cfg.S, L.cfg.N, L.cfg.out
+    k = N // 32
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    A = torch.from_numpy(L.A).to(dev)
+    B = torch.from_numpy(L.B).to(dev)
+    rmin = torch.from_numpy(bq.clip_ratios(L.alpha_min)).to(dev)
+    rmax = torch.from_numpy(bq.clip_ratios(L.alpha_max)).to(dev)
+    W = torch.from_numpy(L.W).to(dev)
+    wq0, we0 = bq.prepare_weight(W, L.A, L.B)
+    del W
+    x0 = torch.from_numpy(L.x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    per_set = S * N * 2 + S * (N // 2 + k) + out * (N // 2 + k) + 4 * S * out
+    R = max(2, math.ceil(args.rotate_bytes / per_set))
+    xs = [x0.clone() for _ in range(R)]
+    wqs = [wq0.clone() for _ in range(R)]
+    wes = [we0.clone() for _ in range(R)]
+    xqs = [torch.empty((S, N // 2), dtype=torch.uint8, device=dev) for _ in range(R)]
+    xes = [torch.empty((S, k), dtype=torch.uint8, device=dev) for _ in range(R)]
+    ys = [torch.empty((S, out), dtype=torch.float32, device=dev) for _ in range(R)]
+    del x0, wq0, we0
+
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    pA, pB, pr1, pr2 = A.data_ptr(), B.data_ptr(), rmin.data_ptr(), rmax.data_ptr()
+    ptr = [(xs[j].data_ptr(), xqs[j].data_ptr(), xes[j].data_ptr(), wqs[j].data_ptr(),
+            wes[j].data_ptr(), ys[j].data_ptr()) for j in range(R)]
+    quant, gemm = bq.quantize_act_raw, bq.gemm_w4a4_raw
+
+    def step(j, ev_mid=None):
+        x, xq, xe, wq, we, y = ptr[j]
+        st = quant(x, S, N, N, pA, pB, pr1, pr2, xq, xe, sh)
+        if ev_mid is not None:
+            ev_mid.record(stream)
+        st |= gemm(xq, xe, wq, we, S, N, out, y, sh)
+        if st:
+            raise RuntimeError(f"library call failed with status {st}")
+
+    for i in range(args.warmup):
+        step(i % R)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * K + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(K):
+        step((args.warmup + i) % R, ev[2 * i + 1])
+        ev[2 * i + 2].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    t_k1 = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(K)) / K * 1e-3
+    t_k2 = sum(ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(K)) / K * 1e-3
+    ms_per_step = (t1 - t0) / K * 1e3
+
+    if args.copy_calibration:
+        # plain copy of known size, outside the timed region, for scaling HBM counters
+        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    # keep the last step's output alive and finite (a cheap sanity check, untimed)
+    last = ys[(args.warmup + K - 1) % R]
+    assert bool(torch.isfinite(last).all().item()), "non-finite GEMM output"
+
+    b1 = k1_bytes(S, N)
+    gbs = b1 / t_k1 / 1e9
+    tflops = k2_flops(S, N, out) / t_k2 / 1e12
+    k2_ai = k2_flops(S, N, out) / k2_bytes(S, N, out)
+    k2_roof = min(FP4_PEAK_TFLOPS, k2_ai * HBM_PEAK_GBS / 1e3)
+    roof_k1 = {"kernel": "quantize_kernel (fused BAT+clip+MXFP4)", "bound": "hbm",
+               "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+               "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+               "avg_us": round(t_k1 * 1e6, 3), "algorithmic_bytes": b1}
+    roof_k2 = {"kernel": "gemm_kernel (MXFP4 scaled MFMA)",
+               "bound": "mfma" if k2_roof >= FP4_PEAK_TFLOPS else "hbm",
+               "achieved": round(tflops, 1), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+               "frac": round(tflops / FP4_PEAK_TFLOPS, 4), "traffic": None,
+               "avg_us": round(t_k2 * 1e6, 3), "algorithmic_flops": k2_flops(S, N, out),
+               "roofline_tflops": round(k2_roof, 1), "frac_of_roofline": round(tflops / k2_roof, 4)}
+    dominant = roof_k2 if t_k2 >= t_k1 else roof_k1
+
+    rec = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "dtype_detail": "K1: bf16 in, fp32 transform/clip, E2M1+E8M0 out; "
+                        "K2: E2M1 x E2M1 scaled MFMA, fp32 accumulate and output",
+        "data": "synthetic",
+        "config": {"workload": f"{L.cfg.name}: S={S} N={N} out={out} (Qwen3-8B-shaped linear "
+                               f"layer, seeded synthetic bf16 activations and fp32 weights)",
+                   "S": S, "N": N, "out": out, "rotated_buffer_sets": R},
+        "gemm": {"value": round(tflops, 1), "unit": "TFLOP/s",
+                 "pct_of_peak": round(100 * tflops / FP4_PEAK_TFLOPS, 2)},
+        "step_gpu_us": round((t_k1 + t_k2) * 1e6, 3),
+        "roofline": dominant,
+        "roofline_kernels": {"quantize": roof_k1, "gemm": roof_k2},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(L, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,144 @@
+/*
+ * batq.h -- C ABI of the BATQuant online W4A4 linear-layer library for AMD MI355X (gfx950).
+ *
+ * The method ("BATQuant: Outlier-resilient MXFP4 Quantization via Learnable Block-wise
+ * Optimization") inserts a block-aligned affine transform before a linear layer: each
+ * 32-element MXFP block x_i of an activation row becomes y_i = x_i P_i with
+ * P_i = B_i (x) A (A 8x8 shared by all blocks, B_i 4x4 private to block i), is clipped to
+ * [sigmoid(alpha_min_i) min(y_i), sigmoid(alpha_max_i) max(y_i)] and quantised to MXFP4.
+ * The weight side is transformed by P^-1 and quantised offline, so the layer output is the
+ * MXFP4 x MXFP4 product of the two (gist.science technical summary, sections 2A-2D;
+ * daily-arxiv summary, method bullets; thelatestinai listing, Figure 3 and Table 1).
+ *
+ * Conventions for every entry point:
+ *  - Sizes are int64_t.  "dev" pointers are device (HBM) memory owned by the caller (for
+ *    example torch tensors); "host" pointers are ordinary host memory.  The library keeps
+ *    no pointer after a call returns and holds no global mutable state.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Device work is
+ *    enqueued on it and the call returns without waiting, unless noted.  Results are valid
+ *    once the stream reaches the work.
+ *  - Every argument is validated on the host before any HIP call, so an invalid call
+ *    returns its error code without touching the GPU.  No call throws.
+ *  - Aliasing between an input and an output buffer is not allowed.  Non-finite inputs
+ *    (Inf/NaN activations, weights or factors) are outside the contract.
+ *
+ * Data formats:
+ *  - bf16 activations: uint16_t bit patterns, row-major [S, ldx], element n of row s at
+ *    x[s*ldx + n]; block i of a row is elements [32i, 32i+32).
+ *  - GPK factors: A fp32 [8][8] row-major; B fp32 [k][4][4] row-major (B[i][r][c] at
+ *    B[16i + 4r + c]), k = N/32.  The transform of one block is evaluated on its row-major
+ *    4x8 view X (X[r][c] = x[8r + c]) as Y = B_i^T (X A): first Z = X A, then Y = B_i^T Z,
+ *    in fp32, each sum a product followed by fused multiply-adds in increasing index order.
+ *  - MXFP4 tensor of R rows: codes uint8_t [R, N/2] row-major, two E2M1 codes per byte,
+ *    element 2j in the low nibble and 2j+1 in the high nibble (E2M1: sign bit 3, magnitude
+ *    codes 0..7 = 0, 0.5, 1, 1.5, 2, 3, 4, 6); scales uint8_t [R, N/32] row-major, E8M0
+ *    (value 2^(byte-127)).  Scale of a block: floor(log2(max|v|)) - 2, clamped to
+ *    [-127, 127]; codes: nearest E2M1 of v / scale, ties to even, saturating at 6.
+ *  - GEMM output: fp32 [S, out] row-major.
+ */
+#ifndef BATQ_H
+#define BATQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum batq_status {
+    BATQ_OK = 0,
+    BATQ_ERR_NULL = 1,        /* a required pointer is NULL                                  */
+    BATQ_ERR_SHAPE = 2,       /* negative size, N not a multiple of 32, ldx < N, or overflow */
+    BATQ_ERR_ALIGN = 3,       /* a pointer or stride breaks the alignment stated below       */
+    BATQ_ERR_UNSUPPORTED = 4, /* valid for the format but beyond this build's limits         */
+    BATQ_ERR_SINGULAR = 5,    /* a GPK factor is not invertible                              */
+    BATQ_ERR_HIP = 6          /* the HIP runtime reported an error (launch, copy, alloc)     */
+} batq_status;
+
+/*
+ * Online activation path: fused block transform + block-wise clipping + MXFP4 quantisation
+ * (gist.science summary, sections 2A-2C and 2D "activation side ... online";
+ * daily-arxiv summary, clipping formula; thelatestinai listing, Figure 2 caption: values
+ * are divided by the block scale before rounding).
+ *
+ *   x      dev  bf16 bits [S, ldx]; 16-byte aligned; ldx >= N and ldx % 8 == 0
+ *   S      rows (tokens), >= 0;  N  in-features, >= 0, N % 32 == 0 (k = N/32 blocks)
+ *   A      dev  fp32 [8][8], 4-byte aligned
+ *   B      dev  fp32 [k][4][4], 16-byte aligned
+ *   r_min, r_max  dev fp32 [k], the clip ratios sigmoid(alpha_min/max) of each block (see
+ *          batq_clip_ratios), 4-byte aligned
+ *   q      dev  out: codes uint8 [S, N/2], 16-byte aligned
+ *   e      dev  out: scales uint8 [S, N/32]
+ * S == 0 or N == 0 is a no-op returning BATQ_OK without reading any pointer.  Per block:
+ * m = min y, M = max y, lo = r_min*m, hi = r_max*M (fp32), y' = min(max(y, lo), hi) (the
+ * upper bound wins if lo > hi), then MXFP4 of y'.  Does not allocate or synchronise.
+ */
+batq_status batq_quantize_act(const uint16_t* x, int64_t S, int64_t N, int64_t ldx,
+                              const float* A, const float* B,
+                              const float* r_min, const float* r_max,
+                              uint8_t* q, uint8_t* e, void* stream);
+
+/*
+ * Offline weight preparation: fold P^-1 into the weights and quantise them to MXFP4 with
+ * round-to-nearest (gist.science summary, section 2D "weight side ... fused offline";
+ * thelatestinai listing, Figure 3 and Tables 6-7 "RTN" weight quantiser).  Keeping
+ * X W^T = (X P)(W P^-T)^T, each weight block becomes B_i^-1 W_i A^-T, computed in the same
+ * form as the activation side with A' = (A^-1)^T and B'_i = (B_i^-1)^T (see
+ * batq_weight_factors), without clipping.
+ *
+ *   W       dev  fp32 [out, N] row-major, 16-byte aligned;  out >= 0, N % 32 == 0
+ *   A_host  host fp32 [8][8];  B_host host fp32 [N/32][4][4]
+ *   wq      dev  out: codes uint8 [out, N/2], 16-byte aligned
+ *   we      dev  out: scales uint8 [out, N/32]
+ * Returns BATQ_ERR_SINGULAR if A or any B_i is not invertible.  Offline step: allocates a
+ * small device buffer for the factors and synchronises `stream` before returning.
+ */
+batq_status batq_prepare_weight(const float* W, int64_t out, int64_t N,
+                                const float* A_host, const float* B_host,
+                                uint8_t* wq, uint8_t* we, void* stream);
+
+/*
+ * W4A4 GEMM: y[s][o] = sum_n dq(xq)[s][n] * dq(wq)[o][n], dq(code, e) = e2m1(code) * 2^(e-127)
+ * (the W4A4 linear layer of the gist.science summary, section 4, and thelatestinai
+ * listing, abstract), on gfx950 scaled MFMA with fp32 accumulation.  Each 32-element block
+ * product is exact; sums across blocks round in fp32.
+ *
+ *   xq, xe  dev  activation codes [S, N/2] (16-byte aligned) and scales [S, N/32]
+ *   wq, we  dev  weight codes [out, N/2] (16-byte aligned) and scales [out, N/32]
+ *   S, out >= 0;  N >= 0, N % 32 == 0
+ *   y       dev  out: fp32 [S, out], 16-byte aligned, overwritten
+ * S == 0 or out == 0 is a no-op; N == 0 writes zeros.  Does not allocate or synchronise.
+ */
+batq_status batq_gemm_w4a4(const uint8_t* xq, const uint8_t* xe,
+                           const uint8_t* wq, const uint8_t* we,
+                           int64_t S, int64_t N, int64_t out, float* y, void* stream);
+
+/*
+ * Host: clip ratios r[i] = fp32(1 / (1 + exp(-alpha[i]))) evaluated in binary64 and rounded
+ * once (daily-arxiv summary, clipping bullet: the sigmoid keeps each ratio in (0, 1);
+ * gist.science summary, section 2C).  The logits are per block, shared by all tokens.
+ *   alpha host fp32 [k];  ratio host fp32 [k] (out);  k >= 0.
+ */
+batq_status batq_clip_ratios(const float* alpha, int64_t k, float* ratio);
+
+/*
+ * Host: the fp32 factors of the offline weight transform, A' = (A^-1)^T and
+ * B'_i = (B_i^-1)^T, each entry the fp32 value nearest to the exact inverse (computed with
+ * 64-bit-mantissa Gauss-Jordan elimination with partial pivoting).  Since
+ * (B_i (x) A)^-1 = B_i^-1 (x) A^-1, these realise P^-T block by block (gist.science
+ * summary, section 2B and 2D).
+ *   A host fp32 [8][8];  B host fp32 [k][4][4];  k >= 0
+ *   A_inv_t host out fp32 [8][8];  B_inv_t host out fp32 [k][4][4]
+ * Returns BATQ_ERR_SINGULAR if a factor is not invertible.
+ */
+batq_status batq_weight_factors(const float* A, const float* B, int64_t k,
+                                float* A_inv_t, float* B_inv_t);
+
+/* Human-readable name of a status code (static storage). */
+const char* batq_status_string(batq_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BATQ_H */

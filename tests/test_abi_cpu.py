@@ -1,0 +1,130 @@
+"""The C ABI on a host without a GPU: the library loads, exports every entry point that
+include/batq.h declares, validates arguments before any HIP call, and its host-side
+parameter steps agree bit for bit with the oracle."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, NULL, SHAPE, ALIGN, UNSUPPORTED, SINGULAR, HIP = range(7)
+
+# plausible, aligned device addresses; validation must fail before anything dereferences them
+D = 1 << 40
+
+
+@pytest.fixture(scope="module")
+def bq():
+    import w4a4_batq_quantize_amd as bq
+    bq.lib()
+    return bq
+
+
+def declared_entry_points():
+    src = open(os.path.join(ROOT, "include", "batq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(batq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_entry_point(bq):
+    names = declared_entry_points()
+    assert names == sorted(["batq_quantize_act", "batq_prepare_weight", "batq_gemm_w4a4",
+                            "batq_clip_ratios", "batq_weight_factors", "batq_status_string"])
+    L = ctypes.CDLL(bq.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(bq.SIGNATURES) == set(names)
+    # internal symbols stay hidden
+    assert not hasattr(L, "_ZN4batq15launch_quantizeEbPKvlllPKfS3_S3_S3_PhS4_P12ihipStream_t")
+
+
+def test_status_strings(bq):
+    for code, name in bq._binding.STATUS.items():
+        assert bq.status_string(code).startswith(name)
+
+
+def test_quantize_act_argument_errors(bq):
+    q = bq.quantize_act_raw
+    # shape
+    assert q(D, -1, 64, 64, D, D, D, D, D, D) == SHAPE
+    assert q(D, 4, 48, 64, D, D, D, D, D, D) == SHAPE            # N % 32
+    assert q(D, 4, 64, 32, D, D, D, D, D, D) == SHAPE            # ldx < N
+    assert q(D, 1 << 40, 64, 1 << 40, D, D, D, D, D, D) == SHAPE  # S * ldx overflows
+    # empty inputs are no-ops that read nothing
+    assert q(0, 0, 64, 64, 0, 0, 0, 0, 0, 0) == OK
+    assert q(0, 5, 0, 0, 0, 0, 0, 0, 0, 0) == OK
+    # null pointers
+    for i in (0, 4, 5, 6, 7, 8, 9):
+        args = [D, 4, 64, 64, D, D, D, D, D, D]
+        args[i] = 0
+        assert q(*args) == NULL, i
+    # alignment
+    assert q(D + 2, 4, 64, 64, D, D, D, D, D, D) == ALIGN        # x not 16-byte aligned
+    assert q(D, 4, 64, 68, D, D, D, D, D, D) == ALIGN            # row stride not 16 bytes
+    assert q(D, 4, 64, 64, D, D + 4, D, D, D, D) == ALIGN        # B
+    assert q(D, 4, 64, 64, D, D, D, D, D + 8, D) == ALIGN        # codes
+    assert q(D, 4, 64, 64, D + 2, D, D, D, D, D) == ALIGN        # A
+
+
+def test_gemm_argument_errors(bq):
+    g = bq.gemm_w4a4_raw
+    assert g(D, D, D, D, -1, 64, 8, D) == SHAPE
+    assert g(D, D, D, D, 4, 40, 8, D) == SHAPE
+    assert g(D, D, D, D, 4, 64, -8, D) == SHAPE
+    assert g(0, 0, 0, 0, 0, 64, 8, 0) == OK
+    assert g(0, 0, 0, 0, 4, 64, 0, 0) == OK
+    assert g(0, D, D, D, 4, 64, 8, D) == NULL
+    assert g(D, D, D, D, 4, 64, 8, 0) == NULL
+    assert g(D, D, D + 1, D, 4, 64, 8, D) == ALIGN
+    assert g(D, D, D, D, 4, 64, 8, D + 4) == ALIGN
+    assert g(D, D, D, D, 1 << 62, 64, 8, D) == SHAPE
+
+
+def test_prepare_weight_argument_errors_and_singular_factors(bq):
+    p = bq.prepare_weight_raw
+    A = np.eye(8, dtype=np.float32)
+    B = np.tile(np.eye(4, dtype=np.float32), (2, 1, 1))
+    a, b = A.ctypes.data, B.ctypes.data
+    assert p(D, 4, 70, a, b, D, D) == SHAPE
+    assert p(D, -4, 64, a, b, D, D) == SHAPE
+    assert p(0, 0, 64, 0, 0, 0, 0) == OK
+    assert p(D, 4, 64, 0, b, D, D) == NULL
+    assert p(D + 4, 4, 64, a, b, D, D) == ALIGN
+    # singular factors are detected on the host, before any device work
+    As = A.copy()
+    As[3] = As[5]
+    assert p(D, 4, 64, As.ctypes.data, b, D, D) == SINGULAR
+    Bs = B.copy()
+    Bs[1, 2] = 0
+    assert p(D, 4, 64, a, Bs.ctypes.data, D, D) == SINGULAR
+    with pytest.raises(bq.BatqError):
+        bq.weight_factors(As, B)
+
+
+def test_clip_ratios_match_oracle_bit_for_bit(bq, orc):
+    for name in ("tiny", "q_proj", "down_proj"):
+        L = wl.make_layer(name, with_weight=False)
+        for a in (L.alpha_min, L.alpha_max):
+            assert np.array_equal(bq.clip_ratios(a), orc.clip_ratio(a))
+    extreme = np.array([0.0, 30.0, -30.0, 88.0, -88.0, 1e-8], dtype=np.float32)
+    assert np.array_equal(bq.clip_ratios(extreme), orc.clip_ratio(extreme))
+
+
+def test_weight_factors_match_oracle_exact_inverse(bq, orc):
+    for name in ("tiny", "q_proj", "down_proj"):
+        L = wl.make_layer(name, with_weight=False)
+        Ai, Bi = bq.weight_factors(L.A, L.B)
+        Ai_o, Bi_o = orc.weight_factors(L.A, L.B)
+        assert np.array_equal(Ai, Ai_o)
+        assert np.array_equal(Bi, Bi_o)
+
+
+def test_binding_fails_loudly_without_library(bq, monkeypatch):
+    monkeypatch.setattr(bq._binding, "_lib", None)
+    monkeypatch.setattr(bq._binding, "LIB_PATH", "/nonexistent/libbatq.so")
+    with pytest.raises(RuntimeError, match="no fallback"):
+        bq._binding.lib()

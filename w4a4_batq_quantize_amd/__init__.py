@@ -1,0 +1,21 @@
+"""BATQuant's online W4A4 linear-layer hot path, native on AMD MI355X (gfx950).
+
+The compute lives in libbatq.so (hand-written HIP kernels behind a C ABI, include/batq.h);
+this package is the thin Python binding over it.
+"""
+from ._binding import (  # noqa: F401
+    LIB_PATH,
+    SIGNATURES,
+    BatqError,
+    clip_ratios,
+    gemm_w4a4,
+    gemm_w4a4_raw,
+    lib,
+    linear_w4a4,
+    prepare_weight,
+    prepare_weight_raw,
+    quantize_act,
+    quantize_act_raw,
+    status_string,
+    weight_factors,
+)

@@ -1,0 +1,180 @@
+"""ctypes binding over libbatq.so: argument marshalling only.
+
+Every step of the path runs in the library's HIP kernels; PyTorch provides device memory
+and the current stream.  If the built library is missing the calls fail loudly; there is
+no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libbatq.so")
+
+STATUS = {0: "BATQ_OK", 1: "BATQ_ERR_NULL", 2: "BATQ_ERR_SHAPE", 3: "BATQ_ERR_ALIGN",
+          4: "BATQ_ERR_UNSUPPORTED", 5: "BATQ_ERR_SINGULAR", 6: "BATQ_ERR_HIP"}
+
+# Every exported entry point and its ctypes signature (the names of include/batq.h).
+_P, _I64, _I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+SIGNATURES = {
+    "batq_quantize_act": [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P],
+    "batq_prepare_weight": [_P, _I64, _I64, _P, _P, _P, _P, _P],
+    "batq_gemm_w4a4": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P],
+    "batq_clip_ratios": [_P, _I64, _P],
+    "batq_weight_factors": [_P, _P, _I64, _P, _P],
+    "batq_status_string": [_I],
+}
+
+
+class BatqError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_string(status)}")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the built library (build it with __graft_entry__.build() or
+    ``python w4a4_batq_quantize_amd/build.py``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; the HIP path has no fallback")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_char_p if name == "batq_status_string" else ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().batq_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise BatqError(fn, status)
+
+
+# ---------------------------------------------------------------------------------------
+# raw entry points (integer device pointers, integer stream handle)
+# ---------------------------------------------------------------------------------------
+
+def quantize_act_raw(x, S, N, ldx, A, B, r_min, r_max, q, e, stream=0) -> int:
+    return lib().batq_quantize_act(x, S, N, ldx, A, B, r_min, r_max, q, e, stream)
+
+
+def gemm_w4a4_raw(xq, xe, wq, we, S, N, out, y, stream=0) -> int:
+    return lib().batq_gemm_w4a4(xq, xe, wq, we, S, N, out, y, stream)
+
+
+def prepare_weight_raw(W, out, N, A_host, B_host, wq, we, stream=0) -> int:
+    return lib().batq_prepare_weight(W, out, N, A_host, B_host, wq, we, stream)
+
+
+# ---------------------------------------------------------------------------------------
+# host helpers
+# ---------------------------------------------------------------------------------------
+
+def _host_f32(a) -> np.ndarray:
+    if hasattr(a, "detach"):
+        a = a.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+
+
+def clip_ratios(alpha) -> np.ndarray:
+    """fp32 sigmoid(alpha) per block (host)."""
+    a = _host_f32(alpha).ravel()
+    r = np.empty_like(a)
+    _check("batq_clip_ratios", lib().batq_clip_ratios(a.ctypes.data, a.size, r.ctypes.data))
+    return r
+
+
+def weight_factors(A, B):
+    """Host fp32 factors (A^-1)^T [8,8] and (B_i^-1)^T [k,4,4] of the offline weight side."""
+    A = _host_f32(A).reshape(8, 8)
+    B = _host_f32(B).reshape(-1, 4, 4)
+    Ai = np.empty_like(A)
+    Bi = np.empty_like(B)
+    _check("batq_weight_factors", lib().batq_weight_factors(
+        A.ctypes.data, B.ctypes.data, B.shape[0], Ai.ctypes.data, Bi.ctypes.data))
+    return Ai, Bi
+
+
+# ---------------------------------------------------------------------------------------
+# torch-tensor entry points
+# ---------------------------------------------------------------------------------------
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _ptr(t) -> int:
+    return t.data_ptr()
+
+
+def quantize_act(x, A, B, r_min, r_max, q=None, e=None, stream=None):
+    """Fused transform + clip + MXFP4 of bf16 activations x [S, N] (row stride may exceed
+    N).  A fp32 [8,8], B fp32 [k,4,4], r_min/r_max fp32 [k] (device).  Returns the codes
+    uint8 [S, N/2] and scales uint8 [S, N/32]."""
+    import torch
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    S, N = x.shape
+    k = N // 32
+    if q is None:
+        q = torch.empty((S, N // 2), dtype=torch.uint8, device=x.device)
+    if e is None:
+        e = torch.empty((S, k), dtype=torch.uint8, device=x.device)
+    for t, dt in ((A, torch.float32), (B, torch.float32), (r_min, torch.float32),
+                  (r_max, torch.float32)):
+        assert t.dtype == dt and t.is_contiguous()
+    _check("batq_quantize_act", quantize_act_raw(
+        _ptr(x), S, N, x.stride(0), _ptr(A), _ptr(B), _ptr(r_min), _ptr(r_max), _ptr(q),
+        _ptr(e), _stream(stream)))
+    return q, e
+
+
+def prepare_weight(W, A_host, B_host, stream=None):
+    """Offline: fp32 weights W [out, N] (device) -> MXFP4 codes [out, N/2] and scales of
+    W P^-T.  A_host [8,8] and B_host [k,4,4] are host arrays; synchronises the stream."""
+    import torch
+    assert W.dtype == torch.float32 and W.is_contiguous() and W.dim() == 2
+    out, N = W.shape
+    A = _host_f32(A_host)
+    B = _host_f32(B_host)
+    assert A.size == 64 and B.size == 16 * (N // 32)
+    wq = torch.empty((out, N // 2), dtype=torch.uint8, device=W.device)
+    we = torch.empty((out, N // 32), dtype=torch.uint8, device=W.device)
+    _check("batq_prepare_weight", prepare_weight_raw(
+        _ptr(W), out, N, A.ctypes.data, B.ctypes.data, _ptr(wq), _ptr(we), _stream(stream)))
+    return wq, we
+
+
+def gemm_w4a4(xq, xe, wq, we, y=None, stream=None):
+    """fp32 y [S, out] = dq(xq, xe) dq(wq, we)^T on scaled MFMA."""
+    import torch
+    S, N = xq.shape[0], xq.shape[1] * 2
+    out = wq.shape[0]
+    for t in (xq, xe, wq, we):
+        assert t.dtype == torch.uint8 and t.is_contiguous()
+    assert wq.shape[1] * 2 == N and xe.shape == (S, N // 32) and we.shape == (out, N // 32)
+    if y is None:
+        y = torch.empty((S, out), dtype=torch.float32, device=xq.device)
+    _check("batq_gemm_w4a4", gemm_w4a4_raw(_ptr(xq), _ptr(xe), _ptr(wq), _ptr(we), S, N, out,
+                                           _ptr(y), _stream(stream)))
+    return y
+
+
+def linear_w4a4(x, A, B, r_min, r_max, wq, we, stream=None):
+    """One pass of the online path: quantise the activations, then the W4A4 GEMM."""
+    xq, xe = quantize_act(x, A, B, r_min, r_max, stream=stream)
+    return gemm_w4a4(xq, xe, wq, we, stream=stream)

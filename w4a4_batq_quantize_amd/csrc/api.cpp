@@ -1,0 +1,159 @@
+// Host side of the C ABI declared in include/batq.h: argument validation (always before
+// any HIP call), the offline parameter steps (clip ratios, inverse GPK factors) and the
+// launches of the fused quantiser and the W4A4 GEMM.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <limits>
+#include <vector>
+
+#include "batq.h"
+#include "internal.h"
+
+#define BATQ_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+batq_status from_hip(hipError_t err) { return err == hipSuccess ? BATQ_OK : BATQ_ERR_HIP; }
+
+// Inverse of an n x n fp32 matrix by Gauss-Jordan elimination with partial pivoting in
+// 64-bit-mantissa arithmetic, stored transposed and rounded once to fp32.  Returns false if
+// a pivot is zero or a result is not finite.
+bool inverse_transposed(const float* M, int n, float* out_t)
+{
+    long double a[8][16];
+    for (int i = 0; i < n; ++i)
+        for (int j = 0; j < 2 * n; ++j)
+            a[i][j] = j < n ? (long double)M[i * n + j] : (long double)(j - n == i);
+    for (int col = 0; col < n; ++col) {
+        int piv = col;
+        for (int r = col + 1; r < n; ++r)
+            if (std::fabs(a[r][col]) > std::fabs(a[piv][col])) piv = r;
+        if (a[piv][col] == 0.0L) return false;
+        if (piv != col)
+            for (int j = 0; j < 2 * n; ++j) std::swap(a[piv][j], a[col][j]);
+        const long double p = a[col][col];
+        for (int j = 0; j < 2 * n; ++j) a[col][j] /= p;
+        for (int r = 0; r < n; ++r) {
+            if (r == col || a[r][col] == 0.0L) continue;
+            const long double f = a[r][col];
+            for (int j = 0; j < 2 * n; ++j) a[r][j] -= f * a[col][j];
+        }
+    }
+    for (int i = 0; i < n; ++i)
+        for (int j = 0; j < n; ++j) {
+            const float v = (float)a[i][n + j];        // (M^-1)[i][j]
+            if (!std::isfinite(v)) return false;
+            out_t[j * n + i] = v;                       // stored transposed
+        }
+    return true;
+}
+
+bool mul_overflows(int64_t a, int64_t b)
+{
+    return a != 0 && b > std::numeric_limits<int64_t>::max() / a;
+}
+
+}  // namespace
+
+BATQ_API const char* batq_status_string(batq_status status)
+{
+    switch (status) {
+        case BATQ_OK: return "BATQ_OK";
+        case BATQ_ERR_NULL: return "BATQ_ERR_NULL: a required pointer is NULL";
+        case BATQ_ERR_SHAPE: return "BATQ_ERR_SHAPE: invalid size";
+        case BATQ_ERR_ALIGN: return "BATQ_ERR_ALIGN: misaligned pointer or stride";
+        case BATQ_ERR_UNSUPPORTED: return "BATQ_ERR_UNSUPPORTED: beyond this build's limits";
+        case BATQ_ERR_SINGULAR: return "BATQ_ERR_SINGULAR: a GPK factor is not invertible";
+        case BATQ_ERR_HIP: return "BATQ_ERR_HIP: HIP runtime error";
+    }
+    return "unknown batq_status";
+}
+
+BATQ_API batq_status batq_clip_ratios(const float* alpha, int64_t k, float* ratio)
+{
+    if (k < 0) return BATQ_ERR_SHAPE;
+    if (k == 0) return BATQ_OK;
+    if (!alpha || !ratio) return BATQ_ERR_NULL;
+    for (int64_t i = 0; i < k; ++i)
+        ratio[i] = (float)(1.0 / (1.0 + std::exp(-(double)alpha[i])));
+    return BATQ_OK;
+}
+
+BATQ_API batq_status batq_weight_factors(const float* A, const float* B, int64_t k,
+                                         float* A_inv_t, float* B_inv_t)
+{
+    if (k < 0) return BATQ_ERR_SHAPE;
+    if (!A || !A_inv_t || (k > 0 && (!B || !B_inv_t))) return BATQ_ERR_NULL;
+    if (!inverse_transposed(A, 8, A_inv_t)) return BATQ_ERR_SINGULAR;
+    for (int64_t i = 0; i < k; ++i)
+        if (!inverse_transposed(B + 16 * i, 4, B_inv_t + 16 * i)) return BATQ_ERR_SINGULAR;
+    return BATQ_OK;
+}
+
+BATQ_API batq_status batq_quantize_act(const uint16_t* x, int64_t S, int64_t N, int64_t ldx,
+                                       const float* A, const float* B, const float* r_min,
+                                       const float* r_max, uint8_t* q, uint8_t* e,
+                                       void* stream)
+{
+    if (S < 0 || N < 0 || N % 32 != 0) return BATQ_ERR_SHAPE;
+    if (S == 0 || N == 0) return BATQ_OK;
+    if (!x || !A || !B || !r_min || !r_max || !q || !e) return BATQ_ERR_NULL;
+    if (ldx < N || mul_overflows(S, ldx)) return BATQ_ERR_SHAPE;
+    if (ldx % 8 != 0 || !aligned(x, 16) || !aligned(B, 16) || !aligned(q, 16) ||
+        !aligned(A, 4) || !aligned(r_min, 4) || !aligned(r_max, 4))
+        return BATQ_ERR_ALIGN;
+    const int64_t k = N / 32;
+    if (k > 64LL * 65535) return BATQ_ERR_UNSUPPORTED;
+    return from_hip(batq::launch_quantize(true, x, S, k, ldx, A, B, r_min, r_max, q, e,
+                                          as_stream(stream)));
+}
+
+BATQ_API batq_status batq_prepare_weight(const float* W, int64_t out, int64_t N,
+                                         const float* A_host, const float* B_host,
+                                         uint8_t* wq, uint8_t* we, void* stream)
+{
+    if (out < 0 || N < 0 || N % 32 != 0) return BATQ_ERR_SHAPE;
+    if (out == 0 || N == 0) return BATQ_OK;
+    if (!W || !A_host || !B_host || !wq || !we) return BATQ_ERR_NULL;
+    if (mul_overflows(out, N)) return BATQ_ERR_SHAPE;
+    if (!aligned(W, 16) || !aligned(wq, 16)) return BATQ_ERR_ALIGN;
+    const int64_t k = N / 32;
+    if (k > 64LL * 65535) return BATQ_ERR_UNSUPPORTED;
+
+    std::vector<float> factors(64 + 16 * k);
+    const batq_status st = batq_weight_factors(A_host, B_host, k, factors.data(),
+                                               factors.data() + 64);
+    if (st != BATQ_OK) return st;
+
+    hipStream_t s = as_stream(stream);
+    float* d = nullptr;
+    if (hipMalloc(&d, factors.size() * sizeof(float)) != hipSuccess) return BATQ_ERR_HIP;
+    hipError_t err = hipMemcpyAsync(d, factors.data(), factors.size() * sizeof(float),
+                                    hipMemcpyHostToDevice, s);
+    if (err == hipSuccess)
+        err = batq::launch_quantize(false, W, out, k, N, d, d + 64, nullptr, nullptr, wq, we, s);
+    const hipError_t sync = hipStreamSynchronize(s);
+    const hipError_t fr = hipFree(d);
+    if (err != hipSuccess || sync != hipSuccess || fr != hipSuccess) return BATQ_ERR_HIP;
+    return BATQ_OK;
+}
+
+BATQ_API batq_status batq_gemm_w4a4(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq,
+                                    const uint8_t* we, int64_t S, int64_t N, int64_t out,
+                                    float* y, void* stream)
+{
+    if (S < 0 || N < 0 || out < 0 || N % 32 != 0) return BATQ_ERR_SHAPE;
+    if (S == 0 || out == 0) return BATQ_OK;
+    if (!y || (N > 0 && (!xq || !xe || !wq || !we))) return BATQ_ERR_NULL;
+    if (mul_overflows(S, out) || mul_overflows(S, N) || mul_overflows(out, N))
+        return BATQ_ERR_SHAPE;
+    if (!aligned(y, 16) || !aligned(xq, 16) || !aligned(wq, 16)) return BATQ_ERR_ALIGN;
+    return from_hip(batq::launch_gemm(xq, xe, wq, we, S, N, out, y, as_stream(stream)));
+}

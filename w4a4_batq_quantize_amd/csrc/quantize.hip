@@ -1,0 +1,182 @@
+// Fused BATQuant block transform + block-wise clipping + MXFP4 quantisation (gfx950).
+//
+// One thread owns one 32-element block of one row (one MXFP4 block): it reads the block
+// (64 B of bf16, or 128 B of fp32 on the weight side), applies Y = B_i^T (X A) on the
+// row-major 4x8 view X of the block (GPK factorisation P_i = B_i (x) A, gist.science
+// summary section 2B; thelatestinai listing Table 1: 12 multiply-adds per element instead
+// of 32 for a full 32x32 P_i), clips the block to [r_min m, r_max M] (daily-arxiv summary,
+// clipping bullet; gist.science section 2C), picks the E8M0 scale from the largest clipped
+// magnitude and writes 16 bytes of E2M1 codes plus one scale byte (values divided by the
+// scale before rounding: thelatestinai listing, Figure 2 caption).
+//
+// Layout on the chip: lanes of a wave take consecutive blocks of one row, so a wave reads
+// one contiguous 4 KB span of a row and writes one contiguous 1 KB span of codes and 64
+// scale bytes; when a row has fewer than 64 blocks a wave covers several whole rows.  A
+// (64 floats, the same for every block) is read through the scalar unit into SGPRs and is
+// a direct operand of every first-stage multiply-add; B_i and the clip ratios are per-lane
+// vector loads that hit in cache (they are 64 B + 8 B per block column for all rows).
+//
+// Arithmetic contract (must match the plain oracle bit for bit): fp32, each sum a product
+// followed by fused multiply-adds in increasing index order, first Z = X A over the
+// contiguous 8-index, then Y = B^T Z over the 4-index; clipping min(max(y, lo), hi) with
+// lo = r_min * min(y), hi = r_max * max(y) (the upper bound wins when lo > hi); scale byte
+// max(E(amax) - 2, 0) with E the fp32 exponent field; E2M1 by v_cvt_scalef32_pk_fp4_f32,
+// whose scale operand contributes only its exponent field, so passing e << 23 divides by
+// 2^(e-127) exactly and rounds once to nearest-even with saturation at 6.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace batq {
+namespace {
+
+constexpr int kWavesPerGroup = 4;
+constexpr int kThreads = 64 * kWavesPerGroup;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Y = B^T (X A) for one block held in registers, X[r][c] = x[8r + c].
+__device__ __forceinline__ void gpk_transform(const float (&x)[32], const float* __restrict__ A,
+                                              const float4 (&b)[4], float (&y)[32])
+{
+    float z[32];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            float acc = x[8 * r] * A[c];
+#pragma unroll
+            for (int qi = 1; qi < 8; ++qi) acc = __builtin_fmaf(x[8 * r + qi], A[8 * qi + c], acc);
+            z[8 * r + c] = acc;
+        }
+    }
+    const float bm[4][4] = {{b[0].x, b[0].y, b[0].z, b[0].w},
+                            {b[1].x, b[1].y, b[1].z, b[1].w},
+                            {b[2].x, b[2].y, b[2].z, b[2].w},
+                            {b[3].x, b[3].y, b[3].z, b[3].w}};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            float acc = bm[0][r] * z[c];
+#pragma unroll
+            for (int qi = 1; qi < 4; ++qi) acc = __builtin_fmaf(bm[qi][r], z[8 * qi + c], acc);
+            y[8 * r + c] = acc;
+        }
+    }
+}
+
+template <bool kAct>
+__global__ void __launch_bounds__(kThreads)
+quantize_kernel(const void* __restrict__ xin, int64_t rows, int64_t k, int64_t ldx,
+                const float* __restrict__ A, const float* __restrict__ B,
+                const float* __restrict__ r_min, const float* __restrict__ r_max,
+                uint8_t* __restrict__ q, uint8_t* __restrict__ e, int lpr_log2)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t row = ((((int64_t)blockIdx.x * kWavesPerGroup + wave) << (6 - lpr_log2)) +
+                         (lane >> lpr_log2));
+    const int64_t blk = (int64_t)blockIdx.y * 64 + (lane & ((1 << lpr_log2) - 1));
+    if (row >= rows || blk >= k) return;
+
+    float x[32];
+    if constexpr (kAct) {
+        const uint4* xp = reinterpret_cast<const uint4*>(
+            static_cast<const uint16_t*>(xin) + row * ldx + 32 * blk);
+        uint4 v[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[t] = xp[t];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint32_t w[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                x[8 * t + 2 * d] = bf16_lo(w[d]);
+                x[8 * t + 2 * d + 1] = bf16_hi(w[d]);
+            }
+        }
+    } else {
+        const float4* xp = reinterpret_cast<const float4*>(
+            static_cast<const float*>(xin) + row * ldx + 32 * blk);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const float4 v = xp[t];
+            x[4 * t] = v.x;
+            x[4 * t + 1] = v.y;
+            x[4 * t + 2] = v.z;
+            x[4 * t + 3] = v.w;
+        }
+    }
+    const float4* bp = reinterpret_cast<const float4*>(B + 16 * blk);
+    float4 b[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) b[t] = bp[t];
+
+    float y[32];
+    gpk_transform(x, A, b, y);
+
+    float amax;
+    if constexpr (kAct) {
+        float m = y[0], M = y[0];
+#pragma unroll
+        for (int j = 1; j < 32; ++j) {
+            m = __builtin_fminf(m, y[j]);
+            M = __builtin_fmaxf(M, y[j]);
+        }
+        const float hi = r_max[blk] * M;
+        const float lo = __builtin_fminf(r_min[blk] * m, hi);   // lo > hi: every value -> hi
+#pragma unroll
+        for (int j = 0; j < 32; ++j) y[j] = __builtin_amdgcn_fmed3f(y[j], lo, hi);
+        amax = __builtin_fmaxf(__builtin_fabsf(__builtin_amdgcn_fmed3f(m, lo, hi)),
+                               __builtin_fabsf(__builtin_amdgcn_fmed3f(M, lo, hi)));
+    } else {
+        amax = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) amax = __builtin_fmaxf(amax, __builtin_fabsf(y[j]));
+    }
+    const int ex = (int)((__float_as_uint(amax) >> 23) & 0xFF) - 2;
+    const uint32_t ebyte = ex > 0 ? (uint32_t)ex : 0u;
+    const float scale = __uint_as_float(ebyte << 23);
+
+    uint32_t w[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        uint32_t acc = 0;
+        acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, y[8 * d + 0], y[8 * d + 1], scale, 0);
+        acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, y[8 * d + 2], y[8 * d + 3], scale, 1);
+        acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, y[8 * d + 4], y[8 * d + 5], scale, 2);
+        acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, y[8 * d + 6], y[8 * d + 7], scale, 3);
+        w[d] = acc;
+    }
+    *reinterpret_cast<uint4*>(q + row * (16 * k) + 16 * blk) = make_uint4(w[0], w[1], w[2], w[3]);
+    e[row * k + blk] = (uint8_t)ebyte;
+}
+
+}  // namespace
+
+hipError_t launch_quantize(bool act, const void* x, int64_t rows, int64_t k, int64_t ldx,
+                           const float* A, const float* B, const float* r_min,
+                           const float* r_max, uint8_t* q, uint8_t* e, hipStream_t stream)
+{
+    // lanes per row: the smallest power of two >= k, capped at one wave
+    int lpr_log2 = 0;
+    while ((1LL << lpr_log2) < k && lpr_log2 < 6) ++lpr_log2;
+    const int64_t rows_per_wave = 64 >> lpr_log2;
+    const int64_t waves = (rows + rows_per_wave - 1) / rows_per_wave;
+    const int64_t gx = (waves + kWavesPerGroup - 1) / kWavesPerGroup;
+    const int64_t gy = (k + 63) / 64;
+    if (gx > 0x7FFFFFFF || gy > 65535) return hipErrorInvalidConfiguration;
+    dim3 grid((unsigned)gx, (unsigned)gy);
+    if (act)
+        hipLaunchKernelGGL(quantize_kernel<true>, grid, dim3(kThreads), 0, stream, x, rows, k,
+                           ldx, A, B, r_min, r_max, q, e, lpr_log2);
+    else
+        hipLaunchKernelGGL(quantize_kernel<false>, grid, dim3(kThreads), 0, stream, x, rows,
+                           k, ldx, A, B, r_min, r_max, q, e, lpr_log2);
+    return hipGetLastError();
+}
+
+}  // namespace batq

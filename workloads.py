@@ -144,3 +144,13 @@ def make_layer(cfg: LayerConfig | str, with_weight: bool = True) -> Layer:
     assert np.linalg.cond(A.astype(np.float64)) < 1e3
     assert np.max(np.linalg.cond(B.astype(np.float64))) < 1e3
     return layer
+
+
+def random_mxfp4(rows: int, N: int, seed, scale_lo: int = 110, scale_hi: int = 145):
+    """Seeded random MXFP4 operands for the GEMM alone: uniformly random code bytes
+    [rows, N/2] and E8M0 scale bytes [rows, N/32] in [scale_lo, scale_hi)."""
+    seed = list(seed) if isinstance(seed, (tuple, list)) else [int(seed)]
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
+    q = rng.integers(0, 256, size=(rows, N // 2), dtype=np.uint8)
+    e = rng.integers(scale_lo, scale_hi, size=(rows, N // 32), dtype=np.uint8)
+    return q, e
