@@ -121,7 +121,8 @@ def main():
     rmin = torch.from_numpy(bq.clip_ratios(L.alpha_min)).to(dev)
     rmax = torch.from_numpy(bq.clip_ratios(L.alpha_max)).to(dev)
     W = torch.from_numpy(L.W).to(dev)
-    wq0, we0 = bq.prepare_weight(W, L.A, L.B)
+    layout = bq.SCALES_MFMA_TILED
+    wq0, we0 = bq.prepare_weight(W, L.A, L.B, layout=layout)
     del W
     x0 = torch.from_numpy(L.x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
 
@@ -131,7 +132,8 @@ def main():
     wqs = [wq0.clone() for _ in range(R)]
     wes = [we0.clone() for _ in range(R)]
     xqs = [torch.empty((S, N // 2), dtype=torch.uint8, device=dev) for _ in range(R)]
-    xes = [torch.empty((S, k), dtype=torch.uint8, device=dev) for _ in range(R)]
+    xes = [torch.empty((bq.scale_bytes(S, N, layout),), dtype=torch.uint8, device=dev)
+           for _ in range(R)]
     ys = [torch.empty((S, out), dtype=torch.float32, device=dev) for _ in range(R)]
     del x0, wq0, we0
 
@@ -144,10 +146,10 @@ def main():
 
     def step(j, ev_mid=None):
         x, xq, xe, wq, we, y = ptr[j]
-        st = quant(x, S, N, N, pA, pB, pr1, pr2, xq, xe, sh)
+        st = quant(x, S, N, N, pA, pB, pr1, pr2, xq, xe, layout, sh)
         if ev_mid is not None:
             ev_mid.record(stream)
-        st |= gemm(xq, xe, wq, we, S, N, out, y, sh)
+        st |= gemm(xq, xe, wq, we, S, N, out, y, layout, sh)
         if st:
             raise RuntimeError(f"library call failed with status {st}")
 
@@ -215,7 +217,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{L.cfg.name}: S={S} N={N} out={out} (Qwen3-8B-shaped linear "
                                f"layer, seeded synthetic bf16 activations and fp32 weights)",
-                   "S": S, "N": N, "out": out, "rotated_buffer_sets": R},
+                   "S": S, "N": N, "out": out, "rotated_buffer_sets": R,
+                   "scale_layout": "mfma_tiled"},
         "gemm": {"value": round(tflops, 1), "unit": "TFLOP/s",
                  "pct_of_peak": round(100 * tflops / FP4_PEAK_TFLOPS, 2)},
         "step_gpu_us": round((t_k1 + t_k2) * 1e6, 3),

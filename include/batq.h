@@ -34,6 +34,16 @@
  *    codes 0..7 = 0, 0.5, 1, 1.5, 2, 3, 4, 6); scales uint8_t [R, N/32] row-major, E8M0
  *    (value 2^(byte-127)).  Scale of a block: floor(log2(max|v|)) - 2, clamped to
  *    [-127, 127]; codes: nearest E2M1 of v / scale, ties to even, saturating at 6.
+ *  - Scale layouts (batq_scale_layout), for a matrix of R rows and k = N/32 blocks:
+ *      BATQ_SCALES_ROW_MAJOR: scale (r, b) at byte r*k + b; R*k bytes.
+ *      BATQ_SCALES_MFMA_TILED: rows grouped in panels of 32, blocks in groups of 8; each
+ *        (panel, group) is one contiguous 256-byte unit holding its 32 rows x 8 bytes, and
+ *        within a row's 8 bytes the blocks of the group are ordered 0,2,4,6,1,3,5,7.  Scale
+ *        (r, b) is at byte ((r/32)*K8 + b/8)*256 + (r%32)*8 + (b%2)*4 + (b%8)/2 with
+ *        K8 = ceil(k/8); the buffer holds ceil(R/32)*32 * K8*8 bytes (equal to R*k when
+ *        R % 32 == 0 and k % 8 == 0).  Bytes of padding rows/blocks are never written and
+ *        never influence a result.  This is the order in which the W4A4 GEMM's matrix
+ *        instructions consume scales: one 256-byte unit per 32 rows per 256 K elements.
  *  - GEMM output: fp32 [S, out] row-major.
  */
 #ifndef BATQ_H
@@ -44,6 +54,11 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+typedef enum batq_scale_layout {
+    BATQ_SCALES_ROW_MAJOR = 0,
+    BATQ_SCALES_MFMA_TILED = 1
+} batq_scale_layout;
 
 typedef enum batq_status {
     BATQ_OK = 0,
@@ -68,7 +83,7 @@ typedef enum batq_status {
  *   r_min, r_max  dev fp32 [k], the clip ratios sigmoid(alpha_min/max) of each block (see
  *          batq_clip_ratios), 4-byte aligned
  *   q      dev  out: codes uint8 [S, N/2], 16-byte aligned
- *   e      dev  out: scales uint8 [S, N/32]
+ *   e      dev  out: scales in `e_layout` (see "Scale layouts" above)
  * S == 0 or N == 0 is a no-op returning BATQ_OK without reading any pointer.  Per block:
  * m = min y, M = max y, lo = r_min*m, hi = r_max*M (fp32), y' = min(max(y, lo), hi) (the
  * upper bound wins if lo > hi), then MXFP4 of y'.  Does not allocate or synchronise.
@@ -76,7 +91,8 @@ typedef enum batq_status {
 batq_status batq_quantize_act(const uint16_t* x, int64_t S, int64_t N, int64_t ldx,
                               const float* A, const float* B,
                               const float* r_min, const float* r_max,
-                              uint8_t* q, uint8_t* e, void* stream);
+                              uint8_t* q, uint8_t* e, batq_scale_layout e_layout,
+                              void* stream);
 
 /*
  * Offline weight preparation: fold P^-1 into the weights and quantise them to MXFP4 with
@@ -89,13 +105,14 @@ batq_status batq_quantize_act(const uint16_t* x, int64_t S, int64_t N, int64_t l
  *   W       dev  fp32 [out, N] row-major, 16-byte aligned;  out >= 0, N % 32 == 0
  *   A_host  host fp32 [8][8];  B_host host fp32 [N/32][4][4]
  *   wq      dev  out: codes uint8 [out, N/2], 16-byte aligned
- *   we      dev  out: scales uint8 [out, N/32]
+ *   we      dev  out: scales in `we_layout`
  * Returns BATQ_ERR_SINGULAR if A or any B_i is not invertible.  Offline step: allocates a
  * small device buffer for the factors and synchronises `stream` before returning.
  */
 batq_status batq_prepare_weight(const float* W, int64_t out, int64_t N,
                                 const float* A_host, const float* B_host,
-                                uint8_t* wq, uint8_t* we, void* stream);
+                                uint8_t* wq, uint8_t* we, batq_scale_layout we_layout,
+                                void* stream);
 
 /*
  * W4A4 GEMM: y[s][o] = sum_n dq(xq)[s][n] * dq(wq)[o][n], dq(code, e) = e2m1(code) * 2^(e-127)
@@ -103,14 +120,17 @@ batq_status batq_prepare_weight(const float* W, int64_t out, int64_t N,
  * listing, abstract), on gfx950 scaled MFMA with fp32 accumulation.  Each 32-element block
  * product is exact; sums across blocks round in fp32.
  *
- *   xq, xe  dev  activation codes [S, N/2] (16-byte aligned) and scales [S, N/32]
- *   wq, we  dev  weight codes [out, N/2] (16-byte aligned) and scales [out, N/32]
+ *   xq, xe  dev  activation codes [S, N/2] (16-byte aligned) and scales
+ *   wq, we  dev  weight codes [out, N/2] (16-byte aligned) and scales
+ *   layout  the layout of both xe and we.  BATQ_SCALES_MFMA_TILED with N % 256 == 0 takes
+ *           the fastest path (scales 256-byte aligned); any other combination is
+ *           supported at lower speed.
  *   S, out >= 0;  N >= 0, N % 32 == 0
  *   y       dev  out: fp32 [S, out], 16-byte aligned, overwritten
  * S == 0 or out == 0 is a no-op; N == 0 writes zeros.  Does not allocate or synchronise.
  */
 batq_status batq_gemm_w4a4(const uint8_t* xq, const uint8_t* xe,
-                           const uint8_t* wq, const uint8_t* we,
+                           const uint8_t* wq, const uint8_t* we, batq_scale_layout layout,
                            int64_t S, int64_t N, int64_t out, float* y, void* stream);
 
 /*

@@ -63,3 +63,30 @@ def assert_gemm_close(y_gpu, y_ref, t_ref, rel=1e-5, what=""):
                            f"{bad[:3].tolist()} err {err[tuple(bad[0])]:.3e} "
                            f"bound {bound[tuple(bad[0])]:.3e}")
     assert np.all(np.isfinite(y_gpu))
+
+
+def tiled_scale_index(rows: int, k: int) -> np.ndarray:
+    """Byte offsets [rows, k] of the MFMA-tiled scale layout, from its definition: 32-row
+    panels x 8-block groups form 256-byte units; within a row's 8 bytes the blocks of the
+    group are ordered 0,2,4,6,1,3,5,7."""
+    r = np.arange(rows, dtype=np.int64)[:, None]
+    b = np.arange(k, dtype=np.int64)[None, :]
+    k8 = (k + 7) // 8
+    return ((r // 32) * k8 + b // 8) * 256 + (r % 32) * 8 + (b % 2) * 4 + (b % 8) // 2
+
+
+def tiled_scale_bytes(rows: int, k: int) -> int:
+    return ((rows + 31) // 32) * 32 * ((k + 7) // 8) * 8
+
+
+def to_tiled_scales(e: np.ndarray, pad: int = 0xFF) -> np.ndarray:
+    """Row-major scales [rows, k] -> flat MFMA-tiled buffer; padding bytes set to `pad`
+    (0xFF is an E8M0 NaN: any use of a padding byte would poison a result)."""
+    rows, k = e.shape
+    out = np.full(tiled_scale_bytes(rows, k), pad, dtype=np.uint8)
+    out[tiled_scale_index(rows, k)] = e
+    return out
+
+
+def from_tiled_scales(buf: np.ndarray, rows: int, k: int) -> np.ndarray:
+    return np.asarray(buf).reshape(-1)[tiled_scale_index(rows, k)]

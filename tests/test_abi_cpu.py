@@ -128,3 +128,30 @@ def test_binding_fails_loudly_without_library(bq, monkeypatch):
     monkeypatch.setattr(bq._binding, "LIB_PATH", "/nonexistent/libbatq.so")
     with pytest.raises(RuntimeError, match="no fallback"):
         bq._binding.lib()
+
+
+def test_invalid_scale_layout_is_rejected(bq):
+    assert bq.quantize_act_raw(D, 4, 64, 64, D, D, D, D, D, D, 7) == UNSUPPORTED
+    assert bq.gemm_w4a4_raw(D, D, D, D, 4, 64, 8, D, 2) == UNSUPPORTED
+    A = np.eye(8, dtype=np.float32)
+    B = np.tile(np.eye(4, dtype=np.float32), (2, 1, 1))
+    assert bq.prepare_weight_raw(D, 4, 64, A.ctypes.data, B.ctypes.data, D, D, 5) == UNSUPPORTED
+
+
+def test_tiled_scale_layout_definition():
+    """The tiled index map is a bijection onto distinct bytes of the stated buffer size,
+    and matches hand-computed offsets of the layout's definition."""
+    from tests.gpu_util import tiled_scale_bytes, tiled_scale_index
+    for rows, k in [(32, 8), (37, 131), (64, 128), (1, 3)]:
+        idx = tiled_scale_index(rows, k)
+        assert len(np.unique(idx)) == rows * k
+        assert idx.max() < tiled_scale_bytes(rows, k)
+    idx = tiled_scale_index(64, 16)
+    # (row 33, block 9): panel 1, group 1 -> unit 1*2 + 1 = 3; row%32 = 1; block%8 = 1 -> 4
+    assert idx[33, 9] == 3 * 256 + 1 * 8 + 4 + 0
+    # (row 0, blocks 0..7) -> bytes 0,4,1,5,2,6,3,7
+    assert list(idx[0, :8]) == [0, 4, 1, 5, 2, 6, 3, 7]
+    assert tiled_scale_bytes(17, 128) == 32 * 128
+    import w4a4_batq_quantize_amd as bq
+    assert bq.scale_bytes(17, 4096, bq.SCALES_MFMA_TILED) == tiled_scale_bytes(17, 128)
+    assert bq.scale_bytes(17, 4096, bq.SCALES_ROW_MAJOR) == 17 * 128

@@ -86,3 +86,46 @@ def test_linear_end_to_end(bq, orc, name):
     wq_ref, we_ref = orc.prepare_weight(L.W, L.A, L.B, nthreads=ORACLE_THREADS)
     y_ref, t_ref = orc.gemm(xq_ref, xe_ref, wq_ref, we_ref, nthreads=ORACLE_THREADS)
     assert_gemm_close(y[rows], y_ref, t_ref, what=name)
+
+
+# ----------------------------------------------------------------------------------------
+# MFMA-tiled scale layout (padding bytes are E8M0 NaN: any use would poison a result)
+# ----------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("S,N,out", [
+    (1, 32, 1), (17, 4096, 100), (129, 4192, 300), (64, 12288, 64), (128, 4096, 128),
+    (256, 1024, 384), (300, 2048, 520), (33, 256, 36),
+])
+def test_gemm_random_operands_tiled_scales(bq, orc, S, N, out):
+    import torch
+    from tests.gpu_util import to_tiled_scales
+    xq, xe = wl.random_mxfp4(S, N, seed=(17, S, N, out))
+    wq, we = wl.random_mxfp4(out, N, seed=(18, S, N, out))
+    y = bq.gemm_w4a4(u8_to_device(xq), u8_to_device(to_tiled_scales(xe)), u8_to_device(wq),
+                     u8_to_device(to_tiled_scales(we)), layout=bq.SCALES_MFMA_TILED)
+    torch.cuda.synchronize()
+    y_ref, t_ref = orc.gemm(xq, xe, wq, we, nthreads=ORACLE_THREADS)
+    assert_gemm_close(to_host(y), y_ref, t_ref, what=f"tiled S={S} N={N} out={out}")
+
+
+@pytest.mark.parametrize("name", ["q_proj", "gate_up", "down_proj", "sweep_s1_n12288",
+                                  "sweep_s16384_n12288"])
+def test_linear_end_to_end_tiled_scales(bq, orc, name):
+    import torch
+    L = wl.make_layer(name)
+    S, N, out = L.cfg.S, L.cfg.N, L.cfg.out
+    print(f"[linear tiled] {name} S={S} N={N} out={out}", flush=True)
+    T = bq.SCALES_MFMA_TILED
+    wq, we = bq.prepare_weight(f32_to_device(L.W), L.A, L.B, layout=T)
+    y = bq.linear_w4a4(bf16_to_device(L.x_bits), f32_to_device(L.A), f32_to_device(L.B),
+                       f32_to_device(bq.clip_ratios(L.alpha_min)),
+                       f32_to_device(bq.clip_ratios(L.alpha_max)), wq, we, layout=T)
+    torch.cuda.synchronize()
+    y = to_host(y)
+    rows = sample_rows(S)
+    rmin, rmax = orc.clip_ratio(L.alpha_min), orc.clip_ratio(L.alpha_max)
+    xq_ref, xe_ref = orc.quantize_act(L.x_bits[rows], L.A, L.B, rmin, rmax,
+                                      nthreads=ORACLE_THREADS)
+    wq_ref, we_ref = orc.prepare_weight(L.W, L.A, L.B, nthreads=ORACLE_THREADS)
+    y_ref, t_ref = orc.gemm(xq_ref, xe_ref, wq_ref, we_ref, nthreads=ORACLE_THREADS)
+    assert_gemm_close(y[rows], y_ref, t_ref, what=f"{name} tiled")

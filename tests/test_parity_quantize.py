@@ -178,3 +178,51 @@ def test_weight_prep_parity(bq, orc, name, rows):
         np.concatenate([[0, out - 1], np.arange(0, out, 61), np.arange(127, out, 128)]))
     wq_ref, we_ref = orc.quantize_weight(L.W[sel], Ai, Bi, nthreads=ORACLE_THREADS)
     assert_codes_equal(wq[sel], we[sel], wq_ref, we_ref, L.W[sel] == 0, what=name)
+
+
+# ----------------------------------------------------------------------------------------
+# MFMA-tiled scale layout
+# ----------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "q_proj", "down_proj", "sweep_s8_n4096"])
+def test_act_parity_tiled_scales(bq, orc, name):
+    import torch
+    from tests.gpu_util import from_tiled_scales
+    L = wl.make_layer(name, with_weight=False)
+    S, N = L.x_bits.shape
+    q, e = bq.quantize_act(bf16_to_device(L.x_bits), f32_to_device(L.A), f32_to_device(L.B),
+                           f32_to_device(bq.clip_ratios(L.alpha_min)),
+                           f32_to_device(bq.clip_ratios(L.alpha_max)),
+                           layout=bq.SCALES_MFMA_TILED)
+    torch.cuda.synchronize()
+    q_ref, e_ref, zero = oracle_act(orc, L)
+    e_rm = from_tiled_scales(to_host(e), S, N // 32)
+    assert_codes_equal(to_host(q), e_rm, q_ref, e_ref, zero, what=f"{name} tiled")
+
+
+def test_act_parity_tiled_scales_ragged(bq, orc):
+    import torch
+    from tests.gpu_util import from_tiled_scales
+    L = wl.make_layer(wl.custom("ragged_t", 37, 4192, 8, seed=31), with_weight=False)
+    S, N = L.x_bits.shape
+    q, e = bq.quantize_act(bf16_to_device(L.x_bits), f32_to_device(L.A), f32_to_device(L.B),
+                           f32_to_device(bq.clip_ratios(L.alpha_min)),
+                           f32_to_device(bq.clip_ratios(L.alpha_max)),
+                           layout=bq.SCALES_MFMA_TILED)
+    torch.cuda.synchronize()
+    q_ref, e_ref, zero = oracle_act(orc, L)
+    assert_codes_equal(to_host(q), from_tiled_scales(to_host(e), S, N // 32), q_ref, e_ref,
+                       zero, what="ragged tiled")
+
+
+@pytest.mark.parametrize("name", ["tiny", "q_proj"])
+def test_weight_prep_parity_tiled_scales(bq, orc, name):
+    import torch
+    from tests.gpu_util import from_tiled_scales
+    L = wl.make_layer(name)
+    wq, we = bq.prepare_weight(f32_to_device(L.W), L.A, L.B, layout=bq.SCALES_MFMA_TILED)
+    torch.cuda.synchronize()
+    wq_ref, we_ref = orc.prepare_weight(L.W, L.A, L.B, nthreads=ORACLE_THREADS)
+    out, N = L.W.shape
+    assert_codes_equal(to_host(wq), from_tiled_scales(to_host(we), out, N // 32), wq_ref,
+                       we_ref, L.W == 0, what=f"{name} weights tiled")

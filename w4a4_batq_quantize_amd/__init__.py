@@ -5,6 +5,8 @@ this package is the thin Python binding over it.
 """
 from ._binding import (  # noqa: F401
     LIB_PATH,
+    SCALES_MFMA_TILED,
+    SCALES_ROW_MAJOR,
     SIGNATURES,
     BatqError,
     clip_ratios,
@@ -16,6 +18,7 @@ from ._binding import (  # noqa: F401
     prepare_weight_raw,
     quantize_act,
     quantize_act_raw,
+    scale_bytes,
     status_string,
     weight_factors,
 )

@@ -20,13 +20,27 @@ STATUS = {0: "BATQ_OK", 1: "BATQ_ERR_NULL", 2: "BATQ_ERR_SHAPE", 3: "BATQ_ERR_AL
 # Every exported entry point and its ctypes signature (the names of include/batq.h).
 _P, _I64, _I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
 SIGNATURES = {
-    "batq_quantize_act": [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P],
-    "batq_prepare_weight": [_P, _I64, _I64, _P, _P, _P, _P, _P],
-    "batq_gemm_w4a4": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P],
+    "batq_quantize_act": [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _I, _P],
+    "batq_prepare_weight": [_P, _I64, _I64, _P, _P, _P, _P, _I, _P],
+    "batq_gemm_w4a4": [_P, _P, _P, _P, _I, _I64, _I64, _I64, _P, _P],
     "batq_clip_ratios": [_P, _I64, _P],
     "batq_weight_factors": [_P, _P, _I64, _P, _P],
     "batq_status_string": [_I],
 }
+
+
+# Scale layouts (batq_scale_layout): row-major [rows, N/32], or the MFMA-tiled order in which
+# the GEMM consumes them (32-row x 8-block units of 256 bytes).
+SCALES_ROW_MAJOR = 0
+SCALES_MFMA_TILED = 1
+
+
+def scale_bytes(rows: int, N: int, layout: int) -> int:
+    """Size in bytes of the scale array of a rows x N MXFP4 tensor in `layout`."""
+    k = N // 32
+    if layout == SCALES_ROW_MAJOR:
+        return rows * k
+    return ((rows + 31) // 32) * 32 * ((k + 7) // 8) * 8
 
 
 class BatqError(RuntimeError):
@@ -67,16 +81,18 @@ def _check(fn: str, status: int) -> None:
 # raw entry points (integer device pointers, integer stream handle)
 # ---------------------------------------------------------------------------------------
 
-def quantize_act_raw(x, S, N, ldx, A, B, r_min, r_max, q, e, stream=0) -> int:
-    return lib().batq_quantize_act(x, S, N, ldx, A, B, r_min, r_max, q, e, stream)
+def quantize_act_raw(x, S, N, ldx, A, B, r_min, r_max, q, e, layout=SCALES_ROW_MAJOR,
+                     stream=0) -> int:
+    return lib().batq_quantize_act(x, S, N, ldx, A, B, r_min, r_max, q, e, layout, stream)
 
 
-def gemm_w4a4_raw(xq, xe, wq, we, S, N, out, y, stream=0) -> int:
-    return lib().batq_gemm_w4a4(xq, xe, wq, we, S, N, out, y, stream)
+def gemm_w4a4_raw(xq, xe, wq, we, S, N, out, y, layout=SCALES_ROW_MAJOR, stream=0) -> int:
+    return lib().batq_gemm_w4a4(xq, xe, wq, we, layout, S, N, out, y, stream)
 
 
-def prepare_weight_raw(W, out, N, A_host, B_host, wq, we, stream=0) -> int:
-    return lib().batq_prepare_weight(W, out, N, A_host, B_host, wq, we, stream)
+def prepare_weight_raw(W, out, N, A_host, B_host, wq, we, layout=SCALES_ROW_MAJOR,
+                       stream=0) -> int:
+    return lib().batq_prepare_weight(W, out, N, A_host, B_host, wq, we, layout, stream)
 
 
 # ---------------------------------------------------------------------------------------
@@ -122,30 +138,38 @@ def _ptr(t) -> int:
     return t.data_ptr()
 
 
-def quantize_act(x, A, B, r_min, r_max, q=None, e=None, stream=None):
+def _scale_tensor(rows, N, layout, device):
+    import torch
+    if layout == SCALES_ROW_MAJOR:
+        return torch.empty((rows, N // 32), dtype=torch.uint8, device=device)
+    return torch.empty((scale_bytes(rows, N, layout),), dtype=torch.uint8, device=device)
+
+
+def quantize_act(x, A, B, r_min, r_max, q=None, e=None, layout=SCALES_ROW_MAJOR, stream=None):
     """Fused transform + clip + MXFP4 of bf16 activations x [S, N] (row stride may exceed
     N).  A fp32 [8,8], B fp32 [k,4,4], r_min/r_max fp32 [k] (device).  Returns the codes
-    uint8 [S, N/2] and scales uint8 [S, N/32]."""
+    uint8 [S, N/2] and the scales: uint8 [S, N/32] row-major, or a flat uint8 buffer in the
+    MFMA-tiled layout."""
     import torch
     assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
     S, N = x.shape
-    k = N // 32
     if q is None:
         q = torch.empty((S, N // 2), dtype=torch.uint8, device=x.device)
     if e is None:
-        e = torch.empty((S, k), dtype=torch.uint8, device=x.device)
+        e = _scale_tensor(S, N, layout, x.device)
     for t, dt in ((A, torch.float32), (B, torch.float32), (r_min, torch.float32),
                   (r_max, torch.float32)):
         assert t.dtype == dt and t.is_contiguous()
     _check("batq_quantize_act", quantize_act_raw(
         _ptr(x), S, N, x.stride(0), _ptr(A), _ptr(B), _ptr(r_min), _ptr(r_max), _ptr(q),
-        _ptr(e), _stream(stream)))
+        _ptr(e), layout, _stream(stream)))
     return q, e
 
 
-def prepare_weight(W, A_host, B_host, stream=None):
+def prepare_weight(W, A_host, B_host, layout=SCALES_ROW_MAJOR, stream=None):
     """Offline: fp32 weights W [out, N] (device) -> MXFP4 codes [out, N/2] and scales of
-    W P^-T.  A_host [8,8] and B_host [k,4,4] are host arrays; synchronises the stream."""
+    W P^-T (in `layout`).  A_host [8,8] and B_host [k,4,4] are host arrays; synchronises
+    the stream."""
     import torch
     assert W.dtype == torch.float32 and W.is_contiguous() and W.dim() == 2
     out, N = W.shape
@@ -153,28 +177,31 @@ def prepare_weight(W, A_host, B_host, stream=None):
     B = _host_f32(B_host)
     assert A.size == 64 and B.size == 16 * (N // 32)
     wq = torch.empty((out, N // 2), dtype=torch.uint8, device=W.device)
-    we = torch.empty((out, N // 32), dtype=torch.uint8, device=W.device)
+    we = _scale_tensor(out, N, layout, W.device)
     _check("batq_prepare_weight", prepare_weight_raw(
-        _ptr(W), out, N, A.ctypes.data, B.ctypes.data, _ptr(wq), _ptr(we), _stream(stream)))
+        _ptr(W), out, N, A.ctypes.data, B.ctypes.data, _ptr(wq), _ptr(we), layout,
+        _stream(stream)))
     return wq, we
 
 
-def gemm_w4a4(xq, xe, wq, we, y=None, stream=None):
-    """fp32 y [S, out] = dq(xq, xe) dq(wq, we)^T on scaled MFMA."""
+def gemm_w4a4(xq, xe, wq, we, y=None, layout=SCALES_ROW_MAJOR, stream=None):
+    """fp32 y [S, out] = dq(xq, xe) dq(wq, we)^T on scaled MFMA; xe and we in `layout`."""
     import torch
     S, N = xq.shape[0], xq.shape[1] * 2
     out = wq.shape[0]
     for t in (xq, xe, wq, we):
         assert t.dtype == torch.uint8 and t.is_contiguous()
-    assert wq.shape[1] * 2 == N and xe.shape == (S, N // 32) and we.shape == (out, N // 32)
+    assert wq.shape[1] * 2 == N
+    assert xe.numel() == scale_bytes(S, N, layout) and we.numel() == scale_bytes(out, N, layout)
     if y is None:
         y = torch.empty((S, out), dtype=torch.float32, device=xq.device)
     _check("batq_gemm_w4a4", gemm_w4a4_raw(_ptr(xq), _ptr(xe), _ptr(wq), _ptr(we), S, N, out,
-                                           _ptr(y), _stream(stream)))
+                                           _ptr(y), layout, _stream(stream)))
     return y
 
 
-def linear_w4a4(x, A, B, r_min, r_max, wq, we, stream=None):
-    """One pass of the online path: quantise the activations, then the W4A4 GEMM."""
-    xq, xe = quantize_act(x, A, B, r_min, r_max, stream=stream)
-    return gemm_w4a4(xq, xe, wq, we, stream=stream)
+def linear_w4a4(x, A, B, r_min, r_max, wq, we, layout=SCALES_ROW_MAJOR, stream=None):
+    """One pass of the online path: quantise the activations, then the W4A4 GEMM (the
+    prepared weight scales `we` must be in `layout`)."""
+    xq, xe = quantize_act(x, A, B, r_min, r_max, layout=layout, stream=stream)
+    return gemm_w4a4(xq, xe, wq, we, layout=layout, stream=stream)

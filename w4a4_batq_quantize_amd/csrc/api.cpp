@@ -55,6 +55,11 @@ bool inverse_transposed(const float* M, int n, float* out_t)
     return true;
 }
 
+bool valid_layout(batq_scale_layout l)
+{
+    return l == BATQ_SCALES_ROW_MAJOR || l == BATQ_SCALES_MFMA_TILED;
+}
+
 bool mul_overflows(int64_t a, int64_t b)
 {
     return a != 0 && b > std::numeric_limits<int64_t>::max() / a;
@@ -100,11 +105,12 @@ BATQ_API batq_status batq_weight_factors(const float* A, const float* B, int64_t
 BATQ_API batq_status batq_quantize_act(const uint16_t* x, int64_t S, int64_t N, int64_t ldx,
                                        const float* A, const float* B, const float* r_min,
                                        const float* r_max, uint8_t* q, uint8_t* e,
-                                       void* stream)
+                                       batq_scale_layout e_layout, void* stream)
 {
     if (S < 0 || N < 0 || N % 32 != 0) return BATQ_ERR_SHAPE;
     if (S == 0 || N == 0) return BATQ_OK;
     if (!x || !A || !B || !r_min || !r_max || !q || !e) return BATQ_ERR_NULL;
+    if (!valid_layout(e_layout)) return BATQ_ERR_UNSUPPORTED;
     if (ldx < N || mul_overflows(S, ldx)) return BATQ_ERR_SHAPE;
     if (ldx % 8 != 0 || !aligned(x, 16) || !aligned(B, 16) || !aligned(q, 16) ||
         !aligned(A, 4) || !aligned(r_min, 4) || !aligned(r_max, 4))
@@ -112,16 +118,19 @@ BATQ_API batq_status batq_quantize_act(const uint16_t* x, int64_t S, int64_t N, 
     const int64_t k = N / 32;
     if (k > 64LL * 65535) return BATQ_ERR_UNSUPPORTED;
     return from_hip(batq::launch_quantize(true, x, S, k, ldx, A, B, r_min, r_max, q, e,
+                                          e_layout == BATQ_SCALES_MFMA_TILED,
                                           as_stream(stream)));
 }
 
 BATQ_API batq_status batq_prepare_weight(const float* W, int64_t out, int64_t N,
                                          const float* A_host, const float* B_host,
-                                         uint8_t* wq, uint8_t* we, void* stream)
+                                         uint8_t* wq, uint8_t* we,
+                                         batq_scale_layout we_layout, void* stream)
 {
     if (out < 0 || N < 0 || N % 32 != 0) return BATQ_ERR_SHAPE;
     if (out == 0 || N == 0) return BATQ_OK;
     if (!W || !A_host || !B_host || !wq || !we) return BATQ_ERR_NULL;
+    if (!valid_layout(we_layout)) return BATQ_ERR_UNSUPPORTED;
     if (mul_overflows(out, N)) return BATQ_ERR_SHAPE;
     if (!aligned(W, 16) || !aligned(wq, 16)) return BATQ_ERR_ALIGN;
     const int64_t k = N / 32;
@@ -138,7 +147,8 @@ BATQ_API batq_status batq_prepare_weight(const float* W, int64_t out, int64_t N,
     hipError_t err = hipMemcpyAsync(d, factors.data(), factors.size() * sizeof(float),
                                     hipMemcpyHostToDevice, s);
     if (err == hipSuccess)
-        err = batq::launch_quantize(false, W, out, k, N, d, d + 64, nullptr, nullptr, wq, we, s);
+        err = batq::launch_quantize(false, W, out, k, N, d, d + 64, nullptr, nullptr, wq, we,
+                                    we_layout == BATQ_SCALES_MFMA_TILED, s);
     const hipError_t sync = hipStreamSynchronize(s);
     const hipError_t fr = hipFree(d);
     if (err != hipSuccess || sync != hipSuccess || fr != hipSuccess) return BATQ_ERR_HIP;
@@ -146,14 +156,16 @@ BATQ_API batq_status batq_prepare_weight(const float* W, int64_t out, int64_t N,
 }
 
 BATQ_API batq_status batq_gemm_w4a4(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq,
-                                    const uint8_t* we, int64_t S, int64_t N, int64_t out,
-                                    float* y, void* stream)
+                                    const uint8_t* we, batq_scale_layout layout, int64_t S,
+                                    int64_t N, int64_t out, float* y, void* stream)
 {
     if (S < 0 || N < 0 || out < 0 || N % 32 != 0) return BATQ_ERR_SHAPE;
     if (S == 0 || out == 0) return BATQ_OK;
     if (!y || (N > 0 && (!xq || !xe || !wq || !we))) return BATQ_ERR_NULL;
+    if (!valid_layout(layout)) return BATQ_ERR_UNSUPPORTED;
     if (mul_overflows(S, out) || mul_overflows(S, N) || mul_overflows(out, N))
         return BATQ_ERR_SHAPE;
     if (!aligned(y, 16) || !aligned(xq, 16) || !aligned(wq, 16)) return BATQ_ERR_ALIGN;
-    return from_hip(batq::launch_gemm(xq, xe, wq, we, S, N, out, y, as_stream(stream)));
+    return from_hip(batq::launch_gemm(xq, xe, wq, we, layout == BATQ_SCALES_MFMA_TILED, S, N,
+                                      out, y, as_stream(stream)));
 }

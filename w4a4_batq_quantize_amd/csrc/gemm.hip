@@ -1,23 +1,23 @@
 // MXFP4 x MXFP4 -> fp32 GEMM on gfx950 scaled MFMA (the W4A4 linear layer).
 //
 // y[s][o] = sum_n dq(x)[s][n] dq(w)[o][n] with dq = e2m1(code) * 2^(e-127) per 32-element
-// block.  The contraction runs on V_MFMA_SCALE_F32_16X16X128_F8F6F4 with both operands in
-// E2M1 (format code 4): one instruction multiplies a 16x128 by a 128x16 tile, every lane
-// supplying 32 consecutive K values (16 bytes) of one row and the E8M0 scale of exactly
-// that 32-element block, so MX blocks map onto lanes one to one and the scales are applied
-// inside the instruction.  Lane l holds row l%16 and K block l/16; the 16x16 fp32 result
-// gives lane l the column l%16 and rows 4(l/16)..4(l/16)+3.
+// block.  The contraction runs on the scaled MFMA instructions with both operands in E2M1
+// (format code 4): each lane supplies 32 consecutive K values (16 bytes) of one row together
+// with the E8M0 scale of exactly that 32-element block, so MX blocks map onto lanes one to
+// one and the block scales are applied inside the instruction.
 //
-// The MFMA "row" operand is the weight tile (out dimension) and the "column" operand is the
-// activation tile (token dimension), so each lane's four accumulator values are four
+// The MFMA row operand is the weight tile (out dimension) and the column operand the
+// activation tile (token dimension), so every group of four accumulator registers is four
 // consecutive output features of one token: one 16-byte store into row-major y.
 //
-// Work decomposition: a 256-thread workgroup (4 waves, 2 x 2) owns a BO x BS output tile;
-// each wave owns (BO/2) x (BS/2).  The K loop advances 128 elements (64 code bytes and 4
-// scale bytes per row) per step; the next step's tiles are fetched into registers while the
-// current step is multiplied out of LDS (two LDS stages, one barrier per step).  Rows past
-// the end of the matrices and K blocks past N/32 are filled with zero codes, which add
-// nothing whatever the scale.
+// Two kernels:
+//  - gemm_dma_kernel, for N % 256 == 0 with 8-byte-aligned scale arrays (all the layer
+//    shapes of interest): V_MFMA_SCALE_F32_32X32X64_F8F6F4 (on gfx950 the FP4 32x32x64
+//    form runs at twice the rate of the FP4 16x16x128 form, measured), operands moved
+//    HBM/L2 -> LDS by global_load_lds_dwordx4 without passing through registers, three LDS
+//    stages in flight;
+//  - gemm_generic_kernel for any other N (ragged K) or alignment: the 16x16x128 form with
+//    register-staged, bounds-checked loads.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -28,174 +28,528 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void gbl_void_t;
 
 constexpr int kThreads = 256;
-constexpr int kCodeBytes = 64;          // code bytes per row per K step (128 elements)
-constexpr int kPitch = kCodeBytes + 16; // LDS row pitch; the 16-byte pad spreads rows over banks
 constexpr int kFmtE2M1 = 4;
+constexpr int kXcds = 8;
 
-template <int BO, int BS>
-struct Smem {
-    uint8_t w[2][BO][kPitch];
-    uint8_t x[2][BS][kPitch];
-    uint8_t ws[2][BO][4];
-    uint8_t xs[2][BS][4];
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8])
+constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
+
+// Workgroup barrier without the memory fence __syncthreads() adds (which would wait for the
+// LDS DMA of the stages still in flight).  The asm statement orders all memory accesses at
+// compiler level; the hardware-level completion of this wave's LDS reads and of the DMA it
+// needs is established by the explicit s_waitcnt placed before it.
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
+// Tile numbering: when the tile count divides evenly, each XCD (own L2) receives a
+// contiguous run of tiles; within the run, groups of `group_o` weight tiles are swept
+// across the activation tiles so neighbouring workgroups share operands.
+__device__ __forceinline__ void tile_origin(int64_t tiles_o, int64_t tiles_s, int64_t group_o,
+                                           int64_t BO, int64_t BS, int64_t& o0, int64_t& s0)
+{
+    const int64_t total = tiles_o * tiles_s;
+    int64_t id = blockIdx.x;
+    if (total % kXcds == 0) id = (id % kXcds) * (total / kXcds) + id / kXcds;
+    const int64_t span = group_o * tiles_s;
+    const int64_t first_o = (id / span) * group_o;
+    const int64_t gsize = tiles_o - first_o < group_o ? tiles_o - first_o : group_o;
+    const int64_t rem = id % span;
+    o0 = (first_o + rem % gsize) * BO;
+    s0 = (rem / gsize) * BS;
+}
+
+// =======================================================================================
+// gemm_dma_kernel<Cfg>: BO (out) x BS (tokens) tile per workgroup
+// =======================================================================================
+//
+// Waves are arranged WO x WS; each owns (BO/WO) x (BS/WS) outputs = TM x TN MFMA tiles of
+// 32 x 32.  A K stage is 256 elements: per tile row 128 code bytes and 8 scale bytes.  LDS
+// stage layout: rows [0, BO) weight rows, [BO, BO+BS) activation rows, 128 bytes each,
+// followed by (BO+BS) x 8 scale bytes.  Within a row the 16-byte chunk c is stored at
+// position c ^ (row % 8): the DMA writes 64 lanes x 16 bytes contiguously, so the layout
+// cannot be padded, and the XOR spreads the 32-row reads of one MFMA operand over all
+// banks.  NB stages are in flight (prefetch distance NB-1).
+//
+// The 32x32x64 operand layout: lane l holds row l%32 and K block l/32 of the K-step, the
+// result gives lane l column l%32 and rows 8(r/4) + 4(l/32) + r%4 for register r.
+
+constexpr int kStageBlocks = 8;
+constexpr int kRowBytes = 16 * kStageBlocks;   // 128
+
+template <int BO_, int BS_, int WO_, int WS_, int NB_, bool TS_, int SB_ = 4>
+struct DmaCfg {
+    static constexpr int BO = BO_, BS = BS_, WO = WO_, WS = WS_, NB = NB_;
+    static constexpr bool TS = TS_;   // scales in the MFMA-tiled layout (else row-major)
+    static constexpr int SB = TS_ ? 4 : SB_;                        // scale DMA bytes per lane
+    static constexpr int kWaves = WO * WS;
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int TM = BO / WO / 32, TN = BS / WS / 32;
+    static constexpr int kRows = BO + BS;
+    static constexpr int kCodeBytes = kRows * kRowBytes;
+    static constexpr int kScaleBytes = kRows * kStageBlocks;
+    static constexpr int kBufBytes = kCodeBytes + kScaleBytes;
+    static constexpr int kCodeDma = kCodeBytes / 1024 / kWaves;     // 1 KB instructions / wave
+    // tiled: one 256-byte unit per 32-row panel per stage; row-major: 8 bytes per row
+    static constexpr int kScaleDma = kScaleBytes / (64 * SB) / kWaves;  // per wave
+    static constexpr int kDmaPerStage = kCodeDma + kScaleDma;
+    static_assert(TM >= 1 && TN >= 1 && BO % (WO * 32) == 0 && BS % (WS * 32) == 0, "tiles");
+    static_assert(kCodeBytes % (1024 * kWaves) == 0, "code DMA split");
+    static_assert((SB == 4 || SB == 2) && kScaleBytes % (64 * SB * kWaves) == 0, "scale DMA");
+    static_assert(BO % 8 == 0 && BO % 32 == 0, "weight rows fill whole DMA instructions");
+    static_assert(NB >= 2 && NB * kBufBytes <= 160 * 1024, "LDS");
+    static_assert(kDmaPerStage * (NB - 1) <= 63, "vmcnt range");
 };
 
-// Per-thread staging registers of one K step.
-template <int BO, int BS>
-struct Stage {
-    static constexpr int kChunks = (BO + BS) * 4;              // 16-byte code chunks
-    static constexpr int kPerThread = kChunks / kThreads;
-    uint4 code[kPerThread];
-    uint32_t scale;                                           // 4 scale bytes of one row
+struct DmaArgs {
+    const uint8_t* xq;
+    const uint8_t* xe;
+    const uint8_t* wq;
+    const uint8_t* we;
+    int64_t S, k, out;
 };
 
-template <int BO, int BS>
-__device__ __forceinline__ void load_stage(Stage<BO, BS>& st, const uint8_t* __restrict__ xq,
-                                           const uint8_t* __restrict__ xe,
-                                           const uint8_t* __restrict__ wq,
-                                           const uint8_t* __restrict__ we, int64_t S,
-                                           int64_t out, int64_t k, int64_t o0, int64_t s0,
-                                           int64_t kt)
+// Per-lane source offsets of this wave's DMA instructions for the tile (stage 0); the
+// stage offset is uniform and added to the base.  Rows past the end are clamped to the
+// last row: their products land in outputs that are never stored.
+template <class C>
+struct DmaPlan {
+    uint32_t code_off[C::kCodeDma];
+    uint32_t scale_off[C::kScaleDma];
+};
+
+template <class C>
+__device__ __forceinline__ void dma_plan(DmaPlan<C>& pl, const DmaArgs& p, int64_t o0,
+                                         int64_t s0, int wave, int lane)
+{
+    const int64_t rowbytes = 16 * p.k;
+#pragma unroll
+    for (int i = 0; i < C::kCodeDma; ++i) {
+        const int inst = wave * C::kCodeDma + i;
+        const int r = inst * 8 + (lane >> 3);              // tile row of this lane
+        const int c = (lane & 7) ^ (lane >> 3);           // global chunk for LDS slot lane&7
+        int64_t row = r < C::BO ? o0 + r : s0 + (r - C::BO);
+        const int64_t last = (r < C::BO ? p.out : p.S) - 1;
+        row = row < last ? row : last;
+        pl.code_off[i] = (uint32_t)(row * rowbytes + 16 * c);
+    }
+    if constexpr (C::TS) {
+        // the unit of panel P at stage ks starts at (P*k/8 + ks)*256; lanes take 4 bytes each
+#pragma unroll
+        for (int j = 0; j < C::kScaleDma; ++j) {
+            const int inst = wave * C::kScaleDma + j;         // panel within the tile
+            const int r = inst * 32;
+            int64_t row = r < C::BO ? o0 + r : s0 + (r - C::BO);
+            const int64_t last = (r < C::BO ? p.out : p.S) - 1;
+            row = row < last ? row : last;
+            pl.scale_off[j] = (uint32_t)((row >> 5) * (p.k >> 3) * 256 + 4 * lane);
+        }
+        return;
+    }
+#pragma unroll
+    for (int j = 0; j < C::kScaleDma; ++j) {
+        constexpr int kLanesPerRow = kStageBlocks / C::SB;
+        const int inst = wave * C::kScaleDma + j;
+        const int r = inst * (64 / kLanesPerRow) + lane / kLanesPerRow;
+        int64_t row = r < C::BO ? o0 + r : s0 + (r - C::BO);
+        const int64_t last = (r < C::BO ? p.out : p.S) - 1;
+        row = row < last ? row : last;
+        pl.scale_off[j] = (uint32_t)(row * p.k + C::SB * (lane % kLanesPerRow));
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void dma_stage(uint8_t* buf, const DmaPlan<C>& pl, const DmaArgs& p,
+                                          int64_t ks, int wave)
+{
+#pragma unroll
+    for (int i = 0; i < C::kCodeDma; ++i) {
+        const int inst = wave * C::kCodeDma + i;
+        const uint8_t* base = (inst * 8 < C::BO ? p.wq : p.xq) + ks * kRowBytes;
+        __builtin_amdgcn_global_load_lds((gbl_void_t*)(base + pl.code_off[i]),
+                                         (lds_void_t*)(buf + inst * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < C::kScaleDma; ++j) {
+        constexpr int kRowsPerInst = C::TS ? 32 : 64 * C::SB / kStageBlocks;
+        const int inst = wave * C::kScaleDma + j;
+        const uint8_t* base = (inst * kRowsPerInst < C::BO ? p.we : p.xe) +
+                              ks * (C::TS ? 256 : kStageBlocks);
+        __builtin_amdgcn_global_load_lds((gbl_void_t*)(base + pl.scale_off[j]),
+                                         (lds_void_t*)(buf + C::kCodeBytes + inst * 64 * C::SB),
+                                         C::SB, 0, 0);
+    }
+}
+
+// Operand fragments of one K-step T (64 elements) out of an LDS stage, 16 bytes per lane
+// per 32-row MFMA operand.
+template <int TM, int TN>
+struct Frags {
+    uint4 a[TM];
+    uint4 b[TN];
+};
+
+template <class C, int T>
+__device__ __forceinline__ void dma_load_frags(Frags<C::TM, C::TN>& f, const uint8_t* buf,
+                                               uint32_t wrow_off, uint32_t xrow_off, int lg,
+                                               int lr7)
+{
+    const uint32_t pos = 16u * (uint32_t)((2 * T + lg) ^ lr7);
+#pragma unroll
+    for (int a = 0; a < C::TM; ++a)
+        f.a[a] = *reinterpret_cast<const uint4*>(buf + wrow_off + pos + 32 * kRowBytes * a);
+#pragma unroll
+    for (int b = 0; b < C::TN; ++b)
+        f.b[b] = *reinterpret_cast<const uint4*>(buf + xrow_off + pos + 32 * kRowBytes * b);
+}
+
+template <class C, int T>
+__device__ __forceinline__ void dma_mfma_frags(v16f (&acc)[C::TM][C::TN],
+                                               const Frags<C::TM, C::TN>& f,
+                                               const uint32_t (&wsc)[2][C::TM],
+                                               const uint32_t (&xsc)[2][C::TN])
+{
+    // tiled scales: byte T of the one dword; row-major: byte 2*(T%2) of word T/2
+    constexpr int kSel = C::TS ? T : 2 * (T & 1);
+    constexpr int kWord = C::TS ? 0 : T >> 1;
+#pragma unroll
+    for (int a = 0; a < C::TM; ++a) {
+        const v8i av = {(int)f.a[a].x, (int)f.a[a].y, (int)f.a[a].z, (int)f.a[a].w, 0, 0, 0, 0};
+#pragma unroll
+        for (int b = 0; b < C::TN; ++b) {
+            const v8i bv = {(int)f.b[b].x, (int)f.b[b].y, (int)f.b[b].z, (int)f.b[b].w, 0, 0, 0, 0};
+            acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                av, bv, acc[a][b], kFmtE2M1, kFmtE2M1, kSel, (int)wsc[kWord][a], kSel,
+                (int)xsc[kWord][b]);
+        }
+    }
+}
+
+// The four K-steps of a stage, software-pipelined: the fragments of step T+1 are requested
+// from LDS before the MFMAs of step T are issued (scheduling fences keep that order), so the
+// LDS latency hides behind the matrix-core work of the previous step.
+template <class C>
+__device__ __forceinline__ void dma_mfma_stage(v16f (&acc)[C::TM][C::TN], const uint8_t* buf,
+                                               int wrow0, int xrow0, int lane)
+{
+    const int lr = lane & 31, lg = lane >> 5, lr7 = lane & 7;
+    const uint32_t wrow_off = (uint32_t)(wrow0 + lr) * kRowBytes;
+    const uint32_t xrow_off = (uint32_t)(C::BO + xrow0 + lr) * kRowBytes;
+    uint32_t wsc[2][C::TM], xsc[2][C::TN];
+    Frags<C::TM, C::TN> f0, f1;
+    if constexpr (C::TS) {
+        // tiled: lane (row, l/32) finds the blocks 2T + l/32 of its row as bytes T of one
+        // dword (the row's 8 bytes are read whole, which keeps these reads distinguishable
+        // from the stage DMA still in flight); both words alias it
+#pragma unroll
+        for (int a = 0; a < C::TM; ++a) {
+            const uint2 v = *reinterpret_cast<const uint2*>(
+                buf + C::kCodeBytes + (wrow0 / 32 + a) * 256 + lr * 8);
+            wsc[0][a] = wsc[1][a] = lg ? v.y : v.x;
+        }
+#pragma unroll
+        for (int b = 0; b < C::TN; ++b) {
+            const uint2 v = *reinterpret_cast<const uint2*>(
+                buf + C::kCodeBytes + ((C::BO + xrow0) / 32 + b) * 256 + lr * 8);
+            xsc[0][b] = xsc[1][b] = lg ? v.y : v.x;
+        }
+        dma_load_frags<C, 0>(f0, buf, wrow_off, xrow_off, lg, lr7);
+        dma_load_frags<C, 1>(f1, buf, wrow_off, xrow_off, lg, lr7);
+    } else {
+        // row-major: the stage's 8 scale bytes of each operand row, pre-shifted so that the
+        // byte select 2*(T%2) picks block 2T + lane/32 from the low (T < 2) or high word
+        uint2 wv[C::TM], xv[C::TN];
+#pragma unroll
+        for (int a = 0; a < C::TM; ++a)
+            wv[a] = *reinterpret_cast<const uint2*>(buf + C::kCodeBytes +
+                                                    (wrow0 + 32 * a + lr) * kStageBlocks);
+#pragma unroll
+        for (int b = 0; b < C::TN; ++b)
+            xv[b] = *reinterpret_cast<const uint2*>(buf + C::kCodeBytes +
+                                                    (C::BO + xrow0 + 32 * b + lr) * kStageBlocks);
+        dma_load_frags<C, 0>(f0, buf, wrow_off, xrow_off, lg, lr7);
+        dma_load_frags<C, 1>(f1, buf, wrow_off, xrow_off, lg, lr7);
+#pragma unroll
+        for (int a = 0; a < C::TM; ++a) {
+            wsc[0][a] = wv[a].x >> (8 * lg);
+            wsc[1][a] = wv[a].y >> (8 * lg);
+        }
+#pragma unroll
+        for (int b = 0; b < C::TN; ++b) {
+            xsc[0][b] = xv[b].x >> (8 * lg);
+            xsc[1][b] = xv[b].y >> (8 * lg);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    dma_mfma_frags<C, 0>(acc, f0, wsc, xsc);
+    __builtin_amdgcn_sched_barrier(0);
+    dma_load_frags<C, 2>(f0, buf, wrow_off, xrow_off, lg, lr7);
+    __builtin_amdgcn_sched_barrier(0);
+    dma_mfma_frags<C, 1>(acc, f1, wsc, xsc);
+    __builtin_amdgcn_sched_barrier(0);
+    dma_load_frags<C, 3>(f1, buf, wrow_off, xrow_off, lg, lr7);
+    __builtin_amdgcn_sched_barrier(0);
+    dma_mfma_frags<C, 2>(acc, f0, wsc, xsc);
+    __builtin_amdgcn_sched_barrier(0);
+    dma_mfma_frags<C, 3>(acc, f1, wsc, xsc);
+}
+
+// One pipeline step: once at most the DMA instructions of the NB-2 following stages are
+// still in flight for this wave, this wave's part of stage s is in `cur`; after the barrier
+// all of it is, and every wave has finished reading `nxt` (stage s-1).  Stage s+NB-1 is then
+// fetched into `nxt` (the final stage again once the end is reached, so the body has no
+// branch and the wait count is constant) and stage s is multiplied out of `cur`.
+template <class C>
+__device__ __forceinline__ void dma_pipeline_step(v16f (&acc)[C::TM][C::TN], uint8_t* cur,
+                                                  uint8_t* nxt, const DmaPlan<C>& pl,
+                                                  const DmaArgs& p, int64_t s, int64_t nst,
+                                                  int wave, int wrow0, int xrow0, int lane)
+{
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(C::kDmaPerStage * (C::NB - 2), 0));
+    barrier_only();
+    const int64_t ahead = s + C::NB - 1;
+    dma_stage<C>(nxt, pl, p, ahead < nst ? ahead : nst - 1, wave);
+    dma_mfma_stage<C>(acc, cur, wrow0, xrow0, lane);
+}
+
+template <class C>
+__global__ void __launch_bounds__(C::kThreads)
+gemm_dma_kernel(DmaArgs p, float* __restrict__ y, int64_t tiles_o, int64_t tiles_s)
+{
+    constexpr int NB = C::NB;
+    __shared__ __attribute__((aligned(16))) uint8_t lds0[C::kBufBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t lds1[C::kBufBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t lds2[NB > 2 ? C::kBufBytes : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t lds3[NB > 3 ? C::kBufBytes : 16];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wrow0 = (wave / C::WS) * (C::BO / C::WO);
+    const int xrow0 = (wave % C::WS) * (C::BS / C::WS);
+    int64_t o0, s0;
+    tile_origin(tiles_o, tiles_s, 4, C::BO, C::BS, o0, s0);
+
+    v16f acc[C::TM][C::TN];
+#pragma unroll
+    for (int a = 0; a < C::TM; ++a)
+#pragma unroll
+        for (int b = 0; b < C::TN; ++b) acc[a][b] = v16f{};
+
+    const int64_t nst = p.k / kStageBlocks;
+    if (nst > 0) {
+        DmaPlan<C> pl;
+        dma_plan<C>(pl, p, o0, s0, wave, lane);
+        uint8_t* bufs[4] = {lds0, lds1, lds2, lds3};
+#pragma unroll
+        for (int i = 0; i < NB - 1; ++i) dma_stage<C>(bufs[i], pl, p, i < nst ? i : nst - 1, wave);
+        // whole rounds of NB stages (buffers rotate), then the remainder
+        const int64_t nfull = nst - nst % NB;
+        int64_t s = 0;
+        for (; s < nfull; s += NB) {
+#pragma unroll
+            for (int i = 0; i < NB; ++i)
+                dma_pipeline_step<C>(acc, bufs[i], bufs[(i + NB - 1) % NB], pl, p, s + i, nst,
+                                     wave, wrow0, xrow0, lane);
+        }
+#pragma unroll
+        for (int i = 0; i < NB - 1; ++i)
+            if (s + i < nst)
+                dma_pipeline_step<C>(acc, bufs[i], bufs[(i + NB - 1) % NB], pl, p, s + i, nst,
+                                     wave, wrow0, xrow0, lane);
+        // the trailing prefetches must land before the workgroup's LDS is released
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    }
+
+    const int lr = lane & 31, lg = lane >> 5;
+    const bool vec_ok = (p.out & 3) == 0;
+#pragma unroll
+    for (int b = 0; b < C::TN; ++b) {
+        const int64_t s = s0 + xrow0 + 32 * b + lr;
+        if (s >= p.S) continue;
+#pragma unroll
+        for (int a = 0; a < C::TM; ++a) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int64_t o = o0 + wrow0 + 32 * a + 8 * g + 4 * lg;
+                float* dst = y + s * p.out + o;
+                const float v0 = acc[a][b][4 * g], v1 = acc[a][b][4 * g + 1];
+                const float v2 = acc[a][b][4 * g + 2], v3 = acc[a][b][4 * g + 3];
+                if (vec_ok && o + 3 < p.out) {
+                    *reinterpret_cast<float4*>(dst) = make_float4(v0, v1, v2, v3);
+                } else {
+                    if (o < p.out) dst[0] = v0;
+                    if (o + 1 < p.out) dst[1] = v1;
+                    if (o + 2 < p.out) dst[2] = v2;
+                    if (o + 3 < p.out) dst[3] = v3;
+                }
+            }
+            // one 32x32 tile at a time: keeps the accumulator-to-VGPR copies short-lived
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+using CfgQ = DmaCfg<256, 128, 2, 2, 3, false>;    // 256 tiles for a 2048 x 4096 output
+using CfgQT = DmaCfg<256, 128, 2, 2, 3, true>;
+
+// =======================================================================================
+// gemm_generic_kernel: any N % 32 == 0, any alignment of the scale arrays
+// =======================================================================================
+//
+// V_MFMA_SCALE_F32_16X16X128_F8F6F4: lane l holds row l%16, K block l/16; the 16x16
+// result gives lane l column l%16 and rows 4(l/16)..4(l/16)+3.  128 x 128 tile, 2 x 2
+// waves, K step of 128 elements (4 blocks) staged through padded LDS rows; the next step is
+// fetched into registers (kept unpacked until they are written to LDS, so nothing waits on
+// them early) while the current one is multiplied.  Rows past the end and K blocks past
+// N/32 are zero codes, which contribute nothing whatever their scale.
+
+constexpr int kGBO = 128, kGBS = 128;
+constexpr int kGPitch = 64 + 16;
+
+struct GenericSmem {
+    uint8_t w[2][kGBO][kGPitch];
+    uint8_t x[2][kGBS][kGPitch];
+    uint8_t ws[2][kGBO][4];
+    uint8_t xs[2][kGBS][4];
+};
+
+struct GenericStage {
+    uint4 code[(kGBO + kGBS) * 4 / kThreads];
+    uint32_t scale[4];
+};
+
+// Byte offset of scale (row, blk) in either layout.
+__device__ __forceinline__ int64_t scale_index(int64_t row, int64_t blk, int64_t k, int tiled)
+{
+    return tiled ? (((row >> 5) * ((k + 7) >> 3) + (blk >> 3)) << 8) + ((row & 31) << 3) +
+                       ((blk & 1) << 2) + ((blk & 7) >> 1)
+                 : row * k + blk;
+}
+
+__device__ __forceinline__ void generic_load(GenericStage& st, const DmaArgs& p, int tiled,
+                                             int64_t o0, int64_t s0, int64_t kt)
 {
     const int tid = threadIdx.x;
-    const int64_t rowbytes = 16 * k;
+    const int64_t rowbytes = 16 * p.k;
 #pragma unroll
-    for (int j = 0; j < Stage<BO, BS>::kPerThread; ++j) {
+    for (int j = 0; j < (kGBO + kGBS) * 4 / kThreads; ++j) {
         const int c = tid + kThreads * j;
         const int r = c >> 2, part = c & 3;
         const int64_t blk = 4 * kt + part;
         uint4 v = make_uint4(0, 0, 0, 0);
-        if (r < BO) {
+        if (r < kGBO) {
             const int64_t o = o0 + r;
-            if (o < out && blk < k)
-                v = *reinterpret_cast<const uint4*>(wq + o * rowbytes + 16 * blk);
+            if (o < p.out && blk < p.k)
+                v = *reinterpret_cast<const uint4*>(p.wq + o * rowbytes + 16 * blk);
         } else {
-            const int64_t s = s0 + (r - BO);
-            if (s < S && blk < k)
-                v = *reinterpret_cast<const uint4*>(xq + s * rowbytes + 16 * blk);
+            const int64_t s = s0 + (r - kGBO);
+            if (s < p.S && blk < p.k)
+                v = *reinterpret_cast<const uint4*>(p.xq + s * rowbytes + 16 * blk);
         }
         st.code[j] = v;
     }
-    // scale bytes: threads [0, BO) take weight rows, [BO, BO + BS) activation rows
-    uint32_t sc = 0x7F7F7F7Fu;
-    if (tid < BO + BS) {
-        const bool isw = tid < BO;
-        const int64_t row = isw ? o0 + tid : s0 + (tid - BO);
-        const bool ok = isw ? row < out : row < S;
-        const uint8_t* src = (isw ? we : xe) + row * k;
-        if (ok) {
-            sc = 0;
+    const bool isw = tid < kGBO;
+    const int64_t row = isw ? o0 + tid : s0 + (tid - kGBO);
+    const bool ok = isw ? row < p.out : row < p.S;
+    const uint8_t* src = isw ? p.we : p.xe;
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const int64_t blk = 4 * kt + b;
-                const uint32_t v = blk < k ? src[blk] : 0x7Fu;
-                sc |= v << (8 * b);
-            }
-        }
+    for (int b = 0; b < 4; ++b) {
+        const int64_t blk = 4 * kt + b;
+        st.scale[b] = (ok && blk < p.k) ? src[scale_index(row, blk, p.k, tiled)] : 0x7Fu;
     }
-    st.scale = sc;
 }
 
-template <int BO, int BS>
-__device__ __forceinline__ void store_stage(Smem<BO, BS>& sm, int buf, const Stage<BO, BS>& st)
+__device__ __forceinline__ void generic_store(GenericSmem& sm, int buf, const GenericStage& st)
 {
     const int tid = threadIdx.x;
 #pragma unroll
-    for (int j = 0; j < Stage<BO, BS>::kPerThread; ++j) {
+    for (int j = 0; j < (kGBO + kGBS) * 4 / kThreads; ++j) {
         const int c = tid + kThreads * j;
         const int r = c >> 2, part = c & 3;
-        uint8_t* dst = r < BO ? &sm.w[buf][r][16 * part] : &sm.x[buf][r - BO][16 * part];
+        uint8_t* dst = r < kGBO ? &sm.w[buf][r][16 * part] : &sm.x[buf][r - kGBO][16 * part];
         *reinterpret_cast<uint4*>(dst) = st.code[j];
     }
-    if (tid < BO + BS) {
-        uint8_t* dst = tid < BO ? sm.ws[buf][tid] : sm.xs[buf][tid - BO];
-        *reinterpret_cast<uint32_t*>(dst) = st.scale;
-    }
+    const uint32_t packed = st.scale[0] | (st.scale[1] << 8) | (st.scale[2] << 16) |
+                            (st.scale[3] << 24);
+    uint8_t* dst = tid < kGBO ? sm.ws[buf][tid] : sm.xs[buf][tid - kGBO];
+    *reinterpret_cast<uint32_t*>(dst) = packed;
 }
 
-template <int BO, int BS>
 __global__ void __launch_bounds__(kThreads)
-gemm_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xe,
-            const uint8_t* __restrict__ wq, const uint8_t* __restrict__ we, int64_t S,
-            int64_t k, int64_t out, float* __restrict__ y, int64_t tiles_o)
+gemm_generic_kernel(DmaArgs p, int tiled, float* __restrict__ y, int64_t tiles_o,
+                    int64_t tiles_s)
 {
-    constexpr int WO = BO / 2, WS = BS / 2;     // per-wave tile
-    constexpr int TO = WO / 16, TS = WS / 16;   // 16x16 MFMA tiles per wave
-    __shared__ Smem<BO, BS> sm;
-
+    __shared__ GenericSmem sm;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int wo = wave >> 1, ws = wave & 1;
-    const int64_t tile = blockIdx.x;
-    const int64_t o0 = (tile % tiles_o) * BO;
-    const int64_t s0 = (tile / tiles_o) * BS;
-    const int64_t ksteps = (k + 3) / 4;
+    const int wo = wave >> 1, wsx = wave & 1;
+    int64_t o0, s0;
+    tile_origin(tiles_o, tiles_s, 1, kGBO, kGBS, o0, s0);
+    const int64_t ksteps = (p.k + 3) / 4;
 
-    v4f acc[TO][TS];
+    v4f acc[4][4];
 #pragma unroll
-    for (int a = 0; a < TO; ++a)
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < TS; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < 4; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    Stage<BO, BS> st;
-    load_stage<BO, BS>(st, xq, xe, wq, we, S, out, k, o0, s0, 0);
-    store_stage<BO, BS>(sm, 0, st);
+    GenericStage st;
+    generic_load(st, p, tiled, o0, s0, 0);
+    generic_store(sm, 0, st);
     __syncthreads();
 
-    const int lr = lane & 15;   // row within a 16-row MFMA tile
-    const int lg = lane >> 4;   // K block within the 128-element step
+    const int lr = lane & 15, lg = lane >> 4;
     for (int64_t kt = 0; kt < ksteps; ++kt) {
         const int buf = (int)(kt & 1);
         const bool more = kt + 1 < ksteps;
-        if (more) load_stage<BO, BS>(st, xq, xe, wq, we, S, out, k, o0, s0, kt + 1);
-
-        uint4 af[TO], bf[TS];
-        int asc[TO], bsc[TS];
+        if (more) generic_load(st, p, tiled, o0, s0, kt + 1);
+        uint4 af[4], bf[4];
+        int asc[4], bsc[4];
 #pragma unroll
-        for (int a = 0; a < TO; ++a) {
-            const int r = wo * WO + 16 * a + lr;
+        for (int a = 0; a < 4; ++a) {
+            const int r = wo * 64 + 16 * a + lr;
             af[a] = *reinterpret_cast<const uint4*>(&sm.w[buf][r][16 * lg]);
             asc[a] = sm.ws[buf][r][lg];
         }
 #pragma unroll
-        for (int b = 0; b < TS; ++b) {
-            const int r = ws * WS + 16 * b + lr;
+        for (int b = 0; b < 4; ++b) {
+            const int r = wsx * 64 + 16 * b + lr;
             bf[b] = *reinterpret_cast<const uint4*>(&sm.x[buf][r][16 * lg]);
             bsc[b] = sm.xs[buf][r][lg];
         }
 #pragma unroll
-        for (int a = 0; a < TO; ++a) {
+        for (int a = 0; a < 4; ++a) {
             const v8i av = {(int)af[a].x, (int)af[a].y, (int)af[a].z, (int)af[a].w, 0, 0, 0, 0};
 #pragma unroll
-            for (int b = 0; b < TS; ++b) {
+            for (int b = 0; b < 4; ++b) {
                 const v8i bv = {(int)bf[b].x, (int)bf[b].y, (int)bf[b].z, (int)bf[b].w, 0, 0, 0, 0};
                 acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                     av, bv, acc[a][b], kFmtE2M1, kFmtE2M1, 0, asc[a], 0, bsc[b]);
             }
         }
-        if (more) store_stage<BO, BS>(sm, buf ^ 1, st);
+        if (more) generic_store(sm, buf ^ 1, st);
         __syncthreads();
     }
 
-    // epilogue: lane holds y[s][o .. o+3] for s = column l%16, o = rows 4(l/16) .. +3
-    const bool vec_ok = (out & 3) == 0;
+    const bool vec_ok = (p.out & 3) == 0;
 #pragma unroll
-    for (int a = 0; a < TO; ++a) {
-        const int64_t o = o0 + wo * WO + 16 * a + 4 * lg;
+    for (int a = 0; a < 4; ++a) {
+        const int64_t o = o0 + wo * 64 + 16 * a + 4 * lg;
 #pragma unroll
-        for (int b = 0; b < TS; ++b) {
-            const int64_t s = s0 + ws * WS + 16 * b + lr;
-            if (s >= S) continue;
-            float* dst = y + s * out + o;
-            if (vec_ok && o + 3 < out) {
+        for (int b = 0; b < 4; ++b) {
+            const int64_t s = s0 + wsx * 64 + 16 * b + lr;
+            if (s >= p.S) continue;
+            float* dst = y + s * p.out + o;
+            if (vec_ok && o + 3 < p.out) {
                 *reinterpret_cast<float4*>(dst) =
                     make_float4(acc[a][b][0], acc[a][b][1], acc[a][b][2], acc[a][b][3]);
             } else {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    if (o + j < out) dst[j] = acc[a][b][j];
+                    if (o + j < p.out) dst[j] = acc[a][b][j];
             }
         }
     }
@@ -204,17 +558,33 @@ gemm_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xe,
 }  // namespace
 
 hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq,
-                       const uint8_t* we, int64_t S, int64_t N, int64_t out, float* y,
-                       hipStream_t stream)
+                       const uint8_t* we, bool tiled_scales, int64_t S, int64_t N,
+                       int64_t out, float* y, hipStream_t stream)
 {
-    constexpr int BO = 128, BS = 128;
-    const int64_t k = N / 32;
-    const int64_t tiles_o = (out + BO - 1) / BO;
-    const int64_t tiles_s = (S + BS - 1) / BS;
-    const int64_t tiles = tiles_o * tiles_s;
-    if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((gemm_kernel<BO, BS>), dim3((unsigned)tiles), dim3(kThreads), 0, stream,
-                       xq, xe, wq, we, S, k, out, y, tiles_o);
+    const DmaArgs p{xq, xe, wq, we, S, N / 32, out};
+    const uintptr_t salign = tiled_scales ? 256 : 8;
+    const bool dma_ok = (p.k % kStageBlocks) == 0 &&
+                        (reinterpret_cast<uintptr_t>(xe) % salign) == 0 &&
+                        (reinterpret_cast<uintptr_t>(we) % salign) == 0 &&
+                        S * 16 * p.k < (1LL << 32) && out * 16 * p.k < (1LL << 32);
+    if (dma_ok) {
+        const int64_t tiles_o = (out + CfgQ::BO - 1) / CfgQ::BO;
+        const int64_t tiles_s = (S + CfgQ::BS - 1) / CfgQ::BS;
+        if (tiles_o * tiles_s > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+        const dim3 grid((unsigned)(tiles_o * tiles_s));
+        if (tiled_scales)
+            hipLaunchKernelGGL(gemm_dma_kernel<CfgQT>, grid, dim3(CfgQT::kThreads), 0, stream,
+                               p, y, tiles_o, tiles_s);
+        else
+            hipLaunchKernelGGL(gemm_dma_kernel<CfgQ>, grid, dim3(CfgQ::kThreads), 0, stream,
+                               p, y, tiles_o, tiles_s);
+        return hipGetLastError();
+    }
+    const int64_t tiles_o = (out + kGBO - 1) / kGBO;
+    const int64_t tiles_s = (S + kGBS - 1) / kGBS;
+    if (tiles_o * tiles_s > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(gemm_generic_kernel, dim3((unsigned)(tiles_o * tiles_s)), dim3(kThreads),
+                       0, stream, p, (int)tiled_scales, y, tiles_o, tiles_s);
     return hipGetLastError();
 }
 

@@ -10,13 +10,16 @@ namespace batq {
 // Fused transform (+ clip) + MXFP4 of `rows` rows of N = 32k elements.
 // Activation mode: bf16 input with row stride ldx, clip ratios r_min/r_max.
 // Weight mode: fp32 input with row stride ldx, no clip (r_min/r_max unused).
+// Scales row-major, or in the MFMA-tiled layout of batq.h when tiled_scales.
 hipError_t launch_quantize(bool act, const void* x, int64_t rows, int64_t k, int64_t ldx,
                            const float* A, const float* B, const float* r_min,
-                           const float* r_max, uint8_t* q, uint8_t* e, hipStream_t stream);
+                           const float* r_max, uint8_t* q, uint8_t* e, bool tiled_scales,
+                           hipStream_t stream);
 
-// MXFP4 x MXFP4 -> fp32 GEMM, y[S, out] = dq(x)[S, N] dq(w)[out, N]^T.
+// MXFP4 x MXFP4 -> fp32 GEMM, y[S, out] = dq(x)[S, N] dq(w)[out, N]^T; both scale
+// arrays in the same layout (tiled_scales: MFMA-tiled, else row-major).
 hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq,
-                       const uint8_t* we, int64_t S, int64_t N, int64_t out, float* y,
-                       hipStream_t stream);
+                       const uint8_t* we, bool tiled_scales, int64_t S, int64_t N,
+                       int64_t out, float* y, hipStream_t stream);
 
 }  // namespace batq

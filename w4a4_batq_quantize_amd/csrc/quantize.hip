@@ -73,7 +73,8 @@ __global__ void __launch_bounds__(kThreads)
 quantize_kernel(const void* __restrict__ xin, int64_t rows, int64_t k, int64_t ldx,
                 const float* __restrict__ A, const float* __restrict__ B,
                 const float* __restrict__ r_min, const float* __restrict__ r_max,
-                uint8_t* __restrict__ q, uint8_t* __restrict__ e, int lpr_log2)
+                uint8_t* __restrict__ q, uint8_t* __restrict__ e, int lpr_log2,
+                int tiled_scales)
 {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -152,14 +153,21 @@ quantize_kernel(const void* __restrict__ xin, int64_t rows, int64_t k, int64_t l
         w[d] = acc;
     }
     *reinterpret_cast<uint4*>(q + row * (16 * k) + 16 * blk) = make_uint4(w[0], w[1], w[2], w[3]);
-    e[row * k + blk] = (uint8_t)ebyte;
+    // scale byte: row-major, or the 256-byte (32 rows x 8 blocks) units the GEMM consumes,
+    // blocks of a unit ordered 0,2,4,6,1,3,5,7 within each row's 8 bytes
+    const int64_t eoff = tiled_scales
+        ? (((row >> 5) * ((k + 7) >> 3) + (blk >> 3)) << 8) + ((row & 31) << 3) +
+              ((blk & 1) << 2) + ((blk & 7) >> 1)
+        : row * k + blk;
+    e[eoff] = (uint8_t)ebyte;
 }
 
 }  // namespace
 
 hipError_t launch_quantize(bool act, const void* x, int64_t rows, int64_t k, int64_t ldx,
                            const float* A, const float* B, const float* r_min,
-                           const float* r_max, uint8_t* q, uint8_t* e, hipStream_t stream)
+                           const float* r_max, uint8_t* q, uint8_t* e, bool tiled_scales,
+                           hipStream_t stream)
 {
     // lanes per row: the smallest power of two >= k, capped at one wave
     int lpr_log2 = 0;
@@ -172,10 +180,10 @@ hipError_t launch_quantize(bool act, const void* x, int64_t rows, int64_t k, int
     dim3 grid((unsigned)gx, (unsigned)gy);
     if (act)
         hipLaunchKernelGGL(quantize_kernel<true>, grid, dim3(kThreads), 0, stream, x, rows, k,
-                           ldx, A, B, r_min, r_max, q, e, lpr_log2);
+                           ldx, A, B, r_min, r_max, q, e, lpr_log2, (int)tiled_scales);
     else
         hipLaunchKernelGGL(quantize_kernel<false>, grid, dim3(kThreads), 0, stream, x, rows,
-                           k, ldx, A, B, r_min, r_max, q, e, lpr_log2);
+                           k, ldx, A, B, r_min, r_max, q, e, lpr_log2, (int)tiled_scales);
     return hipGetLastError();
 }
 
