@@ -161,20 +161,20 @@ __device__ __forceinline__ void dma_plan(DmaPlan<C>& pl, const DmaArgs& p, int64
     }
 }
 
+// DMA instruction d (of kDmaPerStage) of this wave for stage ks: the code instructions
+// first, then the scale instructions.
 template <class C>
-__device__ __forceinline__ void dma_stage(uint8_t* buf, const DmaPlan<C>& pl, const DmaArgs& p,
-                                          int64_t ks, int wave)
+__device__ __forceinline__ void dma_one(uint8_t* buf, const DmaPlan<C>& pl, const DmaArgs& p,
+                                        int64_t ks, int wave, int d)
 {
-#pragma unroll
-    for (int i = 0; i < C::kCodeDma; ++i) {
-        const int inst = wave * C::kCodeDma + i;
+    if (d < C::kCodeDma) {
+        const int inst = wave * C::kCodeDma + d;
         const uint8_t* base = (inst * 8 < C::BO ? p.wq : p.xq) + ks * kRowBytes;
-        __builtin_amdgcn_global_load_lds((gbl_void_t*)(base + pl.code_off[i]),
+        __builtin_amdgcn_global_load_lds((gbl_void_t*)(base + pl.code_off[d]),
                                          (lds_void_t*)(buf + inst * 1024), 16, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < C::kScaleDma; ++j) {
+    } else {
         constexpr int kRowsPerInst = C::TS ? 32 : 64 * C::SB / kStageBlocks;
+        const int j = d - C::kCodeDma;
         const int inst = wave * C::kScaleDma + j;
         const uint8_t* base = (inst * kRowsPerInst < C::BO ? p.we : p.xe) +
                               ks * (C::TS ? 256 : kStageBlocks);
@@ -183,6 +183,30 @@ __device__ __forceinline__ void dma_stage(uint8_t* buf, const DmaPlan<C>& pl, co
                                          C::SB, 0, 0);
     }
 }
+
+template <class C>
+__device__ __forceinline__ void dma_stage(uint8_t* buf, const DmaPlan<C>& pl, const DmaArgs& p,
+                                          int64_t ks, int wave)
+{
+#pragma unroll
+    for (int d = 0; d < C::kDmaPerStage; ++d) dma_one<C>(buf, pl, p, ks, wave, d);
+}
+
+// The DMA of a prefetched stage, issued in pieces between the MFMAs of the current one so
+// that the address unit drains it while the matrix cores work (a DMA instruction holds its
+// wave until the unit accepts it).
+template <class C>
+struct DmaIssue {
+    uint8_t* buf;
+    const DmaPlan<C>* pl;
+    const DmaArgs* p;
+    int64_t ks;
+    int wave;                 // < 0: no DMA issued from this wave
+    __device__ __forceinline__ void operator()(int d) const
+    {
+        if (wave >= 0 && d < C::kDmaPerStage) dma_one<C>(buf, *pl, *p, ks, wave, d);
+    }
+};
 
 // Operand fragments of one K-step T (64 elements) out of an LDS stage, 16 bytes per lane
 // per 32-row MFMA operand.
@@ -210,8 +234,11 @@ template <class C, int T>
 __device__ __forceinline__ void dma_mfma_frags(v16f (&acc)[C::TM][C::TN],
                                                const Frags<C::TM, C::TN>& f,
                                                const uint32_t (&wsc)[2][C::TM],
-                                               const uint32_t (&xsc)[2][C::TN])
+                                               const uint32_t (&xsc)[2][C::TN],
+                                               const DmaIssue<C>& dma)
 {
+    // DMA slots per K-step: one after each row of TN MFMAs
+    constexpr int kSlots = (C::kDmaPerStage + 3) / 4;
     // tiled scales: byte T of the one dword; row-major: byte 2*(T%2) of word T/2
     constexpr int kSel = C::TS ? T : 2 * (T & 1);
     constexpr int kWord = C::TS ? 0 : T >> 1;
@@ -225,6 +252,11 @@ __device__ __forceinline__ void dma_mfma_frags(v16f (&acc)[C::TM][C::TN],
                 av, bv, acc[a][b], kFmtE2M1, kFmtE2M1, kSel, (int)wsc[kWord][a], kSel,
                 (int)xsc[kWord][b]);
         }
+        // this row's share of the K-step's DMA slots
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int d = a * kSlots / C::TM; d < (a + 1) * kSlots / C::TM; ++d) dma(T * kSlots + d);
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -233,7 +265,8 @@ __device__ __forceinline__ void dma_mfma_frags(v16f (&acc)[C::TM][C::TN],
 // LDS latency hides behind the matrix-core work of the previous step.
 template <class C>
 __device__ __forceinline__ void dma_mfma_stage(v16f (&acc)[C::TM][C::TN], const uint8_t* buf,
-                                               int wrow0, int xrow0, int lane)
+                                               int wrow0, int xrow0, int lane,
+                                               const DmaIssue<C>& dma)
 {
     const int lr = lane & 31, lg = lane >> 5, lr7 = lane & 7;
     const uint32_t wrow_off = (uint32_t)(wrow0 + lr) * kRowBytes;
@@ -284,24 +317,24 @@ __device__ __forceinline__ void dma_mfma_stage(v16f (&acc)[C::TM][C::TN], const 
         }
     }
     __builtin_amdgcn_sched_barrier(0);
-    dma_mfma_frags<C, 0>(acc, f0, wsc, xsc);
+    dma_mfma_frags<C, 0>(acc, f0, wsc, xsc, dma);
     __builtin_amdgcn_sched_barrier(0);
     dma_load_frags<C, 2>(f0, buf, wrow_off, xrow_off, lg, lr7);
     __builtin_amdgcn_sched_barrier(0);
-    dma_mfma_frags<C, 1>(acc, f1, wsc, xsc);
+    dma_mfma_frags<C, 1>(acc, f1, wsc, xsc, dma);
     __builtin_amdgcn_sched_barrier(0);
     dma_load_frags<C, 3>(f1, buf, wrow_off, xrow_off, lg, lr7);
     __builtin_amdgcn_sched_barrier(0);
-    dma_mfma_frags<C, 2>(acc, f0, wsc, xsc);
+    dma_mfma_frags<C, 2>(acc, f0, wsc, xsc, dma);
     __builtin_amdgcn_sched_barrier(0);
-    dma_mfma_frags<C, 3>(acc, f1, wsc, xsc);
+    dma_mfma_frags<C, 3>(acc, f1, wsc, xsc, dma);
 }
 
 // One pipeline step: once at most the DMA instructions of the NB-2 following stages are
 // still in flight for this wave, this wave's part of stage s is in `cur`; after the barrier
-// all of it is, and every wave has finished reading `nxt` (stage s-1).  Stage s+NB-1 is then
-// fetched into `nxt` (the final stage again once the end is reached, so the body has no
-// branch and the wait count is constant) and stage s is multiplied out of `cur`.
+// all of it is, and every wave has finished reading `nxt` (stage s-1).  Stage s is then
+// multiplied out of `cur` while stage s+NB-1 is fetched into `nxt` (the final stage again
+// once the end is reached, so the body has no branch and the wait count is constant).
 template <class C>
 __device__ __forceinline__ void dma_pipeline_step(v16f (&acc)[C::TM][C::TN], uint8_t* cur,
                                                   uint8_t* nxt, const DmaPlan<C>& pl,
@@ -311,8 +344,63 @@ __device__ __forceinline__ void dma_pipeline_step(v16f (&acc)[C::TM][C::TN], uin
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(C::kDmaPerStage * (C::NB - 2), 0));
     barrier_only();
     const int64_t ahead = s + C::NB - 1;
-    dma_stage<C>(nxt, pl, p, ahead < nst ? ahead : nst - 1, wave);
-    dma_mfma_stage<C>(acc, cur, wrow0, xrow0, lane);
+    const DmaIssue<C> dma{nxt, &pl, &p, ahead < nst ? ahead : nst - 1, wave};
+    dma_mfma_stage<C>(acc, cur, wrow0, xrow0, lane, dma);
+}
+
+// Store a consumer wave's TM x TN accumulator tiles: lane l of tile (a, b) holds, in its
+// register group g, y[s][o .. o+3] with s = 32b + l%32 and o = 32a + 8g + 4(l/32) relative to
+// the wave's origin.
+template <class C>
+__device__ __forceinline__ void store_tile(const v16f (&acc)[C::TM][C::TN], const DmaArgs& p,
+                                           float* __restrict__ y, int64_t o0, int64_t s0,
+                                           int wrow0, int xrow0, int lane)
+{
+    const int lr = lane & 31, lg = lane >> 5;
+    const bool interior = (p.out & 3) == 0 && o0 + C::BO <= p.out && s0 + C::BS <= p.S;
+    if (interior) {
+        // whole tile inside the output: unconditional 16-byte stores, one 32x32 tile at a
+        // time (keeps the accumulator-to-VGPR copies short-lived)
+        float* base = y + (s0 + xrow0 + lr) * p.out + o0 + wrow0 + 4 * lg;
+#pragma unroll
+        for (int b = 0; b < C::TN; ++b) {
+#pragma unroll
+            for (int a = 0; a < C::TM; ++a) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    *reinterpret_cast<float4*>(base + 32 * b * p.out + 32 * a + 8 * g) =
+                        make_float4(acc[a][b][4 * g], acc[a][b][4 * g + 1], acc[a][b][4 * g + 2],
+                                    acc[a][b][4 * g + 3]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        return;
+    }
+    const bool vec_ok = (p.out & 3) == 0;
+#pragma unroll
+    for (int b = 0; b < C::TN; ++b) {
+        const int64_t s = s0 + xrow0 + 32 * b + lr;
+        if (s >= p.S) continue;
+#pragma unroll
+        for (int a = 0; a < C::TM; ++a) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int64_t o = o0 + wrow0 + 32 * a + 8 * g + 4 * lg;
+                float* dst = y + s * p.out + o;
+                const float v0 = acc[a][b][4 * g], v1 = acc[a][b][4 * g + 1];
+                const float v2 = acc[a][b][4 * g + 2], v3 = acc[a][b][4 * g + 3];
+                if (vec_ok && o + 3 < p.out) {
+                    *reinterpret_cast<float4*>(dst) = make_float4(v0, v1, v2, v3);
+                } else {
+                    if (o < p.out) dst[0] = v0;
+                    if (o + 1 < p.out) dst[1] = v1;
+                    if (o + 2 < p.out) dst[2] = v2;
+                    if (o + 3 < p.out) dst[3] = v3;
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
 }
 
 template <class C>
@@ -363,34 +451,99 @@ gemm_dma_kernel(DmaArgs p, float* __restrict__ y, int64_t tiles_o, int64_t tiles
         __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
     }
 
-    const int lr = lane & 31, lg = lane >> 5;
-    const bool vec_ok = (p.out & 3) == 0;
-#pragma unroll
-    for (int b = 0; b < C::TN; ++b) {
-        const int64_t s = s0 + xrow0 + 32 * b + lr;
-        if (s >= p.S) continue;
-#pragma unroll
-        for (int a = 0; a < C::TM; ++a) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int64_t o = o0 + wrow0 + 32 * a + 8 * g + 4 * lg;
-                float* dst = y + s * p.out + o;
-                const float v0 = acc[a][b][4 * g], v1 = acc[a][b][4 * g + 1];
-                const float v2 = acc[a][b][4 * g + 2], v3 = acc[a][b][4 * g + 3];
-                if (vec_ok && o + 3 < p.out) {
-                    *reinterpret_cast<float4*>(dst) = make_float4(v0, v1, v2, v3);
-                } else {
-                    if (o < p.out) dst[0] = v0;
-                    if (o + 1 < p.out) dst[1] = v1;
-                    if (o + 2 < p.out) dst[2] = v2;
-                    if (o + 3 < p.out) dst[3] = v3;
-                }
-            }
-            // one 32x32 tile at a time: keeps the accumulator-to-VGPR copies short-lived
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
+    store_tile<C>(acc, p, y, o0, s0, wrow0, xrow0, lane);
 }
+
+// =======================================================================================
+// gemm_pc_kernel<Cfg>: the same tile with producer and consumer waves
+// =======================================================================================
+//
+// 2x the waves of the configuration: waves [0, W) multiply (the MFMA issue of a wave never
+// waits on the address unit), waves [W, 2W) only stream stages into LDS with the same
+// per-wave DMA split.  One barrier per stage orders the two roles: before barrier s every
+// producer has waited for its part of stage s; after it, consumers multiply stage s and
+// producers fetch stage s+NB-1 into the buffer consumers finished before the barrier (they
+// drain their LDS reads, lgkmcnt(0), before every barrier).
+template <class C>
+__global__ void __launch_bounds__(2 * C::kThreads)
+gemm_pc_kernel(DmaArgs p, float* __restrict__ y, int64_t tiles_o, int64_t tiles_s)
+{
+    constexpr int NB = C::NB;
+    __shared__ __attribute__((aligned(16))) uint8_t lds0[C::kBufBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t lds1[C::kBufBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t lds2[NB > 2 ? C::kBufBytes : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t lds3[NB > 3 ? C::kBufBytes : 16];
+    uint8_t* bufs[4] = {lds0, lds1, lds2, lds3};
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int64_t o0, s0;
+    tile_origin(tiles_o, tiles_s, 4, C::BO, C::BS, o0, s0);
+    const int64_t nst = p.k / kStageBlocks;
+
+    if (wave >= C::kWaves) {
+        // ---------------- producer ----------------
+        if (nst == 0) return;
+        const int pw = wave - C::kWaves;
+        DmaPlan<C> pl;
+        dma_plan<C>(pl, p, o0, s0, pw, lane);
+#pragma unroll
+        for (int i = 0; i < NB - 1; ++i) dma_stage<C>(bufs[i], pl, p, i < nst ? i : nst - 1, pw);
+        const int64_t nfull = nst - nst % NB;
+        int64_t s = 0;
+        for (; s < nfull; s += NB) {
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm(C::kDmaPerStage * (NB - 2), 0));
+                barrier_only();
+                const int64_t ahead = s + i + NB - 1;
+                dma_stage<C>(bufs[(i + NB - 1) % NB], pl, p, ahead < nst ? ahead : nst - 1, pw);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NB - 1; ++i)
+            if (s + i < nst) {
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm(C::kDmaPerStage * (NB - 2), 0));
+                barrier_only();
+                const int64_t ahead = s + i + NB - 1;
+                dma_stage<C>(bufs[(i + NB - 1) % NB], pl, p, ahead < nst ? ahead : nst - 1, pw);
+            }
+        // the trailing prefetches must land before the workgroup's LDS is released
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+        return;
+    }
+
+    // ---------------- consumer ----------------
+    const int wrow0 = (wave / C::WS) * (C::BO / C::WO);
+    const int xrow0 = (wave % C::WS) * (C::BS / C::WS);
+    v16f acc[C::TM][C::TN];
+#pragma unroll
+    for (int a = 0; a < C::TM; ++a)
+#pragma unroll
+        for (int b = 0; b < C::TN; ++b) acc[a][b] = v16f{};
+    if (nst > 0) {
+        const DmaIssue<C> none{nullptr, nullptr, nullptr, 0, -1};
+        const int64_t nfull = nst - nst % NB;
+        int64_t s = 0;
+        for (; s < nfull; s += NB) {
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+                barrier_only();
+                dma_mfma_stage<C>(acc, bufs[i], wrow0, xrow0, lane, none);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NB - 1; ++i)
+            if (s + i < nst) {
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+                barrier_only();
+                dma_mfma_stage<C>(acc, bufs[i], wrow0, xrow0, lane, none);
+            }
+    }
+    store_tile<C>(acc, p, y, o0, s0, wrow0, xrow0, lane);
+}
+
 
 using CfgQ = DmaCfg<256, 128, 2, 2, 3, false>;    // 256 tiles for a 2048 x 4096 output
 using CfgQT = DmaCfg<256, 128, 2, 2, 3, true>;
@@ -573,8 +726,8 @@ hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq,
         if (tiles_o * tiles_s > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
         const dim3 grid((unsigned)(tiles_o * tiles_s));
         if (tiled_scales)
-            hipLaunchKernelGGL(gemm_dma_kernel<CfgQT>, grid, dim3(CfgQT::kThreads), 0, stream,
-                               p, y, tiles_o, tiles_s);
+            hipLaunchKernelGGL(gemm_pc_kernel<CfgQT>, grid, dim3(2 * CfgQT::kThreads), 0,
+                               stream, p, y, tiles_o, tiles_s);
         else
             hipLaunchKernelGGL(gemm_dma_kernel<CfgQ>, grid, dim3(CfgQ::kThreads), 0, stream,
                                p, y, tiles_o, tiles_s);
