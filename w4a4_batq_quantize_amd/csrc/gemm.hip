@@ -276,7 +276,11 @@ __device__ __forceinline__ void dma_mfma_stage(v16f (&acc)[C::TM][C::TN], const 
     if constexpr (C::TS) {
         // tiled: lane (row, l/32) finds the blocks 2T + l/32 of its row as bytes T of one
         // dword (the row's 8 bytes are read whole, which keeps these reads distinguishable
-        // from the stage DMA still in flight); both words alias it
+        // from the stage DMA still in flight); both words alias it.  The fragment reads go
+        // out first so the scale reads and selects overlap their latency.
+        dma_load_frags<C, 0>(f0, buf, wrow_off, xrow_off, lg, lr7);
+        dma_load_frags<C, 1>(f1, buf, wrow_off, xrow_off, lg, lr7);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int a = 0; a < C::TM; ++a) {
             const uint2 v = *reinterpret_cast<const uint2*>(
@@ -289,8 +293,6 @@ __device__ __forceinline__ void dma_mfma_stage(v16f (&acc)[C::TM][C::TN], const 
                 buf + C::kCodeBytes + ((C::BO + xrow0) / 32 + b) * 256 + lr * 8);
             xsc[0][b] = xsc[1][b] = lg ? v.y : v.x;
         }
-        dma_load_frags<C, 0>(f0, buf, wrow_off, xrow_off, lg, lr7);
-        dma_load_frags<C, 1>(f1, buf, wrow_off, xrow_off, lg, lr7);
     } else {
         // row-major: the stage's 8 scale bytes of each operand row, pre-shifted so that the
         // byte select 2*(T%2) picks block 2T + lane/32 from the low (T < 2) or high word
