@@ -11,7 +11,9 @@ Inputs are resident in HBM before timing starts.  Every step uses the next of R 
 (activations, codes, scales, prepared weights, output), with R chosen so the sets together
 exceed the 256 MB Infinity Cache several times over; the measured rates are therefore HBM
 rates, not cache rates.  Kernel durations come from HIP events recorded on the stream the
-kernels are launched on; the step time is wall clock around the timed steps.
+kernels are launched on: the timed steps run quantiser and GEMM in turn, and each kernel is
+then timed alone over the same number of back-to-back launches, so that its event interval
+holds nothing but its own executions.  The step time is wall clock around the timed steps.
 
 Prints one JSON line.  --gpus above 1 is refused: this path runs on one GPU.
 """
@@ -47,6 +49,24 @@ def k2_flops(S, N, out):
 def k2_bytes(S, N, out):
     """Compulsory bytes of one GEMM launch: both MXFP4 operands once, fp32 output once."""
     return (S + out) * (N // 2 + N // 32) + 4 * S * out
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary (calibrated on a plain copy), or None when there is no summary or the
+    kernel's source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = dict(l.split(": ", 1) for l in open(path).read().splitlines() if ": " in l)
+    try:
+        src = open(os.path.join(ROOT, fields["source_file"].strip()), "rb").read()
+        if hashlib.sha256(src).hexdigest() != fields["source_sha256"].strip():
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, OSError, ValueError):
+        return None
 
 
 def cpu_baseline(L, seconds):
@@ -144,32 +164,45 @@ def main():
             wes[j].data_ptr(), ys[j].data_ptr()) for j in range(R)]
     quant, gemm = bq.quantize_act_raw, bq.gemm_w4a4_raw
 
-    def step(j, ev_mid=None):
-        x, xq, xe, wq, we, y = ptr[j]
-        st = quant(x, S, N, N, pA, pB, pr1, pr2, xq, xe, layout, sh)
-        if ev_mid is not None:
-            ev_mid.record(stream)
-        st |= gemm(xq, xe, wq, we, S, N, out, y, layout, sh)
-        if st:
-            raise RuntimeError(f"library call failed with status {st}")
+    def launch_k1(j):
+        x, xq, xe, _, _, _ = ptr[j]
+        return quant(x, S, N, N, pA, pB, pr1, pr2, xq, xe, layout, sh)
+
+    def launch_k2(j):
+        _, xq, xe, wq, we, y = ptr[j]
+        return gemm(xq, xe, wq, we, S, N, out, y, layout, sh)
+
+    def step(j):
+        if launch_k1(j) | launch_k2(j):
+            raise RuntimeError("library call failed")
+
+    def timed(fn, first, K):
+        """K launches of fn on the rotated sets, back to back on one stream; returns the
+        event-measured GPU time per launch and the wall time per launch (seconds)."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(K):
+            if fn((first + i) % R):
+                raise RuntimeError("library call failed")
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        return e0.elapsed_time(e1) * 1e-3 / K, (t1 - t0) / K
 
     for i in range(args.warmup):
         step(i % R)
     torch.cuda.synchronize()
 
+    # the timed steps: quantise + GEMM per step
     K = args.steps
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * K + 1)]
-    t0 = time.perf_counter()
-    ev[0].record(stream)
-    for i in range(K):
-        step((args.warmup + i) % R, ev[2 * i + 1])
-        ev[2 * i + 2].record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-
-    t_k1 = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(K)) / K * 1e-3
-    t_k2 = sum(ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(K)) / K * 1e-3
-    ms_per_step = (t1 - t0) / K * 1e3
+    t_step_ev, t_step_wall = timed(lambda j: step(j) or 0, args.warmup, K)
+    ms_per_step = t_step_wall * 1e3
+    # per-kernel durations: the same launches, each kernel alone back to back, so that an
+    # event interval holds one kernel's executions and the dispatch gaps between them only
+    t_k1, _ = timed(launch_k1, args.warmup + K, K)
+    t_k2, _ = timed(launch_k2, args.warmup + 2 * K, K)
 
     if args.copy_calibration:
         # plain copy of known size, outside the timed region, for scaling HBM counters
@@ -180,7 +213,7 @@ def main():
         torch.cuda.synchronize()
 
     # keep the last step's output alive and finite (a cheap sanity check, untimed)
-    last = ys[(args.warmup + K - 1) % R]
+    last = ys[(args.warmup + 3 * K - 1) % R]
     assert bool(torch.isfinite(last).all().item()), "non-finite GEMM output"
 
     b1 = k1_bytes(S, N)
@@ -188,14 +221,17 @@ def main():
     tflops = k2_flops(S, N, out) / t_k2 / 1e12
     k2_ai = k2_flops(S, N, out) / k2_bytes(S, N, out)
     k2_roof = min(FP4_PEAK_TFLOPS, k2_ai * HBM_PEAK_GBS / 1e3)
+    tr1 = measured_traffic("quantize_kernel", L.cfg.name)
+    tr2 = measured_traffic("gemm_pc_kernel", L.cfg.name)
     roof_k1 = {"kernel": "quantize_kernel (fused BAT+clip+MXFP4)", "bound": "hbm",
                "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-               "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+               "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": tr1,
                "avg_us": round(t_k1 * 1e6, 3), "algorithmic_bytes": b1}
-    roof_k2 = {"kernel": "gemm_kernel (MXFP4 scaled MFMA)",
+    roof_k2 = {"kernel": "gemm_pc_kernel (MXFP4 scaled MFMA)",
                "bound": "mfma" if k2_roof >= FP4_PEAK_TFLOPS else "hbm",
                "achieved": round(tflops, 1), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
-               "frac": round(tflops / FP4_PEAK_TFLOPS, 4), "traffic": None,
+               "frac": round(tflops / FP4_PEAK_TFLOPS, 4), "traffic": tr2,
+               "algorithmic_bytes": k2_bytes(S, N, out),
                "avg_us": round(t_k2 * 1e6, 3), "algorithmic_flops": k2_flops(S, N, out),
                "roofline_tflops": round(k2_roof, 1), "frac_of_roofline": round(tflops / k2_roof, 4)}
     dominant = roof_k2 if t_k2 >= t_k1 else roof_k1
@@ -221,7 +257,8 @@ def main():
                    "scale_layout": "mfma_tiled"},
         "gemm": {"value": round(tflops, 1), "unit": "TFLOP/s",
                  "pct_of_peak": round(100 * tflops / FP4_PEAK_TFLOPS, 2)},
-        "step_gpu_us": round((t_k1 + t_k2) * 1e6, 3),
+        "step_gpu_us": round(t_step_ev * 1e6, 3),
+        "kernel_us": {"quantize": round(t_k1 * 1e6, 3), "gemm": round(t_k2 * 1e6, 3)},
         "roofline": dominant,
         "roofline_kernels": {"quantize": roof_k1, "gemm": roof_k2},
     }
