@@ -161,27 +161,44 @@ __device__ __forceinline__ void dma_plan(DmaPlan<C>& pl, const DmaArgs& p, int64
     }
 }
 
+// A raw (untyped) buffer resource over `bytes` bytes at `base` (dword 3 = 0x00020000 on gfx9):
+// loads through it take a 32-bit lane offset plus a uniform offset, so the DMA issue needs no
+// per-lane 64-bit address arithmetic on the SIMDs that run the MFMAs (measured: that VALU work
+// slowed the DMA and the MFMAs down when they shared SIMDs); offsets past `bytes` read zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const uint8_t* base, int64_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
 // DMA instruction d (of kDmaPerStage) of this wave for stage ks: the code instructions
-// first, then the scale instructions.
+// first, then the scale instructions.  The launcher guarantees every operand array is
+// smaller than 4 GB.
 template <class C>
 __device__ __forceinline__ void dma_one(uint8_t* buf, const DmaPlan<C>& pl, const DmaArgs& p,
                                         int64_t ks, int wave, int d)
 {
+#if defined(__HIP_DEVICE_COMPILE__)   // the LDS-load builtins exist for the device only
     if (d < C::kCodeDma) {
         const int inst = wave * C::kCodeDma + d;
-        const uint8_t* base = (inst * 8 < C::BO ? p.wq : p.xq) + ks * kRowBytes;
-        __builtin_amdgcn_global_load_lds((gbl_void_t*)(base + pl.code_off[d]),
-                                         (lds_void_t*)(buf + inst * 1024), 16, 0, 0);
+        const bool w = inst * 8 < C::BO;
+        const __amdgpu_buffer_rsrc_t r =
+            buffer_rsrc(w ? p.wq : p.xq, (w ? p.out : p.S) * 16 * p.k);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(buf + inst * 1024), 16,
+                                                 pl.code_off[d], (int)(ks * kRowBytes), 0, 0);
     } else {
         constexpr int kRowsPerInst = C::TS ? 32 : 64 * C::SB / kStageBlocks;
         const int j = d - C::kCodeDma;
         const int inst = wave * C::kScaleDma + j;
-        const uint8_t* base = (inst * kRowsPerInst < C::BO ? p.we : p.xe) +
-                              ks * (C::TS ? 256 : kStageBlocks);
-        __builtin_amdgcn_global_load_lds((gbl_void_t*)(base + pl.scale_off[j]),
-                                         (lds_void_t*)(buf + C::kCodeBytes + inst * 64 * C::SB),
-                                         C::SB, 0, 0);
+        const bool w = inst * kRowsPerInst < C::BO;
+        const int64_t rows = w ? p.out : p.S;
+        const int64_t bytes = C::TS ? ((rows + 31) / 32) * 32 * p.k : rows * p.k;
+        const __amdgpu_buffer_rsrc_t r = buffer_rsrc(w ? p.we : p.xe, bytes);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (lds_void_t*)(buf + C::kCodeBytes + inst * 64 * C::SB), C::SB, pl.scale_off[j],
+            (int)(ks * (C::TS ? 256 : kStageBlocks)), 0, 0);
     }
+#endif
 }
 
 template <class C>
@@ -545,7 +562,6 @@ gemm_pc_kernel(DmaArgs p, float* __restrict__ y, int64_t tiles_o, int64_t tiles_
     }
     store_tile<C>(acc, p, y, o0, s0, wrow0, xrow0, lane);
 }
-
 
 using CfgQ = DmaCfg<256, 128, 2, 2, 3, false>;    // 256 tiles for a 2048 x 4096 output
 using CfgQT = DmaCfg<256, 128, 2, 2, 3, true>;
