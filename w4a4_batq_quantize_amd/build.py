@@ -13,7 +13,7 @@ LIB = os.path.join(PKG, "libbatq.so")
 SOURCES = ["api.cpp", "quantize.hip", "gemm.hip"]
 
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-fvisibility=hidden",
     # bit-exact fp32 chains: no contraction into FMA beyond the explicit ones,
     # fp32 denormals kept
@@ -24,11 +24,7 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -39,7 +35,23 @@ def build(verbose: bool = False) -> str:
             if line.strip():
                 print(line, file=sys.stderr)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode})")
+        raise RuntimeError(f"hipcc failed ({res.returncode}): {' '.join(cmd[-4:])}")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object, then link the shared library; raises on any
+    compiler error."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, src + ".o")
+        _run([hipcc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC,
+              "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 
