@@ -29,6 +29,9 @@ def gpu_gemm(bq, xq, xe, wq, we):
 @pytest.mark.parametrize("S,N,out", [
     (1, 32, 1), (3, 96, 5), (17, 4096, 100), (129, 4192, 300), (200, 256, 257),
     (64, 12288, 64), (128, 4096, 128), (256, 1024, 384), (300, 640, 20),
+    # few tokens (weight-streaming path): ragged out, one and two token columns, K ranges
+    # shorter than the number of waves splitting K
+    (45, 2048, 77), (64, 256, 33), (1, 8192, 4100), (32, 512, 96), (33, 1536, 1),
 ])
 def test_gemm_random_operands_ragged(bq, orc, S, N, out):
     xq, xe = wl.random_mxfp4(S, N, seed=(7, S, N, out))
@@ -95,6 +98,7 @@ def test_linear_end_to_end(bq, orc, name):
 @pytest.mark.parametrize("S,N,out", [
     (1, 32, 1), (17, 4096, 100), (129, 4192, 300), (64, 12288, 64), (128, 4096, 128),
     (256, 1024, 384), (300, 2048, 520), (33, 256, 36),
+    (50, 1024, 130), (2, 512, 31), (63, 4096, 64),
 ])
 def test_gemm_random_operands_tiled_scales(bq, orc, S, N, out):
     import torch

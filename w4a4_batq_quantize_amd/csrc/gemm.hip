@@ -29,6 +29,8 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void gbl_void_t;
 
@@ -726,6 +728,183 @@ gemm_generic_kernel(DmaArgs p, int tiled, float* __restrict__ y, int64_t tiles_o
     }
 }
 
+// =======================================================================================
+// gemm_skinny_kernel<TN, TS>: few tokens (S <= 32 TN), weight-streaming bound
+// =======================================================================================
+//
+// With S <= 64 the output is one or two 32-token columns and the work is reading the
+// weights once (0.53 B per weight element) at HBM speed; a 256 x 128 tile grid would leave
+// most of the chip idle.  Here a workgroup owns 32 output rows and all S tokens, and its
+// kSplit waves split the K range: each wave streams its part of the 32 weight rows (and the
+// tokens' codes, L2-resident) straight into registers through buffer loads, one stage
+// (8 blocks) ahead, and multiplies with the 32x32x64 scaled MFMA.  The kSplit partial
+// tiles are then summed through LDS in wave order (a fixed order: results do not depend on
+// timing) and wave (b, g) stores register group g of token column b.
+// waves per workgroup: 16 for one token column (68 VGPRs), 8 for two (registers)
+template <int TN>
+struct SkinnySplit {
+    static constexpr int value = TN == 1 ? 16 : 8;
+};
+
+template <int TN>
+struct SkinnyStage {
+    v4u w[4];            // K-steps 0..3: 16 bytes of the lane's weight row
+    v4u x[TN][4];        // and of its token rows
+    uint2 ws;            // scale bytes (tiled: .x only; row-major: both words)
+    uint2 xs[TN];
+};
+
+template <int TN, bool TS>
+__device__ __forceinline__ void skinny_load(SkinnyStage<TN>& st, const __amdgpu_buffer_rsrc_t& rw,
+                                            const __amdgpu_buffer_rsrc_t& rx,
+                                            const __amdgpu_buffer_rsrc_t& rwe,
+                                            const __amdgpu_buffer_rsrc_t& rxe, uint32_t wrow,
+                                            const uint32_t (&xrow)[TN], uint32_t wse,
+                                            const uint32_t (&xse)[TN], int64_t k, int ks,
+                                            int lg)
+{
+    const uint32_t rb = 16u * (uint32_t)k;                     // bytes per code row
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const uint32_t c = (uint32_t)ks * kRowBytes + 16u * (2 * t + lg);
+        st.w[t] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(wrow * rb + c), 0, 0);
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+            st.x[b][t] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(xrow[b] * rb + c), 0, 0);
+    }
+    if constexpr (TS) {
+        const uint32_t so = (uint32_t)ks * 256u;
+        st.ws.x = __builtin_amdgcn_raw_buffer_load_b32(rwe, (int)(wse + so), 0, 0);
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+            st.xs[b].x = __builtin_amdgcn_raw_buffer_load_b32(rxe, (int)(xse[b] + so), 0, 0);
+    } else {
+        const uint32_t so = (uint32_t)ks * kStageBlocks;
+        const v2u wv = __builtin_amdgcn_raw_buffer_load_b64(rwe, (int)(wse + so), 0, 0);
+        st.ws = make_uint2(wv.x, wv.y);
+#pragma unroll
+        for (int b = 0; b < TN; ++b) {
+            const v2u xv = __builtin_amdgcn_raw_buffer_load_b64(rxe, (int)(xse[b] + so), 0, 0);
+            st.xs[b] = make_uint2(xv.x, xv.y);
+        }
+    }
+}
+
+template <int TN, bool TS, int T>
+__device__ __forceinline__ void skinny_step(v16f (&acc)[TN], const SkinnyStage<TN>& st, int lg)
+{
+    // tiled: byte T of the one dword; row-major: byte 2(T%2) of word T/2, pre-shifted so the
+    // lane's half (block 2T + lane/32) sits in that byte
+    constexpr int kSel = TS ? T : 2 * (T & 1);
+    const uint32_t wsc = TS ? st.ws.x : (((T >> 1) ? st.ws.y : st.ws.x) >> (8 * lg));
+    const v8i av = {(int)st.w[T].x, (int)st.w[T].y, (int)st.w[T].z, (int)st.w[T].w, 0, 0, 0, 0};
+#pragma unroll
+    for (int b = 0; b < TN; ++b) {
+        const uint32_t xsc = TS ? st.xs[b].x : (((T >> 1) ? st.xs[b].y : st.xs[b].x) >> (8 * lg));
+        const v8i bv = {(int)st.x[b][T].x, (int)st.x[b][T].y, (int)st.x[b][T].z,
+                        (int)st.x[b][T].w, 0, 0, 0, 0};
+        acc[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            av, bv, acc[b], kFmtE2M1, kFmtE2M1, kSel, (int)wsc, kSel, (int)xsc);
+    }
+}
+
+template <int TN, bool TS>
+__device__ __forceinline__ void skinny_stage(v16f (&acc)[TN], const SkinnyStage<TN>& st, int lg)
+{
+    skinny_step<TN, TS, 0>(acc, st, lg);
+    skinny_step<TN, TS, 1>(acc, st, lg);
+    skinny_step<TN, TS, 2>(acc, st, lg);
+    skinny_step<TN, TS, 3>(acc, st, lg);
+}
+
+template <int TN, bool TS>
+__global__ void __launch_bounds__(64 * SkinnySplit<TN>::value)
+gemm_skinny_kernel(DmaArgs p, float* __restrict__ y)
+{
+    constexpr int kSplit = SkinnySplit<TN>::value;
+    static_assert(kSplit >= 4 * TN, "one storing wave per (token column, register group)");
+    __shared__ float red[kSplit][TN][16][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lr = lane & 31, lg = lane >> 5;
+    const int64_t o0 = (int64_t)blockIdx.x * 32;
+    const int64_t k = p.k;
+    const int nst = (int)(k / kStageBlocks);
+    const int s0 = (int)((int64_t)wave * nst / kSplit), s1 = (int)((int64_t)(wave + 1) * nst / kSplit);
+
+    // operand rows of this lane, clamped to the last row (their products are never stored)
+    const uint32_t wrow = (uint32_t)(o0 + lr < p.out ? o0 + lr : p.out - 1);
+    uint32_t xrow[TN];
+#pragma unroll
+    for (int b = 0; b < TN; ++b) xrow[b] = (uint32_t)(32 * b + lr < p.S ? 32 * b + lr : p.S - 1);
+    const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(p.wq, p.out * 16 * k);
+    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(p.xq, p.S * 16 * k);
+    const int64_t k8 = k / 8;
+    const __amdgpu_buffer_rsrc_t rwe =
+        buffer_rsrc(p.we, TS ? ((p.out + 31) / 32) * 256 * k8 : p.out * k);
+    const __amdgpu_buffer_rsrc_t rxe =
+        buffer_rsrc(p.xe, TS ? ((p.S + 31) / 32) * 256 * k8 : p.S * k);
+    // scale offsets of stage 0: tiled (panel unit, row, half) / row-major (row start)
+    const uint32_t wse = TS ? (uint32_t)((wrow >> 5) * k8 * 256 + (wrow & 31) * 8 + 4 * lg)
+                            : wrow * (uint32_t)k;
+    uint32_t xse[TN];
+#pragma unroll
+    for (int b = 0; b < TN; ++b)
+        xse[b] = TS ? (uint32_t)((xrow[b] >> 5) * k8 * 256 + (xrow[b] & 31) * 8 + 4 * lg)
+                    : xrow[b] * (uint32_t)k;
+
+    v16f acc[TN];
+#pragma unroll
+    for (int b = 0; b < TN; ++b) acc[b] = v16f{};
+    if (s0 < s1) {
+        SkinnyStage<TN> cur, nxt;
+        skinny_load<TN, TS>(cur, rw, rx, rwe, rxe, wrow, xrow, wse, xse, k, s0, lg);
+        int s = s0;
+        for (;;) {
+            const bool more = s + 1 < s1;
+            skinny_load<TN, TS>(nxt, rw, rx, rwe, rxe, wrow, xrow, wse, xse, k,
+                                more ? s + 1 : s, lg);
+            skinny_stage<TN, TS>(acc, cur, lg);
+            if (!more) break;
+            const bool more2 = s + 2 < s1;
+            skinny_load<TN, TS>(cur, rw, rx, rwe, rxe, wrow, xrow, wse, xse, k,
+                                more2 ? s + 2 : s + 1, lg);
+            skinny_stage<TN, TS>(acc, nxt, lg);
+            if (!more2) break;
+            s += 2;
+        }
+    }
+    // sum the kSplit partial tiles in wave order
+#pragma unroll
+    for (int b = 0; b < TN; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[wave][b][r][lane] = acc[b][r];
+    __syncthreads();
+    if (wave < 4 * TN) {
+        const int b = wave / 4, g = wave % 4;
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float t = red[0][b][4 * g + i][lane];
+#pragma unroll
+            for (int w = 1; w < kSplit; ++w) t += red[w][b][4 * g + i][lane];
+            v[i] = t;
+        }
+        const int64_t srow = 32 * b + lr;
+        const int64_t o = o0 + 8 * g + 4 * lg;
+        if (srow < p.S) {
+            float* dst = y + srow * p.out + o;
+            if ((p.out & 3) == 0 && o + 3 < p.out) {
+                *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (o + i < p.out) dst[i] = v[i];
+            }
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq,
@@ -738,6 +917,26 @@ hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq,
                         (reinterpret_cast<uintptr_t>(xe) % salign) == 0 &&
                         (reinterpret_cast<uintptr_t>(we) % salign) == 0 &&
                         S * 16 * p.k < (1LL << 32) && out * 16 * p.k < (1LL << 32);
+    if (dma_ok && S <= 64) {
+        // few tokens: weight streaming, K split across the waves of a 32-row workgroup
+        const int64_t tiles_o = (out + 31) / 32;
+        if (tiles_o > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+        const dim3 grid((unsigned)tiles_o);
+        if (S <= 32) {
+            const dim3 block(64 * SkinnySplit<1>::value);
+            if (tiled_scales)
+                hipLaunchKernelGGL((gemm_skinny_kernel<1, true>), grid, block, 0, stream, p, y);
+            else
+                hipLaunchKernelGGL((gemm_skinny_kernel<1, false>), grid, block, 0, stream, p, y);
+        } else {
+            const dim3 block(64 * SkinnySplit<2>::value);
+            if (tiled_scales)
+                hipLaunchKernelGGL((gemm_skinny_kernel<2, true>), grid, block, 0, stream, p, y);
+            else
+                hipLaunchKernelGGL((gemm_skinny_kernel<2, false>), grid, block, 0, stream, p, y);
+        }
+        return hipGetLastError();
+    }
     if (dma_ok) {
         const int64_t tiles_o = (out + CfgQ::BO - 1) / CfgQ::BO;
         const int64_t tiles_s = (S + CfgQ::BS - 1) / CfgQ::BS;
