@@ -375,14 +375,32 @@ __device__ __forceinline__ void dma_pipeline_step(v16f (&acc)[C::TM][C::TN], uin
 template <class C>
 __device__ __forceinline__ void store_tile(const v16f (&acc)[C::TM][C::TN], const DmaArgs& p,
                                            float* __restrict__ y, int64_t o0, int64_t s0,
-                                           int wrow0, int xrow0, int lane)
+                                           int wrow0, int xrow0, int lane, int nt_store = 0)
 {
     const int lr = lane & 31, lg = lane >> 5;
     const bool interior = (p.out & 3) == 0 && o0 + C::BO <= p.out && s0 + C::BS <= p.S;
     if (interior) {
         // whole tile inside the output: unconditional 16-byte stores, one 32x32 tile at a
-        // time (keeps the accumulator-to-VGPR copies short-lived)
+        // time (keeps the accumulator-to-VGPR copies short-lived).  Non-temporal stores when
+        // the launch's data outgrows the Infinity Cache, so the output stream does not evict
+        // the operands other tiles still read.
         float* base = y + (s0 + xrow0 + lr) * p.out + o0 + wrow0 + 4 * lg;
+        if (nt_store) {
+#pragma unroll
+            for (int b = 0; b < C::TN; ++b) {
+#pragma unroll
+                for (int a = 0; a < C::TM; ++a) {
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        __builtin_nontemporal_store(
+                            v4f{acc[a][b][4 * g], acc[a][b][4 * g + 1], acc[a][b][4 * g + 2],
+                                acc[a][b][4 * g + 3]},
+                            reinterpret_cast<v4f*>(base + 32 * b * p.out + 32 * a + 8 * g));
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int b = 0; b < C::TN; ++b) {
 #pragma unroll
@@ -487,7 +505,7 @@ gemm_dma_kernel(DmaArgs p, float* __restrict__ y, int64_t tiles_o, int64_t tiles
 // drain their LDS reads, lgkmcnt(0), before every barrier).
 template <class C>
 __global__ void __launch_bounds__(2 * C::kThreads)
-gemm_pc_kernel(DmaArgs p, float* __restrict__ y, int64_t tiles_o, int64_t tiles_s)
+gemm_pc_kernel(DmaArgs p, float* __restrict__ y, int64_t tiles_o, int64_t tiles_s, int nt_store)
 {
     constexpr int NB = C::NB;
     __shared__ __attribute__((aligned(16))) uint8_t lds0[C::kBufBytes];
@@ -562,7 +580,7 @@ gemm_pc_kernel(DmaArgs p, float* __restrict__ y, int64_t tiles_o, int64_t tiles_
                 dma_mfma_stage<C>(acc, bufs[i], wrow0, xrow0, lane, none);
             }
     }
-    store_tile<C>(acc, p, y, o0, s0, wrow0, xrow0, lane);
+    store_tile<C>(acc, p, y, o0, s0, wrow0, xrow0, lane, nt_store);
 }
 
 using CfgQ = DmaCfg<256, 128, 2, 2, 3, false>;    // 256 tiles for a 2048 x 4096 output
@@ -942,9 +960,15 @@ hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq,
         const int64_t tiles_s = (S + CfgQ::BS - 1) / CfgQ::BS;
         if (tiles_o * tiles_s > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
         const dim3 grid((unsigned)(tiles_o * tiles_s));
+        // output stores bypass the Infinity Cache (256 MB) when the operands alone take more
+        // than a quarter of it: they are re-read by later tile rounds and the output stream
+        // would evict them (measured: S=16384, N=12288 -> 4096, 134 MB of operands, 12%
+        // faster; 45-58 MB of operands, as for gate_up or N=4096, are slower that way)
+        constexpr int64_t kOperandBytesForNt = (int64_t)64 << 20;
+        const int nt = (S + out) * (N / 2 + N / 32) > kOperandBytesForNt ? 1 : 0;
         if (tiled_scales)
             hipLaunchKernelGGL(gemm_pc_kernel<CfgQT>, grid, dim3(2 * CfgQT::kThreads), 0,
-                               stream, p, y, tiles_o, tiles_s);
+                               stream, p, y, tiles_o, tiles_s, nt);
         else
             hipLaunchKernelGGL(gemm_dma_kernel<CfgQ>, grid, dim3(CfgQ::kThreads), 0, stream,
                                p, y, tiles_o, tiles_s);
