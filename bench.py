@@ -106,31 +106,15 @@ def cpu_baseline(L, seconds):
     }
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="q_proj")
-    ap.add_argument("--rotate-bytes", type=float, default=2.0e9,
-                    help="total bytes of the rotated buffer sets")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain device copy of known size (for counter scaling)")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs the path on one GPU only; --gpus must be 1",
-              file=sys.stderr)
-        sys.exit(2)
-
+def measure(name, args):
+    """Time one layer configuration; returns (record, layer)."""
     import numpy as np
     import torch
 
     import w4a4_batq_quantize_amd as bq
     import workloads as wl
 
-    L = wl.make_layer(args.config)
+    L = wl.make_layer(name)
     S, N, out = L.cfg.S, L.cfg.N, L.cfg.out
     k = N // 32
     dev = torch.device("cuda:0")
@@ -147,7 +131,7 @@ def main():
     x0 = torch.from_numpy(L.x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
 
     per_set = S * N * 2 + S * (N // 2 + k) + out * (N // 2 + k) + 4 * S * out
-    R = max(2, math.ceil(args.rotate_bytes / per_set))
+    R = min(1024, max(2, math.ceil(args.rotate_bytes / per_set)))
     xs = [x0.clone() for _ in range(R)]
     wqs = [wq0.clone() for _ in range(R)]
     wes = [we0.clone() for _ in range(R)]
@@ -227,10 +211,16 @@ def main():
                "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": tr1,
                "avg_us": round(t_k1 * 1e6, 3), "algorithmic_bytes": b1}
-    roof_k2 = {"kernel": "gemm_pc_kernel (MXFP4 scaled MFMA)",
-               "bound": "mfma" if k2_roof >= FP4_PEAK_TFLOPS else "hbm",
-               "achieved": round(tflops, 1), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
-               "frac": round(tflops / FP4_PEAK_TFLOPS, 4), "traffic": tr2,
+    hbm_bound = k2_roof < FP4_PEAK_TFLOPS
+    k2_gbs = k2_bytes(S, N, out) / t_k2 / 1e9
+    roof_k2 = {"kernel": ("gemm_skinny_kernel" if S <= 64 else "gemm_pc_kernel")
+                         + " (MXFP4 scaled MFMA)",
+               "bound": "hbm" if hbm_bound else "mfma",
+               "achieved": round(k2_gbs if hbm_bound else tflops, 1),
+               "peak": HBM_PEAK_GBS if hbm_bound else FP4_PEAK_TFLOPS,
+               "unit": "GB/s" if hbm_bound else "TFLOP/s",
+               "frac": round(k2_gbs / HBM_PEAK_GBS if hbm_bound else tflops / FP4_PEAK_TFLOPS, 4),
+               "traffic": tr2, "tflops": round(tflops, 1),
                "algorithmic_bytes": k2_bytes(S, N, out),
                "avg_us": round(t_k2 * 1e6, 3), "algorithmic_flops": k2_flops(S, N, out),
                "roofline_tflops": round(k2_roof, 1), "frac_of_roofline": round(tflops / k2_roof, 4)}
@@ -262,6 +252,36 @@ def main():
         "roofline": dominant,
         "roofline_kernels": {"quantize": roof_k1, "gemm": roof_k2},
     }
+    return rec, L
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="q_proj")
+    ap.add_argument("--rotate-bytes", type=float, default=2.0e9,
+                    help="total bytes of the rotated buffer sets")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain device copy of known size (for counter scaling)")
+    ap.add_argument("--all", action="store_true",
+                    help="measure every layer configuration, one JSON line each (no CPU baseline)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs the path on one GPU only; --gpus must be 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    if args.all:
+        import workloads as wl
+        for name in wl.CONFIGS:
+            rec, _ = measure(name, args)
+            print(json.dumps(rec), flush=True)
+        return
+    rec, L = measure(args.config, args)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(L, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
