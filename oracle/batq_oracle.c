@@ -18,7 +18,10 @@
  *     rounding to E2M1 (thelatestinai listing, Figure 2 caption and the DuQuant++ abstract
  *     on that page; ARCQuant blog, "理论保证" on E8M0 being exponent-only);
  *   - the W4A4 product with weights transformed offline by P^-1 (gist.science section 2D;
- *     thelatestinai listing, Figure 3).
+ *     thelatestinai listing, Figure 3);
+ *   - the W4A8 setting: the same transform and clip with the activations encoded as MXFP8
+ *     (E4M3 elements, one E8M0 scale per 32) against the same MXFP4 weights (gist.science
+ *     section 4 and the daily-arxiv results bullet, W4A8KV16).
  *
  * Where the pages leave a step open, the plainest reading is taken (listed with reasons in
  * the design notes): fp32 arithmetic for the transform with sequential fused multiply-add
@@ -102,6 +105,55 @@ static uint8_t e8m0_scale(float amax)
     return (uint8_t)(x + 127);
 }
 
+/* E4M3 (OCP FP8, the variant without infinities): 4 exponent bits with bias 7, 3 mantissa
+ * bits; magnitude code c = 8E + m gives m/8 * 2^-6 for E = 0 (subnormal) and
+ * (1 + m/8) * 2^(E-7) for E = 1..15, except that E = 15, m = 7 is NaN, so the finite
+ * magnitudes are the 127 codes 0..126 and the largest is 448. */
+static double e4m3_mag(int c)
+{
+    int E = c >> 3, m = c & 7;
+    return E == 0 ? ldexp(m / 8.0, -6) : ldexp(1.0 + m / 8.0, E - 7);
+}
+
+/* Round v to the nearest E4M3 value; on a tie take the even magnitude code (ties to even on
+ * the 3-bit mantissa); magnitudes beyond 448 take 448 (the MX conversion saturates); the
+ * sign bit is copied from v.  A plain search over the 127 finite magnitudes: for |v| <= 448
+ * every distance below is exact in binary64, so ties are seen exactly. */
+static uint8_t e4m3_round(double v)
+{
+    double a = fabs(v);
+    if (a > 448.0) a = 448.0;
+    int best = 0;
+    double best_d = a;
+    for (int c = 1; c <= 126; ++c) {
+        double d = fabs(a - e4m3_mag(c));
+        if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return (uint8_t)((signbit(v) ? 0x80 : 0x00) | best);
+}
+
+static double e4m3_value(uint8_t code)
+{
+    double m = e4m3_mag(code & 0x7F);
+    return (code & 0x80) ? -m : m;
+}
+
+/* MXFP8 scale byte: OCP MX rule with E4M3's largest exponent (8): floor(log2(amax)) - 8,
+ * clamped to the E8M0 range, bias 127; an all-zero block takes byte 0. */
+static uint8_t e8m0_scale_fp8(float amax)
+{
+    if (amax == 0.0f) return 0;
+    int ex;
+    (void)frexpf(amax, &ex);
+    int x = (ex - 1) - 8;
+    if (x < -127) x = -127;
+    if (x > 127) x = 127;
+    return (uint8_t)(x + 127);
+}
+
 /* ------------------------------------------------------------------------------------ */
 /* GPK block transform                                                                   */
 /* ------------------------------------------------------------------------------------ */
@@ -176,6 +228,31 @@ static void clip_quantize_block(const float y[32], int clip, float r_min, float 
         if (yc32) yc32[j] = yc[j];
     }
     for (int b = 0; b < 16; ++b) codes[b] = (uint8_t)(code[2 * b] | (code[2 * b + 1] << 4));
+    *scale = e;
+}
+
+/* Clip (as above) + MXFP8 quantisation of one transformed block: 32 E4M3 code bytes and
+ * the scale byte. */
+static void clip_quantize_block_fp8(const float y[32], float r_min, float r_max,
+                                    uint8_t codes[32], uint8_t* scale)
+{
+    float m = y[0], M = y[0];
+    for (int j = 1; j < 32; ++j) {
+        if (y[j] < m) m = y[j];
+        if (y[j] > M) M = y[j];
+    }
+    float lo = r_min * m;
+    float hi = r_max * M;
+    float yc[32];
+    float amax = 0.0f;
+    for (int j = 0; j < 32; ++j) {
+        float t = y[j] < lo ? lo : y[j];
+        yc[j] = t > hi ? hi : t;
+        if (fabsf(yc[j]) > amax) amax = fabsf(yc[j]);
+    }
+    uint8_t e = e8m0_scale_fp8(amax);
+    double s = ldexp(1.0, (int)e - 127);
+    for (int j = 0; j < 32; ++j) codes[j] = e4m3_round((double)yc[j] / s);
     *scale = e;
 }
 
@@ -316,6 +393,90 @@ void orc_gemm_w4a4(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq, cons
                 uint8_t xc = (n & 1) ? (xb >> 4) : (xb & 0xF);
                 uint8_t wc = (n & 1) ? (wb >> 4) : (wb & 0xF);
                 double xv = ldexp(e2m1_value(xc), (int)xe[s * k + n / 32] - 127);
+                double wv = ldexp(e2m1_value(wc), (int)we[o * k + n / 32] - 127);
+                acc += xv * wv;
+                abs_acc += fabs(xv * wv);
+            }
+            y[a * ncols + b] = acc;
+            t[a * ncols + b] = abs_acc;
+        }
+    }
+}
+
+/* W4A8 activation side: bf16 X [rows, ldx] -> transform -> clip -> MXFP8.
+ * q8 [rows, N] (one E4M3 code per byte), e [rows, N/32]. */
+void orc_quantize_act_fp8(const uint16_t* x, int64_t rows, int64_t N, int64_t ldx,
+                          const float* A, const float* B, const float* r_min,
+                          const float* r_max, uint8_t* q8, uint8_t* e, int nthreads)
+{
+    int64_t k = N / 32;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(static)
+    for (int64_t s = 0; s < rows; ++s) {
+        for (int64_t i = 0; i < k; ++i) {
+            float xb[32], y[32];
+            for (int j = 0; j < 32; ++j) xb[j] = bf16_to_float(x[s * ldx + 32 * i + j]);
+            gpk_transform_block(xb, A, B + 16 * i, y);
+            clip_quantize_block_fp8(y, r_min[i], r_max[i], q8 + s * N + 32 * i, e + s * k + i);
+        }
+    }
+}
+
+/* Clip + MXFP8 of already-transformed fp32 rows (for the reduction pin). */
+void orc_clip_quantize_fp8_f32(const float* y, int64_t rows, int64_t N, const float* r_min,
+                               const float* r_max, uint8_t* q8, uint8_t* e)
+{
+    int64_t k = N / 32;
+    for (int64_t s = 0; s < rows; ++s)
+        for (int64_t i = 0; i < k; ++i)
+            clip_quantize_block_fp8(y + s * N + 32 * i, r_min[i], r_max[i], q8 + s * N + 32 * i,
+                                    e + s * k + i);
+}
+
+void orc_e4m3_round_f32(const float* v, int64_t n, uint8_t* code)
+{
+    for (int64_t t = 0; t < n; ++t) code[t] = e4m3_round((double)v[t]);
+}
+
+void orc_e4m3_value(const uint8_t* code, int64_t n, double* v)
+{
+    for (int64_t t = 0; t < n; ++t) v[t] = e4m3_value(code[t]);
+}
+
+void orc_e8m0_scale_fp8_f32(const float* amax, int64_t n, uint8_t* e)
+{
+    for (int64_t t = 0; t < n; ++t) e[t] = e8m0_scale_fp8(amax[t]);
+}
+
+/* Dequantise MXFP8 rows to fp64. */
+void orc_dequant_fp8(const uint8_t* q8, const uint8_t* e, int64_t rows, int64_t N, double* out)
+{
+    int64_t k = N / 32;
+    for (int64_t s = 0; s < rows; ++s)
+        for (int64_t n = 0; n < N; ++n)
+            out[s * N + n] = ldexp(e4m3_value(q8[s * N + n]), (int)e[s * k + n / 32] - 127);
+}
+
+/* W4A8 GEMM reference in fp64: MXFP8 activations [S, N] x MXFP4 weights [out, N]; same
+ * conventions as orc_gemm_w4a4. */
+void orc_gemm_w4a8(const uint8_t* xq8, const uint8_t* xe, const uint8_t* wq, const uint8_t* we,
+                   int64_t S, int64_t N, int64_t out, const int64_t* rows, int64_t nrows,
+                   const int64_t* cols, int64_t ncols, double* y, double* t, int nthreads)
+{
+    int64_t k = N / 32;
+    if (!rows) nrows = S;
+    if (!cols) ncols = out;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t a = 0; a < nrows; ++a) {
+        int64_t s = rows ? rows[a] : a;
+        for (int64_t b = 0; b < ncols; ++b) {
+            int64_t o = cols ? cols[b] : b;
+            double acc = 0.0, abs_acc = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                uint8_t wb = wq[o * (N / 2) + n / 2];
+                uint8_t wc = (n & 1) ? (wb >> 4) : (wb & 0xF);
+                double xv = ldexp(e4m3_value(xq8[s * N + n]), (int)xe[s * k + n / 32] - 127);
                 double wv = ldexp(e2m1_value(wc), (int)we[o * k + n / 32] - 127);
                 acc += xv * wv;
                 abs_acc += fabs(xv * wv);

@@ -72,6 +72,13 @@ def lib() -> ctypes.CDLL:
     L.orc_e8m0_scale_f32.argtypes = [P, I64, P]
     L.orc_dequant.argtypes = [P, P, I64, I64, P]
     L.orc_gemm_w4a4.argtypes = [P, P, P, P, I64, I64, I64, P, I64, P, I64, P, P, I32]
+    L.orc_quantize_act_fp8.argtypes = [P, I64, I64, I64, P, P, P, P, P, P, I32]
+    L.orc_clip_quantize_fp8_f32.argtypes = [P, I64, I64, P, P, P, P]
+    L.orc_e4m3_round_f32.argtypes = [P, I64, P]
+    L.orc_e4m3_value.argtypes = [P, I64, P]
+    L.orc_e8m0_scale_fp8_f32.argtypes = [P, I64, P]
+    L.orc_dequant_fp8.argtypes = [P, P, I64, I64, P]
+    L.orc_gemm_w4a8.argtypes = [P, P, P, P, I64, I64, I64, P, I64, P, I64, P, P, I32]
     L.orc_max_threads.restype = I32
     _lib = L
     return L
@@ -282,5 +289,85 @@ def gemm(xq, xe, wq, we, rows=None, cols=None, nthreads=1):
     y = np.zeros((nr, nc), dtype=np.float64)
     t = np.zeros((nr, nc), dtype=np.float64)
     lib().orc_gemm_w4a4(_p(xq), _p(xe), _p(wq), _p(we), S, N, out, _p(r), nr, _p(c), nc,
+                        _p(y), _p(t), nthreads)
+    return y, t
+
+
+# ----------------------------------------------------------------------------------------
+# W4A8: MXFP8 (E4M3) activations against the same MXFP4 weights
+# ----------------------------------------------------------------------------------------
+
+def quantize_act_fp8(x_bits, A, B, r_min, r_max, nthreads=1):
+    """bf16 activations [S, N] -> (E4M3 codes [S, N], scales [S, N/32])."""
+    x_bits = np.ascontiguousarray(np.asarray(x_bits))
+    assert x_bits.dtype == np.uint16 and x_bits.ndim == 2
+    S = x_bits.shape[0]
+    B = _c(B, np.float32).reshape(-1, 16)
+    k = B.shape[0]
+    N = 32 * k
+    ldx = x_bits.shape[1]
+    assert ldx >= N
+    q = np.zeros((S, N), dtype=np.uint8)
+    e = np.zeros((S, k), dtype=np.uint8)
+    lib().orc_quantize_act_fp8(_p(x_bits), S, N, ldx, _p(_c(A, np.float32).reshape(64)), _p(B),
+                               _p(_c(r_min, np.float32)), _p(_c(r_max, np.float32)), _p(q),
+                               _p(e), nthreads)
+    return q, e
+
+
+def clip_quantize_fp8_f32(y, r_min, r_max):
+    """Clip + MXFP8 of already-transformed fp32 rows."""
+    y = _c(y, np.float32)
+    rows, N = y.shape
+    q = np.zeros((rows, N), dtype=np.uint8)
+    e = np.zeros((rows, N // 32), dtype=np.uint8)
+    lib().orc_clip_quantize_fp8_f32(_p(y), rows, N, _p(_c(r_min, np.float32)),
+                                    _p(_c(r_max, np.float32)), _p(q), _p(e))
+    return q, e
+
+
+def e4m3_round(v) -> np.ndarray:
+    v = _c(v, np.float32)
+    out = np.zeros(v.shape, dtype=np.uint8)
+    lib().orc_e4m3_round_f32(_p(v), v.size, _p(out))
+    return out
+
+
+def e4m3_value(code) -> np.ndarray:
+    c = _c(code, np.uint8)
+    out = np.zeros(c.shape, dtype=np.float64)
+    lib().orc_e4m3_value(_p(c), c.size, _p(out))
+    return out
+
+
+def e8m0_scale_fp8(amax) -> np.ndarray:
+    a = _c(amax, np.float32)
+    out = np.zeros(a.shape, dtype=np.uint8)
+    lib().orc_e8m0_scale_fp8_f32(_p(a), a.size, _p(out))
+    return out
+
+
+def dequant_fp8(q8, e) -> np.ndarray:
+    q8 = _c(q8, np.uint8)
+    e = _c(e, np.uint8)
+    rows, N = q8.shape
+    out = np.zeros((rows, N), dtype=np.float64)
+    lib().orc_dequant_fp8(_p(q8), _p(e), rows, N, _p(out))
+    return out
+
+
+def gemm_w4a8(xq8, xe, wq, we, rows=None, cols=None, nthreads=1):
+    """fp64 reference of the W4A8 product (MXFP8 activations x MXFP4 weights)."""
+    xq8, xe, wq, we = (_c(a, np.uint8) for a in (xq8, xe, wq, we))
+    S, N = xq8.shape
+    out = wq.shape[0]
+    assert wq.shape[1] * 2 == N and xe.shape == (S, N // 32) and we.shape == (out, N // 32)
+    r = None if rows is None else _c(rows, np.int64)
+    c = None if cols is None else _c(cols, np.int64)
+    nr = S if r is None else r.size
+    nc = out if c is None else c.size
+    y = np.zeros((nr, nc), dtype=np.float64)
+    t = np.zeros((nr, nc), dtype=np.float64)
+    lib().orc_gemm_w4a8(_p(xq8), _p(xe), _p(wq), _p(we), S, N, out, _p(r), nr, _p(c), nc,
                         _p(y), _p(t), nthreads)
     return y, t
