@@ -134,6 +134,46 @@ batq_status batq_gemm_w4a4(const uint8_t* xq, const uint8_t* xe,
                            int64_t S, int64_t N, int64_t out, float* y, void* stream);
 
 /*
+ * W4A8 activation side: the same transform and clip as batq_quantize_act, with each
+ * clipped block encoded as MXFP8 instead of MXFP4 (the W4A8 setting of the gist.science
+ * summary, section 4, and of the daily-arxiv summary, results bullet, W4A8KV16): 32 OCP
+ * E4M3 elements (the FP8 variant without infinities, largest magnitude 448) and one E8M0
+ * scale.  The scale exponent is floor(log2(amax)) - 8 (E4M3's largest exponent is 8),
+ * clamped below at 0; each element is y / 2^(e-127) rounded to the nearest E4M3 value, ties
+ * to the even code, magnitudes beyond 448 saturating to 448.  An all-zero block gets scale 0
+ * and zero codes.
+ *
+ *   x, S, N, ldx, A, B, r_min, r_max, stream: as batq_quantize_act
+ *   q8  dev  out: codes uint8 [S, N] (one E4M3 byte per element), 16-byte aligned
+ *   e   dev  out: scales in `e_layout`, as batq_quantize_act
+ * Same error behaviour as batq_quantize_act.  Does not allocate or synchronise.
+ */
+batq_status batq_quantize_act_mxfp8(const uint16_t* x, int64_t S, int64_t N, int64_t ldx,
+                                    const float* A, const float* B,
+                                    const float* r_min, const float* r_max,
+                                    uint8_t* q8, uint8_t* e, batq_scale_layout e_layout,
+                                    void* stream);
+
+/*
+ * W4A8 GEMM: y[s][o] = sum_n dq8(xq8)[s][n] * dq(wq)[o][n] with dq8(code, e) =
+ * e4m3(code) * 2^(e-127) and dq as in batq_gemm_w4a4 (the W4A8 setting of the gist.science
+ * summary, section 4), on gfx950 scaled MFMA (E2M1 weights x E4M3 activations) with fp32
+ * accumulation.  Each 32-element block product is exact; sums across blocks round in fp32.
+ *
+ *   xq8, xe  dev  activation codes [S, N] (16-byte aligned) and scales (4-byte aligned)
+ *   wq, we   dev  weight codes [out, N/2] (16-byte aligned) and scales (4-byte aligned),
+ *                 as batq_prepare_weight writes them
+ *   layout   the layout of both xe and we
+ *   S, out >= 0;  N >= 0, N % 256 == 0 (BATQ_ERR_UNSUPPORTED otherwise, and when S*N or
+ *            out*N/2 reaches 2^32)
+ *   y        dev  out: fp32 [S, out], 16-byte aligned, overwritten
+ * S == 0 or out == 0 is a no-op; N == 0 writes zeros.  Does not allocate or synchronise.
+ */
+batq_status batq_gemm_w4a8(const uint8_t* xq8, const uint8_t* xe,
+                           const uint8_t* wq, const uint8_t* we, batq_scale_layout layout,
+                           int64_t S, int64_t N, int64_t out, float* y, void* stream);
+
+/*
  * Host: clip ratios r[i] = fp32(1 / (1 + exp(-alpha[i]))) evaluated in binary64 and rounded
  * once (daily-arxiv summary, clipping bullet: the sigmoid keeps each ratio in (0, 1);
  * gist.science summary, section 2C).  The logits are per block, shared by all tokens.

@@ -33,7 +33,8 @@ def declared_entry_points():
 def test_library_exports_every_declared_entry_point(bq):
     names = declared_entry_points()
     assert names == sorted(["batq_quantize_act", "batq_prepare_weight", "batq_gemm_w4a4",
-                            "batq_clip_ratios", "batq_weight_factors", "batq_status_string"])
+                            "batq_clip_ratios", "batq_weight_factors", "batq_status_string",
+                            "batq_quantize_act_mxfp8", "batq_gemm_w4a8"])
     L = ctypes.CDLL(bq.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -82,6 +83,38 @@ def test_gemm_argument_errors(bq):
     assert g(D, D, D + 1, D, 4, 64, 8, D) == ALIGN
     assert g(D, D, D, D, 4, 64, 8, D + 4) == ALIGN
     assert g(D, D, D, D, 1 << 62, 64, 8, D) == SHAPE
+
+
+def test_quantize_act_mxfp8_argument_errors(bq):
+    q = bq.quantize_act_mxfp8_raw
+    assert q(D, -1, 64, 64, D, D, D, D, D, D) == SHAPE
+    assert q(D, 4, 48, 64, D, D, D, D, D, D) == SHAPE
+    assert q(D, 4, 64, 32, D, D, D, D, D, D) == SHAPE
+    assert q(0, 0, 64, 64, 0, 0, 0, 0, 0, 0) == OK
+    assert q(0, 5, 0, 0, 0, 0, 0, 0, 0, 0) == OK
+    for i in (0, 4, 5, 6, 7, 8, 9):
+        args = [D, 4, 64, 64, D, D, D, D, D, D]
+        args[i] = 0
+        assert q(*args) == NULL, i
+    assert q(D + 2, 4, 64, 64, D, D, D, D, D, D) == ALIGN
+    assert q(D, 4, 64, 64, D, D, D, D, D + 8, D) == ALIGN        # FP8 codes
+    assert q(D, 4, 64, 64, D, D, D, D, D, D, layout=7) == UNSUPPORTED
+
+
+def test_gemm_w4a8_argument_errors(bq):
+    g = bq.gemm_w4a8_raw
+    assert g(D, D, D, D, -1, 256, 8, D) == SHAPE
+    assert g(D, D, D, D, 4, 40, 8, D) == SHAPE
+    assert g(0, 0, 0, 0, 0, 256, 8, 0) == OK
+    assert g(0, 0, 0, 0, 4, 256, 0, 0) == OK
+    assert g(0, D, D, D, 4, 256, 8, D) == NULL
+    assert g(D, D, D, D, 4, 256, 8, 0) == NULL
+    assert g(D, D, D + 1, D, 4, 256, 8, D) == ALIGN
+    assert g(D, D + 2, D, D, 4, 256, 8, D) == ALIGN              # activation scales
+    assert g(D, D, D, D, 4, 256, 8, D + 4) == ALIGN
+    assert g(D, D, D, D, 4, 96, 8, D) == UNSUPPORTED               # N % 256
+    assert g(D, D, D, D, 1 << 24, 256, 8, D) == UNSUPPORTED        # S * N >= 2^32
+    assert g(D, D, D, D, 1 << 62, 256, 8, D) == SHAPE
 
 
 def test_prepare_weight_argument_errors_and_singular_factors(bq):

@@ -12,11 +12,16 @@ from ._binding import (  # noqa: F401
     clip_ratios,
     gemm_w4a4,
     gemm_w4a4_raw,
+    gemm_w4a8,
+    gemm_w4a8_raw,
     lib,
     linear_w4a4,
+    linear_w4a8,
     prepare_weight,
     prepare_weight_raw,
     quantize_act,
+    quantize_act_mxfp8,
+    quantize_act_mxfp8_raw,
     quantize_act_raw,
     scale_bytes,
     status_string,

@@ -23,6 +23,8 @@ SIGNATURES = {
     "batq_quantize_act": [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _I, _P],
     "batq_prepare_weight": [_P, _I64, _I64, _P, _P, _P, _P, _I, _P],
     "batq_gemm_w4a4": [_P, _P, _P, _P, _I, _I64, _I64, _I64, _P, _P],
+    "batq_quantize_act_mxfp8": [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _I, _P],
+    "batq_gemm_w4a8": [_P, _P, _P, _P, _I, _I64, _I64, _I64, _P, _P],
     "batq_clip_ratios": [_P, _I64, _P],
     "batq_weight_factors": [_P, _P, _I64, _P, _P],
     "batq_status_string": [_I],
@@ -88,6 +90,16 @@ def quantize_act_raw(x, S, N, ldx, A, B, r_min, r_max, q, e, layout=SCALES_ROW_M
 
 def gemm_w4a4_raw(xq, xe, wq, we, S, N, out, y, layout=SCALES_ROW_MAJOR, stream=0) -> int:
     return lib().batq_gemm_w4a4(xq, xe, wq, we, layout, S, N, out, y, stream)
+
+
+def quantize_act_mxfp8_raw(x, S, N, ldx, A, B, r_min, r_max, q8, e, layout=SCALES_ROW_MAJOR,
+                           stream=0) -> int:
+    return lib().batq_quantize_act_mxfp8(x, S, N, ldx, A, B, r_min, r_max, q8, e, layout,
+                                         stream)
+
+
+def gemm_w4a8_raw(xq8, xe, wq, we, S, N, out, y, layout=SCALES_ROW_MAJOR, stream=0) -> int:
+    return lib().batq_gemm_w4a8(xq8, xe, wq, we, layout, S, N, out, y, stream)
 
 
 def prepare_weight_raw(W, out, N, A_host, B_host, wq, we, layout=SCALES_ROW_MAJOR,
@@ -205,3 +217,49 @@ def linear_w4a4(x, A, B, r_min, r_max, wq, we, layout=SCALES_ROW_MAJOR, stream=N
     prepared weight scales `we` must be in `layout`)."""
     xq, xe = quantize_act(x, A, B, r_min, r_max, layout=layout, stream=stream)
     return gemm_w4a4(xq, xe, wq, we, layout=layout, stream=stream)
+
+
+# ---------------------------------------------------------------------------------------
+# W4A8: MXFP8 (E4M3) activations against the same MXFP4 weights
+# ---------------------------------------------------------------------------------------
+
+def quantize_act_mxfp8(x, A, B, r_min, r_max, q8=None, e=None, layout=SCALES_ROW_MAJOR,
+                       stream=None):
+    """Fused transform + clip + MXFP8 of bf16 activations x [S, N].  Returns the E4M3 codes
+    uint8 [S, N] and the scales (as quantize_act)."""
+    import torch
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    S, N = x.shape
+    if q8 is None:
+        q8 = torch.empty((S, N), dtype=torch.uint8, device=x.device)
+    if e is None:
+        e = _scale_tensor(S, N, layout, x.device)
+    for t in (A, B, r_min, r_max):
+        assert t.dtype == torch.float32 and t.is_contiguous()
+    _check("batq_quantize_act_mxfp8", quantize_act_mxfp8_raw(
+        _ptr(x), S, N, x.stride(0), _ptr(A), _ptr(B), _ptr(r_min), _ptr(r_max), _ptr(q8),
+        _ptr(e), layout, _stream(stream)))
+    return q8, e
+
+
+def gemm_w4a8(xq8, xe, wq, we, y=None, layout=SCALES_ROW_MAJOR, stream=None):
+    """fp32 y [S, out] = dq8(xq8, xe) dq(wq, we)^T on scaled MFMA; xe and we in `layout`."""
+    import torch
+    S, N = xq8.shape
+    out = wq.shape[0]
+    for t in (xq8, xe, wq, we):
+        assert t.dtype == torch.uint8 and t.is_contiguous()
+    assert wq.shape[1] * 2 == N
+    assert xe.numel() == scale_bytes(S, N, layout) and we.numel() == scale_bytes(out, N, layout)
+    if y is None:
+        y = torch.empty((S, out), dtype=torch.float32, device=xq8.device)
+    _check("batq_gemm_w4a8", gemm_w4a8_raw(_ptr(xq8), _ptr(xe), _ptr(wq), _ptr(we), S, N, out,
+                                           _ptr(y), layout, _stream(stream)))
+    return y
+
+
+def linear_w4a8(x, A, B, r_min, r_max, wq, we, layout=SCALES_ROW_MAJOR, stream=None):
+    """The W4A8 pass: MXFP8 activations, then the W4A8 GEMM against the prepared MXFP4
+    weights (scales `we` in `layout`)."""
+    xq8, xe = quantize_act_mxfp8(x, A, B, r_min, r_max, layout=layout, stream=stream)
+    return gemm_w4a8(xq8, xe, wq, we, layout=layout, stream=stream)

@@ -169,3 +169,43 @@ BATQ_API batq_status batq_gemm_w4a4(const uint8_t* xq, const uint8_t* xe, const 
     return from_hip(batq::launch_gemm(xq, xe, wq, we, layout == BATQ_SCALES_MFMA_TILED, S, N,
                                       out, y, as_stream(stream)));
 }
+
+BATQ_API batq_status batq_quantize_act_mxfp8(const uint16_t* x, int64_t S, int64_t N,
+                                             int64_t ldx, const float* A, const float* B,
+                                             const float* r_min, const float* r_max,
+                                             uint8_t* q8, uint8_t* e, batq_scale_layout e_layout,
+                                             void* stream)
+{
+    if (S < 0 || N < 0 || N % 32 != 0) return BATQ_ERR_SHAPE;
+    if (S == 0 || N == 0) return BATQ_OK;
+    if (!x || !A || !B || !r_min || !r_max || !q8 || !e) return BATQ_ERR_NULL;
+    if (!valid_layout(e_layout)) return BATQ_ERR_UNSUPPORTED;
+    if (ldx < N || mul_overflows(S, ldx)) return BATQ_ERR_SHAPE;
+    if (ldx % 8 != 0 || !aligned(x, 16) || !aligned(B, 16) || !aligned(q8, 16) ||
+        !aligned(A, 4) || !aligned(r_min, 4) || !aligned(r_max, 4))
+        return BATQ_ERR_ALIGN;
+    const int64_t k = N / 32;
+    if (k > 64LL * 65535) return BATQ_ERR_UNSUPPORTED;
+    return from_hip(batq::launch_quantize(true, x, S, k, ldx, A, B, r_min, r_max, q8, e,
+                                          e_layout == BATQ_SCALES_MFMA_TILED,
+                                          as_stream(stream), /*fp8=*/true));
+}
+
+BATQ_API batq_status batq_gemm_w4a8(const uint8_t* xq8, const uint8_t* xe, const uint8_t* wq,
+                                    const uint8_t* we, batq_scale_layout layout, int64_t S,
+                                    int64_t N, int64_t out, float* y, void* stream)
+{
+    if (S < 0 || N < 0 || out < 0 || N % 32 != 0) return BATQ_ERR_SHAPE;
+    if (S == 0 || out == 0) return BATQ_OK;
+    if (!y || (N > 0 && (!xq8 || !xe || !wq || !we))) return BATQ_ERR_NULL;
+    if (!valid_layout(layout)) return BATQ_ERR_UNSUPPORTED;
+    if (mul_overflows(S, out) || mul_overflows(S, N) || mul_overflows(out, N))
+        return BATQ_ERR_SHAPE;
+    if (!aligned(y, 16) || !aligned(xq8, 16) || !aligned(wq, 16) || !aligned(xe, 4) ||
+        !aligned(we, 4))
+        return BATQ_ERR_ALIGN;
+    if (N % 256 != 0 || S * N >= (1LL << 32) || out * (N / 2) >= (1LL << 32))
+        return BATQ_ERR_UNSUPPORTED;
+    return from_hip(batq::launch_gemm_w4a8(xq8, xe, wq, we, layout == BATQ_SCALES_MFMA_TILED,
+                                           S, N, out, y, as_stream(stream)));
+}

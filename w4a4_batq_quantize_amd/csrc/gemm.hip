@@ -31,6 +31,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void gbl_void_t;
 
@@ -923,6 +924,283 @@ gemm_skinny_kernel(DmaArgs p, float* __restrict__ y)
     }
 }
 
+// =======================================================================================
+// gemm_w4a8_kernel<TS>: MXFP8 (E4M3) activations x MXFP4 weights, the W4A8 setting
+// =======================================================================================
+//
+// The scaled 32x32x64 MFMA with mixed operand formats: weights E2M1 (format 4, 16 bytes per
+// lane: lane half h holds block h of the K-step), activations E4M3 (format 0, 32 bytes per
+// lane, which hold the same K positions as the E2M1 lanes only as 16-byte halves of both
+// blocks: measured on gfx950, each scale applies to one 32-element K block).  Tile
+// 256 (out) x 128 (tokens), four waves (2 x 2, each 4 x 2 MFMA tiles) at one wave per SIMD,
+// so the 8-dword activation fragments and the accumulators fit in registers; each wave
+// issues its quarter of the next stage's DMA between the MFMA rows of the current stage,
+// two stages in LDS, one barrier per stage.  A stage is 8
+// blocks: 256 weight rows of 128 bytes, 128 activation rows of 256 bytes, then the scale
+// bytes (384 rows x 8; tiled: 12 panel units of 256 bytes).  Chunk c (16 bytes) of row r
+// sits at slot c ^ (r % 8), as in the W4A4 kernels.  67 KB per stage, two stages.
+namespace w4a8 {
+constexpr int BO = 256, BS = 128, WO = 2, WS = 2, TM = 4, TN = 2;
+constexpr int kWaves = WO * WS;
+constexpr int kXRowBytes = 2 * kRowBytes;                     // 256
+constexpr int kWBytes = BO * kRowBytes;                       // 32 KB
+constexpr int kCodeBytes = kWBytes + BS * kXRowBytes;         // 64 KB
+constexpr int kScaleBytes = (BO + BS) * kStageBlocks;         // 3 KB
+constexpr int kBufBytes = kCodeBytes + kScaleBytes;
+constexpr int kCodeDma = kCodeBytes / 1024 / kWaves;          // 16 per producer wave
+constexpr int kScaleDma = kScaleBytes / 256 / kWaves;         // 3 (4 bytes per lane)
+constexpr int kDma = kCodeDma + kScaleDma;
+static_assert(kCodeBytes % (1024 * kWaves) == 0 && kScaleBytes % (256 * kWaves) == 0, "split");
+static_assert(2 * kBufBytes <= 160 * 1024 && kDma <= 63, "LDS / vmcnt");
+}  // namespace w4a8
+
+template <bool TS>
+struct W4A8Plan {
+    uint32_t code_off[w4a8::kCodeDma];
+    uint32_t scale_off[w4a8::kScaleDma];
+};
+
+template <bool TS>
+__device__ __forceinline__ void w4a8_plan(W4A8Plan<TS>& pl, const DmaArgs& p, int64_t o0,
+                                          int64_t s0, int pw, int lane)
+{
+    using namespace w4a8;
+    const int64_t k = p.k;
+#pragma unroll
+    for (int i = 0; i < kCodeDma; ++i) {
+        const int inst = pw * kCodeDma + i;            // 1 KB of LDS each
+        if (inst * 1024 < kWBytes) {
+            const int r = inst * 8 + (lane >> 3);     // 8 weight rows per instruction
+            int64_t row = o0 + r;
+            row = row < p.out ? row : p.out - 1;
+            const int c = (lane & 7) ^ (r & 7);
+            pl.code_off[i] = (uint32_t)(row * 16 * k + 16 * c);
+        } else {
+            const int r = (inst - kWBytes / 1024) * 4 + (lane >> 4);   // 4 activation rows
+            int64_t row = s0 + r;
+            row = row < p.S ? row : p.S - 1;
+            const int c = (lane & 15) ^ (r & 7);
+            pl.code_off[i] = (uint32_t)(row * 32 * k + 16 * c);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kScaleDma; ++j) {
+        const int inst = pw * kScaleDma + j;           // 256 bytes of LDS each
+        // tiled: one 32-row panel unit per instruction; row-major: 32 rows x 8 bytes
+        const int r = inst * 32 + (TS ? 0 : lane >> 1);
+        int64_t row = r < BO ? o0 + r : s0 + (r - BO);
+        const int64_t last = (r < BO ? p.out : p.S) - 1;
+        row = row < last ? row : last;
+        pl.scale_off[j] = TS ? (uint32_t)((row >> 5) * (k >> 3) * 256 + 4 * lane)
+                             : (uint32_t)(row * k + 4 * (lane & 1));
+    }
+}
+
+// DMA instruction d (of kDma) of wave `wave` for stage ks: code instructions, then scales.
+template <bool TS>
+__device__ __forceinline__ void w4a8_dma_one(uint8_t* buf, const W4A8Plan<TS>& pl,
+                                             const DmaArgs& p, int64_t ks, int wave, int d)
+{
+#if defined(__HIP_DEVICE_COMPILE__)   // the LDS-load builtins exist for the device only
+    using namespace w4a8;
+    const int64_t k = p.k;
+    if (d < kCodeDma) {
+        const int inst = wave * kCodeDma + d;
+        const bool w = inst * 1024 < kWBytes;
+        const __amdgpu_buffer_rsrc_t r =
+            w ? buffer_rsrc(p.wq, p.out * 16 * k) : buffer_rsrc(p.xq, p.S * 32 * k);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(buf + inst * 1024), 16,
+                                                 pl.code_off[d],
+                                                 (int)(ks * (w ? kRowBytes : kXRowBytes)), 0, 0);
+    } else {
+        const int j = d - kCodeDma;
+        const int inst = wave * kScaleDma + j;
+        const int64_t k8 = k / 8;
+        const __amdgpu_buffer_rsrc_t r =
+            inst * 32 < BO ? buffer_rsrc(p.we, TS ? ((p.out + 31) / 32) * 256 * k8 : p.out * k)
+                           : buffer_rsrc(p.xe, TS ? ((p.S + 31) / 32) * 256 * k8 : p.S * k);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(buf + kCodeBytes + inst * 256),
+                                                 4, pl.scale_off[j],
+                                                 (int)(ks * (TS ? 256 : kStageBlocks)), 0, 0);
+    }
+#endif
+}
+
+template <bool TS>
+struct W4A8Issue {
+    uint8_t* buf;
+    const W4A8Plan<TS>* pl;
+    const DmaArgs* p;
+    int64_t ks;
+    int wave;
+    __device__ __forceinline__ void operator()(int d) const
+    {
+        if (d < w4a8::kDma) w4a8_dma_one<TS>(buf, *pl, *p, ks, wave, d);
+    }
+};
+
+struct W4A8Frags {
+    v4u a[w4a8::TM];       // 16 bytes of the lane's weight row
+    v8i b[w4a8::TN];       // 32 bytes of the lane's token row
+};
+
+template <int T>
+__device__ __forceinline__ void w4a8_frags(W4A8Frags& f, const uint8_t* buf, int wrow0,
+                                           int xrow0, int lr, int lg)
+{
+    using namespace w4a8;
+    const int lr7 = lr & 7;
+    const uint32_t wpos = 16u * (uint32_t)((2 * T + lg) ^ lr7);
+    // E4M3 operand: lane half h holds elements [16h, 16h+16) of both blocks of the K-step
+    // (bytes 0-15 from block 2T, bytes 16-31 from block 2T+1), i.e. 16-byte chunks 4T + h
+    // and 4T + 2 + h of the stage row; the scale of lane half h still belongs to block 2T+h
+    const uint32_t x0 = 16u * (uint32_t)((4 * T + lg) ^ lr7);
+    const uint32_t x1 = 16u * (uint32_t)((4 * T + 2 + lg) ^ lr7);
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+        f.a[a] = *reinterpret_cast<const v4u*>(buf + (wrow0 + 32 * a + lr) * kRowBytes + wpos);
+#pragma unroll
+    for (int b = 0; b < TN; ++b) {
+        const uint8_t* row = buf + kWBytes + (xrow0 + 32 * b + lr) * kXRowBytes;
+        const v4i lo = *reinterpret_cast<const v4i*>(row + x0);
+        const v4i hi = *reinterpret_cast<const v4i*>(row + x1);
+        f.b[b] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+}
+
+template <bool TS, int T>
+__device__ __forceinline__ void w4a8_mfma(v16f (&acc)[w4a8::TM][w4a8::TN], const W4A8Frags& f,
+                                          const uint32_t (&wsc)[2][w4a8::TM],
+                                          const uint32_t (&xsc)[2][w4a8::TN],
+                                          const W4A8Issue<TS>& dma)
+{
+    constexpr int kSlots = (w4a8::kDma + 3) / 4;   // DMA instructions per K-step
+    using namespace w4a8;
+    constexpr int kFmtE4M3 = 0;
+    constexpr int kSel = TS ? T : 2 * (T & 1);
+    constexpr int kWord = TS ? 0 : T >> 1;
+#pragma unroll
+    for (int a = 0; a < TM; ++a) {
+        const v8i av = {(int)f.a[a].x, (int)f.a[a].y, (int)f.a[a].z, (int)f.a[a].w, 0, 0, 0, 0};
+#pragma unroll
+        for (int b = 0; b < TN; ++b) {
+            acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                av, f.b[b], acc[a][b], kFmtE2M1, kFmtE4M3, kSel, (int)wsc[kWord][a], kSel,
+                (int)xsc[kWord][b]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int d = a * kSlots / TM; d < (a + 1) * kSlots / TM; ++d) dma(T * kSlots + d);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// The four K-steps of a stage, the fragments of step T+1 requested before the MFMAs of T.
+template <bool TS>
+__device__ __forceinline__ void w4a8_stage(v16f (&acc)[w4a8::TM][w4a8::TN], const uint8_t* buf,
+                                           int wrow0, int xrow0, int lane,
+                                           const W4A8Issue<TS>& dma)
+{
+    using namespace w4a8;
+    const int lr = lane & 31, lg = lane >> 5;
+    uint32_t wsc[2][TM], xsc[2][TN];
+    W4A8Frags f0, f1;
+    w4a8_frags<0>(f0, buf, wrow0, xrow0, lr, lg);
+    w4a8_frags<1>(f1, buf, wrow0, xrow0, lr, lg);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (TS) {
+        // lane (row, half) finds blocks 2T + half of its row as bytes T of one dword
+#pragma unroll
+        for (int a = 0; a < TM; ++a) {
+            const uint2 v = *reinterpret_cast<const uint2*>(buf + kCodeBytes +
+                                                            (wrow0 / 32 + a) * 256 + lr * 8);
+            wsc[0][a] = wsc[1][a] = lg ? v.y : v.x;
+        }
+#pragma unroll
+        for (int b = 0; b < TN; ++b) {
+            const uint2 v = *reinterpret_cast<const uint2*>(
+                buf + kCodeBytes + ((BO + xrow0) / 32 + b) * 256 + lr * 8);
+            xsc[0][b] = xsc[1][b] = lg ? v.y : v.x;
+        }
+    } else {
+        // the row's 8 scale bytes, shifted so byte 2(T%2) of word T/2 is block 2T + half
+#pragma unroll
+        for (int a = 0; a < TM; ++a) {
+            const uint2 v = *reinterpret_cast<const uint2*>(
+                buf + kCodeBytes + (wrow0 + 32 * a + lr) * kStageBlocks);
+            wsc[0][a] = v.x >> (8 * lg);
+            wsc[1][a] = v.y >> (8 * lg);
+        }
+#pragma unroll
+        for (int b = 0; b < TN; ++b) {
+            const uint2 v = *reinterpret_cast<const uint2*>(
+                buf + kCodeBytes + (BO + xrow0 + 32 * b + lr) * kStageBlocks);
+            xsc[0][b] = v.x >> (8 * lg);
+            xsc[1][b] = v.y >> (8 * lg);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    w4a8_mfma<TS, 0>(acc, f0, wsc, xsc, dma);
+    __builtin_amdgcn_sched_barrier(0);
+    w4a8_frags<2>(f0, buf, wrow0, xrow0, lr, lg);
+    __builtin_amdgcn_sched_barrier(0);
+    w4a8_mfma<TS, 1>(acc, f1, wsc, xsc, dma);
+    __builtin_amdgcn_sched_barrier(0);
+    w4a8_frags<3>(f1, buf, wrow0, xrow0, lr, lg);
+    __builtin_amdgcn_sched_barrier(0);
+    w4a8_mfma<TS, 2>(acc, f0, wsc, xsc, dma);
+    __builtin_amdgcn_sched_barrier(0);
+    w4a8_mfma<TS, 3>(acc, f1, wsc, xsc, dma);
+}
+
+// Tile config for the shared epilogue (store_tile reads BO, BS, TM, TN only).
+using CfgW4A8 = DmaCfg<256, 128, 2, 2, 2, true>;
+
+template <bool TS>
+__global__ void __launch_bounds__(64 * w4a8::kWaves)
+gemm_w4a8_kernel(DmaArgs p, float* __restrict__ y, int64_t tiles_o, int64_t tiles_s,
+                 int nt_store)
+{
+    using namespace w4a8;
+    __shared__ __attribute__((aligned(16))) uint8_t lds0[kBufBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t lds1[kBufBytes];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int wrow0 = (wave / WS) * (BO / WO);
+    const int xrow0 = (wave % WS) * (BS / WS);
+    int64_t o0, s0;
+    tile_origin(tiles_o, tiles_s, 4, BO, BS, o0, s0);
+    const int64_t nst = p.k / kStageBlocks;
+
+    v16f acc[TM][TN];
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TN; ++b) acc[a][b] = v16f{};
+    if (nst > 0) {
+        W4A8Plan<TS> pl;
+        w4a8_plan<TS>(pl, p, o0, s0, wave, lane);
+#pragma unroll
+        for (int d = 0; d < kDma; ++d) w4a8_dma_one<TS>(lds0, pl, p, 0, wave, d);
+        // stage s is multiplied out of one buffer while stage s+1 (the last stage again at
+        // the end, so every pass issues the same DMA) streams into the other
+        for (int64_t s = 0; s < nst; s += 2) {
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+            barrier_only();
+            w4a8_stage<TS>(acc, lds0, wrow0, xrow0, lane,
+                           W4A8Issue<TS>{lds1, &pl, &p, s + 1 < nst ? s + 1 : nst - 1, wave});
+            if (s + 1 >= nst) break;
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+            barrier_only();
+            w4a8_stage<TS>(acc, lds1, wrow0, xrow0, lane,
+                           W4A8Issue<TS>{lds0, &pl, &p, s + 2 < nst ? s + 2 : nst - 1, wave});
+        }
+        // the trailing prefetch must land before the workgroup's LDS is released
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    }
+    store_tile<CfgW4A8>(acc, p, y, o0, s0, wrow0, xrow0, lane, nt_store);
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq,
@@ -979,6 +1257,29 @@ hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq,
     if (tiles_o * tiles_s > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(gemm_generic_kernel, dim3((unsigned)(tiles_o * tiles_s)), dim3(kThreads),
                        0, stream, p, (int)tiled_scales, y, tiles_o, tiles_s);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_w4a8(const uint8_t* xq8, const uint8_t* xe, const uint8_t* wq,
+                            const uint8_t* we, bool tiled_scales, int64_t S, int64_t N,
+                            int64_t out, float* y, hipStream_t stream)
+{
+    const DmaArgs p{xq8, xe, wq, we, S, N / 32, out};
+    if ((p.k % kStageBlocks) != 0 || (reinterpret_cast<uintptr_t>(xe) % 4) != 0 ||
+        (reinterpret_cast<uintptr_t>(we) % 4) != 0 || S * 32 * p.k >= (1LL << 32) ||
+        out * 16 * p.k >= (1LL << 32))
+        return hipErrorNotSupported;
+    const int64_t tiles_o = (out + w4a8::BO - 1) / w4a8::BO;
+    const int64_t tiles_s = (S + w4a8::BS - 1) / w4a8::BS;
+    if (tiles_o * tiles_s > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    const int nt = (S * 2 + out) * (N / 2 + N / 32) > (64LL << 20) ? 1 : 0;
+    const dim3 grid((unsigned)(tiles_o * tiles_s)), block(64 * w4a8::kWaves);
+    if (tiled_scales)
+        hipLaunchKernelGGL(gemm_w4a8_kernel<true>, grid, block, 0, stream, p, y, tiles_o,
+                           tiles_s, nt);
+    else
+        hipLaunchKernelGGL(gemm_w4a8_kernel<false>, grid, block, 0, stream, p, y, tiles_o,
+                           tiles_s, nt);
     return hipGetLastError();
 }
 

@@ -11,15 +11,23 @@ namespace batq {
 // Activation mode: bf16 input with row stride ldx, clip ratios r_min/r_max.
 // Weight mode: fp32 input with row stride ldx, no clip (r_min/r_max unused).
 // Scales row-major, or in the MFMA-tiled layout of batq.h when tiled_scales.
+// fp8 (activation mode only): MXFP8 output, codes [rows, N] one E4M3 byte per element.
 hipError_t launch_quantize(bool act, const void* x, int64_t rows, int64_t k, int64_t ldx,
                            const float* A, const float* B, const float* r_min,
                            const float* r_max, uint8_t* q, uint8_t* e, bool tiled_scales,
-                           hipStream_t stream);
+                           hipStream_t stream, bool fp8 = false);
 
 // MXFP4 x MXFP4 -> fp32 GEMM, y[S, out] = dq(x)[S, N] dq(w)[out, N]^T; both scale
 // arrays in the same layout (tiled_scales: MFMA-tiled, else row-major).
 hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq,
                        const uint8_t* we, bool tiled_scales, int64_t S, int64_t N,
                        int64_t out, float* y, hipStream_t stream);
+
+// W4A8: MXFP8 (E4M3) activations xq8 [S, N] (one byte per element) x MXFP4 weights.
+// Requires N % 256 == 0 and 4-byte (tiled) / 8-byte (row-major) aligned scale arrays;
+// returns hipErrorNotSupported otherwise.
+hipError_t launch_gemm_w4a8(const uint8_t* xq8, const uint8_t* xe, const uint8_t* wq,
+                            const uint8_t* we, bool tiled_scales, int64_t S, int64_t N,
+                            int64_t out, float* y, hipStream_t stream);
 
 }  // namespace batq

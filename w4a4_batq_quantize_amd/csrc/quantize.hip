@@ -68,7 +68,12 @@ __device__ __forceinline__ void gpk_transform(const float (&x)[32], const float*
     }
 }
 
-template <bool kAct>
+// kFp8 (activations only): MXFP8 output, one E4M3 code byte per element (the W4A8
+// setting).  Same transform and clip; the scale exponent is floor(log2 amax) - 8 (E4M3's
+// largest exponent), and the conversion instruction, exact round-to-nearest-even otherwise,
+// returns NaN above 448 where MX saturates, so the clip bounds are first clamped into
+// [-448 s, 448 s] (a clamp of a clamp is the clamp to the clamped bounds).
+template <bool kAct, bool kFp8 = false>
 __global__ void __launch_bounds__(kThreads)
 quantize_kernel(const void* __restrict__ xin, int64_t rows, int64_t k, int64_t ldx,
                 const float* __restrict__ A, const float* __restrict__ B,
@@ -76,6 +81,7 @@ quantize_kernel(const void* __restrict__ xin, int64_t rows, int64_t k, int64_t l
                 uint8_t* __restrict__ q, uint8_t* __restrict__ e, int lpr_log2,
                 int tiled_scales)
 {
+    static_assert(kAct || !kFp8, "MXFP8 is an activation-side format");
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int64_t row = ((((int64_t)blockIdx.x * kWavesPerGroup + wave) << (6 - lpr_log2)) +
@@ -120,6 +126,7 @@ quantize_kernel(const void* __restrict__ xin, int64_t rows, int64_t k, int64_t l
     gpk_transform(x, A, b, y);
 
     float amax;
+    float lo = 0.0f, hi = 0.0f;
     if constexpr (kAct) {
         float m = y[0], M = y[0];
 #pragma unroll
@@ -127,10 +134,8 @@ quantize_kernel(const void* __restrict__ xin, int64_t rows, int64_t k, int64_t l
             m = __builtin_fminf(m, y[j]);
             M = __builtin_fmaxf(M, y[j]);
         }
-        const float hi = r_max[blk] * M;
-        const float lo = __builtin_fminf(r_min[blk] * m, hi);   // lo > hi: every value -> hi
-#pragma unroll
-        for (int j = 0; j < 32; ++j) y[j] = __builtin_amdgcn_fmed3f(y[j], lo, hi);
+        hi = r_max[blk] * M;
+        lo = __builtin_fminf(r_min[blk] * m, hi);   // lo > hi: every value -> hi
         amax = __builtin_fmaxf(__builtin_fabsf(__builtin_amdgcn_fmed3f(m, lo, hi)),
                                __builtin_fabsf(__builtin_amdgcn_fmed3f(M, lo, hi)));
     } else {
@@ -138,21 +143,49 @@ quantize_kernel(const void* __restrict__ xin, int64_t rows, int64_t k, int64_t l
 #pragma unroll
         for (int j = 0; j < 32; ++j) amax = __builtin_fmaxf(amax, __builtin_fabsf(y[j]));
     }
-    const int ex = (int)((__float_as_uint(amax) >> 23) & 0xFF) - 2;
+    const int ex = (int)((__float_as_uint(amax) >> 23) & 0xFF) - (kFp8 ? 8 : 2);
     const uint32_t ebyte = ex > 0 ? (uint32_t)ex : 0u;
     const float scale = __uint_as_float(ebyte << 23);
 
-    uint32_t w[4];
+    if constexpr (kFp8) {
+        // 448 * 2^(e - 127) = 1.75 * 2^(e - 119): fp32 exponent field e + 8, mantissa 0.75
+        const float sat = __uint_as_float(((ebyte + 8u) << 23) | 0x00600000u);
+        const float L = __builtin_amdgcn_fmed3f(lo, -sat, sat);
+        const float H = __builtin_amdgcn_fmed3f(hi, -sat, sat);
+        typedef short v2i16 __attribute__((ext_vector_type(2)));
+        uint32_t w[8];
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        uint32_t acc = 0;
-        acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, y[8 * d + 0], y[8 * d + 1], scale, 0);
-        acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, y[8 * d + 2], y[8 * d + 3], scale, 1);
-        acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, y[8 * d + 4], y[8 * d + 5], scale, 2);
-        acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, y[8 * d + 6], y[8 * d + 7], scale, 3);
-        w[d] = acc;
+        for (int d = 0; d < 8; ++d) {
+            v2i16 acc = {0, 0};
+            acc = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(
+                acc, __builtin_amdgcn_fmed3f(y[4 * d + 0], L, H),
+                __builtin_amdgcn_fmed3f(y[4 * d + 1], L, H), scale, false);
+            acc = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(
+                acc, __builtin_amdgcn_fmed3f(y[4 * d + 2], L, H),
+                __builtin_amdgcn_fmed3f(y[4 * d + 3], L, H), scale, true);
+            w[d] = (uint32_t)(uint16_t)acc[0] | ((uint32_t)(uint16_t)acc[1] << 16);
+        }
+        uint4* qp = reinterpret_cast<uint4*>(q + row * (32 * k) + 32 * blk);
+        qp[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        qp[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    } else {
+        if constexpr (kAct) {
+#pragma unroll
+            for (int j = 0; j < 32; ++j) y[j] = __builtin_amdgcn_fmed3f(y[j], lo, hi);
+        }
+        uint32_t w[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            uint32_t acc = 0;
+            acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, y[8 * d + 0], y[8 * d + 1], scale, 0);
+            acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, y[8 * d + 2], y[8 * d + 3], scale, 1);
+            acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, y[8 * d + 4], y[8 * d + 5], scale, 2);
+            acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, y[8 * d + 6], y[8 * d + 7], scale, 3);
+            w[d] = acc;
+        }
+        *reinterpret_cast<uint4*>(q + row * (16 * k) + 16 * blk) =
+            make_uint4(w[0], w[1], w[2], w[3]);
     }
-    *reinterpret_cast<uint4*>(q + row * (16 * k) + 16 * blk) = make_uint4(w[0], w[1], w[2], w[3]);
     // scale byte: row-major, or the 256-byte (32 rows x 8 blocks) units the GEMM consumes,
     // blocks of a unit ordered 0,2,4,6,1,3,5,7 within each row's 8 bytes
     const int64_t eoff = tiled_scales
@@ -167,7 +200,7 @@ quantize_kernel(const void* __restrict__ xin, int64_t rows, int64_t k, int64_t l
 hipError_t launch_quantize(bool act, const void* x, int64_t rows, int64_t k, int64_t ldx,
                            const float* A, const float* B, const float* r_min,
                            const float* r_max, uint8_t* q, uint8_t* e, bool tiled_scales,
-                           hipStream_t stream)
+                           hipStream_t stream, bool fp8)
 {
     // lanes per row: the smallest power of two >= k, capped at one wave
     int lpr_log2 = 0;
@@ -178,7 +211,10 @@ hipError_t launch_quantize(bool act, const void* x, int64_t rows, int64_t k, int
     const int64_t gy = (k + 63) / 64;
     if (gx > 0x7FFFFFFF || gy > 65535) return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)gx, (unsigned)gy);
-    if (act)
+    if (act && fp8)
+        hipLaunchKernelGGL((quantize_kernel<true, true>), grid, dim3(kThreads), 0, stream, x,
+                           rows, k, ldx, A, B, r_min, r_max, q, e, lpr_log2, (int)tiled_scales);
+    else if (act)
         hipLaunchKernelGGL(quantize_kernel<true>, grid, dim3(kThreads), 0, stream, x, rows, k,
                            ldx, A, B, r_min, r_max, q, e, lpr_log2, (int)tiled_scales);
     else

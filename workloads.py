@@ -154,3 +154,15 @@ def random_mxfp4(rows: int, N: int, seed, scale_lo: int = 110, scale_hi: int = 1
     q = rng.integers(0, 256, size=(rows, N // 2), dtype=np.uint8)
     e = rng.integers(scale_lo, scale_hi, size=(rows, N // 32), dtype=np.uint8)
     return q, e
+
+
+def random_mxfp8(rows: int, N: int, seed, scale_lo: int = 110, scale_hi: int = 145):
+    """Seeded random MXFP8 (E4M3) operands for the GEMM alone: code bytes [rows, N], uniform
+    over the 254 non-NaN E4M3 encodings (the two NaN bytes 0x7F and 0xFF are moved down to
+    0x7E and 0xFE), and E8M0 scale bytes [rows, N/32] in [scale_lo, scale_hi)."""
+    seed = list(seed) if isinstance(seed, (tuple, list)) else [int(seed)]
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
+    q = rng.integers(0, 256, size=(rows, N), dtype=np.uint8)
+    q[(q & 0x7F) == 0x7F] -= 1
+    e = rng.integers(scale_lo, scale_hi, size=(rows, N // 32), dtype=np.uint8)
+    return q, e
