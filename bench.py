@@ -31,24 +31,29 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "fused BAT+clip+MXFP4 quantize GB/s; W4A4 MXFP4 GEMM TFLOPS (% of peak)"
+METRIC_W4A8 = "fused BAT+clip+MXFP8 quantize GB/s; W4A8 (MXFP4 x MXFP8) GEMM TFLOPS (% of peak)"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 FP4_PEAK_TFLOPS = 10100.0        # MI355X dense MXFP4 MFMA
+FP8_PEAK_TFLOPS = 5000.0         # MI355X dense MXFP8 MFMA (rate of E2M1 x E4M3 as well)
 
 
-def k1_bytes(S, N):
-    """Algorithmic bytes of one quantiser launch: bf16 in (2 B/elem), codes out (0.5 B/elem),
-    scales out (1 B per 32 elem), plus the parameters (A, B_i, two ratios per block)."""
+def k1_bytes(S, N, code_bytes=0.5):
+    """Algorithmic bytes of one quantiser launch: bf16 in (2 B/elem), codes out (0.5 B/elem
+    for MXFP4, 1 B for MXFP8), scales out (1 B per 32 elem), plus the parameters (A, B_i,
+    two ratios per block)."""
     k = N // 32
-    return S * N * 2 + S * N // 2 + S * k + 256 + 64 * k + 8 * k
+    return S * N * 2 + int(S * N * code_bytes) + S * k + 256 + 64 * k + 8 * k
 
 
 def k2_flops(S, N, out):
     return 2 * S * N * out
 
 
-def k2_bytes(S, N, out):
-    """Compulsory bytes of one GEMM launch: both MXFP4 operands once, fp32 output once."""
-    return (S + out) * (N // 2 + N // 32) + 4 * S * out
+def k2_bytes(S, N, out, act_code_bytes=0.5):
+    """Compulsory bytes of one GEMM launch: both operands once (activation codes 0.5 or
+    1 B/elem, weight codes 0.5 B/elem, one scale byte per 32), fp32 output once."""
+    return (int(S * N * act_code_bytes) + S * (N // 32) + out * (N // 2 + N // 32)
+            + 4 * S * out)
 
 
 def measured_traffic(kernel: str, workload: str):
@@ -69,7 +74,7 @@ def measured_traffic(kernel: str, workload: str):
         return None
 
 
-def cpu_baseline(L, seconds):
+def cpu_baseline(L, seconds, w4a8=False):
     """The oracle as it stands, on a bounded sample of token rows of the same layer:
     quantise the sampled rows and compute every output of those rows."""
     import numpy as np
@@ -83,9 +88,10 @@ def cpu_baseline(L, seconds):
     def run(rows):
         idx = np.linspace(0, S - 1, rows).astype(np.int64)
         t0 = time.perf_counter()
-        xq, xe = oracle.quantize_act(L.x_bits[idx], L.A, L.B, r1, r2, nthreads=threads)
+        quant = oracle.quantize_act_fp8 if w4a8 else oracle.quantize_act
+        xq, xe = quant(L.x_bits[idx], L.A, L.B, r1, r2, nthreads=threads)
         t1 = time.perf_counter()
-        oracle.gemm(xq, xe, wq, we, nthreads=threads)
+        (oracle.gemm_w4a8 if w4a8 else oracle.gemm)(xq, xe, wq, we, nthreads=threads)
         t2 = time.perf_counter()
         return t1 - t0, t2 - t1
 
@@ -94,7 +100,7 @@ def cpu_baseline(L, seconds):
     rows = int(min(S, max(probe, probe * seconds / max(tq + tg, 1e-6))))
     tq, tg = run(rows)
     return {
-        "value": round(k1_bytes(rows, N) / tq / 1e9, 4),
+        "value": round(k1_bytes(rows, N, 1.0 if w4a8 else 0.5) / tq / 1e9, 4),
         "unit": "GB/s",
         "gemm_value": round(k2_flops(rows, N, out) / tg / 1e12, 6),
         "gemm_unit": "TFLOP/s",
@@ -117,6 +123,9 @@ def measure(name, args):
     L = wl.make_layer(name)
     S, N, out = L.cfg.S, L.cfg.N, L.cfg.out
     k = N // 32
+    w4a8 = args.precision == "w4a8"
+    cb = 1.0 if w4a8 else 0.5                 # activation code bytes per element
+    peak = FP8_PEAK_TFLOPS if w4a8 else FP4_PEAK_TFLOPS
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -130,12 +139,12 @@ def measure(name, args):
     del W
     x0 = torch.from_numpy(L.x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
 
-    per_set = S * N * 2 + S * (N // 2 + k) + out * (N // 2 + k) + 4 * S * out
+    per_set = S * N * 2 + S * (int(N * cb) + k) + out * (N // 2 + k) + 4 * S * out
     R = min(1024, max(2, math.ceil(args.rotate_bytes / per_set)))
     xs = [x0.clone() for _ in range(R)]
     wqs = [wq0.clone() for _ in range(R)]
     wes = [we0.clone() for _ in range(R)]
-    xqs = [torch.empty((S, N // 2), dtype=torch.uint8, device=dev) for _ in range(R)]
+    xqs = [torch.empty((S, int(N * cb)), dtype=torch.uint8, device=dev) for _ in range(R)]
     xes = [torch.empty((bq.scale_bytes(S, N, layout),), dtype=torch.uint8, device=dev)
            for _ in range(R)]
     ys = [torch.empty((S, out), dtype=torch.float32, device=dev) for _ in range(R)]
@@ -146,7 +155,8 @@ def measure(name, args):
     pA, pB, pr1, pr2 = A.data_ptr(), B.data_ptr(), rmin.data_ptr(), rmax.data_ptr()
     ptr = [(xs[j].data_ptr(), xqs[j].data_ptr(), xes[j].data_ptr(), wqs[j].data_ptr(),
             wes[j].data_ptr(), ys[j].data_ptr()) for j in range(R)]
-    quant, gemm = bq.quantize_act_raw, bq.gemm_w4a4_raw
+    quant, gemm = ((bq.quantize_act_mxfp8_raw, bq.gemm_w4a8_raw) if w4a8 else
+                   (bq.quantize_act_raw, bq.gemm_w4a4_raw))
 
     def launch_k1(j):
         x, xq, xe, _, _, _ = ptr[j]
@@ -175,6 +185,11 @@ def measure(name, args):
         t1 = time.perf_counter()
         return e0.elapsed_time(e1) * 1e-3 / K, (t1 - t0) / K
 
+    # every set's activation codes and scales are written once before anything is timed, so
+    # the GEMM-alone launches below never read buffers the quantiser has not filled
+    for j in range(R):
+        if launch_k1(j):
+            raise RuntimeError("library call failed")
     for i in range(args.warmup):
         step(i % R)
     torch.cuda.synchronize()
@@ -200,34 +215,39 @@ def measure(name, args):
     last = ys[(args.warmup + 3 * K - 1) % R]
     assert bool(torch.isfinite(last).all().item()), "non-finite GEMM output"
 
-    b1 = k1_bytes(S, N)
+    b1 = k1_bytes(S, N, cb)
+    b2 = k2_bytes(S, N, out, cb)
     gbs = b1 / t_k1 / 1e9
     tflops = k2_flops(S, N, out) / t_k2 / 1e12
-    k2_ai = k2_flops(S, N, out) / k2_bytes(S, N, out)
-    k2_roof = min(FP4_PEAK_TFLOPS, k2_ai * HBM_PEAK_GBS / 1e3)
-    tr1 = measured_traffic("quantize_kernel", L.cfg.name)
-    tr2 = measured_traffic("gemm_pc_kernel", L.cfg.name)
-    roof_k1 = {"kernel": "quantize_kernel (fused BAT+clip+MXFP4)", "bound": "hbm",
+    k2_ai = k2_flops(S, N, out) / b2
+    k2_roof = min(peak, k2_ai * HBM_PEAK_GBS / 1e3)
+    k1_name = "quantize_kernel_mxfp8" if w4a8 else "quantize_kernel"
+    k2_name = ("gemm_w4a8_kernel" if w4a8 else
+               "gemm_skinny_kernel" if S <= 64 else "gemm_pc_kernel")
+    tr1 = measured_traffic(k1_name, L.cfg.name)
+    tr2 = measured_traffic(k2_name, L.cfg.name)
+    roof_k1 = {"kernel": f"{k1_name} (fused BAT+clip+{'MXFP8' if w4a8 else 'MXFP4'})",
+               "bound": "hbm",
                "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": tr1,
                "avg_us": round(t_k1 * 1e6, 3), "algorithmic_bytes": b1}
-    hbm_bound = k2_roof < FP4_PEAK_TFLOPS
-    k2_gbs = k2_bytes(S, N, out) / t_k2 / 1e9
-    roof_k2 = {"kernel": ("gemm_skinny_kernel" if S <= 64 else "gemm_pc_kernel")
-                         + " (MXFP4 scaled MFMA)",
+    hbm_bound = k2_roof < peak
+    k2_gbs = b2 / t_k2 / 1e9
+    roof_k2 = {"kernel": k2_name + (" (E2M1 x E4M3 scaled MFMA)" if w4a8 else
+                                    " (MXFP4 scaled MFMA)"),
                "bound": "hbm" if hbm_bound else "mfma",
                "achieved": round(k2_gbs if hbm_bound else tflops, 1),
-               "peak": HBM_PEAK_GBS if hbm_bound else FP4_PEAK_TFLOPS,
+               "peak": HBM_PEAK_GBS if hbm_bound else peak,
                "unit": "GB/s" if hbm_bound else "TFLOP/s",
-               "frac": round(k2_gbs / HBM_PEAK_GBS if hbm_bound else tflops / FP4_PEAK_TFLOPS, 4),
+               "frac": round(k2_gbs / HBM_PEAK_GBS if hbm_bound else tflops / peak, 4),
                "traffic": tr2, "tflops": round(tflops, 1),
-               "algorithmic_bytes": k2_bytes(S, N, out),
+               "algorithmic_bytes": b2,
                "avg_us": round(t_k2 * 1e6, 3), "algorithmic_flops": k2_flops(S, N, out),
                "roofline_tflops": round(k2_roof, 1), "frac_of_roofline": round(tflops / k2_roof, 4)}
     dominant = roof_k2 if t_k2 >= t_k1 else roof_k1
 
     rec = {
-        "metric": METRIC,
+        "metric": METRIC_W4A8 if w4a8 else METRIC,
         "value": round(gbs, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -237,16 +257,18 @@ def measure(name, args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4",
-        "dtype_detail": "K1: bf16 in, fp32 transform/clip, E2M1+E8M0 out; "
-                        "K2: E2M1 x E2M1 scaled MFMA, fp32 accumulate and output",
+        "dtype": "mxfp8/mxfp4" if w4a8 else "mxfp4",
+        "dtype_detail": ("K1: bf16 in, fp32 transform/clip, E4M3+E8M0 out; K2: E2M1 weights x "
+                         "E4M3 activations scaled MFMA, fp32 accumulate and output" if w4a8 else
+                         "K1: bf16 in, fp32 transform/clip, E2M1+E8M0 out; "
+                         "K2: E2M1 x E2M1 scaled MFMA, fp32 accumulate and output"),
         "data": "synthetic",
         "config": {"workload": f"{L.cfg.name}: S={S} N={N} out={out} (Qwen3-8B-shaped linear "
                                f"layer, seeded synthetic bf16 activations and fp32 weights)",
                    "S": S, "N": N, "out": out, "rotated_buffer_sets": R,
                    "scale_layout": "mfma_tiled"},
         "gemm": {"value": round(tflops, 1), "unit": "TFLOP/s",
-                 "pct_of_peak": round(100 * tflops / FP4_PEAK_TFLOPS, 2)},
+                 "pct_of_peak": round(100 * tflops / peak, 2)},
         "step_gpu_us": round(t_step_ev * 1e6, 3),
         "kernel_us": {"quantize": round(t_k1 * 1e6, 3), "gemm": round(t_k2 * 1e6, 3)},
         "roofline": dominant,
@@ -267,11 +289,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for counter scaling)")
+    ap.add_argument("--precision", choices=("w4a4", "w4a8"), default="w4a4",
+                    help="w4a8: MXFP8 activations against the MXFP4 weights")
     ap.add_argument("--all", action="store_true",
                     help="measure every layer configuration, one JSON line each (no CPU baseline)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs the path on one GPU only; --gpus must be 1",
+        print("bench.py: the path runs on one GPU; --gpus must be 1",
               file=sys.stderr)
         sys.exit(2)
 
@@ -283,7 +307,7 @@ def main():
         return
     rec, L = measure(args.config, args)
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(L, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline(L, args.cpu_seconds, args.precision == "w4a8")
     print(json.dumps(rec), flush=True)
 
 
