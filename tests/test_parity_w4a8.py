@@ -150,6 +150,10 @@ def gpu_gemm8(bq, xq8, xe, wq, we, tiled=False):
     (1, 256, 1), (3, 256, 5), (17, 4096, 100), (129, 4352, 300), (200, 256, 257),
     (64, 12288, 64), (128, 4096, 128), (256, 1024, 384), (300, 768, 20), (45, 2048, 77),
     (260, 512, 515),
+    # few tokens (weight-streaming kernel): one and two token columns, ragged out, K ranges
+    # shorter than the number of waves splitting K
+    (33, 1280, 1), (2, 512, 31), (63, 4096, 64), (1, 8192, 4100), (64, 256, 33),
+    (32, 512, 96), (40, 2048, 77),
 ])
 def test_gemm8_random_operands_ragged(bq, orc, S, N, out, tiled):
     xq8, xe = wl.random_mxfp8(S, N, seed=(27, S, N, out))

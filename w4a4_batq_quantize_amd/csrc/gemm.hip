@@ -765,16 +765,17 @@ struct SkinnySplit {
     static constexpr int value = TN == 1 ? 16 : 8;
 };
 
-template <int TN>
+template <int TN, bool F8>
 struct SkinnyStage {
-    v4u w[4];            // K-steps 0..3: 16 bytes of the lane's weight row
-    v4u x[TN][4];        // and of its token rows
-    uint2 ws;            // scale bytes (tiled: .x only; row-major: both words)
+    v4u w[4];                 // K-steps 0..3: 16 bytes of the lane's weight row
+    v4u x[TN][4][F8 ? 2 : 1]; // and of its token rows (E4M3: 32 bytes, two halves)
+    uint2 ws;                 // scale bytes (tiled: .x only; row-major: both words)
     uint2 xs[TN];
 };
 
-template <int TN, bool TS>
-__device__ __forceinline__ void skinny_load(SkinnyStage<TN>& st, const __amdgpu_buffer_rsrc_t& rw,
+template <int TN, bool TS, bool F8>
+__device__ __forceinline__ void skinny_load(SkinnyStage<TN, F8>& st,
+                                            const __amdgpu_buffer_rsrc_t& rw,
                                             const __amdgpu_buffer_rsrc_t& rx,
                                             const __amdgpu_buffer_rsrc_t& rwe,
                                             const __amdgpu_buffer_rsrc_t& rxe, uint32_t wrow,
@@ -782,14 +783,26 @@ __device__ __forceinline__ void skinny_load(SkinnyStage<TN>& st, const __amdgpu_
                                             const uint32_t (&xse)[TN], int64_t k, int ks,
                                             int lg)
 {
-    const uint32_t rb = 16u * (uint32_t)k;                     // bytes per code row
+    const uint32_t rb = 16u * (uint32_t)k;                     // bytes per weight code row
+    const uint32_t xrb = (F8 ? 32u : 16u) * (uint32_t)k;       // bytes per token code row
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const uint32_t c = (uint32_t)ks * kRowBytes + 16u * (2 * t + lg);
         st.w[t] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(wrow * rb + c), 0, 0);
 #pragma unroll
-        for (int b = 0; b < TN; ++b)
-            st.x[b][t] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(xrow[b] * rb + c), 0, 0);
+        for (int b = 0; b < TN; ++b) {
+            if constexpr (F8) {
+                // E4M3 lane half h: chunks 4t + h and 4t + 2 + h of the 256-byte stage row
+                const uint32_t c8 = (uint32_t)ks * 2 * kRowBytes + 16u * (4 * t + lg);
+                st.x[b][t][0] =
+                    __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(xrow[b] * xrb + c8), 0, 0);
+                st.x[b][t][1] =
+                    __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(xrow[b] * xrb + c8 + 32), 0, 0);
+            } else {
+                st.x[b][t][0] =
+                    __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(xrow[b] * xrb + c), 0, 0);
+            }
+        }
     }
     if constexpr (TS) {
         const uint32_t so = (uint32_t)ks * 256u;
@@ -809,34 +822,42 @@ __device__ __forceinline__ void skinny_load(SkinnyStage<TN>& st, const __amdgpu_
     }
 }
 
-template <int TN, bool TS, int T>
-__device__ __forceinline__ void skinny_step(v16f (&acc)[TN], const SkinnyStage<TN>& st, int lg)
+template <int TN, bool TS, bool F8, int T>
+__device__ __forceinline__ void skinny_step(v16f (&acc)[TN], const SkinnyStage<TN, F8>& st,
+                                            int lg)
 {
     // tiled: byte T of the one dword; row-major: byte 2(T%2) of word T/2, pre-shifted so the
     // lane's half (block 2T + lane/32) sits in that byte
     constexpr int kSel = TS ? T : 2 * (T & 1);
+    constexpr int kFmtX = F8 ? 0 : kFmtE2M1;                   // 0: E4M3
     const uint32_t wsc = TS ? st.ws.x : (((T >> 1) ? st.ws.y : st.ws.x) >> (8 * lg));
     const v8i av = {(int)st.w[T].x, (int)st.w[T].y, (int)st.w[T].z, (int)st.w[T].w, 0, 0, 0, 0};
 #pragma unroll
     for (int b = 0; b < TN; ++b) {
         const uint32_t xsc = TS ? st.xs[b].x : (((T >> 1) ? st.xs[b].y : st.xs[b].x) >> (8 * lg));
-        const v8i bv = {(int)st.x[b][T].x, (int)st.x[b][T].y, (int)st.x[b][T].z,
-                        (int)st.x[b][T].w, 0, 0, 0, 0};
+        const v4u u = st.x[b][T][0];
+        v8i bv = {(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
+        if constexpr (F8) {
+            const v4u v = st.x[b][T][F8 ? 1 : 0];
+            bv = v8i{(int)u.x, (int)u.y, (int)u.z, (int)u.w, (int)v.x, (int)v.y, (int)v.z, (int)v.w};
+        }
         acc[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            av, bv, acc[b], kFmtE2M1, kFmtE2M1, kSel, (int)wsc, kSel, (int)xsc);
+            av, bv, acc[b], kFmtE2M1, kFmtX, kSel, (int)wsc, kSel, (int)xsc);
     }
 }
 
-template <int TN, bool TS>
-__device__ __forceinline__ void skinny_stage(v16f (&acc)[TN], const SkinnyStage<TN>& st, int lg)
+template <int TN, bool TS, bool F8>
+__device__ __forceinline__ void skinny_stage(v16f (&acc)[TN], const SkinnyStage<TN, F8>& st,
+                                             int lg)
 {
-    skinny_step<TN, TS, 0>(acc, st, lg);
-    skinny_step<TN, TS, 1>(acc, st, lg);
-    skinny_step<TN, TS, 2>(acc, st, lg);
-    skinny_step<TN, TS, 3>(acc, st, lg);
+    skinny_step<TN, TS, F8, 0>(acc, st, lg);
+    skinny_step<TN, TS, F8, 1>(acc, st, lg);
+    skinny_step<TN, TS, F8, 2>(acc, st, lg);
+    skinny_step<TN, TS, F8, 3>(acc, st, lg);
 }
 
-template <int TN, bool TS>
+// F8: the tokens' codes are E4M3 (one byte per element, the W4A8 setting)
+template <int TN, bool TS, bool F8 = false>
 __global__ void __launch_bounds__(64 * SkinnySplit<TN>::value)
 gemm_skinny_kernel(DmaArgs p, float* __restrict__ y)
 {
@@ -857,7 +878,7 @@ gemm_skinny_kernel(DmaArgs p, float* __restrict__ y)
 #pragma unroll
     for (int b = 0; b < TN; ++b) xrow[b] = (uint32_t)(32 * b + lr < p.S ? 32 * b + lr : p.S - 1);
     const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(p.wq, p.out * 16 * k);
-    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(p.xq, p.S * 16 * k);
+    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(p.xq, p.S * (F8 ? 32 : 16) * k);
     const int64_t k8 = k / 8;
     const __amdgpu_buffer_rsrc_t rwe =
         buffer_rsrc(p.we, TS ? ((p.out + 31) / 32) * 256 * k8 : p.out * k);
@@ -876,19 +897,19 @@ gemm_skinny_kernel(DmaArgs p, float* __restrict__ y)
 #pragma unroll
     for (int b = 0; b < TN; ++b) acc[b] = v16f{};
     if (s0 < s1) {
-        SkinnyStage<TN> cur, nxt;
-        skinny_load<TN, TS>(cur, rw, rx, rwe, rxe, wrow, xrow, wse, xse, k, s0, lg);
+        SkinnyStage<TN, F8> cur, nxt;
+        skinny_load<TN, TS, F8>(cur, rw, rx, rwe, rxe, wrow, xrow, wse, xse, k, s0, lg);
         int s = s0;
         for (;;) {
             const bool more = s + 1 < s1;
-            skinny_load<TN, TS>(nxt, rw, rx, rwe, rxe, wrow, xrow, wse, xse, k,
+            skinny_load<TN, TS, F8>(nxt, rw, rx, rwe, rxe, wrow, xrow, wse, xse, k,
                                 more ? s + 1 : s, lg);
-            skinny_stage<TN, TS>(acc, cur, lg);
+            skinny_stage<TN, TS, F8>(acc, cur, lg);
             if (!more) break;
             const bool more2 = s + 2 < s1;
-            skinny_load<TN, TS>(cur, rw, rx, rwe, rxe, wrow, xrow, wse, xse, k,
+            skinny_load<TN, TS, F8>(cur, rw, rx, rwe, rxe, wrow, xrow, wse, xse, k,
                                 more2 ? s + 2 : s + 1, lg);
-            skinny_stage<TN, TS>(acc, nxt, lg);
+            skinny_stage<TN, TS, F8>(acc, nxt, lg);
             if (!more2) break;
             s += 2;
         }
@@ -1269,6 +1290,28 @@ hipError_t launch_gemm_w4a8(const uint8_t* xq8, const uint8_t* xe, const uint8_t
         (reinterpret_cast<uintptr_t>(we) % 4) != 0 || S * 32 * p.k >= (1LL << 32) ||
         out * 16 * p.k >= (1LL << 32))
         return hipErrorNotSupported;
+    const bool s8 = (reinterpret_cast<uintptr_t>(xe) % 8) == 0 &&
+                    (reinterpret_cast<uintptr_t>(we) % 8) == 0;
+    if (S <= 64 && (tiled_scales || s8)) {
+        // few tokens: the weight-streaming kernel with E4M3 token codes
+        const int64_t tiles_w = (out + 31) / 32;
+        if (tiles_w > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+        const dim3 grid((unsigned)tiles_w);
+        if (S <= 32) {
+            const dim3 block(64 * SkinnySplit<1>::value);
+            if (tiled_scales)
+                hipLaunchKernelGGL((gemm_skinny_kernel<1, true, true>), grid, block, 0, stream, p, y);
+            else
+                hipLaunchKernelGGL((gemm_skinny_kernel<1, false, true>), grid, block, 0, stream, p, y);
+        } else {
+            const dim3 block(64 * SkinnySplit<2>::value);
+            if (tiled_scales)
+                hipLaunchKernelGGL((gemm_skinny_kernel<2, true, true>), grid, block, 0, stream, p, y);
+            else
+                hipLaunchKernelGGL((gemm_skinny_kernel<2, false, true>), grid, block, 0, stream, p, y);
+        }
+        return hipGetLastError();
+    }
     const int64_t tiles_o = (out + w4a8::BO - 1) / w4a8::BO;
     const int64_t tiles_s = (S + w4a8::BS - 1) / w4a8::BS;
     if (tiles_o * tiles_s > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
