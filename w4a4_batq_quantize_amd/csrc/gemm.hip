@@ -73,9 +73,12 @@ __device__ __forceinline__ void tile_origin(int64_t tiles_o, int64_t tiles_s, in
 // 32 x 32.  A K stage is 256 elements: per tile row 128 code bytes and 8 scale bytes.  LDS
 // stage layout: rows [0, BO) weight rows, [BO, BO+BS) activation rows, 128 bytes each,
 // followed by (BO+BS) x 8 scale bytes.  Within a row the 16-byte chunk c is stored at
-// position c ^ (row % 8): the DMA writes 64 lanes x 16 bytes contiguously, so the layout
-// cannot be padded, and the XOR spreads the 32-row reads of one MFMA operand over all
-// banks.  NB stages are in flight (prefetch distance NB-1).
+// position c ^ ((row / 2) % 8): the DMA writes 64 lanes x 16 bytes contiguously, so the
+// layout cannot be padded.  gfx950's LDS has 64 banks (256 bytes per bank row, measured: a
+// conflict-free ds_read_b128 pattern reaches ~217 B/clk per CU, and an XOR by row % 8 only
+// ~120), so two 128-byte rows share a bank row and the XOR key is the row pair: the 16
+// lanes served together (rows r..r+15 of one operand, one chunk) then hit 16 distinct
+// 16-byte bank groups.  NB stages are in flight (prefetch distance NB-1).
 //
 // The 32x32x64 operand layout: lane l holds row l%32 and K block l/32 of the K-step, the
 // result gives lane l column l%32 and rows 8(r/4) + 4(l/32) + r%4 for register r.
@@ -133,7 +136,7 @@ __device__ __forceinline__ void dma_plan(DmaPlan<C>& pl, const DmaArgs& p, int64
     for (int i = 0; i < C::kCodeDma; ++i) {
         const int inst = wave * C::kCodeDma + i;
         const int r = inst * 8 + (lane >> 3);              // tile row of this lane
-        const int c = (lane & 7) ^ (lane >> 3);           // global chunk for LDS slot lane&7
+        const int c = (lane & 7) ^ ((r >> 1) & 7);        // global chunk for LDS slot lane&7
         int64_t row = r < C::BO ? o0 + r : s0 + (r - C::BO);
         const int64_t last = (r < C::BO ? p.out : p.S) - 1;
         row = row < last ? row : last;
@@ -288,7 +291,7 @@ __device__ __forceinline__ void dma_mfma_stage(v16f (&acc)[C::TM][C::TN], const 
                                                int wrow0, int xrow0, int lane,
                                                const DmaIssue<C>& dma)
 {
-    const int lr = lane & 31, lg = lane >> 5, lr7 = lane & 7;
+    const int lr = lane & 31, lg = lane >> 5, lr7 = (lane >> 1) & 7;
     const uint32_t wrow_off = (uint32_t)(wrow0 + lr) * kRowBytes;
     const uint32_t xrow_off = (uint32_t)(C::BO + xrow0 + lr) * kRowBytes;
     uint32_t wsc[2][C::TM], xsc[2][C::TN];
@@ -350,6 +353,88 @@ __device__ __forceinline__ void dma_mfma_stage(v16f (&acc)[C::TM][C::TN], const 
     dma_mfma_frags<C, 2>(acc, f0, wsc, xsc, dma);
     __builtin_amdgcn_sched_barrier(0);
     dma_mfma_frags<C, 3>(acc, f1, wsc, xsc, dma);
+}
+
+// ---- consumer pipeline of gemm_pc_kernel ----
+// The scale bytes of one stage for this lane, in the selects the MFMAs take (as in
+// dma_mfma_stage).
+template <class C>
+struct StageScales {
+    uint32_t w[2][C::TM], x[2][C::TN];
+};
+
+template <class C>
+__device__ __forceinline__ void pc_read_scales(StageScales<C>& sc, const uint8_t* buf, int wrow0,
+                                               int xrow0, int lr, int lg)
+{
+    if constexpr (C::TS) {
+        // the lane's own dword of its row's 8 bytes (64 lanes, 64 distinct dwords)
+#pragma unroll
+        for (int a = 0; a < C::TM; ++a)
+            sc.w[0][a] = sc.w[1][a] = *reinterpret_cast<const uint32_t*>(
+                buf + C::kCodeBytes + (wrow0 / 32 + a) * 256 + lr * 8 + 4 * lg);
+#pragma unroll
+        for (int b = 0; b < C::TN; ++b)
+            sc.x[0][b] = sc.x[1][b] = *reinterpret_cast<const uint32_t*>(
+                buf + C::kCodeBytes + ((C::BO + xrow0) / 32 + b) * 256 + lr * 8 + 4 * lg);
+    } else {
+#pragma unroll
+        for (int a = 0; a < C::TM; ++a) {
+            const uint2 v = *reinterpret_cast<const uint2*>(buf + C::kCodeBytes +
+                                                            (wrow0 + 32 * a + lr) * kStageBlocks);
+            sc.w[0][a] = v.x >> (8 * lg);
+            sc.w[1][a] = v.y >> (8 * lg);
+        }
+#pragma unroll
+        for (int b = 0; b < C::TN; ++b) {
+            const uint2 v = *reinterpret_cast<const uint2*>(
+                buf + C::kCodeBytes + (C::BO + xrow0 + 32 * b + lr) * kStageBlocks);
+            sc.x[0][b] = v.x >> (8 * lg);
+            sc.x[1][b] = v.y >> (8 * lg);
+        }
+    }
+}
+
+// One stage of a consumer wave.  On entry f0 holds K-step 0 of `cur`, f1 K-step 1 (maybe in
+// flight) and sc its scales.  The barrier that hands over the next stage sits before the
+// stage's last MFMA group rather than at the start of the next stage: by then every LDS
+// read of `cur` has been issued, and once they have landed (lgkmcnt(0)) the producers may
+// refill `cur`'s buffer while the last MFMAs run; the next stage's scales and first
+// fragments are read in their shadow, so a stage starts without waiting on LDS.
+template <class C, bool kNext>
+__device__ __forceinline__ void pc_stage(v16f (&acc)[C::TM][C::TN], const uint8_t* cur,
+                                         const uint8_t* nxt,
+                                         Frags<C::TM, C::TN>& f0, Frags<C::TM, C::TN>& f1,
+                                         StageScales<C>& sc, int wrow0, int xrow0, int lane)
+{
+    const int lr = lane & 31, lg = lane >> 5, lr7 = (lane >> 1) & 7;
+    const uint32_t wrow_off = (uint32_t)(wrow0 + lr) * kRowBytes;
+    const uint32_t xrow_off = (uint32_t)(C::BO + xrow0 + lr) * kRowBytes;
+    const DmaIssue<C> none{nullptr, nullptr, nullptr, 0, -1};
+    dma_mfma_frags<C, 0>(acc, f0, sc.w, sc.x, none);
+    __builtin_amdgcn_sched_barrier(0);
+    dma_load_frags<C, 2>(f0, cur, wrow_off, xrow_off, lg, lr7);
+    __builtin_amdgcn_sched_barrier(0);
+    dma_mfma_frags<C, 1>(acc, f1, sc.w, sc.x, none);
+    __builtin_amdgcn_sched_barrier(0);
+    dma_load_frags<C, 3>(f1, cur, wrow_off, xrow_off, lg, lr7);
+    __builtin_amdgcn_sched_barrier(0);
+    dma_mfma_frags<C, 2>(acc, f0, sc.w, sc.x, none);
+    __builtin_amdgcn_sched_barrier(0);
+    StageScales<C> sn;
+    if constexpr (kNext) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+        barrier_only();
+        pc_read_scales<C>(sn, nxt, wrow0, xrow0, lr, lg);
+        dma_load_frags<C, 0>(f0, nxt, wrow_off, xrow_off, lg, lr7);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    dma_mfma_frags<C, 3>(acc, f1, sc.w, sc.x, none);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kNext) {
+        dma_load_frags<C, 1>(f1, nxt, wrow_off, xrow_off, lg, lr7);
+        sc = sn;
+    }
 }
 
 // One pipeline step: once at most the DMA instructions of the NB-2 following stages are
@@ -562,24 +647,38 @@ gemm_pc_kernel(DmaArgs p, float* __restrict__ y, int64_t tiles_o, int64_t tiles_
 #pragma unroll
         for (int b = 0; b < C::TN; ++b) acc[a][b] = v16f{};
     if (nst > 0) {
-        const DmaIssue<C> none{nullptr, nullptr, nullptr, 0, -1};
-        const int64_t nfull = nst - nst % NB;
+        // barrier 0 hands over stage 0; barrier s (s >= 1) is taken inside stage s-1
+        const int lr = lane & 31, lg = lane >> 5, lr7 = (lane >> 1) & 7;
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+        barrier_only();
+        Frags<C::TM, C::TN> f0, f1;
+        StageScales<C> sc;
+        pc_read_scales<C>(sc, bufs[0], wrow0, xrow0, lr, lg);
+        const uint32_t wrow_off = (uint32_t)(wrow0 + lr) * kRowBytes;
+        const uint32_t xrow_off = (uint32_t)(C::BO + xrow0 + lr) * kRowBytes;
+        dma_load_frags<C, 0>(f0, bufs[0], wrow_off, xrow_off, lg, lr7);
+        dma_load_frags<C, 1>(f1, bufs[0], wrow_off, xrow_off, lg, lr7);
+        // stages 0 .. nst-2 are followed by another (stage t lives in buffer t % NB); the
+        // last one is peeled so that every buffer index stays a compile-time constant
+        const int64_t nmain = nst - 1;
+        const int64_t nfull = nmain - nmain % NB;
         int64_t s = 0;
         for (; s < nfull; s += NB) {
 #pragma unroll
-            for (int i = 0; i < NB; ++i) {
-                __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
-                barrier_only();
-                dma_mfma_stage<C>(acc, bufs[i], wrow0, xrow0, lane, none);
-            }
+            for (int i = 0; i < NB; ++i)
+                pc_stage<C, true>(acc, bufs[i], bufs[(i + 1) % NB], f0, f1, sc, wrow0, xrow0,
+                                  lane);
         }
 #pragma unroll
         for (int i = 0; i < NB - 1; ++i)
-            if (s + i < nst) {
-                __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
-                barrier_only();
-                dma_mfma_stage<C>(acc, bufs[i], wrow0, xrow0, lane, none);
-            }
+            if (s + i < nmain)
+                pc_stage<C, true>(acc, bufs[i], bufs[(i + 1) % NB], f0, f1, sc, wrow0, xrow0,
+                                  lane);
+        const int last = (int)(nmain % NB);
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+            if (last == i)
+                pc_stage<C, false>(acc, bufs[i], bufs[i], f0, f1, sc, wrow0, xrow0, lane);
     }
     store_tile<C>(acc, p, y, o0, s0, wrow0, xrow0, lane, nt_store);
 }
@@ -958,8 +1057,9 @@ gemm_skinny_kernel(DmaArgs p, float* __restrict__ y)
 // issues its quarter of the next stage's DMA between the MFMA rows of the current stage,
 // two stages in LDS, one barrier per stage.  A stage is 8
 // blocks: 256 weight rows of 128 bytes, 128 activation rows of 256 bytes, then the scale
-// bytes (384 rows x 8; tiled: 12 panel units of 256 bytes).  Chunk c (16 bytes) of row r
-// sits at slot c ^ (r % 8), as in the W4A4 kernels.  67 KB per stage, two stages.
+// bytes (384 rows x 8; tiled: 12 panel units of 256 bytes).  Chunk c (16 bytes) of a weight
+// row r sits at slot c ^ ((r / 2) % 8), as in the W4A4 kernels; an activation row fills a
+// whole 256-byte bank row, so its chunks are keyed by r % 16.  67 KB per stage, two stages.
 namespace w4a8 {
 constexpr int BO = 256, BS = 128, WO = 2, WS = 2, TM = 4, TN = 2;
 constexpr int kWaves = WO * WS;
@@ -994,13 +1094,13 @@ __device__ __forceinline__ void w4a8_plan(W4A8Plan<TS>& pl, const DmaArgs& p, in
             const int r = inst * 8 + (lane >> 3);     // 8 weight rows per instruction
             int64_t row = o0 + r;
             row = row < p.out ? row : p.out - 1;
-            const int c = (lane & 7) ^ (r & 7);
+            const int c = (lane & 7) ^ ((r >> 1) & 7);
             pl.code_off[i] = (uint32_t)(row * 16 * k + 16 * c);
         } else {
             const int r = (inst - kWBytes / 1024) * 4 + (lane >> 4);   // 4 activation rows
             int64_t row = s0 + r;
             row = row < p.S ? row : p.S - 1;
-            const int c = (lane & 15) ^ (r & 7);
+            const int c = (lane & 15) ^ (r & 15);
             pl.code_off[i] = (uint32_t)(row * 32 * k + 16 * c);
         }
     }
@@ -1070,13 +1170,13 @@ __device__ __forceinline__ void w4a8_frags(W4A8Frags& f, const uint8_t* buf, int
                                            int xrow0, int lr, int lg)
 {
     using namespace w4a8;
-    const int lr7 = lr & 7;
+    const int lr7 = (lr >> 1) & 7, lr15 = lr & 15;
     const uint32_t wpos = 16u * (uint32_t)((2 * T + lg) ^ lr7);
     // E4M3 operand: lane half h holds elements [16h, 16h+16) of both blocks of the K-step
     // (bytes 0-15 from block 2T, bytes 16-31 from block 2T+1), i.e. 16-byte chunks 4T + h
     // and 4T + 2 + h of the stage row; the scale of lane half h still belongs to block 2T+h
-    const uint32_t x0 = 16u * (uint32_t)((4 * T + lg) ^ lr7);
-    const uint32_t x1 = 16u * (uint32_t)((4 * T + 2 + lg) ^ lr7);
+    const uint32_t x0 = 16u * (uint32_t)((4 * T + lg) ^ lr15);
+    const uint32_t x1 = 16u * (uint32_t)((4 * T + 2 + lg) ^ lr15);
 #pragma unroll
     for (int a = 0; a < TM; ++a)
         f.a[a] = *reinterpret_cast<const v4u*>(buf + (wrow0 + 32 * a + lr) * kRowBytes + wpos);
