@@ -21,7 +21,10 @@
  *     thelatestinai listing, Figure 3);
  *   - the W4A8 setting: the same transform and clip with the activations encoded as MXFP8
  *     (E4M3 elements, one E8M0 scale per 32) against the same MXFP4 weights (gist.science
- *     section 4 and the daily-arxiv results bullet, W4A8KV16).
+ *     section 4 and the daily-arxiv results bullet, W4A8KV16);
+ *   - the other transform forms that thelatestinai listing's Table 1 compares against GPK:
+ *     a full 32x32 P_i per block ("w/o decomposition") and P_i = B_i (x) A_i with a private
+ *     A_i per block (naive Kronecker); block Hadamard is GPK with Hadamard factors.
  *
  * Where the pages leave a step open, the plainest reading is taken (listed with reasons in
  * the design notes): fp32 arithmetic for the transform with sequential fused multiply-add
@@ -183,6 +186,31 @@ static void gpk_transform_block(const float x[32], const float A[64], const floa
     }
 }
 
+/* y = x P for one block with a full 32x32 P (row-major, y_j = sum_m x_m P[m][j]): each
+ * y_j is a plain product for m = 0 followed by fmaf for m = 1..31 in increasing m. */
+static void full_transform_block(const float x[32], const float P[1024], float y[32])
+{
+    for (int j = 0; j < 32; ++j) {
+        float acc = x[0] * P[j];
+        for (int m = 1; m < 32; ++m) acc = fmaf(x[m], P[32 * m + j], acc);
+        y[j] = acc;
+    }
+}
+
+/* Transform selector shared by the variant entry points:
+ *   0 GPK:       F0 = A [8][8] (one for all blocks), F1 = B [k][4][4]
+ *   1 Kronecker: F0 = A [k][8][8] (private per block), F1 = B [k][4][4]
+ *   2 full:      F0 = P [k][32][32], F1 unused
+ * Forms 0 and 1 use the reshape evaluation of gpk_transform_block. */
+static void transform_block(int form, const float x[32], const float* F0, const float* F1,
+                            int64_t i, float y[32])
+{
+    if (form == 2)
+        full_transform_block(x, F0 + 1024 * i, y);
+    else
+        gpk_transform_block(x, F0 + (form == 1 ? 64 * i : 0), F1 + 16 * i, y);
+}
+
 /* ------------------------------------------------------------------------------------ */
 /* Clip + MXFP4 quantisation of one transformed block                                    */
 /* ------------------------------------------------------------------------------------ */
@@ -309,6 +337,55 @@ void orc_quantize_weight(const float* W, int64_t rows, int64_t N,
                                 NULL, NULL);
         }
     }
+}
+
+/* Activation side with a transform form (see transform_block): bf16 X -> transform ->
+ * clip -> MXFP4. */
+void orc_quantize_act_form(const uint16_t* x, int64_t rows, int64_t N, int64_t ldx, int form,
+                           const float* F0, const float* F1, const float* r_min,
+                           const float* r_max, uint8_t* q, uint8_t* e, int nthreads)
+{
+    int64_t k = N / 32;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(static)
+    for (int64_t s = 0; s < rows; ++s) {
+        for (int64_t i = 0; i < k; ++i) {
+            float xb[32], y[32];
+            for (int j = 0; j < 32; ++j) xb[j] = bf16_to_float(x[s * ldx + 32 * i + j]);
+            transform_block(form, xb, F0, F1, i, y);
+            clip_quantize_block(y, 1, r_min[i], r_max[i], q + s * (N / 2) + 16 * i,
+                                e + s * k + i, NULL, NULL);
+        }
+    }
+}
+
+/* Weight side with a transform form: fp32 W -> transform with the inverse factors of that
+ * form (transposed inverses, as for orc_quantize_weight) -> MXFP4 without clipping. */
+void orc_quantize_weight_form(const float* W, int64_t rows, int64_t N, int form,
+                              const float* F0, const float* F1, uint8_t* q, uint8_t* e,
+                              int nthreads)
+{
+    int64_t k = N / 32;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(static)
+    for (int64_t o = 0; o < rows; ++o) {
+        for (int64_t i = 0; i < k; ++i) {
+            float y[32];
+            transform_block(form, W + o * N + 32 * i, F0, F1, i, y);
+            clip_quantize_block(y, 0, 1.0f, 1.0f, q + o * (N / 2) + 16 * i, e + o * k + i,
+                                NULL, NULL);
+        }
+    }
+}
+
+/* The transform of a form alone on fp32 rows (for the pins). */
+void orc_transform_form_f32(const float* x, int64_t rows, int64_t N, int form,
+                            const float* F0, const float* F1, float* y)
+{
+    int64_t k = N / 32;
+    for (int64_t s = 0; s < rows; ++s)
+        for (int64_t i = 0; i < k; ++i)
+            transform_block(form, x + s * N + 32 * i, F0, F1, i, y + s * N + 32 * i);
 }
 
 /* The transform alone (fp32 y [rows, N]) on fp32 input, for the structural pins. */

@@ -79,6 +79,9 @@ def lib() -> ctypes.CDLL:
     L.orc_e8m0_scale_fp8_f32.argtypes = [P, I64, P]
     L.orc_dequant_fp8.argtypes = [P, P, I64, I64, P]
     L.orc_gemm_w4a8.argtypes = [P, P, P, P, I64, I64, I64, P, I64, P, I64, P, P, I32]
+    L.orc_quantize_act_form.argtypes = [P, I64, I64, I64, I32, P, P, P, P, P, P, I32]
+    L.orc_quantize_weight_form.argtypes = [P, I64, I64, I32, P, P, P, P, I32]
+    L.orc_transform_form_f32.argtypes = [P, I64, I64, I32, P, P, P]
     L.orc_max_threads.restype = I32
     _lib = L
     return L
@@ -371,3 +374,78 @@ def gemm_w4a8(xq8, xe, wq, we, rows=None, cols=None, nthreads=1):
     lib().orc_gemm_w4a8(_p(xq8), _p(xe), _p(wq), _p(we), S, N, out, _p(r), nr, _p(c), nc,
                         _p(y), _p(t), nthreads)
     return y, t
+
+
+# ----------------------------------------------------------------------------------------
+# Transform forms compared in thelatestinai listing's Table 1: GPK (form 0), naive
+# Kronecker with a private A_i per block (form 1), a full 32x32 P_i per block (form 2)
+# ----------------------------------------------------------------------------------------
+
+FORM_GPK, FORM_KRONECKER, FORM_FULL = 0, 1, 2
+
+
+def _form_factors(form, F0, F1, k):
+    if form == FORM_FULL:
+        F0 = _c(F0, np.float32).reshape(k, 1024)
+        F1 = np.zeros(16 * k, dtype=np.float32)
+    else:
+        F0 = _c(F0, np.float32).reshape(-1)
+        assert F0.size == (64 if form == FORM_GPK else 64 * k)
+        F1 = _c(F1, np.float32).reshape(k, 16)
+    return F0, F1
+
+
+def quantize_act_form(x_bits, form, F0, F1, r_min, r_max, nthreads=1):
+    """bf16 activations [S, N] -> (codes [S, N/2], scales [S, N/32]) with transform `form`:
+    F0 = A [8,8] / A_i [k,8,8] / P_i [k,32,32], F1 = B_i [k,4,4] (unused for the full form)."""
+    x_bits = np.ascontiguousarray(np.asarray(x_bits))
+    assert x_bits.dtype == np.uint16 and x_bits.ndim == 2
+    S, ldx = x_bits.shape
+    r_min = _c(r_min, np.float32)
+    k = r_min.size
+    N = 32 * k
+    F0, F1 = _form_factors(form, F0, F1, k)
+    q = np.zeros((S, N // 2), dtype=np.uint8)
+    e = np.zeros((S, k), dtype=np.uint8)
+    lib().orc_quantize_act_form(_p(x_bits), S, N, ldx, form, _p(F0), _p(F1), _p(r_min),
+                                _p(_c(r_max, np.float32)), _p(q), _p(e), nthreads)
+    return q, e
+
+
+def transform_form_f32(x, form, F0, F1) -> np.ndarray:
+    x = _c(x, np.float32)
+    rows, N = x.shape
+    F0, F1 = _form_factors(form, F0, F1, N // 32)
+    y = np.zeros_like(x)
+    lib().orc_transform_form_f32(_p(x), rows, N, form, _p(F0), _p(F1), _p(y))
+    return y
+
+
+def weight_factors_form(form, F0, F1, k):
+    """Transposed fp32 inverses of a form's factors (nearest fp32 to the exact inverse):
+    the weight block becomes P_i^-1 applied on the right transposed, W_i P_i^-T."""
+    if form == FORM_GPK:
+        return weight_factors(F0, F1)
+    B = np.asarray(F1, dtype=np.float32).reshape(-1, 4, 4) if form != FORM_FULL else None
+    if form == FORM_KRONECKER:
+        A = np.asarray(F0, dtype=np.float32).reshape(k, 8, 8)
+        Ai = np.stack([np.ascontiguousarray(exact_inverse_f32(a).T) for a in A])
+        Bi = np.stack([np.ascontiguousarray(exact_inverse_f32(b).T) for b in B])
+        return np.ascontiguousarray(Ai), np.ascontiguousarray(Bi)
+    P = np.asarray(F0, dtype=np.float32).reshape(k, 32, 32)
+    Pi = np.stack([np.ascontiguousarray(exact_inverse_f32(m).T) for m in P])
+    return np.ascontiguousarray(Pi), None
+
+
+def prepare_weight_form(W, form, F0, F1, nthreads=1):
+    """Offline weight preparation for a transform form: inverse factors, transform, MXFP4."""
+    W = _c(W, np.float32)
+    rows, N = W.shape
+    k = N // 32
+    G0, G1 = weight_factors_form(form, F0, F1, k)
+    G0, G1 = _form_factors(form, G0, G1, k)
+    q = np.zeros((rows, N // 2), dtype=np.uint8)
+    e = np.zeros((rows, k), dtype=np.uint8)
+    lib().orc_quantize_weight_form(_p(W), rows, N, form, _p(G0), _p(G1), _p(q), _p(e),
+                                   nthreads)
+    return q, e
