@@ -37,12 +37,16 @@ FP4_PEAK_TFLOPS = 10100.0        # MI355X dense MXFP4 MFMA
 FP8_PEAK_TFLOPS = 5000.0         # MI355X dense MXFP8 MFMA (rate of E2M1 x E4M3 as well)
 
 
-def k1_bytes(S, N, code_bytes=0.5):
+FORMS = {"gpk": 0, "kronecker": 1, "full": 2}
+
+
+def k1_bytes(S, N, code_bytes=0.5, form="gpk"):
     """Algorithmic bytes of one quantiser launch: bf16 in (2 B/elem), codes out (0.5 B/elem
-    for MXFP4, 1 B for MXFP8), scales out (1 B per 32 elem), plus the parameters (A, B_i,
-    two ratios per block)."""
+    for MXFP4, 1 B for MXFP8), scales out (1 B per 32 elem), plus the parameters (GPK: A and
+    B_i; Kronecker: A_i and B_i; full: P_i; two ratios per block)."""
     k = N // 32
-    return S * N * 2 + int(S * N * code_bytes) + S * k + 256 + 64 * k + 8 * k
+    params = {"gpk": 256 + 64 * k, "kronecker": 256 * k + 64 * k, "full": 4096 * k}[form]
+    return S * N * 2 + int(S * N * code_bytes) + S * k + params + 8 * k
 
 
 def k2_flops(S, N, out):
@@ -124,6 +128,9 @@ def measure(name, args):
     S, N, out = L.cfg.S, L.cfg.N, L.cfg.out
     k = N // 32
     w4a8 = args.precision == "w4a8"
+    form = getattr(args, "form", "gpk")
+    if w4a8 and form != "gpk":
+        raise SystemExit("bench.py: --form applies to the W4A4 path")
     cb = 1.0 if w4a8 else 0.5                 # activation code bytes per element
     peak = FP8_PEAK_TFLOPS if w4a8 else FP4_PEAK_TFLOPS
     dev = torch.device("cuda:0")
@@ -135,7 +142,14 @@ def measure(name, args):
     rmax = torch.from_numpy(bq.clip_ratios(L.alpha_max)).to(dev)
     W = torch.from_numpy(L.W).to(dev)
     layout = bq.SCALES_MFMA_TILED
-    wq0, we0 = bq.prepare_weight(W, L.A, L.B, layout=layout)
+    if form == "gpk":
+        wq0, we0 = bq.prepare_weight(W, L.A, L.B, layout=layout)
+    else:
+        # seeded near-identity factors of the chosen form (thelatestinai listing, Table 1)
+        F0h, F1h = wl.form_factors(FORMS[form], k, seed=(61, FORMS[form], N))
+        wq0, we0 = bq.prepare_weight_form(W, FORMS[form], F0h, F1h, layout=layout)
+        A = torch.from_numpy(F0h).to(dev)
+        B = torch.from_numpy(F1h).to(dev) if F1h is not None else None
     del W
     x0 = torch.from_numpy(L.x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
 
@@ -152,11 +166,17 @@ def measure(name, args):
 
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
-    pA, pB, pr1, pr2 = A.data_ptr(), B.data_ptr(), rmin.data_ptr(), rmax.data_ptr()
+    pA, pr1, pr2 = A.data_ptr(), rmin.data_ptr(), rmax.data_ptr()
+    pB = B.data_ptr() if B is not None else 0
     ptr = [(xs[j].data_ptr(), xqs[j].data_ptr(), xes[j].data_ptr(), wqs[j].data_ptr(),
             wes[j].data_ptr(), ys[j].data_ptr()) for j in range(R)]
     quant, gemm = ((bq.quantize_act_mxfp8_raw, bq.gemm_w4a8_raw) if w4a8 else
                    (bq.quantize_act_raw, bq.gemm_w4a4_raw))
+    if form != "gpk":
+        fid = FORMS[form]
+
+        def quant(x, S_, N_, ldx, a, b, r1, r2, xq, xe, lay, st):
+            return bq.quantize_act_form_raw(x, S_, N_, ldx, fid, a, b, r1, r2, xq, xe, lay, st)
 
     def launch_k1(j):
         x, xq, xe, _, _, _ = ptr[j]
@@ -215,7 +235,7 @@ def measure(name, args):
     last = ys[(args.warmup + 3 * K - 1) % R]
     assert bool(torch.isfinite(last).all().item()), "non-finite GEMM output"
 
-    b1 = k1_bytes(S, N, cb)
+    b1 = k1_bytes(S, N, cb, form)
     b2 = k2_bytes(S, N, out, cb)
     gbs = b1 / t_k1 / 1e9
     tflops = k2_flops(S, N, out) / t_k2 / 1e12
@@ -224,9 +244,10 @@ def measure(name, args):
     k1_name = "quantize_kernel_mxfp8" if w4a8 else "quantize_kernel"
     k2_name = ("gemm_w4a8_kernel" if w4a8 else
                "gemm_skinny_kernel" if S <= 64 else "gemm_pc_kernel")
-    tr1 = measured_traffic(k1_name, L.cfg.name)
+    tr1 = measured_traffic(k1_name, L.cfg.name) if form == "gpk" else None
     tr2 = measured_traffic(k2_name, L.cfg.name)
-    roof_k1 = {"kernel": f"{k1_name} (fused BAT+clip+{'MXFP8' if w4a8 else 'MXFP4'})",
+    roof_k1 = {"kernel": f"{k1_name} (fused BAT+clip+{'MXFP8' if w4a8 else 'MXFP4'}"
+                         + ("" if form == "gpk" else f", {form} transform") + ")",
                "bound": "hbm",
                "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": tr1,
@@ -266,7 +287,7 @@ def measure(name, args):
         "config": {"workload": f"{L.cfg.name}: S={S} N={N} out={out} (Qwen3-8B-shaped linear "
                                f"layer, seeded synthetic bf16 activations and fp32 weights)",
                    "S": S, "N": N, "out": out, "rotated_buffer_sets": R,
-                   "scale_layout": "mfma_tiled"},
+                   "scale_layout": "mfma_tiled", "transform": form},
         "gemm": {"value": round(tflops, 1), "unit": "TFLOP/s",
                  "pct_of_peak": round(100 * tflops / peak, 2)},
         "step_gpu_us": round(t_step_ev * 1e6, 3),
@@ -291,6 +312,9 @@ def main():
                     help="also run a plain device copy of known size (for counter scaling)")
     ap.add_argument("--precision", choices=("w4a4", "w4a8"), default="w4a4",
                     help="w4a8: MXFP8 activations against the MXFP4 weights")
+    ap.add_argument("--form", choices=tuple(FORMS), default="gpk",
+                    help="transform form of the quantiser (thelatestinai listing, Table 1): "
+                         "gpk (the method), kronecker (private A_i), full (32x32 P_i)")
     ap.add_argument("--all", action="store_true",
                     help="measure every layer configuration, one JSON line each (no CPU baseline)")
     args = ap.parse_args()
@@ -307,7 +331,8 @@ def main():
         return
     rec, L = measure(args.config, args)
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(L, args.cpu_seconds, args.precision == "w4a8")
+        if args.form == "gpk":
+            rec["cpu_baseline"] = cpu_baseline(L, args.cpu_seconds, args.precision == "w4a8")
     print(json.dumps(rec), flush=True)
 
 

@@ -60,6 +60,18 @@ typedef enum batq_scale_layout {
     BATQ_SCALES_MFMA_TILED = 1
 } batq_scale_layout;
 
+/*
+ * Transform forms of the block-wise affine transform P_i (thelatestinai listing, Table 1,
+ * which compares their parameter counts and costs): GPK (P_i = B_i (x) A with one A for all
+ * blocks, the method), naive Kronecker (P_i = B_i (x) A_i, a private A_i per block) and the
+ * full 32x32 P_i ("w/o decomposition").  Block Hadamard is GPK with Hadamard factors.
+ */
+typedef enum batq_transform {
+    BATQ_TRANSFORM_GPK = 0,
+    BATQ_TRANSFORM_KRONECKER = 1,
+    BATQ_TRANSFORM_FULL = 2
+} batq_transform;
+
 typedef enum batq_status {
     BATQ_OK = 0,
     BATQ_ERR_NULL = 1,        /* a required pointer is NULL                                  */
@@ -172,6 +184,41 @@ batq_status batq_quantize_act_mxfp8(const uint16_t* x, int64_t S, int64_t N, int
 batq_status batq_gemm_w4a8(const uint8_t* xq8, const uint8_t* xe,
                            const uint8_t* wq, const uint8_t* we, batq_scale_layout layout,
                            int64_t S, int64_t N, int64_t out, float* y, void* stream);
+
+/*
+ * Activation side with a chosen transform form (thelatestinai listing, Table 1; see
+ * batq_transform): the same clip and MXFP4 encode as batq_quantize_act, after
+ *   GPK:       Y = B_i^T (X A) on the row-major 4x8 view, as batq_quantize_act;
+ *   KRONECKER: the same with A_i in place of A;
+ *   FULL:      y_j = x_0 P_i[0][j], then fused multiply-adds over m = 1..31 in increasing m
+ *              (y = x P_i, x a row vector).
+ *   F0  dev  fp32: GPK A [8][8] (4-byte aligned); KRONECKER A [N/32][8][8]; FULL
+ *            P [N/32][32][32] (both 16-byte aligned)
+ *   F1  dev  fp32 B [N/32][4][4] (16-byte aligned) for GPK and KRONECKER; ignored (may be
+ *            NULL) for FULL
+ *   other arguments as batq_quantize_act.  BATQ_ERR_UNSUPPORTED for an unknown form or
+ *   layout.  Does not allocate or synchronise.
+ */
+batq_status batq_quantize_act_form(const uint16_t* x, int64_t S, int64_t N, int64_t ldx,
+                                   batq_transform form, const float* F0, const float* F1,
+                                   const float* r_min, const float* r_max,
+                                   uint8_t* q, uint8_t* e, batq_scale_layout e_layout,
+                                   void* stream);
+
+/*
+ * Offline weight preparation for a transform form: each weight block becomes W_i P_i^-T
+ * (X W^T = (X P)(W P^-T)^T; gist.science summary, section 2D), computed in the activation
+ * form with the transposed inverses of the factors (each the fp32 value nearest to the
+ * exact inverse, 64-bit-mantissa Gauss-Jordan on the host), then MXFP4 without clipping.
+ *   W dev fp32 [out, N] (16-byte aligned); F0_host / F1_host host factors as in
+ *   batq_quantize_act_form; wq / we / we_layout as batq_prepare_weight.
+ * Returns BATQ_ERR_SINGULAR if a factor is not invertible.  Offline step: allocates a device
+ * buffer for the factors and synchronises `stream` before returning.
+ */
+batq_status batq_prepare_weight_form(const float* W, int64_t out, int64_t N,
+                                     batq_transform form, const float* F0_host,
+                                     const float* F1_host, uint8_t* wq, uint8_t* we,
+                                     batq_scale_layout we_layout, void* stream);
 
 /*
  * Host: clip ratios r[i] = fp32(1 / (1 + exp(-alpha[i]))) evaluated in binary64 and rounded

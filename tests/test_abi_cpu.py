@@ -34,7 +34,8 @@ def test_library_exports_every_declared_entry_point(bq):
     names = declared_entry_points()
     assert names == sorted(["batq_quantize_act", "batq_prepare_weight", "batq_gemm_w4a4",
                             "batq_clip_ratios", "batq_weight_factors", "batq_status_string",
-                            "batq_quantize_act_mxfp8", "batq_gemm_w4a8"])
+                            "batq_quantize_act_mxfp8", "batq_gemm_w4a8",
+                            "batq_quantize_act_form", "batq_prepare_weight_form"])
     L = ctypes.CDLL(bq.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -115,6 +116,34 @@ def test_gemm_w4a8_argument_errors(bq):
     assert g(D, D, D, D, 4, 96, 8, D) == UNSUPPORTED               # N % 256
     assert g(D, D, D, D, 1 << 24, 256, 8, D) == UNSUPPORTED        # S * N >= 2^32
     assert g(D, D, D, D, 1 << 62, 256, 8, D) == SHAPE
+
+
+def test_transform_form_argument_errors_and_singular_factors(bq):
+    q = bq.quantize_act_form_raw
+    G, K, F = bq.TRANSFORM_GPK, bq.TRANSFORM_KRONECKER, bq.TRANSFORM_FULL
+    assert q(D, -1, 64, 64, F, D, 0, D, D, D, D) == SHAPE
+    assert q(D, 4, 48, 64, K, D, D, D, D, D, D) == SHAPE
+    assert q(0, 0, 64, 64, 5, 0, 0, 0, 0, 0, 0) == OK           # empty: nothing read
+    assert q(D, 4, 64, 64, 5, D, D, D, D, D, D) == UNSUPPORTED   # unknown form
+    assert q(D, 4, 64, 64, K, D, 0, D, D, D, D) == NULL          # Kronecker needs B
+    # (every case below stops in validation: no launch with these fake pointers)
+    assert q(D + 2, 4, 64, 64, F, D, 0, D, D, D, D) == ALIGN     # full form: F1 may be NULL
+    assert q(D, 4, 64, 64, F, D + 4, 0, D, D, D, D) == ALIGN     # P_i must be 16-aligned
+    assert q(D, 4, 64, 64, G, D + 2, D, D, D, D, D) == ALIGN     # a shared A: 4-aligned
+    assert q(D, 4, 64, 64, K, D, D + 8, D, D, D, D) == ALIGN
+    p = bq.prepare_weight_form_raw
+    k = 2
+    P = np.tile(np.eye(32, dtype=np.float32), (k, 1, 1))
+    assert p(D, 4, 64, 7, P.ctypes.data, 0, D, D) == UNSUPPORTED
+    assert p(D, 4, 64, K, P.ctypes.data, 0, D, D) == NULL
+    assert p(D, 4, 70, F, P.ctypes.data, 0, D, D) == SHAPE
+    Ps = P.copy()
+    Ps[1, 5] = Ps[1, 9]
+    assert p(D, 4, 64, F, Ps.ctypes.data, 0, D, D) == SINGULAR   # checked before device work
+    A = np.tile(np.eye(8, dtype=np.float32), (k, 1, 1))
+    A[0, 2] = 0
+    B = np.tile(np.eye(4, dtype=np.float32), (k, 1, 1))
+    assert p(D, 4, 64, K, A.ctypes.data, B.ctypes.data, D, D) == SINGULAR
 
 
 def test_prepare_weight_argument_errors_and_singular_factors(bq):

@@ -8,6 +8,9 @@ from ._binding import (  # noqa: F401
     SCALES_MFMA_TILED,
     SCALES_ROW_MAJOR,
     SIGNATURES,
+    TRANSFORM_FULL,
+    TRANSFORM_GPK,
+    TRANSFORM_KRONECKER,
     BatqError,
     clip_ratios,
     gemm_w4a4,
@@ -18,8 +21,12 @@ from ._binding import (  # noqa: F401
     linear_w4a4,
     linear_w4a8,
     prepare_weight,
+    prepare_weight_form,
+    prepare_weight_form_raw,
     prepare_weight_raw,
     quantize_act,
+    quantize_act_form,
+    quantize_act_form_raw,
     quantize_act_mxfp8,
     quantize_act_mxfp8_raw,
     quantize_act_raw,

@@ -25,6 +25,8 @@ SIGNATURES = {
     "batq_gemm_w4a4": [_P, _P, _P, _P, _I, _I64, _I64, _I64, _P, _P],
     "batq_quantize_act_mxfp8": [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _I, _P],
     "batq_gemm_w4a8": [_P, _P, _P, _P, _I, _I64, _I64, _I64, _P, _P],
+    "batq_quantize_act_form": [_P, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _I, _P],
+    "batq_prepare_weight_form": [_P, _I64, _I64, _I, _P, _P, _P, _P, _I, _P],
     "batq_clip_ratios": [_P, _I64, _P],
     "batq_weight_factors": [_P, _P, _I64, _P, _P],
     "batq_status_string": [_I],
@@ -35,6 +37,12 @@ SIGNATURES = {
 # the GEMM consumes them (32-row x 8-block units of 256 bytes).
 SCALES_ROW_MAJOR = 0
 SCALES_MFMA_TILED = 1
+
+# Transform forms (batq_transform): GPK, naive Kronecker with a private A_i per block, full
+# 32x32 P_i per block.
+TRANSFORM_GPK = 0
+TRANSFORM_KRONECKER = 1
+TRANSFORM_FULL = 2
 
 
 def scale_bytes(rows: int, N: int, layout: int) -> int:
@@ -100,6 +108,18 @@ def quantize_act_mxfp8_raw(x, S, N, ldx, A, B, r_min, r_max, q8, e, layout=SCALE
 
 def gemm_w4a8_raw(xq8, xe, wq, we, S, N, out, y, layout=SCALES_ROW_MAJOR, stream=0) -> int:
     return lib().batq_gemm_w4a8(xq8, xe, wq, we, layout, S, N, out, y, stream)
+
+
+def quantize_act_form_raw(x, S, N, ldx, form, F0, F1, r_min, r_max, q, e,
+                          layout=SCALES_ROW_MAJOR, stream=0) -> int:
+    return lib().batq_quantize_act_form(x, S, N, ldx, form, F0, F1, r_min, r_max, q, e, layout,
+                                        stream)
+
+
+def prepare_weight_form_raw(W, out, N, form, F0_host, F1_host, wq, we,
+                            layout=SCALES_ROW_MAJOR, stream=0) -> int:
+    return lib().batq_prepare_weight_form(W, out, N, form, F0_host, F1_host, wq, we, layout,
+                                          stream)
 
 
 def prepare_weight_raw(W, out, N, A_host, B_host, wq, we, layout=SCALES_ROW_MAJOR,
@@ -263,3 +283,43 @@ def linear_w4a8(x, A, B, r_min, r_max, wq, we, layout=SCALES_ROW_MAJOR, stream=N
     weights (scales `we` in `layout`)."""
     xq8, xe = quantize_act_mxfp8(x, A, B, r_min, r_max, layout=layout, stream=stream)
     return gemm_w4a8(xq8, xe, wq, we, layout=layout, stream=stream)
+
+
+# ---------------------------------------------------------------------------------------
+# Transform forms (GPK, naive Kronecker, full P_i)
+# ---------------------------------------------------------------------------------------
+
+def quantize_act_form(x, form, F0, F1, r_min, r_max, q=None, e=None, layout=SCALES_ROW_MAJOR,
+                      stream=None):
+    """Transform (of the given form) + clip + MXFP4 of bf16 activations x [S, N].  F0 / F1
+    device fp32: GPK A [8,8] / B [k,4,4]; KRONECKER A [k,8,8] / B [k,4,4]; FULL P [k,32,32] /
+    None."""
+    import torch
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    S, N = x.shape
+    if q is None:
+        q = torch.empty((S, N // 2), dtype=torch.uint8, device=x.device)
+    if e is None:
+        e = _scale_tensor(S, N, layout, x.device)
+    for t in (F0, r_min, r_max) + ((F1,) if F1 is not None else ()):
+        assert t.dtype == torch.float32 and t.is_contiguous()
+    _check("batq_quantize_act_form", quantize_act_form_raw(
+        _ptr(x), S, N, x.stride(0), form, _ptr(F0), _ptr(F1) if F1 is not None else 0,
+        _ptr(r_min), _ptr(r_max), _ptr(q), _ptr(e), layout, _stream(stream)))
+    return q, e
+
+
+def prepare_weight_form(W, form, F0_host, F1_host, layout=SCALES_ROW_MAJOR, stream=None):
+    """Offline: fp32 weights W [out, N] (device) -> MXFP4 codes and scales of W P^-T for a
+    transform form; F0_host / F1_host host arrays as for quantize_act_form."""
+    import torch
+    assert W.dtype == torch.float32 and W.is_contiguous() and W.dim() == 2
+    out, N = W.shape
+    F0 = _host_f32(F0_host)
+    F1 = _host_f32(F1_host) if F1_host is not None else None
+    wq = torch.empty((out, N // 2), dtype=torch.uint8, device=W.device)
+    we = _scale_tensor(out, N, layout, W.device)
+    _check("batq_prepare_weight_form", prepare_weight_form_raw(
+        _ptr(W), out, N, form, F0.ctypes.data, F1.ctypes.data if F1 is not None else 0,
+        _ptr(wq), _ptr(we), layout, _stream(stream)))
+    return wq, we

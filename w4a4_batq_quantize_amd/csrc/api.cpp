@@ -22,12 +22,12 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 batq_status from_hip(hipError_t err) { return err == hipSuccess ? BATQ_OK : BATQ_ERR_HIP; }
 
-// Inverse of an n x n fp32 matrix by Gauss-Jordan elimination with partial pivoting in
-// 64-bit-mantissa arithmetic, stored transposed and rounded once to fp32.  Returns false if
-// a pivot is zero or a result is not finite.
+// Inverse of an n x n fp32 matrix (n <= 32) by Gauss-Jordan elimination with partial
+// pivoting in 64-bit-mantissa arithmetic, stored transposed and rounded once to fp32.
+// Returns false if a pivot is zero or a result is not finite.
 bool inverse_transposed(const float* M, int n, float* out_t)
 {
-    long double a[8][16];
+    static thread_local long double a[32][64];
     for (int i = 0; i < n; ++i)
         for (int j = 0; j < 2 * n; ++j)
             a[i][j] = j < n ? (long double)M[i * n + j] : (long double)(j - n == i);
@@ -54,6 +54,18 @@ bool inverse_transposed(const float* M, int n, float* out_t)
         }
     return true;
 }
+
+bool valid_form(batq_transform t)
+{
+    return t == BATQ_TRANSFORM_GPK || t == BATQ_TRANSFORM_KRONECKER || t == BATQ_TRANSFORM_FULL;
+}
+
+// number of floats of the two factor arrays of a transform form with k blocks
+int64_t factor0_floats(batq_transform t, int64_t k)
+{
+    return t == BATQ_TRANSFORM_GPK ? 64 : t == BATQ_TRANSFORM_KRONECKER ? 64 * k : 1024 * k;
+}
+int64_t factor1_floats(batq_transform t, int64_t k) { return t == BATQ_TRANSFORM_FULL ? 0 : 16 * k; }
 
 bool valid_layout(batq_scale_layout l)
 {
@@ -208,4 +220,69 @@ BATQ_API batq_status batq_gemm_w4a8(const uint8_t* xq8, const uint8_t* xe, const
         return BATQ_ERR_UNSUPPORTED;
     return from_hip(batq::launch_gemm_w4a8(xq8, xe, wq, we, layout == BATQ_SCALES_MFMA_TILED,
                                            S, N, out, y, as_stream(stream)));
+}
+
+BATQ_API batq_status batq_quantize_act_form(const uint16_t* x, int64_t S, int64_t N, int64_t ldx,
+                                            batq_transform form, const float* F0,
+                                            const float* F1, const float* r_min,
+                                            const float* r_max, uint8_t* q, uint8_t* e,
+                                            batq_scale_layout e_layout, void* stream)
+{
+    if (S < 0 || N < 0 || N % 32 != 0) return BATQ_ERR_SHAPE;
+    if (S == 0 || N == 0) return BATQ_OK;
+    if (!valid_form(form) || !valid_layout(e_layout)) return BATQ_ERR_UNSUPPORTED;
+    if (!x || !F0 || (form != BATQ_TRANSFORM_FULL && !F1) || !r_min || !r_max || !q || !e)
+        return BATQ_ERR_NULL;
+    if (ldx < N || mul_overflows(S, ldx)) return BATQ_ERR_SHAPE;
+    if (ldx % 8 != 0 || !aligned(x, 16) || !aligned(q, 16) || !aligned(r_min, 4) ||
+        !aligned(r_max, 4) || !aligned(F0, form == BATQ_TRANSFORM_GPK ? 4 : 16) ||
+        (form != BATQ_TRANSFORM_FULL && !aligned(F1, 16)))
+        return BATQ_ERR_ALIGN;
+    const int64_t k = N / 32;
+    if (k > 64LL * 65535) return BATQ_ERR_UNSUPPORTED;
+    return from_hip(batq::launch_quantize(true, x, S, k, ldx, F0, F1, r_min, r_max, q, e,
+                                          e_layout == BATQ_SCALES_MFMA_TILED,
+                                          as_stream(stream), false, (int)form));
+}
+
+BATQ_API batq_status batq_prepare_weight_form(const float* W, int64_t out, int64_t N,
+                                              batq_transform form, const float* F0_host,
+                                              const float* F1_host, uint8_t* wq, uint8_t* we,
+                                              batq_scale_layout we_layout, void* stream)
+{
+    if (out < 0 || N < 0 || N % 32 != 0) return BATQ_ERR_SHAPE;
+    if (out == 0 || N == 0) return BATQ_OK;
+    if (!valid_form(form) || !valid_layout(we_layout)) return BATQ_ERR_UNSUPPORTED;
+    if (!W || !F0_host || (form != BATQ_TRANSFORM_FULL && !F1_host) || !wq || !we)
+        return BATQ_ERR_NULL;
+    if (mul_overflows(out, N)) return BATQ_ERR_SHAPE;
+    if (!aligned(W, 16) || !aligned(wq, 16)) return BATQ_ERR_ALIGN;
+    const int64_t k = N / 32;
+    if (k > 64LL * 65535) return BATQ_ERR_UNSUPPORTED;
+
+    // transposed inverses of every factor: F0 part then F1 part, each 16-byte aligned
+    const int64_t n0 = factor0_floats(form, k), n1 = factor1_floats(form, k);
+    std::vector<float> factors(n0 + n1);
+    const int64_t m0 = form == BATQ_TRANSFORM_GPK ? 1 : k;
+    const int d0 = form == BATQ_TRANSFORM_FULL ? 32 : 8;
+    for (int64_t i = 0; i < m0; ++i)
+        if (!inverse_transposed(F0_host + i * d0 * d0, d0, factors.data() + i * d0 * d0))
+            return BATQ_ERR_SINGULAR;
+    for (int64_t i = 0; i < n1 / 16; ++i)
+        if (!inverse_transposed(F1_host + 16 * i, 4, factors.data() + n0 + 16 * i))
+            return BATQ_ERR_SINGULAR;
+
+    hipStream_t s = as_stream(stream);
+    float* d = nullptr;
+    if (hipMalloc(&d, factors.size() * sizeof(float)) != hipSuccess) return BATQ_ERR_HIP;
+    hipError_t err = hipMemcpyAsync(d, factors.data(), factors.size() * sizeof(float),
+                                    hipMemcpyHostToDevice, s);
+    if (err == hipSuccess)
+        err = batq::launch_quantize(false, W, out, k, N, d, n1 ? d + n0 : nullptr, nullptr,
+                                    nullptr, wq, we, we_layout == BATQ_SCALES_MFMA_TILED, s,
+                                    false, (int)form);
+    const hipError_t sync = hipStreamSynchronize(s);
+    const hipError_t fr = hipFree(d);
+    if (err != hipSuccess || sync != hipSuccess || fr != hipSuccess) return BATQ_ERR_HIP;
+    return BATQ_OK;
 }

@@ -12,10 +12,13 @@ namespace batq {
 // Weight mode: fp32 input with row stride ldx, no clip (r_min/r_max unused).
 // Scales row-major, or in the MFMA-tiled layout of batq.h when tiled_scales.
 // fp8 (activation mode only): MXFP8 output, codes [rows, N] one E4M3 byte per element.
+// form: 0 GPK (A [8][8], B [k][4][4]); 1 Kronecker with private A_i (A [k][8][8], B as
+// GPK); 2 full P_i (A [k][32][32], B unused).  Forms 1 and 2 need 16-byte aligned A and do
+// not combine with fp8 (hipErrorNotSupported).
 hipError_t launch_quantize(bool act, const void* x, int64_t rows, int64_t k, int64_t ldx,
                            const float* A, const float* B, const float* r_min,
                            const float* r_max, uint8_t* q, uint8_t* e, bool tiled_scales,
-                           hipStream_t stream, bool fp8 = false);
+                           hipStream_t stream, bool fp8 = false, int form = 0);
 
 // MXFP4 x MXFP4 -> fp32 GEMM, y[S, out] = dq(x)[S, N] dq(w)[out, N]^T; both scale
 // arrays in the same layout (tiled_scales: MFMA-tiled, else row-major).

@@ -68,12 +68,47 @@ __device__ __forceinline__ void gpk_transform(const float (&x)[32], const float*
     }
 }
 
+// y = x P for one block with a full 32x32 P (y_j = sum_m x_m P[m][j]): a product for m = 0,
+// then one fused multiply-add per m in increasing m (thelatestinai listing, Table 1, the
+// "w/o decomposition" form).  The rows of P stream in as 16-byte loads; every row of the
+// activations reads the same P_i, so they come from cache.
+__device__ __forceinline__ void full_transform(const float (&x)[32], const float* __restrict__ P,
+                                               float (&y)[32])
+{
+    const float4* pr = reinterpret_cast<const float4*>(P);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const float4 v = pr[t];
+        y[4 * t] = x[0] * v.x;
+        y[4 * t + 1] = x[0] * v.y;
+        y[4 * t + 2] = x[0] * v.z;
+        y[4 * t + 3] = x[0] * v.w;
+    }
+#pragma unroll 4
+    for (int m = 1; m < 32; ++m) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const float4 v = pr[8 * m + t];
+            y[4 * t] = __builtin_fmaf(x[m], v.x, y[4 * t]);
+            y[4 * t + 1] = __builtin_fmaf(x[m], v.y, y[4 * t + 1]);
+            y[4 * t + 2] = __builtin_fmaf(x[m], v.z, y[4 * t + 2]);
+            y[4 * t + 3] = __builtin_fmaf(x[m], v.w, y[4 * t + 3]);
+        }
+    }
+}
+
+// kForm selects the transform (thelatestinai listing, Table 1): 0 GPK, A [8][8] shared by
+// every block (read through the scalar unit); 1 naive Kronecker, a private A_i [8][8] per
+// block, same reshape evaluation; 2 a full 32x32 P_i per block (A points at P [k][32][32],
+// B is unused).  For forms 1 and 2 a workgroup owns one block column (blockIdx.x) and its
+// threads take consecutive rows, so A_i / P_i (and B_i) are uniform across the wave and
+// come through the scalar unit as FMA operands, like GPK's A.
 // kFp8 (activations only): MXFP8 output, one E4M3 code byte per element (the W4A8
 // setting).  Same transform and clip; the scale exponent is floor(log2 amax) - 8 (E4M3's
 // largest exponent), and the conversion instruction, exact round-to-nearest-even otherwise,
 // returns NaN above 448 where MX saturates, so the clip bounds are first clamped into
 // [-448 s, 448 s] (a clamp of a clamp is the clamp to the clamped bounds).
-template <bool kAct, bool kFp8 = false>
+template <bool kAct, bool kFp8 = false, int kForm = 0>
 __global__ void __launch_bounds__(kThreads)
 quantize_kernel(const void* __restrict__ xin, int64_t rows, int64_t k, int64_t ldx,
                 const float* __restrict__ A, const float* __restrict__ B,
@@ -84,9 +119,15 @@ quantize_kernel(const void* __restrict__ xin, int64_t rows, int64_t k, int64_t l
     static_assert(kAct || !kFp8, "MXFP8 is an activation-side format");
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int64_t row = ((((int64_t)blockIdx.x * kWavesPerGroup + wave) << (6 - lpr_log2)) +
-                         (lane >> lpr_log2));
-    const int64_t blk = (int64_t)blockIdx.y * 64 + (lane & ((1 << lpr_log2) - 1));
+    int64_t row, blk;
+    if constexpr (kForm != 0) {
+        blk = blockIdx.x;
+        row = (int64_t)blockIdx.y * kThreads + threadIdx.x;
+    } else {
+        row = ((((int64_t)blockIdx.x * kWavesPerGroup + wave) << (6 - lpr_log2)) +
+               (lane >> lpr_log2));
+        blk = (int64_t)blockIdx.y * 64 + (lane & ((1 << lpr_log2) - 1));
+    }
     if (row >= rows || blk >= k) return;
 
     float x[32];
@@ -117,13 +158,16 @@ quantize_kernel(const void* __restrict__ xin, int64_t rows, int64_t k, int64_t l
             x[4 * t + 3] = v.w;
         }
     }
-    const float4* bp = reinterpret_cast<const float4*>(B + 16 * blk);
-    float4 b[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) b[t] = bp[t];
-
     float y[32];
-    gpk_transform(x, A, b, y);
+    if constexpr (kForm == 2) {
+        full_transform(x, A + 1024 * blk, y);
+    } else {
+        const float4* bp = reinterpret_cast<const float4*>(B + 16 * blk);
+        float4 b[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) b[t] = bp[t];
+        gpk_transform(x, kForm == 1 ? A + 64 * blk : A, b, y);
+    }
 
     float amax;
     float lo = 0.0f, hi = 0.0f;
@@ -200,8 +244,9 @@ quantize_kernel(const void* __restrict__ xin, int64_t rows, int64_t k, int64_t l
 hipError_t launch_quantize(bool act, const void* x, int64_t rows, int64_t k, int64_t ldx,
                            const float* A, const float* B, const float* r_min,
                            const float* r_max, uint8_t* q, uint8_t* e, bool tiled_scales,
-                           hipStream_t stream, bool fp8)
+                           hipStream_t stream, bool fp8, int form)
 {
+    if (form < 0 || form > 2 || (fp8 && form != 0)) return hipErrorNotSupported;
     // lanes per row: the smallest power of two >= k, capped at one wave
     int lpr_log2 = 0;
     while ((1LL << lpr_log2) < k && lpr_log2 < 6) ++lpr_log2;
@@ -211,7 +256,26 @@ hipError_t launch_quantize(bool act, const void* x, int64_t rows, int64_t k, int
     const int64_t gy = (k + 63) / 64;
     if (gx > 0x7FFFFFFF || gy > 65535) return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)gx, (unsigned)gy);
-    if (act && fp8)
+    if (form != 0) {
+        // one block column per workgroup, kThreads rows each
+        const int64_t gr = (rows + kThreads - 1) / kThreads;
+        if (k > 0x7FFFFFFF || gr > 65535) return hipErrorInvalidConfiguration;
+        grid = dim3((unsigned)k, (unsigned)gr);
+    }
+    const int ts = (int)tiled_scales;
+    if (form == 1 && act)
+        hipLaunchKernelGGL((quantize_kernel<true, false, 1>), grid, dim3(kThreads), 0, stream,
+                           x, rows, k, ldx, A, B, r_min, r_max, q, e, lpr_log2, ts);
+    else if (form == 1)
+        hipLaunchKernelGGL((quantize_kernel<false, false, 1>), grid, dim3(kThreads), 0, stream,
+                           x, rows, k, ldx, A, B, r_min, r_max, q, e, lpr_log2, ts);
+    else if (form == 2 && act)
+        hipLaunchKernelGGL((quantize_kernel<true, false, 2>), grid, dim3(kThreads), 0, stream,
+                           x, rows, k, ldx, A, B, r_min, r_max, q, e, lpr_log2, ts);
+    else if (form == 2)
+        hipLaunchKernelGGL((quantize_kernel<false, false, 2>), grid, dim3(kThreads), 0, stream,
+                           x, rows, k, ldx, A, B, r_min, r_max, q, e, lpr_log2, ts);
+    else if (act && fp8)
         hipLaunchKernelGGL((quantize_kernel<true, true>), grid, dim3(kThreads), 0, stream, x,
                            rows, k, ldx, A, B, r_min, r_max, q, e, lpr_log2, (int)tiled_scales);
     else if (act)

@@ -166,3 +166,20 @@ def random_mxfp8(rows: int, N: int, seed, scale_lo: int = 110, scale_hi: int = 1
     q[(q & 0x7F) == 0x7F] -= 1
     e = rng.integers(scale_lo, scale_hi, size=(rows, N // 32), dtype=np.uint8)
     return q, e
+
+
+def form_factors(form: int, k: int, seed):
+    """Seeded near-identity factors for a transform form (0 GPK, 1 Kronecker with private
+    A_i, 2 full 32x32 P_i), drawn like the GPK factors of make_layer: identity plus 0.1 N(0,1)
+    (0.05 for the 32x32 P_i).  Returns (F0, F1); F1 is None for the full form."""
+    seed = list(seed) if isinstance(seed, (tuple, list)) else [int(seed)]
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
+    if form == 2:
+        P = np.eye(32) + 0.05 * rng.standard_normal((k, 32, 32))
+        return P.astype(np.float32), None
+    B = (np.eye(4) + 0.1 * rng.standard_normal((k, 4, 4))).astype(np.float32)
+    if form == 1:
+        A = (np.eye(8) + 0.1 * rng.standard_normal((k, 8, 8))).astype(np.float32)
+    else:
+        A = (np.eye(8) + 0.1 * rng.standard_normal((8, 8))).astype(np.float32)
+    return A, B
