@@ -53,11 +53,13 @@ def k2_flops(S, N, out):
     return 2 * S * N * out
 
 
-def k2_bytes(S, N, out, act_code_bytes=0.5):
+def k2_bytes(S, N, out, act_code_bytes=0.5, epilogue="f32"):
     """Compulsory bytes of one GEMM launch: both operands once (activation codes 0.5 or
-    1 B/elem, weight codes 0.5 B/elem, one scale byte per 32), fp32 output once."""
+    1 B/elem, weight codes 0.5 B/elem, one scale byte per 32), the output once (fp32 4 B or
+    bf16 2 B per element) and, with a residual, the bf16 residual once."""
+    out_b = {"f32": 4, "bf16": 2, "bf16_residual": 4}[epilogue]
     return (int(S * N * act_code_bytes) + S * (N // 32) + out * (N // 2 + N // 32)
-            + 4 * S * out)
+            + out_b * S * out)
 
 
 def measured_traffic(kernel: str, workload: str):
@@ -129,6 +131,7 @@ def measure(name, args):
     k = N // 32
     w4a8 = args.precision == "w4a8"
     form = getattr(args, "form", "gpk")
+    epilogue = getattr(args, "epilogue", "f32")
     if w4a8 and form != "gpk":
         raise SystemExit("bench.py: --form applies to the W4A4 path")
     cb = 1.0 if w4a8 else 0.5                 # activation code bytes per element
@@ -161,7 +164,10 @@ def measure(name, args):
     xqs = [torch.empty((S, int(N * cb)), dtype=torch.uint8, device=dev) for _ in range(R)]
     xes = [torch.empty((bq.scale_bytes(S, N, layout),), dtype=torch.uint8, device=dev)
            for _ in range(R)]
-    ys = [torch.empty((S, out), dtype=torch.float32, device=dev) for _ in range(R)]
+    ydt = torch.float32 if epilogue == "f32" else torch.bfloat16
+    ys = [torch.empty((S, out), dtype=ydt, device=dev) for _ in range(R)]
+    resid = (torch.randn((S, out), device=dev).to(torch.bfloat16)
+             if epilogue == "bf16_residual" else None)
     del x0, wq0, we0
 
     stream = torch.cuda.current_stream()
@@ -181,6 +187,13 @@ def measure(name, args):
     def launch_k1(j):
         x, xq, xe, _, _, _ = ptr[j]
         return quant(x, S, N, N, pA, pB, pr1, pr2, xq, xe, layout, sh)
+
+    if epilogue != "f32":
+        gemm_out = bq.gemm_w4a8_out_raw if w4a8 else bq.gemm_w4a4_out_raw
+        pres = resid.data_ptr() if resid is not None else 0
+
+        def gemm(xq, xe, wq, we, S_, N_, out_, y, lay, st):
+            return gemm_out(xq, xe, wq, we, S_, N_, out_, y, bq.OUT_BF16, pres, lay, st)
 
     def launch_k2(j):
         _, xq, xe, wq, we, y = ptr[j]
@@ -236,7 +249,7 @@ def measure(name, args):
     assert bool(torch.isfinite(last).all().item()), "non-finite GEMM output"
 
     b1 = k1_bytes(S, N, cb, form)
-    b2 = k2_bytes(S, N, out, cb)
+    b2 = k2_bytes(S, N, out, cb, epilogue)
     gbs = b1 / t_k1 / 1e9
     tflops = k2_flops(S, N, out) / t_k2 / 1e12
     k2_ai = k2_flops(S, N, out) / b2
@@ -245,7 +258,7 @@ def measure(name, args):
     k2_name = ("gemm_w4a8_kernel" if w4a8 else
                "gemm_skinny_kernel" if S <= 64 else "gemm_pc_kernel")
     tr1 = measured_traffic(k1_name, L.cfg.name) if form == "gpk" else None
-    tr2 = measured_traffic(k2_name, L.cfg.name)
+    tr2 = measured_traffic(k2_name, L.cfg.name) if epilogue == "f32" else None
     roof_k1 = {"kernel": f"{k1_name} (fused BAT+clip+{'MXFP8' if w4a8 else 'MXFP4'}"
                          + ("" if form == "gpk" else f", {form} transform") + ")",
                "bound": "hbm",
@@ -287,7 +300,8 @@ def measure(name, args):
         "config": {"workload": f"{L.cfg.name}: S={S} N={N} out={out} (Qwen3-8B-shaped linear "
                                f"layer, seeded synthetic bf16 activations and fp32 weights)",
                    "S": S, "N": N, "out": out, "rotated_buffer_sets": R,
-                   "scale_layout": "mfma_tiled", "transform": form},
+                   "scale_layout": "mfma_tiled", "transform": form,
+                   "gemm_output": epilogue},
         "gemm": {"value": round(tflops, 1), "unit": "TFLOP/s",
                  "pct_of_peak": round(100 * tflops / peak, 2)},
         "step_gpu_us": round(t_step_ev * 1e6, 3),
@@ -315,6 +329,9 @@ def main():
     ap.add_argument("--form", choices=tuple(FORMS), default="gpk",
                     help="transform form of the quantiser (thelatestinai listing, Table 1): "
                          "gpk (the method), kronecker (private A_i), full (32x32 P_i)")
+    ap.add_argument("--epilogue", choices=("f32", "bf16", "bf16_residual"), default="f32",
+                    help="GEMM output: fp32 (the defined output), bf16, or bf16 plus a bf16 "
+                         "residual")
     ap.add_argument("--all", action="store_true",
                     help="measure every layer configuration, one JSON line each (no CPU baseline)")
     args = ap.parse_args()

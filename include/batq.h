@@ -72,6 +72,12 @@ typedef enum batq_transform {
     BATQ_TRANSFORM_FULL = 2
 } batq_transform;
 
+/* Output element type of the GEMMs' epilogue variants. */
+typedef enum batq_out_type {
+    BATQ_OUT_F32 = 0,
+    BATQ_OUT_BF16 = 1
+} batq_out_type;
+
 typedef enum batq_status {
     BATQ_OK = 0,
     BATQ_ERR_NULL = 1,        /* a required pointer is NULL                                  */
@@ -219,6 +225,28 @@ batq_status batq_prepare_weight_form(const float* W, int64_t out, int64_t N,
                                      batq_transform form, const float* F0_host,
                                      const float* F1_host, uint8_t* wq, uint8_t* we,
                                      batq_scale_layout we_layout, void* stream);
+
+/*
+ * The GEMMs with a fused epilogue, for the layer's neighbours (a residual connection and a
+ * bf16 consumer): out[s][o] = round(acc[s][o] + res[s][o]) where acc is the fp32 result of
+ * batq_gemm_w4a4 / batq_gemm_w4a8 (same kernels, same accumulation), res an optional bf16
+ * residual converted exactly to fp32 and added with one fp32 rounding, and round() the
+ * identity for BATQ_OUT_F32 or fp32 -> bf16 to nearest, ties to even, for BATQ_OUT_BF16.
+ * The pages define the linear layer only (gist.science summary, section 4); this is the
+ * plain reading of its output feeding the next layer.
+ *   y         dev  out: [S, out] of y_type, 16-byte aligned, overwritten
+ *   residual  dev  bf16 [S, out] (16-byte aligned) or NULL
+ *   other arguments and errors as batq_gemm_w4a4 / batq_gemm_w4a8 (BATQ_ERR_UNSUPPORTED
+ *   also for an unknown y_type).  Does not allocate or synchronise.
+ */
+batq_status batq_gemm_w4a4_out(const uint8_t* xq, const uint8_t* xe,
+                               const uint8_t* wq, const uint8_t* we, batq_scale_layout layout,
+                               int64_t S, int64_t N, int64_t out, void* y,
+                               batq_out_type y_type, const uint16_t* residual, void* stream);
+batq_status batq_gemm_w4a8_out(const uint8_t* xq8, const uint8_t* xe,
+                               const uint8_t* wq, const uint8_t* we, batq_scale_layout layout,
+                               int64_t S, int64_t N, int64_t out, void* y,
+                               batq_out_type y_type, const uint16_t* residual, void* stream);
 
 /*
  * Host: clip ratios r[i] = fp32(1 / (1 + exp(-alpha[i]))) evaluated in binary64 and rounded

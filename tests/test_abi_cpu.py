@@ -35,7 +35,8 @@ def test_library_exports_every_declared_entry_point(bq):
     assert names == sorted(["batq_quantize_act", "batq_prepare_weight", "batq_gemm_w4a4",
                             "batq_clip_ratios", "batq_weight_factors", "batq_status_string",
                             "batq_quantize_act_mxfp8", "batq_gemm_w4a8",
-                            "batq_quantize_act_form", "batq_prepare_weight_form"])
+                            "batq_quantize_act_form", "batq_prepare_weight_form",
+                            "batq_gemm_w4a4_out", "batq_gemm_w4a8_out"])
     L = ctypes.CDLL(bq.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -144,6 +145,16 @@ def test_transform_form_argument_errors_and_singular_factors(bq):
     A[0, 2] = 0
     B = np.tile(np.eye(4, dtype=np.float32), (k, 1, 1))
     assert p(D, 4, 64, K, A.ctypes.data, B.ctypes.data, D, D) == SINGULAR
+
+
+def test_gemm_epilogue_argument_errors(bq):
+    for g, n in ((bq.gemm_w4a4_out_raw, 64), (bq.gemm_w4a8_out_raw, 256)):
+        assert g(D, D, D, D, -1, n, 8, D) == SHAPE
+        assert g(0, 0, 0, 0, 0, n, 8, 0) == OK
+        assert g(D, D, D, D, 4, n, 8, 0) == NULL
+        assert g(D, D, D, D, 4, n, 8, D, 3) == UNSUPPORTED            # unknown output type
+        assert g(D, D, D, D, 4, n, 8, D, 1, D + 8) == ALIGN           # residual alignment
+        assert g(D, D, D, D, 4, n, 8, D + 8, 1) == ALIGN              # output alignment
 
 
 def test_prepare_weight_argument_errors_and_singular_factors(bq):

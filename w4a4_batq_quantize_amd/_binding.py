@@ -25,6 +25,8 @@ SIGNATURES = {
     "batq_gemm_w4a4": [_P, _P, _P, _P, _I, _I64, _I64, _I64, _P, _P],
     "batq_quantize_act_mxfp8": [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _I, _P],
     "batq_gemm_w4a8": [_P, _P, _P, _P, _I, _I64, _I64, _I64, _P, _P],
+    "batq_gemm_w4a4_out": [_P, _P, _P, _P, _I, _I64, _I64, _I64, _P, _I, _P, _P],
+    "batq_gemm_w4a8_out": [_P, _P, _P, _P, _I, _I64, _I64, _I64, _P, _I, _P, _P],
     "batq_quantize_act_form": [_P, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _I, _P],
     "batq_prepare_weight_form": [_P, _I64, _I64, _I, _P, _P, _P, _P, _I, _P],
     "batq_clip_ratios": [_P, _I64, _P],
@@ -40,6 +42,9 @@ SCALES_MFMA_TILED = 1
 
 # Transform forms (batq_transform): GPK, naive Kronecker with a private A_i per block, full
 # 32x32 P_i per block.
+OUT_F32 = 0
+OUT_BF16 = 1
+
 TRANSFORM_GPK = 0
 TRANSFORM_KRONECKER = 1
 TRANSFORM_FULL = 2
@@ -120,6 +125,18 @@ def prepare_weight_form_raw(W, out, N, form, F0_host, F1_host, wq, we,
                             layout=SCALES_ROW_MAJOR, stream=0) -> int:
     return lib().batq_prepare_weight_form(W, out, N, form, F0_host, F1_host, wq, we, layout,
                                           stream)
+
+
+def gemm_w4a4_out_raw(xq, xe, wq, we, S, N, out, y, y_type=0, residual=0,
+                      layout=SCALES_ROW_MAJOR, stream=0) -> int:
+    return lib().batq_gemm_w4a4_out(xq, xe, wq, we, layout, S, N, out, y, y_type, residual,
+                                    stream)
+
+
+def gemm_w4a8_out_raw(xq8, xe, wq, we, S, N, out, y, y_type=0, residual=0,
+                      layout=SCALES_ROW_MAJOR, stream=0) -> int:
+    return lib().batq_gemm_w4a8_out(xq8, xe, wq, we, layout, S, N, out, y, y_type, residual,
+                                    stream)
 
 
 def prepare_weight_raw(W, out, N, A_host, B_host, wq, we, layout=SCALES_ROW_MAJOR,
@@ -323,3 +340,36 @@ def prepare_weight_form(W, form, F0_host, F1_host, layout=SCALES_ROW_MAJOR, stre
         _ptr(W), out, N, form, F0.ctypes.data, F1.ctypes.data if F1 is not None else 0,
         _ptr(wq), _ptr(we), layout, _stream(stream)))
     return wq, we
+
+
+# ---------------------------------------------------------------------------------------
+# GEMM epilogue: bf16 output and/or a bf16 residual
+# ---------------------------------------------------------------------------------------
+
+def gemm_out(xq, xe, wq, we, out_dtype=None, residual=None, y=None, layout=SCALES_ROW_MAJOR,
+             w4a8=False, stream=None):
+    """W4A4 (or, with w4a8=True, W4A8: xq holds E4M3 codes [S, N]) GEMM with the fused
+    epilogue y = round(acc + residual): out_dtype torch.float32 (default) or torch.bfloat16,
+    residual a bf16 [S, out] tensor or None."""
+    import torch
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    assert out_dtype in (torch.float32, torch.bfloat16)
+    S = xq.shape[0]
+    N = xq.shape[1] if w4a8 else xq.shape[1] * 2
+    out = wq.shape[0]
+    for t in (xq, xe, wq, we):
+        assert t.dtype == torch.uint8 and t.is_contiguous()
+    assert wq.shape[1] * 2 == N
+    assert xe.numel() == scale_bytes(S, N, layout) and we.numel() == scale_bytes(out, N, layout)
+    if residual is not None:
+        assert residual.dtype == torch.bfloat16 and residual.shape == (S, out)
+        assert residual.is_contiguous()
+    if y is None:
+        y = torch.empty((S, out), dtype=out_dtype, device=xq.device)
+    assert y.dtype == out_dtype and y.shape == (S, out) and y.is_contiguous()
+    yt = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32
+    fn, raw = (("batq_gemm_w4a8_out", gemm_w4a8_out_raw) if w4a8 else
+               ("batq_gemm_w4a4_out", gemm_w4a4_out_raw))
+    _check(fn, raw(_ptr(xq), _ptr(xe), _ptr(wq), _ptr(we), S, N, out, _ptr(y), yt,
+                   _ptr(residual) if residual is not None else 0, layout, _stream(stream)))
+    return y

@@ -286,3 +286,44 @@ BATQ_API batq_status batq_prepare_weight_form(const float* W, int64_t out, int64
     if (err != hipSuccess || sync != hipSuccess || fr != hipSuccess) return BATQ_ERR_HIP;
     return BATQ_OK;
 }
+
+BATQ_API batq_status batq_gemm_w4a4_out(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq,
+                                        const uint8_t* we, batq_scale_layout layout, int64_t S,
+                                        int64_t N, int64_t out, void* y, batq_out_type y_type,
+                                        const uint16_t* residual, void* stream)
+{
+    if (S < 0 || N < 0 || out < 0 || N % 32 != 0) return BATQ_ERR_SHAPE;
+    if (S == 0 || out == 0) return BATQ_OK;
+    if (!y || (N > 0 && (!xq || !xe || !wq || !we))) return BATQ_ERR_NULL;
+    if (!valid_layout(layout) || (y_type != BATQ_OUT_F32 && y_type != BATQ_OUT_BF16))
+        return BATQ_ERR_UNSUPPORTED;
+    if (mul_overflows(S, out) || mul_overflows(S, N) || mul_overflows(out, N))
+        return BATQ_ERR_SHAPE;
+    if (!aligned(y, 16) || !aligned(xq, 16) || !aligned(wq, 16) || !aligned(residual, 16))
+        return BATQ_ERR_ALIGN;
+    return from_hip(batq::launch_gemm(xq, xe, wq, we, layout == BATQ_SCALES_MFMA_TILED, S, N,
+                                      out, static_cast<float*>(y), as_stream(stream), residual,
+                                      y_type == BATQ_OUT_BF16));
+}
+
+BATQ_API batq_status batq_gemm_w4a8_out(const uint8_t* xq8, const uint8_t* xe, const uint8_t* wq,
+                                        const uint8_t* we, batq_scale_layout layout, int64_t S,
+                                        int64_t N, int64_t out, void* y, batq_out_type y_type,
+                                        const uint16_t* residual, void* stream)
+{
+    if (S < 0 || N < 0 || out < 0 || N % 32 != 0) return BATQ_ERR_SHAPE;
+    if (S == 0 || out == 0) return BATQ_OK;
+    if (!y || (N > 0 && (!xq8 || !xe || !wq || !we))) return BATQ_ERR_NULL;
+    if (!valid_layout(layout) || (y_type != BATQ_OUT_F32 && y_type != BATQ_OUT_BF16))
+        return BATQ_ERR_UNSUPPORTED;
+    if (mul_overflows(S, out) || mul_overflows(S, N) || mul_overflows(out, N))
+        return BATQ_ERR_SHAPE;
+    if (!aligned(y, 16) || !aligned(xq8, 16) || !aligned(wq, 16) || !aligned(xe, 4) ||
+        !aligned(we, 4) || !aligned(residual, 16))
+        return BATQ_ERR_ALIGN;
+    if (N % 256 != 0 || S * N >= (1LL << 32) || out * (N / 2) >= (1LL << 32))
+        return BATQ_ERR_UNSUPPORTED;
+    return from_hip(batq::launch_gemm_w4a8(xq8, xe, wq, we, layout == BATQ_SCALES_MFMA_TILED,
+                                           S, N, out, static_cast<float*>(y), as_stream(stream),
+                                           residual, y_type == BATQ_OUT_BF16));
+}

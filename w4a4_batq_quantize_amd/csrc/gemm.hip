@@ -116,7 +116,62 @@ struct DmaArgs {
     const uint8_t* wq;
     const uint8_t* we;
     int64_t S, k, out;
+    // epilogue: optional bf16 residual [S, out] added in fp32, and bf16 output (round to
+    // nearest even) instead of fp32
+    const uint16_t* res;
+    int out_bf16;
 };
+
+// fp32 -> bf16, round to nearest, ties to even (outputs are finite)
+__device__ __forceinline__ uint32_t bf16_rne(float v)
+{
+    const uint32_t u = __float_as_uint(v);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Four consecutive outputs y[s][o .. o+3] (the first `valid` of them inside the matrix)
+// through the epilogue; `vec`: 16-byte fp32 / 8-byte bf16 accesses are aligned and legal.
+__device__ __forceinline__ void epi_store4(const DmaArgs& p, float* __restrict__ y, int64_t s,
+                                           int64_t o, float v0, float v1, float v2, float v3,
+                                           int valid, bool vec)
+{
+    float v[4] = {v0, v1, v2, v3};
+    const int64_t idx = s * p.out + o;
+    const bool full = vec && valid >= 4;
+    if (p.res) {
+        if (full) {
+            const uint2 r = *reinterpret_cast<const uint2*>(p.res + idx);
+            v[0] += __uint_as_float(r.x << 16);
+            v[1] += __uint_as_float(r.x & 0xFFFF0000u);
+            v[2] += __uint_as_float(r.y << 16);
+            v[3] += __uint_as_float(r.y & 0xFFFF0000u);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (j < valid) v[j] += __uint_as_float((uint32_t)p.res[idx + j] << 16);
+        }
+    }
+    if (p.out_bf16) {
+        uint16_t* d = reinterpret_cast<uint16_t*>(y) + idx;
+        if (full) {
+            *reinterpret_cast<uint2*>(d) = make_uint2(bf16_rne(v[0]) | (bf16_rne(v[1]) << 16),
+                                                      bf16_rne(v[2]) | (bf16_rne(v[3]) << 16));
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (j < valid) d[j] = (uint16_t)bf16_rne(v[j]);
+        }
+    } else {
+        float* d = y + idx;
+        if (full) {
+            *reinterpret_cast<float4*>(d) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (j < valid) d[j] = v[j];
+        }
+    }
+}
 
 // Per-lane source offsets of this wave's DMA instructions for the tile (stage 0); the
 // stage offset is uniform and added to the base.  Rows past the end are clamped to the
@@ -464,6 +519,27 @@ __device__ __forceinline__ void store_tile(const v16f (&acc)[C::TM][C::TN], cons
                                            int wrow0, int xrow0, int lane, int nt_store = 0)
 {
     const int lr = lane & 31, lg = lane >> 5;
+    if (p.res || p.out_bf16) {
+        // epilogue with a residual and/or bf16 output
+        const bool vec = (p.out & 3) == 0;
+#pragma unroll
+        for (int b = 0; b < C::TN; ++b) {
+            const int64_t s = s0 + xrow0 + 32 * b + lr;
+            if (s >= p.S) continue;
+#pragma unroll
+            for (int a = 0; a < C::TM; ++a) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int64_t o = o0 + wrow0 + 32 * a + 8 * g + 4 * lg;
+                    if (o >= p.out) continue;
+                    epi_store4(p, y, s, o, acc[a][b][4 * g], acc[a][b][4 * g + 1],
+                               acc[a][b][4 * g + 2], acc[a][b][4 * g + 3],
+                               (int)(p.out - o < 4 ? p.out - o : 4), vec);
+                }
+            }
+        }
+        return;
+    }
     const bool interior = (p.out & 3) == 0 && o0 + C::BO <= p.out && s0 + C::BS <= p.S;
     if (interior) {
         // whole tile inside the output: unconditional 16-byte stores, one 32x32 tile at a
@@ -826,6 +902,7 @@ gemm_generic_kernel(DmaArgs p, int tiled, float* __restrict__ y, int64_t tiles_o
     }
 
     const bool vec_ok = (p.out & 3) == 0;
+    const bool epi = p.res || p.out_bf16;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
         const int64_t o = o0 + wo * 64 + 16 * a + 4 * lg;
@@ -833,6 +910,12 @@ gemm_generic_kernel(DmaArgs p, int tiled, float* __restrict__ y, int64_t tiles_o
         for (int b = 0; b < 4; ++b) {
             const int64_t s = s0 + wsx * 64 + 16 * b + lr;
             if (s >= p.S) continue;
+            if (epi) {
+                if (o < p.out)
+                    epi_store4(p, y, s, o, acc[a][b][0], acc[a][b][1], acc[a][b][2],
+                               acc[a][b][3], (int)(p.out - o < 4 ? p.out - o : 4), vec_ok);
+                continue;
+            }
             float* dst = y + s * p.out + o;
             if (vec_ok && o + 3 < p.out) {
                 *reinterpret_cast<float4*>(dst) =
@@ -1031,7 +1114,11 @@ gemm_skinny_kernel(DmaArgs p, float* __restrict__ y)
         }
         const int64_t srow = 32 * b + lr;
         const int64_t o = o0 + 8 * g + 4 * lg;
-        if (srow < p.S) {
+        if (srow < p.S && (p.res || p.out_bf16)) {
+            if (o < p.out)
+                epi_store4(p, y, srow, o, v[0], v[1], v[2], v[3],
+                           (int)(p.out - o < 4 ? p.out - o : 4), (p.out & 3) == 0);
+        } else if (srow < p.S) {
             float* dst = y + srow * p.out + o;
             if ((p.out & 3) == 0 && o + 3 < p.out) {
                 *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
@@ -1326,9 +1413,10 @@ gemm_w4a8_kernel(DmaArgs p, float* __restrict__ y, int64_t tiles_o, int64_t tile
 
 hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq,
                        const uint8_t* we, bool tiled_scales, int64_t S, int64_t N,
-                       int64_t out, float* y, hipStream_t stream)
+                       int64_t out, float* y, hipStream_t stream, const uint16_t* res,
+                       bool out_bf16)
 {
-    const DmaArgs p{xq, xe, wq, we, S, N / 32, out};
+    const DmaArgs p{xq, xe, wq, we, S, N / 32, out, res, out_bf16 ? 1 : 0};
     const uintptr_t salign = tiled_scales ? 256 : 8;
     const bool dma_ok = (p.k % kStageBlocks) == 0 &&
                         (reinterpret_cast<uintptr_t>(xe) % salign) == 0 &&
@@ -1383,9 +1471,10 @@ hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq,
 
 hipError_t launch_gemm_w4a8(const uint8_t* xq8, const uint8_t* xe, const uint8_t* wq,
                             const uint8_t* we, bool tiled_scales, int64_t S, int64_t N,
-                            int64_t out, float* y, hipStream_t stream)
+                            int64_t out, float* y, hipStream_t stream, const uint16_t* res,
+                       bool out_bf16)
 {
-    const DmaArgs p{xq8, xe, wq, we, S, N / 32, out};
+    const DmaArgs p{xq8, xe, wq, we, S, N / 32, out, res, out_bf16 ? 1 : 0};
     if ((p.k % kStageBlocks) != 0 || (reinterpret_cast<uintptr_t>(xe) % 4) != 0 ||
         (reinterpret_cast<uintptr_t>(we) % 4) != 0 || S * 32 * p.k >= (1LL << 32) ||
         out * 16 * p.k >= (1LL << 32))

@@ -22,15 +22,19 @@ hipError_t launch_quantize(bool act, const void* x, int64_t rows, int64_t k, int
 
 // MXFP4 x MXFP4 -> fp32 GEMM, y[S, out] = dq(x)[S, N] dq(w)[out, N]^T; both scale
 // arrays in the same layout (tiled_scales: MFMA-tiled, else row-major).
+// Epilogue (both GEMMs): res, when not null, is a bf16 [S, out] residual added in fp32;
+// out_bf16 stores bf16 (round to nearest even) instead of fp32 (y then points at bf16).
 hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq,
                        const uint8_t* we, bool tiled_scales, int64_t S, int64_t N,
-                       int64_t out, float* y, hipStream_t stream);
+                       int64_t out, float* y, hipStream_t stream,
+                       const uint16_t* res = nullptr, bool out_bf16 = false);
 
 // W4A8: MXFP8 (E4M3) activations xq8 [S, N] (one byte per element) x MXFP4 weights.
 // Requires N % 256 == 0 and 4-byte (tiled) / 8-byte (row-major) aligned scale arrays;
 // returns hipErrorNotSupported otherwise.
 hipError_t launch_gemm_w4a8(const uint8_t* xq8, const uint8_t* xe, const uint8_t* wq,
                             const uint8_t* we, bool tiled_scales, int64_t S, int64_t N,
-                            int64_t out, float* y, hipStream_t stream);
+                            int64_t out, float* y, hipStream_t stream,
+                            const uint16_t* res = nullptr, bool out_bf16 = false);
 
 }  // namespace batq
