@@ -22,6 +22,9 @@
  *   - the W4A8 setting: the same transform and clip with the activations encoded as MXFP8
  *     (E4M3 elements, one E8M0 scale per 32) against the same MXFP4 weights (gist.science
  *     section 4 and the daily-arxiv results bullet, W4A8KV16);
+ *   - the layer's input normalisation fused in front of the quantiser (RMSNorm, the step
+ *     before every linear layer of the models the pages quantise; not defined on the pages,
+ *     so its arithmetic is this file's contract: see orc_rmsnorm_f32);
  *   - the other transform forms that thelatestinai listing's Table 1 compares against GPK:
  *     a full 32x32 P_i per block ("w/o decomposition") and P_i = B_i (x) A_i with a private
  *     A_i per block (naive Kronecker); block Hadamard is GPK with Hadamard factors.
@@ -39,6 +42,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #ifdef _OPENMP
@@ -386,6 +390,64 @@ void orc_transform_form_f32(const float* x, int64_t rows, int64_t N, int form,
     for (int64_t s = 0; s < rows; ++s)
         for (int64_t i = 0; i < k; ++i)
             transform_block(form, x + s * N + 32 * i, F0, F1, i, y + s * N + 32 * i);
+}
+
+/* RMSNorm of bf16 rows: x_hat[j] = (x[j] * r) * gamma[j], r = 1 / sqrt(T / N + eps), where
+ * T is the row's sum of squares taken as: per 32-element block, x_0^2 then fmaf(x_j, x_j, .)
+ * in increasing j; the k block sums, padded with zeros to the next power of two K, are
+ * added by halving (for h = K/2, K/4, .., 1: t[b] += t[b + h] for b < h); T = t[0].  Every
+ * operation is one fp32 rounding (division and square root correctly rounded).
+ * x_hat [rows, N] fp32; r_out [rows] (may be NULL). */
+void orc_rmsnorm_f32(const uint16_t* x, int64_t rows, int64_t N, int64_t ldx,
+                     const float* gamma, float eps, float* x_hat, float* r_out)
+{
+    int64_t k = N / 32;
+    int64_t K = 1;
+    while (K < k) K *= 2;
+    for (int64_t s = 0; s < rows; ++s) {
+        float t[1 << 16];
+        for (int64_t b = 0; b < K; ++b) t[b] = 0.0f;
+        for (int64_t b = 0; b < k; ++b) {
+            float v0 = bf16_to_float(x[s * ldx + 32 * b]);
+            float acc = v0 * v0;
+            for (int j = 1; j < 32; ++j) {
+                float v = bf16_to_float(x[s * ldx + 32 * b + j]);
+                acc = fmaf(v, v, acc);
+            }
+            t[b] = acc;
+        }
+        for (int64_t h = K / 2; h >= 1; h /= 2)
+            for (int64_t b = 0; b < h; ++b) t[b] = t[b] + t[b + h];
+        float mean = t[0] / (float)N;
+        float d = mean + eps;
+        float r = 1.0f / sqrtf(d);
+        if (r_out) r_out[s] = r;
+        for (int64_t j = 0; j < N; ++j) {
+            float v = bf16_to_float(x[s * ldx + j]);
+            float u = v * r;
+            x_hat[s * N + j] = u * gamma[j];
+        }
+    }
+}
+
+/* RMSNorm (as orc_rmsnorm_f32) fused in front of the activation quantiser: transform, clip
+ * and MXFP4 of the normalised fp32 rows, as orc_quantize_act. */
+void orc_quantize_act_rmsnorm(const uint16_t* x, int64_t rows, int64_t N, int64_t ldx,
+                              const float* gamma, float eps, const float* A, const float* B,
+                              const float* r_min, const float* r_max, uint8_t* q, uint8_t* e)
+{
+    int64_t k = N / 32;
+    float* xh = (float*)malloc(sizeof(float) * (size_t)N);
+    for (int64_t s = 0; s < rows; ++s) {
+        orc_rmsnorm_f32(x + s * ldx, 1, N, ldx, gamma, eps, xh, NULL);
+        for (int64_t i = 0; i < k; ++i) {
+            float y[32];
+            gpk_transform_block(xh + 32 * i, A, B + 16 * i, y);
+            clip_quantize_block(y, 1, r_min[i], r_max[i], q + s * (N / 2) + 16 * i,
+                                e + s * k + i, NULL, NULL);
+        }
+    }
+    free(xh);
 }
 
 /* The transform alone (fp32 y [rows, N]) on fp32 input, for the structural pins. */

@@ -80,6 +80,9 @@ def lib() -> ctypes.CDLL:
     L.orc_dequant_fp8.argtypes = [P, P, I64, I64, P]
     L.orc_gemm_w4a8.argtypes = [P, P, P, P, I64, I64, I64, P, I64, P, I64, P, P, I32]
     L.orc_quantize_act_form.argtypes = [P, I64, I64, I64, I32, P, P, P, P, P, P, I32]
+    L.orc_rmsnorm_f32.argtypes = [P, I64, I64, I64, P, ctypes.c_float, P, P]
+    L.orc_quantize_act_rmsnorm.argtypes = [P, I64, I64, I64, P, ctypes.c_float, P, P, P, P, P,
+                                           P]
     L.orc_quantize_weight_form.argtypes = [P, I64, I64, I32, P, P, P, P, I32]
     L.orc_transform_form_f32.argtypes = [P, I64, I64, I32, P, P, P]
     L.orc_max_threads.restype = I32
@@ -448,4 +451,37 @@ def prepare_weight_form(W, form, F0, F1, nthreads=1):
     e = np.zeros((rows, k), dtype=np.uint8)
     lib().orc_quantize_weight_form(_p(W), rows, N, form, _p(G0), _p(G1), _p(q), _p(e),
                                    nthreads)
+    return q, e
+
+
+# ----------------------------------------------------------------------------------------
+# RMSNorm in front of the quantiser (arithmetic contract in orc_rmsnorm_f32)
+# ----------------------------------------------------------------------------------------
+
+def rmsnorm(x_bits, gamma, eps):
+    """bf16 rows [S, N] -> (normalised fp32 rows [S, N], r [S])."""
+    x_bits = np.ascontiguousarray(np.asarray(x_bits))
+    assert x_bits.dtype == np.uint16 and x_bits.ndim == 2
+    S, ldx = x_bits.shape
+    gamma = _c(gamma, np.float32)
+    N = gamma.size
+    xh = np.zeros((S, N), dtype=np.float32)
+    r = np.zeros(S, dtype=np.float32)
+    lib().orc_rmsnorm_f32(_p(x_bits), S, N, ldx, _p(gamma), float(eps), _p(xh), _p(r))
+    return xh, r
+
+
+def quantize_act_rmsnorm(x_bits, gamma, eps, A, B, r_min, r_max):
+    """RMSNorm + transform + clip + MXFP4 of bf16 rows [S, N]."""
+    x_bits = np.ascontiguousarray(np.asarray(x_bits))
+    S, ldx = x_bits.shape
+    gamma = _c(gamma, np.float32)
+    N = gamma.size
+    k = N // 32
+    q = np.zeros((S, N // 2), dtype=np.uint8)
+    e = np.zeros((S, k), dtype=np.uint8)
+    lib().orc_quantize_act_rmsnorm(_p(x_bits), S, N, ldx, _p(gamma), float(eps),
+                                   _p(_c(A, np.float32).reshape(64)),
+                                   _p(_c(B, np.float32).reshape(-1)), _p(_c(r_min, np.float32)),
+                                   _p(_c(r_max, np.float32)), _p(q), _p(e))
     return q, e
