@@ -132,6 +132,9 @@ def measure(name, args):
     w4a8 = args.precision == "w4a8"
     form = getattr(args, "form", "gpk")
     epilogue = getattr(args, "epilogue", "f32")
+    rms = getattr(args, "rmsnorm", False)
+    if rms and (w4a8 or form != "gpk"):
+        raise SystemExit("bench.py: --rmsnorm applies to the W4A4 GPK quantiser")
     if w4a8 and form != "gpk":
         raise SystemExit("bench.py: --form applies to the W4A4 path")
     cb = 1.0 if w4a8 else 0.5                 # activation code bytes per element
@@ -178,6 +181,13 @@ def measure(name, args):
             wes[j].data_ptr(), ys[j].data_ptr()) for j in range(R)]
     quant, gemm = ((bq.quantize_act_mxfp8_raw, bq.gemm_w4a8_raw) if w4a8 else
                    (bq.quantize_act_raw, bq.gemm_w4a4_raw))
+    if rms:
+        gamma = (1 + 0.1 * torch.randn(N, device=dev)).float().contiguous()
+        pg = gamma.data_ptr()
+
+        def quant(x, S_, N_, ldx, a, b, r1, r2, xq, xe, lay, st):
+            return bq.quantize_act_rmsnorm_raw(x, S_, N_, ldx, pg, 1e-6, a, b, r1, r2, xq, xe,
+                                               lay, st)
     if form != "gpk":
         fid = FORMS[form]
 
@@ -248,7 +258,7 @@ def measure(name, args):
     last = ys[(args.warmup + 3 * K - 1) % R]
     assert bool(torch.isfinite(last).all().item()), "non-finite GEMM output"
 
-    b1 = k1_bytes(S, N, cb, form)
+    b1 = k1_bytes(S, N, cb, form) + (4 * N if rms else 0)
     b2 = k2_bytes(S, N, out, cb, epilogue)
     gbs = b1 / t_k1 / 1e9
     tflops = k2_flops(S, N, out) / t_k2 / 1e12
@@ -257,10 +267,11 @@ def measure(name, args):
     k1_name = "quantize_kernel_mxfp8" if w4a8 else "quantize_kernel"
     k2_name = ("gemm_w4a8_kernel" if w4a8 else
                "gemm_skinny_kernel" if S <= 64 else "gemm_pc_kernel")
-    tr1 = measured_traffic(k1_name, L.cfg.name) if form == "gpk" else None
+    tr1 = measured_traffic(k1_name, L.cfg.name) if form == "gpk" and not rms else None
     tr2 = measured_traffic(k2_name, L.cfg.name) if epilogue == "f32" else None
     roof_k1 = {"kernel": f"{k1_name} (fused BAT+clip+{'MXFP8' if w4a8 else 'MXFP4'}"
-                         + ("" if form == "gpk" else f", {form} transform") + ")",
+                         + ("" if form == "gpk" else f", {form} transform")
+                         + (", RMSNorm prologue" if rms else "") + ")",
                "bound": "hbm",
                "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": tr1,
@@ -301,7 +312,7 @@ def measure(name, args):
                                f"layer, seeded synthetic bf16 activations and fp32 weights)",
                    "S": S, "N": N, "out": out, "rotated_buffer_sets": R,
                    "scale_layout": "mfma_tiled", "transform": form,
-                   "gemm_output": epilogue},
+                   "gemm_output": epilogue, "rmsnorm_prologue": rms},
         "gemm": {"value": round(tflops, 1), "unit": "TFLOP/s",
                  "pct_of_peak": round(100 * tflops / peak, 2)},
         "step_gpu_us": round(t_step_ev * 1e6, 3),
@@ -332,6 +343,8 @@ def main():
     ap.add_argument("--epilogue", choices=("f32", "bf16", "bf16_residual"), default="f32",
                     help="GEMM output: fp32 (the defined output), bf16, or bf16 plus a bf16 "
                          "residual")
+    ap.add_argument("--rmsnorm", action="store_true",
+                    help="quantise through the RMSNorm-fused quantiser (gamma [N], eps 1e-6)")
     ap.add_argument("--all", action="store_true",
                     help="measure every layer configuration, one JSON line each (no CPU baseline)")
     args = ap.parse_args()
@@ -348,7 +361,7 @@ def main():
         return
     rec, L = measure(args.config, args)
     if not args.no_cpu_baseline:
-        if args.form == "gpk":
+        if args.form == "gpk" and not args.rmsnorm:
             rec["cpu_baseline"] = cpu_baseline(L, args.cpu_seconds, args.precision == "w4a8")
     print(json.dumps(rec), flush=True)
 

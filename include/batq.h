@@ -249,6 +249,26 @@ batq_status batq_gemm_w4a8_out(const uint8_t* xq8, const uint8_t* xe,
                                batq_out_type y_type, const uint16_t* residual, void* stream);
 
 /*
+ * The layer's input RMSNorm fused in front of the activation quantiser (the step before
+ * each quantised linear layer of the models the pages evaluate; the pages do not define its
+ * arithmetic, so it is fixed here): per row, the sum of squares T is taken per 32-block as
+ * x_0^2 followed by fused multiply-adds in increasing index order, and the block sums,
+ * zero-padded to the next power of two, are added by repeated halving (t[b] += t[b + h] for
+ * h = K/2, K/4, .., 1); r = 1 / sqrt(T / N + eps) with correctly rounded division and square
+ * root; x_hat_j = (x_j * r) * gamma_j, each product rounded to fp32.  x_hat then goes
+ * through exactly the transform, clip and MXFP4 encode of batq_quantize_act.
+ *   x, S, N, ldx, A, B, r_min, r_max, q, e, e_layout, stream: as batq_quantize_act
+ *   gamma  dev  fp32 [N] RMSNorm weight, 16-byte aligned;  eps >= 0, finite
+ *   N <= 16384 (BATQ_ERR_UNSUPPORTED beyond).  Does not allocate or synchronise.
+ */
+batq_status batq_quantize_act_rmsnorm(const uint16_t* x, int64_t S, int64_t N, int64_t ldx,
+                                      const float* gamma, float eps,
+                                      const float* A, const float* B,
+                                      const float* r_min, const float* r_max,
+                                      uint8_t* q, uint8_t* e, batq_scale_layout e_layout,
+                                      void* stream);
+
+/*
  * Host: clip ratios r[i] = fp32(1 / (1 + exp(-alpha[i]))) evaluated in binary64 and rounded
  * once (daily-arxiv summary, clipping bullet: the sigmoid keeps each ratio in (0, 1);
  * gist.science summary, section 2C).  The logits are per block, shared by all tokens.

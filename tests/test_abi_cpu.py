@@ -36,7 +36,8 @@ def test_library_exports_every_declared_entry_point(bq):
                             "batq_clip_ratios", "batq_weight_factors", "batq_status_string",
                             "batq_quantize_act_mxfp8", "batq_gemm_w4a8",
                             "batq_quantize_act_form", "batq_prepare_weight_form",
-                            "batq_gemm_w4a4_out", "batq_gemm_w4a8_out"])
+                            "batq_gemm_w4a4_out", "batq_gemm_w4a8_out",
+                            "batq_quantize_act_rmsnorm"])
     L = ctypes.CDLL(bq.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -155,6 +156,17 @@ def test_gemm_epilogue_argument_errors(bq):
         assert g(D, D, D, D, 4, n, 8, D, 3) == UNSUPPORTED            # unknown output type
         assert g(D, D, D, D, 4, n, 8, D, 1, D + 8) == ALIGN           # residual alignment
         assert g(D, D, D, D, 4, n, 8, D + 8, 1) == ALIGN              # output alignment
+
+
+def test_rmsnorm_argument_errors(bq):
+    q = bq.quantize_act_rmsnorm_raw
+    assert q(D, 4, 48, 64, D, 1e-6, D, D, D, D, D, D) == SHAPE
+    assert q(0, 0, 64, 64, 0, 1e-6, 0, 0, 0, 0, 0, 0) == OK
+    assert q(D, 4, 64, 64, 0, 1e-6, D, D, D, D, D, D) == NULL           # gamma
+    assert q(D, 4, 64, 64, D + 4, 1e-6, D, D, D, D, D, D) == ALIGN      # gamma alignment
+    assert q(D, 4, 64, 64, D, -1.0, D, D, D, D, D, D) == SHAPE          # eps < 0
+    assert q(D, 4, 64, 64, D, float("nan"), D, D, D, D, D, D) == SHAPE
+    assert q(D, 4, 32 * 513, 32 * 513 + 8, D, 1e-6, D, D, D, D, D, D) == UNSUPPORTED
 
 
 def test_prepare_weight_argument_errors_and_singular_factors(bq):

@@ -25,6 +25,8 @@ SIGNATURES = {
     "batq_gemm_w4a4": [_P, _P, _P, _P, _I, _I64, _I64, _I64, _P, _P],
     "batq_quantize_act_mxfp8": [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _I, _P],
     "batq_gemm_w4a8": [_P, _P, _P, _P, _I, _I64, _I64, _I64, _P, _P],
+    "batq_quantize_act_rmsnorm": [_P, _I64, _I64, _I64, _P, ctypes.c_float, _P, _P, _P, _P, _P,
+                                  _P, _I, _P],
     "batq_gemm_w4a4_out": [_P, _P, _P, _P, _I, _I64, _I64, _I64, _P, _I, _P, _P],
     "batq_gemm_w4a8_out": [_P, _P, _P, _P, _I, _I64, _I64, _I64, _P, _I, _P, _P],
     "batq_quantize_act_form": [_P, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _I, _P],
@@ -137,6 +139,12 @@ def gemm_w4a8_out_raw(xq8, xe, wq, we, S, N, out, y, y_type=0, residual=0,
                       layout=SCALES_ROW_MAJOR, stream=0) -> int:
     return lib().batq_gemm_w4a8_out(xq8, xe, wq, we, layout, S, N, out, y, y_type, residual,
                                     stream)
+
+
+def quantize_act_rmsnorm_raw(x, S, N, ldx, gamma, eps, A, B, r_min, r_max, q, e,
+                             layout=SCALES_ROW_MAJOR, stream=0) -> int:
+    return lib().batq_quantize_act_rmsnorm(x, S, N, ldx, gamma, eps, A, B, r_min, r_max, q, e,
+                                           layout, stream)
 
 
 def prepare_weight_raw(W, out, N, A_host, B_host, wq, we, layout=SCALES_ROW_MAJOR,
@@ -373,3 +381,26 @@ def gemm_out(xq, xe, wq, we, out_dtype=None, residual=None, y=None, layout=SCALE
     _check(fn, raw(_ptr(xq), _ptr(xe), _ptr(wq), _ptr(we), S, N, out, _ptr(y), yt,
                    _ptr(residual) if residual is not None else 0, layout, _stream(stream)))
     return y
+
+
+# ---------------------------------------------------------------------------------------
+# RMSNorm fused in front of the quantiser
+# ---------------------------------------------------------------------------------------
+
+def quantize_act_rmsnorm(x, gamma, eps, A, B, r_min, r_max, q=None, e=None,
+                         layout=SCALES_ROW_MAJOR, stream=None):
+    """RMSNorm (gamma fp32 [N] on the device, eps) + transform + clip + MXFP4 of bf16
+    activations x [S, N]; returns the codes and scales as quantize_act."""
+    import torch
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    S, N = x.shape
+    if q is None:
+        q = torch.empty((S, N // 2), dtype=torch.uint8, device=x.device)
+    if e is None:
+        e = _scale_tensor(S, N, layout, x.device)
+    for t in (gamma, A, B, r_min, r_max):
+        assert t.dtype == torch.float32 and t.is_contiguous()
+    _check("batq_quantize_act_rmsnorm", quantize_act_rmsnorm_raw(
+        _ptr(x), S, N, x.stride(0), _ptr(gamma), float(eps), _ptr(A), _ptr(B), _ptr(r_min),
+        _ptr(r_max), _ptr(q), _ptr(e), layout, _stream(stream)))
+    return q, e

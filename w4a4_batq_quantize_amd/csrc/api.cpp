@@ -327,3 +327,26 @@ BATQ_API batq_status batq_gemm_w4a8_out(const uint8_t* xq8, const uint8_t* xe, c
                                            S, N, out, static_cast<float*>(y), as_stream(stream),
                                            residual, y_type == BATQ_OUT_BF16));
 }
+
+BATQ_API batq_status batq_quantize_act_rmsnorm(const uint16_t* x, int64_t S, int64_t N,
+                                               int64_t ldx, const float* gamma, float eps,
+                                               const float* A, const float* B,
+                                               const float* r_min, const float* r_max,
+                                               uint8_t* q, uint8_t* e,
+                                               batq_scale_layout e_layout, void* stream)
+{
+    if (S < 0 || N < 0 || N % 32 != 0) return BATQ_ERR_SHAPE;
+    if (S == 0 || N == 0) return BATQ_OK;
+    if (!x || !gamma || !A || !B || !r_min || !r_max || !q || !e) return BATQ_ERR_NULL;
+    if (!valid_layout(e_layout)) return BATQ_ERR_UNSUPPORTED;
+    if (ldx < N || mul_overflows(S, ldx)) return BATQ_ERR_SHAPE;
+    if (ldx % 8 != 0 || !aligned(x, 16) || !aligned(B, 16) || !aligned(q, 16) ||
+        !aligned(gamma, 16) || !aligned(A, 4) || !aligned(r_min, 4) || !aligned(r_max, 4))
+        return BATQ_ERR_ALIGN;
+    if (!(eps >= 0.0f) || !std::isfinite(eps)) return BATQ_ERR_SHAPE;
+    const int64_t k = N / 32;
+    if (k > 512 || S > 0x7FFFFFFF) return BATQ_ERR_UNSUPPORTED;
+    return from_hip(batq::launch_rmsnorm_quantize(x, S, k, ldx, gamma, eps, A, B, r_min, r_max,
+                                                  q, e, e_layout == BATQ_SCALES_MFMA_TILED,
+                                                  as_stream(stream)));
+}

@@ -97,67 +97,17 @@ __device__ __forceinline__ void full_transform(const float (&x)[32], const float
     }
 }
 
-// kForm selects the transform (thelatestinai listing, Table 1): 0 GPK, A [8][8] shared by
-// every block (read through the scalar unit); 1 naive Kronecker, a private A_i [8][8] per
-// block, same reshape evaluation; 2 a full 32x32 P_i per block (A points at P [k][32][32],
-// B is unused).  For forms 1 and 2 a workgroup owns one block column (blockIdx.x) and its
-// threads take consecutive rows, so A_i / P_i (and B_i) are uniform across the wave and
-// come through the scalar unit as FMA operands, like GPK's A.
-// kFp8 (activations only): MXFP8 output, one E4M3 code byte per element (the W4A8
-// setting).  Same transform and clip; the scale exponent is floor(log2 amax) - 8 (E4M3's
-// largest exponent), and the conversion instruction, exact round-to-nearest-even otherwise,
-// returns NaN above 448 where MX saturates, so the clip bounds are first clamped into
-// [-448 s, 448 s] (a clamp of a clamp is the clamp to the clamped bounds).
-template <bool kAct, bool kFp8 = false, int kForm = 0>
-__global__ void __launch_bounds__(kThreads)
-quantize_kernel(const void* __restrict__ xin, int64_t rows, int64_t k, int64_t ldx,
-                const float* __restrict__ A, const float* __restrict__ B,
-                const float* __restrict__ r_min, const float* __restrict__ r_max,
-                uint8_t* __restrict__ q, uint8_t* __restrict__ e, int lpr_log2,
-                int tiled_scales)
+// Transform, clip, encode and store one block held in registers (row, blk), shared by the
+// quantisers.
+template <bool kAct, bool kFp8, int kForm>
+__device__ __forceinline__ void quantize_block(float (&x)[32], const float* __restrict__ A,
+                                               const float* __restrict__ B,
+                                               const float* __restrict__ r_min,
+                                               const float* __restrict__ r_max,
+                                               uint8_t* __restrict__ q, uint8_t* __restrict__ e,
+                                               int64_t row, int64_t blk, int64_t k,
+                                               int tiled_scales)
 {
-    static_assert(kAct || !kFp8, "MXFP8 is an activation-side format");
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    int64_t row, blk;
-    if constexpr (kForm != 0) {
-        blk = blockIdx.x;
-        row = (int64_t)blockIdx.y * kThreads + threadIdx.x;
-    } else {
-        row = ((((int64_t)blockIdx.x * kWavesPerGroup + wave) << (6 - lpr_log2)) +
-               (lane >> lpr_log2));
-        blk = (int64_t)blockIdx.y * 64 + (lane & ((1 << lpr_log2) - 1));
-    }
-    if (row >= rows || blk >= k) return;
-
-    float x[32];
-    if constexpr (kAct) {
-        const uint4* xp = reinterpret_cast<const uint4*>(
-            static_cast<const uint16_t*>(xin) + row * ldx + 32 * blk);
-        uint4 v[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) v[t] = xp[t];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const uint32_t w[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                x[8 * t + 2 * d] = bf16_lo(w[d]);
-                x[8 * t + 2 * d + 1] = bf16_hi(w[d]);
-            }
-        }
-    } else {
-        const float4* xp = reinterpret_cast<const float4*>(
-            static_cast<const float*>(xin) + row * ldx + 32 * blk);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const float4 v = xp[t];
-            x[4 * t] = v.x;
-            x[4 * t + 1] = v.y;
-            x[4 * t + 2] = v.z;
-            x[4 * t + 3] = v.w;
-        }
-    }
     float y[32];
     if constexpr (kForm == 2) {
         full_transform(x, A + 1024 * blk, y);
@@ -239,6 +189,179 @@ quantize_kernel(const void* __restrict__ xin, int64_t rows, int64_t k, int64_t l
     e[eoff] = (uint8_t)ebyte;
 }
 
+// kForm selects the transform (thelatestinai listing, Table 1): 0 GPK, A [8][8] shared by
+// every block (read through the scalar unit); 1 naive Kronecker, a private A_i [8][8] per
+// block, same reshape evaluation; 2 a full 32x32 P_i per block (A points at P [k][32][32],
+// B is unused).  For forms 1 and 2 a workgroup owns one block column (blockIdx.x) and its
+// threads take consecutive rows, so A_i / P_i (and B_i) are uniform across the wave and
+// come through the scalar unit as FMA operands, like GPK's A.
+// kFp8 (activations only): MXFP8 output, one E4M3 code byte per element (the W4A8
+// setting).  Same transform and clip; the scale exponent is floor(log2 amax) - 8 (E4M3's
+// largest exponent), and the conversion instruction, exact round-to-nearest-even otherwise,
+// returns NaN above 448 where MX saturates, so the clip bounds are first clamped into
+// [-448 s, 448 s] (a clamp of a clamp is the clamp to the clamped bounds).
+template <bool kAct, bool kFp8 = false, int kForm = 0>
+__global__ void __launch_bounds__(kThreads)
+quantize_kernel(const void* __restrict__ xin, int64_t rows, int64_t k, int64_t ldx,
+                const float* __restrict__ A, const float* __restrict__ B,
+                const float* __restrict__ r_min, const float* __restrict__ r_max,
+                uint8_t* __restrict__ q, uint8_t* __restrict__ e, int lpr_log2,
+                int tiled_scales)
+{
+    static_assert(kAct || !kFp8, "MXFP8 is an activation-side format");
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    int64_t row, blk;
+    if constexpr (kForm != 0) {
+        blk = blockIdx.x;
+        row = (int64_t)blockIdx.y * kThreads + threadIdx.x;
+    } else {
+        row = ((((int64_t)blockIdx.x * kWavesPerGroup + wave) << (6 - lpr_log2)) +
+               (lane >> lpr_log2));
+        blk = (int64_t)blockIdx.y * 64 + (lane & ((1 << lpr_log2) - 1));
+    }
+    if (row >= rows || blk >= k) return;
+
+    float x[32];
+    if constexpr (kAct) {
+        const uint4* xp = reinterpret_cast<const uint4*>(
+            static_cast<const uint16_t*>(xin) + row * ldx + 32 * blk);
+        uint4 v[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[t] = xp[t];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint32_t w[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                x[8 * t + 2 * d] = bf16_lo(w[d]);
+                x[8 * t + 2 * d + 1] = bf16_hi(w[d]);
+            }
+        }
+    } else {
+        const float4* xp = reinterpret_cast<const float4*>(
+            static_cast<const float*>(xin) + row * ldx + 32 * blk);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const float4 v = xp[t];
+            x[4 * t] = v.x;
+            x[4 * t + 1] = v.y;
+            x[4 * t + 2] = v.z;
+            x[4 * t + 3] = v.w;
+        }
+    }
+    quantize_block<kAct, kFp8, kForm>(x, A, B, r_min, r_max, q, e, row, blk, k, tiled_scales);
+}
+
+// ---------------------------------------------------------------------------------------
+// RMSNorm fused in front of the activation quantiser
+// ---------------------------------------------------------------------------------------
+//
+// TPR threads per row (64, 128 or 256: the padded block count clamped to that range), one
+// or two blocks per thread held in registers from load to store, 256 / TPR rows per
+// workgroup.  Arithmetic contract (as the oracle's orc_rmsnorm_f32): block sums of squares
+// x_0^2 then fmaf in increasing j; the block sums, zero-padded to K = the next power of two
+// >= k, added by halving (t[b] += t[b + h], h = K/2 .. 1); r = 1 / sqrt(T / N + eps) with
+// correctly rounded division and square root; x_hat = (x r) gamma, two roundings; then the
+// GPK transform, clip and MXFP4 of quantize_block.  Thread i of a row holds blocks i and
+// i + TPR: the step h = TPR (K = 2 TPR) is inside the thread, the steps with 64 <= h < TPR
+// cross waves through LDS, those with h < 64 cross lanes inside the wave; fp32 addition is
+// commutative, so the operand order of each step does not change its result.
+constexpr int kRmsThreads = 256;
+
+__device__ __forceinline__ void load_bf16_block(const uint16_t* __restrict__ src, float (&x)[32])
+{
+    const uint4* xp = reinterpret_cast<const uint4*>(src);
+    uint4 v[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) v[t] = xp[t];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const uint32_t w[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            x[8 * t + 2 * d] = bf16_lo(w[d]);
+            x[8 * t + 2 * d + 1] = bf16_hi(w[d]);
+        }
+    }
+}
+
+__device__ __forceinline__ float block_sum_squares(const float (&x)[32])
+{
+    float acc = x[0] * x[0];
+#pragma unroll
+    for (int j = 1; j < 32; ++j) acc = __builtin_fmaf(x[j], x[j], acc);
+    return acc;
+}
+
+__device__ __forceinline__ void rms_scale(float (&x)[32], const float* __restrict__ g, float r)
+{
+    const float4* gp = reinterpret_cast<const float4*>(g);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const float4 v = gp[t];
+        x[4 * t] = (x[4 * t] * r) * v.x;
+        x[4 * t + 1] = (x[4 * t + 1] * r) * v.y;
+        x[4 * t + 2] = (x[4 * t + 2] * r) * v.z;
+        x[4 * t + 3] = (x[4 * t + 3] * r) * v.w;
+    }
+}
+
+template <int TPR>
+__global__ void __launch_bounds__(kRmsThreads)
+rmsnorm_quantize_kernel(const uint16_t* __restrict__ xin, int64_t rows, int64_t k, int64_t ldx,
+                        const float* __restrict__ gamma, float eps,
+                        const float* __restrict__ A, const float* __restrict__ B,
+                        const float* __restrict__ r_min, const float* __restrict__ r_max,
+                        uint8_t* __restrict__ q, uint8_t* __restrict__ e, int kpow2,
+                        int tiled_scales)
+{
+    constexpr int kRows = kRmsThreads / TPR;
+    __shared__ float part[kRmsThreads];
+    __shared__ float total[kRows];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int rt = tid % TPR, rl = tid / TPR;
+    const int64_t row = (int64_t)blockIdx.x * kRows + rl;
+    const bool live = row < rows;                    // dead rows still take every barrier
+    const uint16_t* xr = xin + row * ldx;
+    const int64_t b0 = rt, b1 = rt + TPR;
+    const bool has0 = live && b0 < k, has1 = live && b1 < k;
+    float x0[32], x1[32];
+    float s0 = 0.0f, s1 = 0.0f;
+    if (has0) {
+        load_bf16_block(xr + 32 * b0, x0);
+        s0 = block_sum_squares(x0);
+    }
+    if (has1) {
+        load_bf16_block(xr + 32 * b1, x1);
+        s1 = block_sum_squares(x1);
+    }
+    float v = kpow2 > TPR ? s0 + s1 : s0;            // step h = TPR
+    for (int h = (kpow2 < TPR ? kpow2 : TPR) / 2; h >= 64; h /= 2) {
+        part[tid] = v;
+        __syncthreads();
+        if (rt < h) v = v + part[tid + h];
+        __syncthreads();
+    }
+    for (int h = (kpow2 < 64 ? kpow2 : 64) / 2; h >= 1; h /= 2) {
+        const float o = __shfl_down(v, h, 64);
+        if (lane < h) v = v + o;
+    }
+    if (rt == 0) total[rl] = v;
+    __syncthreads();
+    const float T = total[rl];
+    const float mean = T / (float)(32 * k);
+    const float r = 1.0f / __builtin_sqrtf(mean + eps);
+    if (has0) {
+        rms_scale(x0, gamma + 32 * b0, r);
+        quantize_block<true, false, 0>(x0, A, B, r_min, r_max, q, e, row, b0, k, tiled_scales);
+    }
+    if (has1) {
+        rms_scale(x1, gamma + 32 * b1, r);
+        quantize_block<true, false, 0>(x1, A, B, r_min, r_max, q, e, row, b1, k, tiled_scales);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_quantize(bool act, const void* x, int64_t rows, int64_t k, int64_t ldx,
@@ -284,6 +407,36 @@ hipError_t launch_quantize(bool act, const void* x, int64_t rows, int64_t k, int
     else
         hipLaunchKernelGGL(quantize_kernel<false>, grid, dim3(kThreads), 0, stream, x, rows,
                            k, ldx, A, B, r_min, r_max, q, e, lpr_log2, (int)tiled_scales);
+    return hipGetLastError();
+}
+
+}  // namespace batq
+
+namespace batq {
+
+hipError_t launch_rmsnorm_quantize(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx,
+                                   const float* gamma, float eps, const float* A,
+                                   const float* B, const float* r_min, const float* r_max,
+                                   uint8_t* q, uint8_t* e, bool tiled_scales,
+                                   hipStream_t stream)
+{
+    if (k < 1 || k > 2 * kRmsThreads) return hipErrorNotSupported;
+    int kpow2 = 1;
+    while (kpow2 < k) kpow2 *= 2;
+    const int tpr = kpow2 < 64 ? 64 : kpow2 > kRmsThreads ? kRmsThreads : kpow2;
+    const int64_t groups = (rows + kRmsThreads / tpr - 1) / (kRmsThreads / tpr);
+    if (groups > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)groups), block(kRmsThreads);
+    const int ts = (int)tiled_scales;
+    if (tpr == 64)
+        hipLaunchKernelGGL(rmsnorm_quantize_kernel<64>, grid, block, 0, stream, x, rows, k, ldx,
+                           gamma, eps, A, B, r_min, r_max, q, e, kpow2, ts);
+    else if (tpr == 128)
+        hipLaunchKernelGGL(rmsnorm_quantize_kernel<128>, grid, block, 0, stream, x, rows, k,
+                           ldx, gamma, eps, A, B, r_min, r_max, q, e, kpow2, ts);
+    else
+        hipLaunchKernelGGL(rmsnorm_quantize_kernel<256>, grid, block, 0, stream, x, rows, k,
+                           ldx, gamma, eps, A, B, r_min, r_max, q, e, kpow2, ts);
     return hipGetLastError();
 }
 
