@@ -25,6 +25,10 @@
  *   - the layer's input normalisation fused in front of the quantiser (RMSNorm, the step
  *     before every linear layer of the models the pages quantise; not defined on the pages,
  *     so its arithmetic is this file's contract: see orc_rmsnorm_f32);
+ *   - the KV-cache settings (W4A8KV8, W4A8KV4: thelatestinai listing, Tables 2, 3 and 5;
+ *     BAT covers self-attention including the KV caches: gist.science section 2D): K/V rows
+ *     transformed, clipped and encoded as MXFP8 or MXFP4 into cache slots; queries
+ *     transformed by P^-T (and attention outputs by P^-1) without quantisation;
  *   - the other transform forms that thelatestinai listing's Table 1 compares against GPK:
  *     a full 32x32 P_i per block ("w/o decomposition") and P_i = B_i (x) A_i with a private
  *     A_i per block (naive Kronecker); block Hadamard is GPK with Hadamard factors.
@@ -448,6 +452,67 @@ void orc_quantize_act_rmsnorm(const uint16_t* x, int64_t rows, int64_t N, int64_
         }
     }
     free(xh);
+}
+
+/* KV cache: row t of x (bf16 [T, ldx], N = heads x head_dim) is transformed, clipped and
+ * encoded (fmt 4: MXFP4, codes [slots, N/2]; fmt 8: MXFP8, codes [slots, N]) into cache row
+ * slots[t] (scales [slots, N/32] row-major); a negative slot skips the row and leaves the
+ * cache untouched there. */
+void orc_quantize_kv(const uint16_t* x, int64_t T, int64_t N, int64_t ldx, const int64_t* slots,
+                     int fmt, const float* A, const float* B, const float* r_min,
+                     const float* r_max, uint8_t* cache_q, uint8_t* cache_e)
+{
+    int64_t k = N / 32;
+    int64_t qrow = fmt == 8 ? N : N / 2;
+    for (int64_t t = 0; t < T; ++t) {
+        int64_t slot = slots[t];
+        if (slot < 0) continue;
+        for (int64_t i = 0; i < k; ++i) {
+            float xb[32], y[32];
+            for (int j = 0; j < 32; ++j) xb[j] = bf16_to_float(x[t * ldx + 32 * i + j]);
+            gpk_transform_block(xb, A, B + 16 * i, y);
+            if (fmt == 8)
+                clip_quantize_block_fp8(y, r_min[i], r_max[i], cache_q + slot * qrow + 32 * i,
+                                        cache_e + slot * k + i);
+            else
+                clip_quantize_block(y, 1, r_min[i], r_max[i], cache_q + slot * qrow + 16 * i,
+                                    cache_e + slot * k + i, NULL, NULL);
+        }
+    }
+}
+
+/* The GPK transform of rows without quantisation: x bf16 (x_bf16 != 0) or fp32 [rows, ldx]
+ * -> y fp32 [rows, N], with whatever factors the caller passes (P for K/V rows, the
+ * transposed inverses for queries, the inverses for attention outputs). */
+void orc_transform_rows(const void* x, int x_bf16, int64_t rows, int64_t N, int64_t ldx,
+                        const float* A, const float* B, float* y)
+{
+    int64_t k = N / 32;
+    for (int64_t s = 0; s < rows; ++s)
+        for (int64_t i = 0; i < k; ++i) {
+            float xb[32];
+            for (int j = 0; j < 32; ++j)
+                xb[j] = x_bf16 ? bf16_to_float(((const uint16_t*)x)[s * ldx + 32 * i + j])
+                               : ((const float*)x)[s * ldx + 32 * i + j];
+            gpk_transform_block(xb, A, B + 16 * i, y + s * N + 32 * i);
+        }
+}
+
+/* fp32 -> bf16 bit pattern, nearest with ties to the even pattern, by comparing the two
+ * neighbouring bf16 values exactly (finite inputs whose rounding stays finite). */
+void orc_f32_to_bf16(const float* v, int64_t n, uint16_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        uint32_t u;
+        memcpy(&u, &v[i], 4);
+        uint32_t lo = u & 0xFFFF0000u, hi = lo + 0x10000u; /* truncation and the next one */
+        float flo, fhi;
+        memcpy(&flo, &lo, 4);
+        memcpy(&fhi, &hi, 4);
+        double dlo = fabs((double)v[i] - (double)flo), dhi = fabs((double)fhi - (double)v[i]);
+        uint32_t pick = dlo < dhi ? lo : dhi < dlo ? hi : (((lo >> 16) & 1) ? hi : lo);
+        out[i] = (uint16_t)(pick >> 16);
+    }
 }
 
 /* The transform alone (fp32 y [rows, N]) on fp32 input, for the structural pins. */

@@ -81,6 +81,9 @@ def lib() -> ctypes.CDLL:
     L.orc_gemm_w4a8.argtypes = [P, P, P, P, I64, I64, I64, P, I64, P, I64, P, P, I32]
     L.orc_quantize_act_form.argtypes = [P, I64, I64, I64, I32, P, P, P, P, P, P, I32]
     L.orc_rmsnorm_f32.argtypes = [P, I64, I64, I64, P, ctypes.c_float, P, P]
+    L.orc_quantize_kv.argtypes = [P, I64, I64, I64, P, I32, P, P, P, P, P, P]
+    L.orc_transform_rows.argtypes = [P, I32, I64, I64, I64, P, P, P]
+    L.orc_f32_to_bf16.argtypes = [P, I64, P]
     L.orc_quantize_act_rmsnorm.argtypes = [P, I64, I64, I64, P, ctypes.c_float, P, P, P, P, P,
                                            P]
     L.orc_quantize_weight_form.argtypes = [P, I64, I64, I32, P, P, P, P, I32]
@@ -485,3 +488,49 @@ def quantize_act_rmsnorm(x_bits, gamma, eps, A, B, r_min, r_max):
                                    _p(_c(B, np.float32).reshape(-1)), _p(_c(r_min, np.float32)),
                                    _p(_c(r_max, np.float32)), _p(q), _p(e))
     return q, e
+
+
+# ----------------------------------------------------------------------------------------
+# KV caches (W4A8KV8 / W4A8KV4): BAT + MXFP8 / MXFP4 of K and V rows into cache slots;
+# queries by P^-T and attention outputs by P^-1 without quantisation
+# ----------------------------------------------------------------------------------------
+
+def quantize_kv(x_bits, slots, fmt, A, B, r_min, r_max, cache_q, cache_e):
+    """Write the quantised rows of x (bf16 bits [T, N]) into cache rows `slots` (negative:
+    skipped); cache_q [num_slots, N/2 (fmt 4) or N (fmt 8)], cache_e [num_slots, N/32] are
+    updated in place."""
+    x_bits = np.ascontiguousarray(np.asarray(x_bits))
+    assert x_bits.dtype == np.uint16 and x_bits.ndim == 2 and fmt in (4, 8)
+    T, ldx = x_bits.shape
+    B = _c(B, np.float32).reshape(-1)
+    N = 32 * (B.size // 16)
+    slots = _c(slots, np.int64)
+    assert slots.size == T and cache_q.flags.c_contiguous and cache_e.flags.c_contiguous
+    assert cache_q.shape[1] == (N if fmt == 8 else N // 2) and cache_e.shape[1] == N // 32
+    assert slots.max(initial=-1) < cache_q.shape[0]
+    lib().orc_quantize_kv(_p(x_bits), T, N, ldx, _p(slots), fmt,
+                          _p(_c(A, np.float32).reshape(64)), _p(B), _p(_c(r_min, np.float32)),
+                          _p(_c(r_max, np.float32)), _p(cache_q), _p(cache_e))
+
+
+def transform_rows(x, A, B, x_is_bf16_bits=False) -> np.ndarray:
+    """GPK transform of rows (bf16 bit patterns or fp32 [rows, N]) -> fp32 [rows, N]."""
+    x = np.ascontiguousarray(np.asarray(x))
+    if x_is_bf16_bits:
+        assert x.dtype == np.uint16
+    else:
+        x = x.astype(np.float32)
+    rows, ldx = x.shape
+    B = _c(B, np.float32).reshape(-1)
+    N = 32 * (B.size // 16)
+    y = np.zeros((rows, N), dtype=np.float32)
+    lib().orc_transform_rows(_p(x), int(x_is_bf16_bits), rows, N, ldx,
+                             _p(_c(A, np.float32).reshape(64)), _p(B), _p(y))
+    return y
+
+
+def f32_to_bf16(v) -> np.ndarray:
+    v = _c(v, np.float32)
+    out = np.zeros(v.shape, dtype=np.uint16)
+    lib().orc_f32_to_bf16(_p(v), v.size, _p(out))
+    return out
