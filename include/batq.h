@@ -268,6 +268,67 @@ batq_status batq_quantize_act_rmsnorm(const uint16_t* x, int64_t S, int64_t N, i
                                       uint8_t* q, uint8_t* e, batq_scale_layout e_layout,
                                       void* stream);
 
+/* Element format of a quantised KV cache (W4A8KV4 / W4A8KV8 settings). */
+typedef enum batq_kv_format {
+    BATQ_KV_MXFP4 = 4,   /* E2M1 codes, two per byte, low nibble first: [rows][N/2] */
+    BATQ_KV_MXFP8 = 8,   /* E4M3 codes, one per byte: [rows][N] */
+} batq_kv_format;
+
+/*
+ * KV cache write: the quantised keys or values of T new tokens stored into a cache of
+ * num_slots rows through a slot map.  The pages run the method on attention blocks with
+ * their KV caches (gist.science summary, section 2D) and report 8- and 4-bit caches
+ * (thelatestinai listing, captions of Tables 2, 3 and 5: W4A8KV8, W4A8KV4); the cache
+ * rows go through the same block transform, block clip and MX encoding as activations
+ * (plain reading: each K/V row, N = kv heads x head dim, is one activation row), so k P
+ * and q P^-T keep the attention scores q k^T.
+ *   x       dev  bf16 [T, ldx], rows of N = 32k values (16-byte aligned, ldx % 8 == 0)
+ *   slots   dev  int64 [T]: cache row of token t; a value < 0 or >= num_slots skips the
+ *                token (the cache row is left as it was)
+ *   fmt     BATQ_KV_MXFP4 or BATQ_KV_MXFP8 (element codes as batq_quantize_act or
+ *           batq_quantize_act_mxfp8)
+ *   A, B, r_min, r_max  dev, as batq_quantize_act
+ *   cache_q dev  [num_slots][N/2] (MXFP4) or [num_slots][N] (MXFP8) bytes, 16-byte aligned
+ *   cache_e dev  [num_slots][N/32] E8M0 scales, row-major
+ * Two tokens mapped to one slot race (either may win).  Does not allocate or synchronise.
+ */
+batq_status batq_quantize_kv(const uint16_t* x, int64_t T, int64_t N, int64_t ldx,
+                             const int64_t* slots, int64_t num_slots, batq_kv_format fmt,
+                             const float* A, const float* B, const float* r_min,
+                             const float* r_max, uint8_t* cache_q, uint8_t* cache_e,
+                             void* stream);
+
+/*
+ * The block transform alone, y_i = B_i^T X_i A on each 32-block (same arithmetic as the
+ * transform inside batq_quantize_act), for the unquantised side of attention with a
+ * transformed cache: queries take the factors of P^-T (batq_weight_factors of the kv head
+ * they attend to), attention outputs over transformed values take those of P^-1 (the
+ * transposed A^-1, B_i^-1) (gist.science summary, section 2B and 2D).
+ *   x       dev  [rows, ldx] of x_type (BATQ_OUT_F32 or BATQ_OUT_BF16 names the element type;
+ *                16-byte aligned; ldx % 4 == 0 for fp32, % 8 for bf16)
+ *   A, B    dev  fp32 [8][8] and [N/32][4][4] (B 16-byte aligned)
+ *   y       dev  [rows, N] dense of y_type; bf16 output is rounded to nearest, ties to even
+ * Does not allocate or synchronise.
+ */
+batq_status batq_transform_rows(const void* x, batq_out_type x_type, int64_t rows, int64_t N,
+                                int64_t ldx, const float* A, const float* B, void* y,
+                                batq_out_type y_type, void* stream);
+
+/*
+ * MX rows back to numbers: y[r][j] = code value * 2^(e - 127) (exact in fp32; bf16 output
+ * rounded to nearest, ties to even), reading cache rows selected by an optional index (the
+ * slots of a sequence).  OCP MX element decoding (gist.science summary, section 1; the
+ * element values of E2M1 and E4M3); NaN encodings (scale 0xFF, E4M3 S.1111.111) give NaN.
+ *   q, e     dev  cache as written by batq_quantize_kv ([src_rows] rows; q 16-byte aligned)
+ *   index    dev  int64 [rows] or NULL (then rows <= src_rows and row r reads row r); an
+ *                 entry outside [0, src_rows) gives a zero row
+ *   y        dev  [rows, N] dense of y_type, 16-byte aligned
+ * Does not allocate or synchronise.
+ */
+batq_status batq_dequantize_rows(const uint8_t* q, const uint8_t* e, int64_t src_rows, int64_t N,
+                                 batq_kv_format fmt, const int64_t* index, int64_t rows,
+                                 void* y, batq_out_type y_type, void* stream);
+
 /*
  * Host: clip ratios r[i] = fp32(1 / (1 + exp(-alpha[i]))) evaluated in binary64 and rounded
  * once (daily-arxiv summary, clipping bullet: the sigmoid keeps each ratio in (0, 1);

@@ -54,6 +54,20 @@ def assert_codes_equal(q_gpu, e_gpu, q_ref, e_ref, exact_zero=None, what=""):
                            f"{bad[:4].tolist()} gpu {cg[tuple(bad[0])]:x} ref {cr[tuple(bad[0])]:x}")
 
 
+def assert_fp8_codes_equal(q_gpu, e_gpu, q_ref, e_ref, exact_zero, what=""):
+    """Scales and E4M3 code bytes bit-exact, except that where the oracle's clipped value is
+    exactly +-0 either zero byte (0x00 or 0x80) is accepted."""
+    assert q_gpu.shape == q_ref.shape and e_gpu.shape == e_ref.shape, what
+    bad_e = np.argwhere(e_gpu != e_ref)
+    assert bad_e.size == 0, f"{what}: {len(bad_e)} scale mismatches, first {bad_e[:4].tolist()}"
+    diff = q_gpu != q_ref
+    diff &= ~(exact_zero & ((q_gpu & 0x7F) == 0) & ((q_ref & 0x7F) == 0))
+    bad = np.argwhere(diff)
+    assert bad.size == 0, (f"{what}: {len(bad)} code mismatches, first (row, elem) "
+                           f"{bad[:4].tolist()} gpu {q_gpu[tuple(bad[0])]:#04x} "
+                           f"ref {q_ref[tuple(bad[0])]:#04x}")
+
+
 def assert_gemm_close(y_gpu, y_ref, t_ref, rel=1e-5, what=""):
     """|y_gpu - y_ref| <= rel * sum|terms| elementwise (fp32 accumulation across blocks)."""
     err = np.abs(y_gpu.astype(np.float64) - y_ref)

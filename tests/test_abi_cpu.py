@@ -37,7 +37,8 @@ def test_library_exports_every_declared_entry_point(bq):
                             "batq_quantize_act_mxfp8", "batq_gemm_w4a8",
                             "batq_quantize_act_form", "batq_prepare_weight_form",
                             "batq_gemm_w4a4_out", "batq_gemm_w4a8_out",
-                            "batq_quantize_act_rmsnorm"])
+                            "batq_quantize_act_rmsnorm", "batq_quantize_kv",
+                            "batq_transform_rows", "batq_dequantize_rows"])
     L = ctypes.CDLL(bq.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -167,6 +168,38 @@ def test_rmsnorm_argument_errors(bq):
     assert q(D, 4, 64, 64, D, -1.0, D, D, D, D, D, D) == SHAPE          # eps < 0
     assert q(D, 4, 64, 64, D, float("nan"), D, D, D, D, D, D) == SHAPE
     assert q(D, 4, 32 * 513, 32 * 513 + 8, D, 1e-6, D, D, D, D, D, D) == UNSUPPORTED
+
+
+def test_kv_cache_argument_errors(bq):
+    kv = bq.quantize_kv_raw
+    F4, F8 = bq.KV_MXFP4, bq.KV_MXFP8
+    assert kv(D, 4, 48, 64, D, 10, F4, D, D, D, D, D, D) == SHAPE       # N % 32
+    assert kv(D, 4, 64, 64, D, -1, F4, D, D, D, D, D, D) == SHAPE       # num_slots < 0
+    assert kv(D, 4, 64, 64, D, 10, 6, D, D, D, D, D, D) == UNSUPPORTED  # unknown format
+    assert kv(0, 0, 64, 64, 0, 10, F8, 0, 0, 0, 0, 0, 0) == OK          # no tokens
+    assert kv(D, 4, 64, 64, 0, 10, F4, D, D, D, D, D, D) == NULL        # slots
+    assert kv(D, 4, 64, 32, D, 10, F4, D, D, D, D, D, D) == SHAPE       # ldx < N
+    assert kv(D, 4, 64, 64, D + 4, 10, F4, D, D, D, D, D, D) == ALIGN   # slots alignment
+    assert kv(D, 4, 64, 64, D, 10, F8, D, D, D, D, D + 8, D) == ALIGN   # cache alignment
+    assert kv(D, 4, 64, 68, D, 10, F4, D, D, D, D, D, D) == ALIGN       # ldx % 8
+    t = bq.transform_rows_raw
+    assert t(D, 0, 4, 48, 64, D, D, D, 0) == SHAPE
+    assert t(D, 2, 4, 64, 64, D, D, D, 0) == UNSUPPORTED                # unknown input type
+    assert t(D, 0, 4, 64, 64, D, D, D, 2) == UNSUPPORTED                # unknown output type
+    assert t(0, 0, 0, 64, 64, 0, 0, 0, 0) == OK
+    assert t(D, 0, 4, 64, 64, D, 0, D, 0) == NULL
+    assert t(D, 0, 4, 64, 66, D, D, D, 0) == ALIGN                      # fp32 ldx % 4
+    assert t(D, 1, 4, 64, 68, D, D, D, 0) == ALIGN                      # bf16 ldx % 8
+    assert t(D, 0, 4, 64, 68, D, D, D + 8, 1) == ALIGN                  # output alignment
+    d = bq.dequantize_rows_raw
+    assert d(D, D, 4, 48, F4, 0, 4, D, 0) == SHAPE
+    assert d(D, D, 4, 64, F4, 0, 5, D, 0) == SHAPE                      # rows > src without index
+    assert d(D, D, 4, 64, 5, 0, 4, D, 0) == UNSUPPORTED
+    assert d(D, D, 4, 64, F8, 0, 4, D, 3) == UNSUPPORTED
+    assert d(0, 0, 0, 64, F4, 0, 0, 0, 0) == OK
+    assert d(D, D, 4, 64, F4, 0, 4, 0, 0) == NULL                       # output
+    assert d(D, D, 4, 64, F8, D + 4, 9, D, 0) == ALIGN                  # index alignment
+    assert d(D + 8, D, 4, 64, F4, 0, 4, D, 1) == ALIGN                  # codes alignment
 
 
 def test_prepare_weight_argument_errors_and_singular_factors(bq):

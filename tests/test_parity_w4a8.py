@@ -8,7 +8,8 @@ import numpy as np
 import pytest
 
 import workloads as wl
-from tests.gpu_util import (ORACLE_THREADS, assert_gemm_close, bf16_to_device,
+from tests.gpu_util import (ORACLE_THREADS, assert_fp8_codes_equal, assert_gemm_close,
+                            bf16_to_device,
                             f32_to_device, from_tiled_scales, to_host, to_tiled_scales,
                             u8_to_device)
 from tests.mfma_fp8_model import HW_TRUNCATION_REL, gemm_w4a8_mfma_model
@@ -25,20 +26,6 @@ def bq():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     bq.lib()
     return bq
-
-
-def assert_fp8_codes_equal(q_gpu, e_gpu, q_ref, e_ref, exact_zero, what=""):
-    """Scales and E4M3 code bytes bit-exact, except that where the oracle's clipped value is
-    exactly +-0 either zero byte (0x00 or 0x80) is accepted."""
-    assert q_gpu.shape == q_ref.shape and e_gpu.shape == e_ref.shape, what
-    bad_e = np.argwhere(e_gpu != e_ref)
-    assert bad_e.size == 0, f"{what}: {len(bad_e)} scale mismatches, first {bad_e[:4].tolist()}"
-    diff = q_gpu != q_ref
-    diff &= ~(exact_zero & ((q_gpu & 0x7F) == 0) & ((q_ref & 0x7F) == 0))
-    bad = np.argwhere(diff)
-    assert bad.size == 0, (f"{what}: {len(bad)} code mismatches, first (row, elem) "
-                           f"{bad[:4].tolist()} gpu {q_gpu[tuple(bad[0])]:#04x} "
-                           f"ref {q_ref[tuple(bad[0])]:#04x}")
 
 
 def run_act8(bq, L, ldx=None, layout=0):

@@ -31,6 +31,9 @@ SIGNATURES = {
     "batq_gemm_w4a8_out": [_P, _P, _P, _P, _I, _I64, _I64, _I64, _P, _I, _P, _P],
     "batq_quantize_act_form": [_P, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _I, _P],
     "batq_prepare_weight_form": [_P, _I64, _I64, _I, _P, _P, _P, _P, _I, _P],
+    "batq_quantize_kv": [_P, _I64, _I64, _I64, _P, _I64, _I, _P, _P, _P, _P, _P, _P, _P],
+    "batq_transform_rows": [_P, _I, _I64, _I64, _I64, _P, _P, _P, _I, _P],
+    "batq_dequantize_rows": [_P, _P, _I64, _I64, _I, _P, _I64, _P, _I, _P],
     "batq_clip_ratios": [_P, _I64, _P],
     "batq_weight_factors": [_P, _P, _I64, _P, _P],
     "batq_status_string": [_I],
@@ -42,14 +45,19 @@ SIGNATURES = {
 SCALES_ROW_MAJOR = 0
 SCALES_MFMA_TILED = 1
 
-# Transform forms (batq_transform): GPK, naive Kronecker with a private A_i per block, full
-# 32x32 P_i per block.
+# Element types (batq_out_type) of GEMM outputs and of transformed / dequantised rows.
 OUT_F32 = 0
 OUT_BF16 = 1
 
+# Transform forms (batq_transform): GPK, naive Kronecker with a private A_i per block, full
+# 32x32 P_i per block.
 TRANSFORM_GPK = 0
 TRANSFORM_KRONECKER = 1
 TRANSFORM_FULL = 2
+
+# KV-cache element formats (batq_kv_format).
+KV_MXFP4 = 4
+KV_MXFP8 = 8
 
 
 def scale_bytes(rows: int, N: int, layout: int) -> int:
@@ -145,6 +153,20 @@ def quantize_act_rmsnorm_raw(x, S, N, ldx, gamma, eps, A, B, r_min, r_max, q, e,
                              layout=SCALES_ROW_MAJOR, stream=0) -> int:
     return lib().batq_quantize_act_rmsnorm(x, S, N, ldx, gamma, eps, A, B, r_min, r_max, q, e,
                                            layout, stream)
+
+
+def quantize_kv_raw(x, T, N, ldx, slots, num_slots, fmt, A, B, r_min, r_max, cache_q, cache_e,
+                    stream=0) -> int:
+    return lib().batq_quantize_kv(x, T, N, ldx, slots, num_slots, fmt, A, B, r_min, r_max,
+                                  cache_q, cache_e, stream)
+
+
+def transform_rows_raw(x, x_type, rows, N, ldx, A, B, y, y_type, stream=0) -> int:
+    return lib().batq_transform_rows(x, x_type, rows, N, ldx, A, B, y, y_type, stream)
+
+
+def dequantize_rows_raw(q, e, src_rows, N, fmt, index, rows, y, y_type, stream=0) -> int:
+    return lib().batq_dequantize_rows(q, e, src_rows, N, fmt, index, rows, y, y_type, stream)
 
 
 def prepare_weight_raw(W, out, N, A_host, B_host, wq, we, layout=SCALES_ROW_MAJOR,
@@ -404,3 +426,75 @@ def quantize_act_rmsnorm(x, gamma, eps, A, B, r_min, r_max, q=None, e=None,
         _ptr(x), S, N, x.stride(0), _ptr(gamma), float(eps), _ptr(A), _ptr(B), _ptr(r_min),
         _ptr(r_max), _ptr(q), _ptr(e), layout, _stream(stream)))
     return q, e
+
+
+# ---------------------------------------------------------------------------------------
+# KV caches (MXFP4 / MXFP8 rows written through a slot map) and the transform of rows
+# ---------------------------------------------------------------------------------------
+
+def quantize_kv(x, slots, fmt, A, B, r_min, r_max, cache_q, cache_e, stream=None):
+    """Transform + clip + MX encoding of K or V rows x (bf16 [T, N]) written into cache rows
+    slots[t] (int64 [T]; out-of-range slots skip the token).  cache_q uint8 [num_slots, N/2]
+    (KV_MXFP4) or [num_slots, N] (KV_MXFP8), cache_e uint8 [num_slots, N/32]; updated in
+    place."""
+    import torch
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    T, N = x.shape
+    num_slots = cache_q.shape[0]
+    assert slots.dtype == torch.int64 and slots.is_contiguous() and slots.numel() == T
+    assert cache_q.dtype == torch.uint8 and cache_q.is_contiguous()
+    assert cache_e.dtype == torch.uint8 and cache_e.is_contiguous()
+    assert cache_q.shape == (num_slots, N // 2 if fmt == KV_MXFP4 else N)
+    assert cache_e.shape == (num_slots, N // 32)
+    for t in (A, B, r_min, r_max):
+        assert t.dtype == torch.float32 and t.is_contiguous()
+    _check("batq_quantize_kv", quantize_kv_raw(
+        _ptr(x), T, N, x.stride(0), _ptr(slots), num_slots, fmt, _ptr(A), _ptr(B), _ptr(r_min),
+        _ptr(r_max), _ptr(cache_q), _ptr(cache_e), _stream(stream)))
+    return cache_q, cache_e
+
+
+def _elem_type(dtype):
+    import torch
+    assert dtype in (torch.float32, torch.bfloat16)
+    return OUT_BF16 if dtype == torch.bfloat16 else OUT_F32
+
+
+def transform_rows(x, A, B, out_dtype=None, y=None, stream=None):
+    """y = block transform of the rows of x (fp32 or bf16 [rows, N]) with factors A [8, 8],
+    B [N/32, 4, 4] (device fp32), no quantisation; y fp32 (default) or bf16."""
+    import torch
+    assert x.dim() == 2 and x.stride(1) == 1
+    rows, N = x.shape
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    if y is None:
+        y = torch.empty((rows, N), dtype=out_dtype, device=x.device)
+    assert y.dtype == out_dtype and y.shape == (rows, N) and y.is_contiguous()
+    for t in (A, B):
+        assert t.dtype == torch.float32 and t.is_contiguous()
+    _check("batq_transform_rows", transform_rows_raw(
+        _ptr(x), _elem_type(x.dtype), rows, N, x.stride(0), _ptr(A), _ptr(B), _ptr(y),
+        _elem_type(out_dtype), _stream(stream)))
+    return y
+
+
+def dequantize_rows(cache_q, cache_e, fmt, index=None, out_dtype=None, y=None, stream=None):
+    """Cache rows (all, or those listed in the int64 index) back to fp32 (default) or bf16
+    [rows, N]; an index entry outside the cache gives a zero row."""
+    import torch
+    src_rows = cache_q.shape[0]
+    N = cache_q.shape[1] * 2 if fmt == KV_MXFP4 else cache_q.shape[1]
+    assert cache_q.dtype == torch.uint8 and cache_q.is_contiguous()
+    assert cache_e.dtype == torch.uint8 and cache_e.is_contiguous()
+    assert cache_e.shape == (src_rows, N // 32)
+    if index is not None:
+        assert index.dtype == torch.int64 and index.is_contiguous()
+    rows = src_rows if index is None else index.numel()
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    if y is None:
+        y = torch.empty((rows, N), dtype=out_dtype, device=cache_q.device)
+    assert y.dtype == out_dtype and y.shape == (rows, N) and y.is_contiguous()
+    _check("batq_dequantize_rows", dequantize_rows_raw(
+        _ptr(cache_q), _ptr(cache_e), src_rows, N, fmt, _ptr(index) if index is not None else 0,
+        rows, _ptr(y), _elem_type(out_dtype), _stream(stream)))
+    return y

@@ -350,3 +350,63 @@ BATQ_API batq_status batq_quantize_act_rmsnorm(const uint16_t* x, int64_t S, int
                                                   q, e, e_layout == BATQ_SCALES_MFMA_TILED,
                                                   as_stream(stream)));
 }
+
+BATQ_API batq_status batq_quantize_kv(const uint16_t* x, int64_t T, int64_t N, int64_t ldx,
+                                      const int64_t* slots, int64_t num_slots,
+                                      batq_kv_format fmt, const float* A, const float* B,
+                                      const float* r_min, const float* r_max,
+                                      uint8_t* cache_q, uint8_t* cache_e, void* stream)
+{
+    if (T < 0 || N < 0 || N % 32 != 0 || num_slots < 0) return BATQ_ERR_SHAPE;
+    if (fmt != BATQ_KV_MXFP4 && fmt != BATQ_KV_MXFP8) return BATQ_ERR_UNSUPPORTED;
+    if (T == 0 || N == 0) return BATQ_OK;
+    if (!x || !slots || !A || !B || !r_min || !r_max || !cache_q || !cache_e)
+        return BATQ_ERR_NULL;
+    if (ldx < N || mul_overflows(T, ldx) || mul_overflows(num_slots, N)) return BATQ_ERR_SHAPE;
+    if (ldx % 8 != 0 || !aligned(x, 16) || !aligned(B, 16) || !aligned(cache_q, 16) ||
+        !aligned(slots, 8) || !aligned(A, 4) || !aligned(r_min, 4) || !aligned(r_max, 4))
+        return BATQ_ERR_ALIGN;
+    return from_hip(batq::launch_quantize_kv(x, T, N / 32, ldx, slots, num_slots,
+                                             fmt == BATQ_KV_MXFP8, A, B, r_min, r_max,
+                                             cache_q, cache_e, as_stream(stream)));
+}
+
+BATQ_API batq_status batq_transform_rows(const void* x, batq_out_type x_type, int64_t rows,
+                                         int64_t N, int64_t ldx, const float* A,
+                                         const float* B, void* y, batq_out_type y_type,
+                                         void* stream)
+{
+    if (rows < 0 || N < 0 || N % 32 != 0) return BATQ_ERR_SHAPE;
+    if ((x_type != BATQ_OUT_F32 && x_type != BATQ_OUT_BF16) ||
+        (y_type != BATQ_OUT_F32 && y_type != BATQ_OUT_BF16))
+        return BATQ_ERR_UNSUPPORTED;
+    if (rows == 0 || N == 0) return BATQ_OK;
+    if (!x || !A || !B || !y) return BATQ_ERR_NULL;
+    if (ldx < N || mul_overflows(rows, ldx) || mul_overflows(rows, N)) return BATQ_ERR_SHAPE;
+    const bool xb = x_type == BATQ_OUT_BF16;
+    if (ldx % (xb ? 8 : 4) != 0 || !aligned(x, 16) || !aligned(B, 16) || !aligned(y, 16) ||
+        !aligned(A, 4))
+        return BATQ_ERR_ALIGN;
+    return from_hip(batq::launch_transform_rows(x, xb, rows, N / 32, ldx, A, B, y,
+                                                y_type == BATQ_OUT_BF16, as_stream(stream)));
+}
+
+BATQ_API batq_status batq_dequantize_rows(const uint8_t* q, const uint8_t* e, int64_t src_rows,
+                                          int64_t N, batq_kv_format fmt, const int64_t* index,
+                                          int64_t rows, void* y, batq_out_type y_type,
+                                          void* stream)
+{
+    if (src_rows < 0 || rows < 0 || N < 0 || N % 32 != 0) return BATQ_ERR_SHAPE;
+    if ((fmt != BATQ_KV_MXFP4 && fmt != BATQ_KV_MXFP8) ||
+        (y_type != BATQ_OUT_F32 && y_type != BATQ_OUT_BF16))
+        return BATQ_ERR_UNSUPPORTED;
+    if (!index && rows > src_rows) return BATQ_ERR_SHAPE;
+    if (rows == 0 || N == 0) return BATQ_OK;
+    if (!y || (src_rows > 0 && (!q || !e)) || (!index && !q)) return BATQ_ERR_NULL;
+    if (mul_overflows(rows, N) || mul_overflows(src_rows, N)) return BATQ_ERR_SHAPE;
+    if (!aligned(q, 16) || !aligned(y, 16) || (index && !aligned(index, 8)))
+        return BATQ_ERR_ALIGN;
+    return from_hip(batq::launch_dequantize_rows(q, e, rows, N / 32, fmt == BATQ_KV_MXFP8,
+                                                 index, src_rows, y, y_type == BATQ_OUT_BF16,
+                                                 as_stream(stream)));
+}

@@ -28,6 +28,26 @@ hipError_t launch_rmsnorm_quantize(const uint16_t* x, int64_t rows, int64_t k, i
                                    uint8_t* q, uint8_t* e, bool tiled_scales,
                                    hipStream_t stream);
 
+// KV cache: rows of x (bf16, k blocks) transformed, clipped and encoded (MXFP8 when fp8,
+// else MXFP4) into cache rows slots[row] (row-major scales); slots < 0 or >= num_slots skip.
+hipError_t launch_quantize_kv(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx,
+                              const int64_t* slots, int64_t num_slots, bool fp8,
+                              const float* A, const float* B, const float* r_min,
+                              const float* r_max, uint8_t* q, uint8_t* e, hipStream_t stream);
+
+// y [rows, 32k] = GPK transform of x (bf16 or fp32 rows, stride ldx) with factors A, B;
+// y fp32 or bf16 (round to nearest even), dense.
+hipError_t launch_transform_rows(const void* x, bool x_bf16, int64_t rows, int64_t k,
+                                 int64_t ldx, const float* A, const float* B, void* y,
+                                 bool y_bf16, hipStream_t stream);
+
+// y [rows, 32k] = dequantised MX rows (MXFP8 when fp8, else MXFP4; row-major scales);
+// output row r reads source row index[r] (r when index is null), zeros when outside
+// [0, src_rows).
+hipError_t launch_dequantize_rows(const uint8_t* q, const uint8_t* e, int64_t rows, int64_t k,
+                                  bool fp8, const int64_t* index, int64_t src_rows, void* y,
+                                  bool y_bf16, hipStream_t stream);
+
 // MXFP4 x MXFP4 -> fp32 GEMM, y[S, out] = dq(x)[S, N] dq(w)[out, N]^T; both scale
 // arrays in the same layout (tiled_scales: MFMA-tiled, else row-major).
 // Epilogue (both GEMMs): res, when not null, is a bf16 [S, out] residual added in fp32;

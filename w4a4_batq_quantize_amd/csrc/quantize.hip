@@ -362,6 +362,182 @@ rmsnorm_quantize_kernel(const uint16_t* __restrict__ xin, int64_t rows, int64_t 
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// KV caches (W4A8KV8 / W4A8KV4) and the transform of rows without quantisation
+// ---------------------------------------------------------------------------------------
+
+// The activation quantiser's mapping (lanes take consecutive blocks of a row), each row
+// written to cache row slots[row]; negative slots and slots >= num_slots are skipped.
+template <bool kFp8>
+__global__ void __launch_bounds__(kThreads)
+quantize_kv_kernel(const uint16_t* __restrict__ xin, int64_t rows, int64_t k, int64_t ldx,
+                   const int64_t* __restrict__ slots, int64_t num_slots,
+                   const float* __restrict__ A, const float* __restrict__ B,
+                   const float* __restrict__ r_min, const float* __restrict__ r_max,
+                   uint8_t* __restrict__ q, uint8_t* __restrict__ e, int lpr_log2)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t row = ((((int64_t)blockIdx.x * kWavesPerGroup + wave) << (6 - lpr_log2)) +
+                         (lane >> lpr_log2));
+    const int64_t blk = (int64_t)blockIdx.y * 64 + (lane & ((1 << lpr_log2) - 1));
+    if (row >= rows || blk >= k) return;
+    const int64_t slot = slots[row];
+    if (slot < 0 || slot >= num_slots) return;
+    float x[32];
+    load_bf16_block(xin + row * ldx + 32 * blk, x);
+    quantize_block<true, kFp8, 0>(x, A, B, r_min, r_max, q, e, slot, blk, k, 0);
+}
+
+// y = GPK transform of x with the given factors (P for K/V rows, the transposed inverses for
+// queries, the inverses for attention outputs), one lane per (row, block).
+template <bool kInBf16, bool kOutBf16>
+__global__ void __launch_bounds__(kThreads)
+transform_rows_kernel(const void* __restrict__ xin, int64_t rows, int64_t k, int64_t ldx,
+                      const float* __restrict__ A, const float* __restrict__ B,
+                      void* __restrict__ yout, int lpr_log2)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t row = ((((int64_t)blockIdx.x * kWavesPerGroup + wave) << (6 - lpr_log2)) +
+                         (lane >> lpr_log2));
+    const int64_t blk = (int64_t)blockIdx.y * 64 + (lane & ((1 << lpr_log2) - 1));
+    if (row >= rows || blk >= k) return;
+    float x[32];
+    if constexpr (kInBf16) {
+        load_bf16_block(static_cast<const uint16_t*>(xin) + row * ldx + 32 * blk, x);
+    } else {
+        const float4* xp = reinterpret_cast<const float4*>(static_cast<const float*>(xin) +
+                                                           row * ldx + 32 * blk);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const float4 v = xp[t];
+            x[4 * t] = v.x;
+            x[4 * t + 1] = v.y;
+            x[4 * t + 2] = v.z;
+            x[4 * t + 3] = v.w;
+        }
+    }
+    const float4* bp = reinterpret_cast<const float4*>(B + 16 * blk);
+    float4 b[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) b[t] = bp[t];
+    float y[32];
+    gpk_transform(x, A, b, y);
+    const int64_t off = row * 32 * k + 32 * blk;
+    if constexpr (kOutBf16) {
+        uint4* yp = reinterpret_cast<uint4*>(static_cast<uint16_t*>(yout) + off);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            uint32_t w[4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t u0 = __float_as_uint(y[8 * t + 2 * d]);
+                const uint32_t u1 = __float_as_uint(y[8 * t + 2 * d + 1]);
+                w[d] = ((u0 + 0x7FFFu + ((u0 >> 16) & 1u)) >> 16) |
+                       (((u1 + 0x7FFFu + ((u1 >> 16) & 1u)) >> 16) << 16);
+            }
+            yp[t] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    } else {
+        float4* yp = reinterpret_cast<float4*>(static_cast<float*>(yout) + off);
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+            yp[t] = make_float4(y[4 * t], y[4 * t + 1], y[4 * t + 2], y[4 * t + 3]);
+    }
+}
+
+// Dequantise MX rows (MXFP4 codes [., N/2] or MXFP8 codes [., N], scales [., N/32]
+// row-major): output row r is source row index[r] (or r without an index); an index outside
+// [0, src_rows) gives a zero row.  Values are code value * 2^(e - 127), exact in fp32 (bf16
+// output: rounded to nearest even).
+template <bool kFp8, bool kOutBf16>
+__global__ void __launch_bounds__(kThreads)
+dequantize_rows_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ e,
+                       int64_t rows, int64_t k, const int64_t* __restrict__ index,
+                       int64_t src_rows, void* __restrict__ yout, int lpr_log2)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t row = ((((int64_t)blockIdx.x * kWavesPerGroup + wave) << (6 - lpr_log2)) +
+                         (lane >> lpr_log2));
+    const int64_t blk = (int64_t)blockIdx.y * 64 + (lane & ((1 << lpr_log2) - 1));
+    if (row >= rows || blk >= k) return;
+    const int64_t src = index ? index[row] : row;
+    float v[32];
+    if (src < 0 || src >= src_rows) {
+#pragma unroll
+        for (int j = 0; j < 32; ++j) v[j] = 0.0f;
+    } else {
+        const uint32_t eb = e[src * k + blk];
+        // 2^(eb - 127): the exponent field itself, the subnormal 2^-127 for eb = 0, NaN for
+        // the E8M0 NaN byte 0xFF
+        const float s = eb == 255u ? __uint_as_float(0x7FC00000u)
+                        : eb       ? __uint_as_float(eb << 23)
+                                   : __uint_as_float(0x00400000u);
+        if constexpr (kFp8) {
+            const uint4* qp = reinterpret_cast<const uint4*>(q + src * 32 * k + 32 * blk);
+            const uint4 c0 = qp[0], c1 = qp[1];
+            const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+            for (int j = 0; j < 32; ++j) {
+                const uint32_t c = (w[j >> 2] >> (8 * (j & 3))) & 0xFFu;
+                const uint32_t f = (c >> 3) & 15u, m = c & 7u;
+                // E4M3: (8 + m) 2^(f - 10) for f > 0, m 2^-9 for f = 0 (exact in fp32)
+                float mag = f ? (float)(8u + m) * __uint_as_float((f + 117u) << 23)
+                              : (float)m * __uint_as_float(118u << 23);
+                if ((c & 0x7Fu) == 0x7Fu) mag = __uint_as_float(0x7FC00000u);   // E4M3 NaN
+                v[j] = ((c & 0x80u) ? -mag : mag) * s;
+            }
+        } else {
+            const uint4 cw = *reinterpret_cast<const uint4*>(q + src * 16 * k + 16 * blk);
+            const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
+            // E2M1 magnitudes in halves: 0, 1, 2, 3, 4, 6, 8, 12
+            constexpr uint32_t kHalves = 0xC8643210u;
+#pragma unroll
+            for (int j = 0; j < 32; ++j) {
+                const uint32_t c = (w[j >> 3] >> (4 * (j & 7))) & 15u;
+                const float mag = (float)((kHalves >> (4 * (c & 7u))) & 15u) * 0.5f;
+                v[j] = ((c & 8u) ? -mag : mag) * s;
+            }
+        }
+    }
+    const int64_t off = row * 32 * k + 32 * blk;
+    if constexpr (kOutBf16) {
+        uint4* yp = reinterpret_cast<uint4*>(static_cast<uint16_t*>(yout) + off);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            uint32_t w[4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t u0 = __float_as_uint(v[8 * t + 2 * d]);
+                const uint32_t u1 = __float_as_uint(v[8 * t + 2 * d + 1]);
+                w[d] = ((u0 + 0x7FFFu + ((u0 >> 16) & 1u)) >> 16) |
+                       (((u1 + 0x7FFFu + ((u1 >> 16) & 1u)) >> 16) << 16);
+            }
+            yp[t] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    } else {
+        float4* yp = reinterpret_cast<float4*>(static_cast<float*>(yout) + off);
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+            yp[t] = make_float4(v[4 * t], v[4 * t + 1], v[4 * t + 2], v[4 * t + 3]);
+    }
+}
+
+// grid of the lane-per-block kernels for rows of k blocks
+dim3 block_grid(int64_t rows, int64_t k, int& lpr_log2, bool& ok)
+{
+    lpr_log2 = 0;
+    while ((1LL << lpr_log2) < k && lpr_log2 < 6) ++lpr_log2;
+    const int64_t rows_per_wave = 64 >> lpr_log2;
+    const int64_t waves = (rows + rows_per_wave - 1) / rows_per_wave;
+    const int64_t gx = (waves + kWavesPerGroup - 1) / kWavesPerGroup;
+    const int64_t gy = (k + 63) / 64;
+    ok = gx <= 0x7FFFFFFF && gy <= 65535;
+    return dim3((unsigned)(ok ? gx : 1), (unsigned)(ok ? gy : 1));
+}
+
 }  // namespace
 
 hipError_t launch_quantize(bool act, const void* x, int64_t rows, int64_t k, int64_t ldx,
@@ -437,6 +613,76 @@ hipError_t launch_rmsnorm_quantize(const uint16_t* x, int64_t rows, int64_t k, i
     else
         hipLaunchKernelGGL(rmsnorm_quantize_kernel<256>, grid, block, 0, stream, x, rows, k,
                            ldx, gamma, eps, A, B, r_min, r_max, q, e, kpow2, ts);
+    return hipGetLastError();
+}
+
+}  // namespace batq
+
+namespace batq {
+
+hipError_t launch_quantize_kv(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx,
+                              const int64_t* slots, int64_t num_slots, bool fp8,
+                              const float* A, const float* B, const float* r_min,
+                              const float* r_max, uint8_t* q, uint8_t* e, hipStream_t stream)
+{
+    int lpr;
+    bool ok;
+    const dim3 grid = block_grid(rows, k, lpr, ok);
+    if (!ok) return hipErrorInvalidConfiguration;
+    if (fp8)
+        hipLaunchKernelGGL(quantize_kv_kernel<true>, grid, dim3(kThreads), 0, stream, x, rows,
+                           k, ldx, slots, num_slots, A, B, r_min, r_max, q, e, lpr);
+    else
+        hipLaunchKernelGGL(quantize_kv_kernel<false>, grid, dim3(kThreads), 0, stream, x, rows,
+                           k, ldx, slots, num_slots, A, B, r_min, r_max, q, e, lpr);
+    return hipGetLastError();
+}
+
+hipError_t launch_transform_rows(const void* x, bool x_bf16, int64_t rows, int64_t k,
+                                 int64_t ldx, const float* A, const float* B, void* y,
+                                 bool y_bf16, hipStream_t stream)
+{
+    int lpr;
+    bool ok;
+    const dim3 grid = block_grid(rows, k, lpr, ok);
+    if (!ok) return hipErrorInvalidConfiguration;
+    const dim3 blk(kThreads);
+    if (x_bf16 && y_bf16)
+        hipLaunchKernelGGL((transform_rows_kernel<true, true>), grid, blk, 0, stream, x, rows,
+                           k, ldx, A, B, y, lpr);
+    else if (x_bf16)
+        hipLaunchKernelGGL((transform_rows_kernel<true, false>), grid, blk, 0, stream, x, rows,
+                           k, ldx, A, B, y, lpr);
+    else if (y_bf16)
+        hipLaunchKernelGGL((transform_rows_kernel<false, true>), grid, blk, 0, stream, x, rows,
+                           k, ldx, A, B, y, lpr);
+    else
+        hipLaunchKernelGGL((transform_rows_kernel<false, false>), grid, blk, 0, stream, x, rows,
+                           k, ldx, A, B, y, lpr);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequantize_rows(const uint8_t* q, const uint8_t* e, int64_t rows, int64_t k,
+                                  bool fp8, const int64_t* index, int64_t src_rows, void* y,
+                                  bool y_bf16, hipStream_t stream)
+{
+    int lpr;
+    bool ok;
+    const dim3 grid = block_grid(rows, k, lpr, ok);
+    if (!ok) return hipErrorInvalidConfiguration;
+    const dim3 blk(kThreads);
+    if (fp8 && y_bf16)
+        hipLaunchKernelGGL((dequantize_rows_kernel<true, true>), grid, blk, 0, stream, q, e,
+                           rows, k, index, src_rows, y, lpr);
+    else if (fp8)
+        hipLaunchKernelGGL((dequantize_rows_kernel<true, false>), grid, blk, 0, stream, q, e,
+                           rows, k, index, src_rows, y, lpr);
+    else if (y_bf16)
+        hipLaunchKernelGGL((dequantize_rows_kernel<false, true>), grid, blk, 0, stream, q, e,
+                           rows, k, index, src_rows, y, lpr);
+    else
+        hipLaunchKernelGGL((dequantize_rows_kernel<false, false>), grid, blk, 0, stream, q, e,
+                           rows, k, index, src_rows, y, lpr);
     return hipGetLastError();
 }
 

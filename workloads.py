@@ -63,6 +63,17 @@ CONFIGS: dict[str, LayerConfig] = {
 }
 
 
+# K/V projection outputs of the evaluated 8B model (8 kv heads x head dim 128: rows of
+# N = 1024), as written into the KV cache: a prefill chunk of 2048 tokens and a decode step of
+# 64 sequences (one token each).  Keys carry a few strong channels.
+KV_CONFIGS: dict[str, LayerConfig] = {
+    "kv_prefill": LayerConfig("kv_prefill", 2048, 1024, 0, seed=(7,),
+                              outliers=("channels_uniform", 4, 10.0, 50.0)),
+    "kv_decode": LayerConfig("kv_decode", 64, 1024, 0, seed=(8,),
+                             outliers=("channels_uniform", 4, 10.0, 50.0)),
+}
+
+
 @dataclass
 class Layer:
     cfg: LayerConfig
@@ -95,7 +106,7 @@ def custom(name: str, S: int, N: int, out: int, seed, act="normal",
 
 def make_layer(cfg: LayerConfig | str, with_weight: bool = True) -> Layer:
     if isinstance(cfg, str):
-        cfg = CONFIGS[cfg]
+        cfg = CONFIGS[cfg] if cfg in CONFIGS else KV_CONFIGS[cfg]
     assert cfg.N % 32 == 0 and cfg.N > 0
     S, N, out, k = cfg.S, cfg.N, cfg.out, cfg.k
     ss = np.random.SeedSequence(list(cfg.seed))
@@ -183,3 +194,15 @@ def form_factors(form: int, k: int, seed):
     else:
         A = (np.eye(8) + 0.1 * rng.standard_normal((8, 8))).astype(np.float32)
     return A, B
+
+
+def kv_slots(T: int, num_slots: int, seed, skip: float = 0.0) -> np.ndarray:
+    """Seeded slot map of T tokens into a cache of num_slots rows: distinct rows drawn
+    without replacement, then a fraction `skip` of the tokens set to -1 (padding tokens that
+    are not cached).  int64 [T]."""
+    assert T <= num_slots
+    seed = list(seed) if isinstance(seed, (tuple, list)) else [int(seed)]
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
+    slots = rng.choice(num_slots, size=T, replace=False).astype(np.int64)
+    slots[rng.random(T) < skip] = -1
+    return slots
