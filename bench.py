@@ -15,6 +15,10 @@ kernels are launched on: the timed steps run quantiser and GEMM in turn, and eac
 then timed alone over the same number of back-to-back launches, so that its event interval
 holds nothing but its own executions.  The step time is wall clock around the timed steps.
 
+With --kv mxfp4|mxfp8 it measures the KV-cache side instead (slot-mapped cache writes of K
+and V rows, the query and attention-output transforms, the dequantisation of cache rows) on
+the K/V projection shapes kv_prefill (default) or kv_decode.
+
 Prints one JSON line.  --gpus above 1 is refused: this path runs on one GPU.
 """
 from __future__ import annotations
@@ -118,6 +122,24 @@ def cpu_baseline(L, seconds, w4a8=False):
     }
 
 
+def time_launches(stream, fn, first, K, R):
+    """K launches of fn on the rotated sets (fn(j) for set j = (first + i) % R), back to back
+    on one stream; returns the event-measured GPU time per launch and the wall time per
+    launch (seconds).  The events are recorded on the stream the kernels are launched on."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(K):
+        if fn((first + i) % R):
+            raise RuntimeError("library call failed")
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return e0.elapsed_time(e1) * 1e-3 / K, (t1 - t0) / K
+
+
 def measure(name, args):
     """Time one layer configuration; returns (record, layer)."""
     import numpy as np
@@ -214,19 +236,7 @@ def measure(name, args):
             raise RuntimeError("library call failed")
 
     def timed(fn, first, K):
-        """K launches of fn on the rotated sets, back to back on one stream; returns the
-        event-measured GPU time per launch and the wall time per launch (seconds)."""
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        e0.record(stream)
-        for i in range(K):
-            if fn((first + i) % R):
-                raise RuntimeError("library call failed")
-        e1.record(stream)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        return e0.elapsed_time(e1) * 1e-3 / K, (t1 - t0) / K
+        return time_launches(stream, fn, first, K, R)
 
     # every set's activation codes and scales are written once before anything is timed, so
     # the GEMM-alone launches below never read buffers the quantiser has not filled
@@ -323,6 +333,190 @@ def measure(name, args):
     return rec, L
 
 
+# KV-cache side of attention with a transformed, quantised cache (W4A8KV8 / W4A8KV4), on the
+# evaluated 8B model's attention shape: 8 kv heads x head dim 128, 32 query heads (GQA 4).
+KV_HEADS, HEAD_DIM, GQA_GROUP = 8, 128, 4
+METRIC_KV = "KV-cache write: fused BAT+clip+{fmt} into slot-mapped cache rows GB/s"
+
+
+def kv_write_bytes(T, N, code_bytes):
+    """Algorithmic bytes of one cache write: bf16 rows in, codes and scales out, the slot map
+    (8 B per token), GPK factors and two ratios per block."""
+    k = N // 32
+    return T * N * 2 + int(T * N * code_bytes) + T * k + 8 * T + 256 + 64 * k + 8 * k
+
+
+def transform_bytes(rows, N, in_b=2, out_b=2):
+    return rows * N * (in_b + out_b) + 256 + 64 * (N // 32)
+
+
+def dequant_bytes(rows, N, code_bytes, out_b=2):
+    return rows * (int(N * code_bytes) + N // 32 + 8) + rows * N * out_b
+
+
+def cpu_baseline_kv(L, fmt, seconds):
+    """The oracle's slot-mapped cache write (single-threaded C) over the whole workload,
+    repeated for about `seconds`."""
+    import numpy as np
+    from oracle import oracle
+    import workloads as wl
+    T, N = L.x_bits.shape
+    r1, r2 = oracle.clip_ratio(L.alpha_min), oracle.clip_ratio(L.alpha_max)
+    slots = wl.kv_slots(T, 2 * T, seed=(67,))
+    cq = np.zeros((2 * T, N // 2 if fmt == 4 else N), dtype=np.uint8)
+    ce = np.zeros((2 * T, N // 32), dtype=np.uint8)
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.quantize_kv(L.x_bits, slots, fmt, L.A, L.B, r1, r2, cq, ce)
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(n * kv_write_bytes(T, N, 0.5 if fmt == 4 else 1.0) / dt / 1e9, 4),
+            "unit": "GB/s", "seconds": round(dt, 2), "cores": 1, "kind": "oracle",
+            "sample": f"{n} full passes over the {T} token rows (plain C oracle, one thread)"}
+
+
+def measure_kv(name, args):
+    """Time the KV path on one configuration: cache writes of K and V rows, the query
+    transform (P^-T per kv head) and the attention-output transform (P^-1), and the
+    dequantisation of the written cache rows."""
+    import numpy as np
+    import torch
+
+    import w4a4_batq_quantize_amd as bq
+    import workloads as wl
+
+    fmt = bq.KV_MXFP4 if args.kv == "mxfp4" else bq.KV_MXFP8
+    cb = 0.5 if fmt == bq.KV_MXFP4 else 1.0
+    L = wl.make_layer(name, with_weight=False)
+    T, N = L.x_bits.shape
+    assert N == KV_HEADS * HEAD_DIM
+    k = N // 32
+    Nq = N * GQA_GROUP
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    # factors: K rows use the layer's (A, B), V rows their own; queries take P_K^-T of the kv
+    # head they attend to, attention outputs P_V^-1
+    Av, Bv = wl.form_factors(0, k, seed=(68, N))
+    Aki, Bki = bq.weight_factors(L.A, L.B)
+    Avi, Bvi = bq.weight_factors(Av, Bv)
+    kd = HEAD_DIM // 32
+    per_q = lambda Bx: np.concatenate([Bx[(h // GQA_GROUP) * kd:(h // GQA_GROUP + 1) * kd]
+                                       for h in range(KV_HEADS * GQA_GROUP)])
+    Aq, Bq = Aki, per_q(Bki)
+    Ao, Bo = Avi.T, per_q(np.transpose(Bvi, (0, 2, 1)))
+    dA, dB, dAv, dBv = f32(L.A), f32(L.B), f32(Av), f32(Bv)
+    dAq, dBq, dAo, dBo = f32(Aq), f32(Bq), f32(Ao), f32(Bo)
+    rmin = f32(bq.clip_ratios(L.alpha_min))
+    rmax = f32(bq.clip_ratios(L.alpha_max))
+
+    per_set = (2 * T * N * 2 + 4 * T * Nq * 2 + 2 * T * (int(N * cb) + k) + 8 * T
+               + T * N * 2)
+    R = min(1024, max(2, math.ceil(args.rotate_bytes / per_set)))
+    num_slots = R * T
+    perm = torch.from_numpy(wl.kv_slots(num_slots, num_slots, seed=(69, T))).to(dev)
+    slots = [perm[j * T:(j + 1) * T].contiguous() for j in range(R)]
+    xk0 = torch.from_numpy(L.x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    xks = [xk0.clone() for _ in range(R)]
+    xvs = [xk0.flip(0).contiguous() for _ in range(R)]
+    qs = [torch.randn((T, Nq), device=dev).to(torch.bfloat16) for _ in range(R)]
+    os_ = [torch.randn((T, Nq), device=dev).to(torch.bfloat16) for _ in range(R)]
+    qts = [torch.empty((T, Nq), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+    ots = [torch.empty((T, Nq), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+    cols = int(N * cb)
+    kq = torch.zeros((num_slots, cols), dtype=torch.uint8, device=dev)
+    ke = torch.zeros((num_slots, k), dtype=torch.uint8, device=dev)
+    vq = torch.zeros_like(kq)
+    ve = torch.zeros_like(ke)
+    deq = [torch.empty((T, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+    del xk0
+
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    BF = bq.OUT_BF16
+
+    def write_k(j):
+        return bq.quantize_kv_raw(xks[j].data_ptr(), T, N, N, slots[j].data_ptr(), num_slots,
+                                  fmt, dA.data_ptr(), dB.data_ptr(), rmin.data_ptr(),
+                                  rmax.data_ptr(), kq.data_ptr(), ke.data_ptr(), sh)
+
+    def write_v(j):
+        return bq.quantize_kv_raw(xvs[j].data_ptr(), T, N, N, slots[j].data_ptr(), num_slots,
+                                  fmt, dAv.data_ptr(), dBv.data_ptr(), rmin.data_ptr(),
+                                  rmax.data_ptr(), vq.data_ptr(), ve.data_ptr(), sh)
+
+    def tq(j):
+        return bq.transform_rows_raw(qs[j].data_ptr(), BF, T, Nq, Nq, dAq.data_ptr(),
+                                     dBq.data_ptr(), qts[j].data_ptr(), BF, sh)
+
+    def to(j):
+        return bq.transform_rows_raw(os_[j].data_ptr(), BF, T, Nq, Nq, dAo.data_ptr(),
+                                     dBo.data_ptr(), ots[j].data_ptr(), BF, sh)
+
+    def dq(j):
+        return bq.dequantize_rows_raw(kq.data_ptr(), ke.data_ptr(), num_slots, N, fmt,
+                                      slots[j].data_ptr(), T, deq[j].data_ptr(), BF, sh)
+
+    def step(j):
+        return write_k(j) | write_v(j) | tq(j) | to(j)
+
+    for j in range(R):
+        if write_k(j) | write_v(j):
+            raise RuntimeError("library call failed")
+    for i in range(args.warmup):
+        if step(i % R):
+            raise RuntimeError("library call failed")
+    torch.cuda.synchronize()
+    K = args.steps
+    t_step_ev, t_step_wall = time_launches(stream, step, args.warmup, K, R)
+    t_kv, _ = time_launches(stream, write_k, args.warmup + K, K, R)
+    t_tr, _ = time_launches(stream, tq, args.warmup + 2 * K, K, R)
+    t_dq, _ = time_launches(stream, dq, args.warmup + 3 * K, K, R)
+    assert bool(torch.isfinite(deq[0].float()).all().item()), "non-finite dequantised rows"
+
+    def roof(kernel, b, t):
+        a = b / t / 1e9
+        return {"kernel": kernel, "bound": "hbm", "achieved": round(a, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(a / HBM_PEAK_GBS, 4),
+                "traffic": None, "avg_us": round(t * 1e6, 3), "algorithmic_bytes": b}
+
+    b_kv = kv_write_bytes(T, N, cb)
+    fname = "MXFP4" if fmt == bq.KV_MXFP4 else "MXFP8"
+    r_kv = roof(f"quantize_kv_kernel (slot-mapped BAT+clip+{fname} cache write)", b_kv, t_kv)
+    r_tr = roof("transform_rows_kernel (query transform, bf16 in and out)",
+                transform_bytes(T, Nq), t_tr)
+    r_dq = roof(f"dequantize_rows_kernel ({fname} cache rows by slot -> bf16)",
+                dequant_bytes(T, N, cb), t_dq)
+    dominant = max((r_kv, r_tr), key=lambda r: r["avg_us"])
+    return {
+        "metric": METRIC_KV.format(fmt=fname),
+        "value": r_kv["achieved"],
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(t_step_wall * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": fname.lower(),
+        "dtype_detail": f"bf16 K/V rows in, fp32 transform/clip, {fname} codes + E8M0 "
+                        "scales out; transforms bf16 in/out with fp32 arithmetic",
+        "data": "synthetic",
+        "config": {"workload": f"{name}: T={T} tokens, K/V rows N={N} ({KV_HEADS} kv heads x "
+                               f"{HEAD_DIM}), {KV_HEADS * GQA_GROUP} query heads, scattered "
+                               f"cache slots, seeded synthetic bf16 data",
+                   "T": T, "N": N, "query_N": Nq, "num_slots": num_slots,
+                   "rotated_buffer_sets": R, "kv_format": fname},
+        "step": "cache write of K and V rows + query transform + attention-output transform",
+        "step_gpu_us": round(t_step_ev * 1e6, 3),
+        "kernel_us": {"quantize_kv": r_kv["avg_us"], "transform_rows": r_tr["avg_us"],
+                      "dequantize_rows": r_dq["avg_us"]},
+        "roofline": dominant,
+        "roofline_kernels": {"quantize_kv": r_kv, "transform_rows": r_tr,
+                             "dequantize_rows": r_dq},
+    }, L, fmt
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -345,6 +539,9 @@ def main():
                          "residual")
     ap.add_argument("--rmsnorm", action="store_true",
                     help="quantise through the RMSNorm-fused quantiser (gamma [N], eps 1e-6)")
+    ap.add_argument("--kv", choices=("mxfp4", "mxfp8"), default=None,
+                    help="measure the KV-cache path instead (cache format; --config kv_prefill "
+                         "or kv_decode)")
     ap.add_argument("--all", action="store_true",
                     help="measure every layer configuration, one JSON line each (no CPU baseline)")
     args = ap.parse_args()
@@ -353,6 +550,13 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.kv:
+        name = "kv_prefill" if args.config == "q_proj" else args.config
+        rec, L, fmt = measure_kv(name, args)
+        if not args.no_cpu_baseline:
+            rec["cpu_baseline"] = cpu_baseline_kv(L, fmt, args.cpu_seconds)
+        print(json.dumps(rec), flush=True)
+        return
     if args.all:
         import workloads as wl
         for name in wl.CONFIGS:

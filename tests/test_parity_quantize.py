@@ -81,6 +81,11 @@ def test_act_parity_prefill_sampled_rows(bq, orc, name):
     (37, 4192, 4256, 3),     # k=131: ragged against 64-block waves, padded rows
     (130, 2048, 2048, 4),    # several rows per wave and ragged row count
     (5, 64 * 32 * 3 + 32, 6208, 5),   # k=193
+    # shapes large enough for the row-group kernels (2 and 4 rows per lane), ragged tails
+    (2047, 4096, 4104, 6),
+    (1025, 4160, 4160, 7),   # k=130
+    (2049, 12288, 12288, 8),
+    (4099, 8224, 8232, 9),   # k=257
 ])
 def test_act_parity_ragged_and_strided(bq, orc, S, N, ldx, seed):
     L = wl.make_layer(wl.custom("ragged", S, N, 8, seed=seed), with_weight=False)
@@ -200,10 +205,11 @@ def test_act_parity_tiled_scales(bq, orc, name):
     assert_codes_equal(to_host(q), e_rm, q_ref, e_ref, zero, what=f"{name} tiled")
 
 
-def test_act_parity_tiled_scales_ragged(bq, orc):
+@pytest.mark.parametrize("S,N", [(37, 4192), (2050, 4160), (4097, 12288)])
+def test_act_parity_tiled_scales_ragged(bq, orc, S, N):
     import torch
     from tests.gpu_util import from_tiled_scales
-    L = wl.make_layer(wl.custom("ragged_t", 37, 4192, 8, seed=31), with_weight=False)
+    L = wl.make_layer(wl.custom("ragged_t", S, N, 8, seed=31), with_weight=False)
     S, N = L.x_bits.shape
     q, e = bq.quantize_act(bf16_to_device(L.x_bits), f32_to_device(L.A), f32_to_device(L.B),
                            f32_to_device(bq.clip_ratios(L.alpha_min)),

@@ -80,6 +80,7 @@ def test_act8_parity_tiled_scales(bq, orc, name):
 @pytest.mark.parametrize("S,N,ldx,seed", [
     (1, 32, 32, 1), (3, 96, 104, 2), (37, 4192, 4256, 3), (130, 2048, 2048, 4),
     (5, 64 * 32 * 3 + 32, 6208, 5),
+    (2047, 4096, 4104, 6), (4099, 8224, 8232, 7),   # row-group kernels, ragged tails
 ])
 def test_act8_parity_ragged_and_strided(bq, orc, S, N, ldx, seed):
     L = wl.make_layer(wl.custom("ragged", S, N, 8, seed=seed), with_weight=False)

@@ -37,33 +37,33 @@ constexpr int kThreads = 64 * kWavesPerGroup;
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// Y = B^T (X A) for one block held in registers, X[r][c] = x[8r + c].
+// Y = B^T (X A) for one block held in registers, X[r][c] = x[8r + c].  Z = X A is formed a
+// row at a time and each row s is folded into every row of Y at once, so only one row of Z
+// is live; every sum keeps its order (a product, then fused multiply-adds in increasing
+// index order: z[s][c] over the 8 terms of A's column, y[r][c] over s = 0..3).
 __device__ __forceinline__ void gpk_transform(const float (&x)[32], const float* __restrict__ A,
                                               const float4 (&b)[4], float (&y)[32])
 {
-    float z[32];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            float acc = x[8 * r] * A[c];
-#pragma unroll
-            for (int qi = 1; qi < 8; ++qi) acc = __builtin_fmaf(x[8 * r + qi], A[8 * qi + c], acc);
-            z[8 * r + c] = acc;
-        }
-    }
     const float bm[4][4] = {{b[0].x, b[0].y, b[0].z, b[0].w},
                             {b[1].x, b[1].y, b[1].z, b[1].w},
                             {b[2].x, b[2].y, b[2].z, b[2].w},
                             {b[3].x, b[3].y, b[3].z, b[3].w}};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int s = 0; s < 4; ++s) {
+        float zs[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-            float acc = bm[0][r] * z[c];
+            float acc = x[8 * s] * A[c];
 #pragma unroll
-            for (int qi = 1; qi < 4; ++qi) acc = __builtin_fmaf(bm[qi][r], z[8 * qi + c], acc);
-            y[8 * r + c] = acc;
+            for (int qi = 1; qi < 8; ++qi) acc = __builtin_fmaf(x[8 * s + qi], A[8 * qi + c], acc);
+            zs[c] = acc;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                y[8 * r + c] = s == 0 ? bm[0][r] * zs[c]
+                                      : __builtin_fmaf(bm[s][r], zs[c], y[8 * r + c]);
         }
     }
 }
@@ -97,26 +97,74 @@ __device__ __forceinline__ void full_transform(const float (&x)[32], const float
     }
 }
 
+// The per-block parameters a lane needs besides A: B_i (GPK and Kronecker forms) and the
+// two clip ratios (activations).
+struct BlockParams {
+    float4 b[4];
+    float rmin, rmax;
+};
+
+template <bool kAct, int kForm>
+__device__ __forceinline__ BlockParams load_block_params(const float* __restrict__ B,
+                                                         const float* __restrict__ r_min,
+                                                         const float* __restrict__ r_max,
+                                                         int64_t blk)
+{
+    BlockParams p;
+    if constexpr (kForm != 2) {
+        const float4* bp = reinterpret_cast<const float4*>(B + 16 * blk);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) p.b[t] = bp[t];
+    }
+    if constexpr (kAct) {
+        p.rmin = r_min[blk];
+        p.rmax = r_max[blk];
+    }
+    return p;
+}
+
+// An empty asm that takes one value of each of the block's loads (its parameters and its
+// four 16-byte pieces of x): every one of them is issued before this point, so the lane
+// waits for one round trip instead of a chain (the compiler otherwise issues the parameter
+// loads after the transform that precedes their use).
+// A (8x8, wave-uniform) as four 16-dword scalar loads, taken whole by an empty asm so that
+// none of them is left until after the vector loads have completed.
+__device__ __forceinline__ void pin_uniform_a(const float* __restrict__ A)
+{
+    typedef float f32x16 __attribute__((ext_vector_type(16)));
+    const f32x16* a = reinterpret_cast<const f32x16*>(A);
+    asm volatile("" ::"s"(a[0]), "s"(a[1]), "s"(a[2]), "s"(a[3]));
+}
+
+template <bool kAct, int kForm>
+__device__ __forceinline__ void issue_together(const float* __restrict__ A, const BlockParams& p,
+                                               const float (&x)[32])
+{
+    static_assert(kForm == 0, "GPK lane mapping only");
+    pin_uniform_a(A);
+    if constexpr (kAct)
+        asm volatile("" ::"v"(p.b[0].x), "v"(p.b[1].x), "v"(p.b[2].x), "v"(p.b[3].x),
+                     "v"(p.rmin), "v"(p.rmax), "v"(x[0]), "v"(x[8]), "v"(x[16]), "v"(x[24]));
+    else
+        asm volatile("" ::"v"(p.b[0].x), "v"(p.b[1].x), "v"(p.b[2].x), "v"(p.b[3].x),
+                     "v"(x[0]), "v"(x[4]), "v"(x[8]), "v"(x[12]), "v"(x[16]), "v"(x[20]),
+                     "v"(x[24]), "v"(x[28]));
+}
+
 // Transform, clip, encode and store one block held in registers (row, blk), shared by the
-// quantisers.
+// quantisers; the parameters come preloaded.
 template <bool kAct, bool kFp8, int kForm>
 __device__ __forceinline__ void quantize_block(float (&x)[32], const float* __restrict__ A,
-                                               const float* __restrict__ B,
-                                               const float* __restrict__ r_min,
-                                               const float* __restrict__ r_max,
+                                               const BlockParams& p,
                                                uint8_t* __restrict__ q, uint8_t* __restrict__ e,
                                                int64_t row, int64_t blk, int64_t k,
-                                               int tiled_scales)
+                                               int tiled_scales, bool store = true)
 {
     float y[32];
     if constexpr (kForm == 2) {
         full_transform(x, A + 1024 * blk, y);
     } else {
-        const float4* bp = reinterpret_cast<const float4*>(B + 16 * blk);
-        float4 b[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) b[t] = bp[t];
-        gpk_transform(x, kForm == 1 ? A + 64 * blk : A, b, y);
+        gpk_transform(x, kForm == 1 ? A + 64 * blk : A, p.b, y);
     }
 
     float amax;
@@ -128,8 +176,8 @@ __device__ __forceinline__ void quantize_block(float (&x)[32], const float* __re
             m = __builtin_fminf(m, y[j]);
             M = __builtin_fmaxf(M, y[j]);
         }
-        hi = r_max[blk] * M;
-        lo = __builtin_fminf(r_min[blk] * m, hi);   // lo > hi: every value -> hi
+        hi = p.rmax * M;
+        lo = __builtin_fminf(p.rmin * m, hi);        // lo > hi: every value -> hi
         amax = __builtin_fmaxf(__builtin_fabsf(__builtin_amdgcn_fmed3f(m, lo, hi)),
                                __builtin_fabsf(__builtin_amdgcn_fmed3f(M, lo, hi)));
     } else {
@@ -159,9 +207,11 @@ __device__ __forceinline__ void quantize_block(float (&x)[32], const float* __re
                 __builtin_amdgcn_fmed3f(y[4 * d + 3], L, H), scale, true);
             w[d] = (uint32_t)(uint16_t)acc[0] | ((uint32_t)(uint16_t)acc[1] << 16);
         }
-        uint4* qp = reinterpret_cast<uint4*>(q + row * (32 * k) + 32 * blk);
-        qp[0] = make_uint4(w[0], w[1], w[2], w[3]);
-        qp[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        if (store) {
+            uint4* qp = reinterpret_cast<uint4*>(q + row * (32 * k) + 32 * blk);
+            qp[0] = make_uint4(w[0], w[1], w[2], w[3]);
+            qp[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        }
     } else {
         if constexpr (kAct) {
 #pragma unroll
@@ -177,8 +227,9 @@ __device__ __forceinline__ void quantize_block(float (&x)[32], const float* __re
             acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, y[8 * d + 6], y[8 * d + 7], scale, 3);
             w[d] = acc;
         }
-        *reinterpret_cast<uint4*>(q + row * (16 * k) + 16 * blk) =
-            make_uint4(w[0], w[1], w[2], w[3]);
+        if (store)
+            *reinterpret_cast<uint4*>(q + row * (16 * k) + 16 * blk) =
+                make_uint4(w[0], w[1], w[2], w[3]);
     }
     // scale byte: row-major, or the 256-byte (32 rows x 8 blocks) units the GEMM consumes,
     // blocks of a unit ordered 0,2,4,6,1,3,5,7 within each row's 8 bytes
@@ -186,7 +237,21 @@ __device__ __forceinline__ void quantize_block(float (&x)[32], const float* __re
         ? (((row >> 5) * ((k + 7) >> 3) + (blk >> 3)) << 8) + ((row & 31) << 3) +
               ((blk & 1) << 2) + ((blk & 7) >> 1)
         : row * k + blk;
-    e[eoff] = (uint8_t)ebyte;
+    if (store) e[eoff] = (uint8_t)ebyte;
+}
+
+// The same with the parameters loaded here.
+template <bool kAct, bool kFp8, int kForm>
+__device__ __forceinline__ void quantize_block(float (&x)[32], const float* __restrict__ A,
+                                               const float* __restrict__ B,
+                                               const float* __restrict__ r_min,
+                                               const float* __restrict__ r_max,
+                                               uint8_t* __restrict__ q, uint8_t* __restrict__ e,
+                                               int64_t row, int64_t blk, int64_t k,
+                                               int tiled_scales)
+{
+    const BlockParams p = load_block_params<kAct, kForm>(B, r_min, r_max, blk);
+    quantize_block<kAct, kFp8, kForm>(x, A, p, q, e, row, blk, k, tiled_scales);
 }
 
 // kForm selects the transform (thelatestinai listing, Table 1): 0 GPK, A [8][8] shared by
@@ -200,29 +265,11 @@ __device__ __forceinline__ void quantize_block(float (&x)[32], const float* __re
 // largest exponent), and the conversion instruction, exact round-to-nearest-even otherwise,
 // returns NaN above 448 where MX saturates, so the clip bounds are first clamped into
 // [-448 s, 448 s] (a clamp of a clamp is the clamp to the clamped bounds).
-template <bool kAct, bool kFp8 = false, int kForm = 0>
-__global__ void __launch_bounds__(kThreads)
-quantize_kernel(const void* __restrict__ xin, int64_t rows, int64_t k, int64_t ldx,
-                const float* __restrict__ A, const float* __restrict__ B,
-                const float* __restrict__ r_min, const float* __restrict__ r_max,
-                uint8_t* __restrict__ q, uint8_t* __restrict__ e, int lpr_log2,
-                int tiled_scales)
+// One block of x (bf16 activations or fp32 weights) into fp32 registers.
+template <bool kAct>
+__device__ __forceinline__ void load_block(const void* __restrict__ xin, int64_t row, int64_t ldx,
+                                           int64_t blk, float (&x)[32])
 {
-    static_assert(kAct || !kFp8, "MXFP8 is an activation-side format");
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    int64_t row, blk;
-    if constexpr (kForm != 0) {
-        blk = blockIdx.x;
-        row = (int64_t)blockIdx.y * kThreads + threadIdx.x;
-    } else {
-        row = ((((int64_t)blockIdx.x * kWavesPerGroup + wave) << (6 - lpr_log2)) +
-               (lane >> lpr_log2));
-        blk = (int64_t)blockIdx.y * 64 + (lane & ((1 << lpr_log2) - 1));
-    }
-    if (row >= rows || blk >= k) return;
-
-    float x[32];
     if constexpr (kAct) {
         const uint4* xp = reinterpret_cast<const uint4*>(
             static_cast<const uint16_t*>(xin) + row * ldx + 32 * blk);
@@ -250,7 +297,35 @@ quantize_kernel(const void* __restrict__ xin, int64_t rows, int64_t k, int64_t l
             x[4 * t + 3] = v.w;
         }
     }
-    quantize_block<kAct, kFp8, kForm>(x, A, B, r_min, r_max, q, e, row, blk, k, tiled_scales);
+}
+
+template <bool kAct, bool kFp8 = false, int kForm = 0>
+__global__ void __launch_bounds__(kThreads)
+quantize_kernel(const void* __restrict__ xin, int64_t rows, int64_t k, int64_t ldx,
+                const float* __restrict__ A, const float* __restrict__ B,
+                const float* __restrict__ r_min, const float* __restrict__ r_max,
+                uint8_t* __restrict__ q, uint8_t* __restrict__ e, int lpr_log2,
+                int tiled_scales)
+{
+    static_assert(kAct || !kFp8, "MXFP8 is an activation-side format");
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    int64_t row, blk;
+    if constexpr (kForm != 0) {
+        blk = blockIdx.x;
+        row = (int64_t)blockIdx.y * kThreads + threadIdx.x;
+    } else {
+        row = ((((int64_t)blockIdx.x * kWavesPerGroup + wave) << (6 - lpr_log2)) +
+               (lane >> lpr_log2));
+        blk = (int64_t)blockIdx.y * 64 + (lane & ((1 << lpr_log2) - 1));
+    }
+    if (row >= rows || blk >= k) return;
+
+    const BlockParams p = load_block_params<kAct, kForm>(B, r_min, r_max, blk);
+    float x[32];
+    load_block<kAct>(xin, row, ldx, blk, x);
+    if constexpr (kForm == 0) issue_together<kAct, kForm>(A, p, x);
+    quantize_block<kAct, kFp8, kForm>(x, A, p, q, e, row, blk, k, tiled_scales);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -382,11 +457,19 @@ quantize_kv_kernel(const uint16_t* __restrict__ xin, int64_t rows, int64_t k, in
                          (lane >> lpr_log2));
     const int64_t blk = (int64_t)blockIdx.y * 64 + (lane & ((1 << lpr_log2) - 1));
     if (row >= rows || blk >= k) return;
+    // the row is in bounds whatever its slot: it is loaded and encoded unconditionally (so
+    // its loads go out together with the slot's), and only the stores depend on the slot
+    const BlockParams p = load_block_params<true, 0>(B, r_min, r_max, blk);
     const int64_t slot = slots[row];
-    if (slot < 0 || slot >= num_slots) return;
     float x[32];
     load_bf16_block(xin + row * ldx + 32 * blk, x);
-    quantize_block<true, kFp8, 0>(x, A, B, r_min, r_max, q, e, slot, blk, k, 0);
+    // as issue_together, with the slot's load among them (instead of the row's loads
+    // waiting behind its test)
+    pin_uniform_a(A);
+    asm volatile("" ::"v"(slot), "v"(p.b[0].x), "v"(p.b[1].x), "v"(p.b[2].x), "v"(p.b[3].x),
+                 "v"(p.rmin), "v"(p.rmax), "v"(x[0]), "v"(x[8]), "v"(x[16]), "v"(x[24]));
+    const bool keep = slot >= 0 && slot < num_slots;
+    quantize_block<true, kFp8, 0>(x, A, p, q, e, keep ? slot : 0, blk, k, 0, keep);
 }
 
 // y = GPK transform of x with the given factors (P for K/V rows, the transposed inverses for
@@ -551,8 +634,8 @@ hipError_t launch_quantize(bool act, const void* x, int64_t rows, int64_t k, int
     while ((1LL << lpr_log2) < k && lpr_log2 < 6) ++lpr_log2;
     const int64_t rows_per_wave = 64 >> lpr_log2;
     const int64_t waves = (rows + rows_per_wave - 1) / rows_per_wave;
-    const int64_t gx = (waves + kWavesPerGroup - 1) / kWavesPerGroup;
     const int64_t gy = (k + 63) / 64;
+    const int64_t gx = (waves + kWavesPerGroup - 1) / kWavesPerGroup;
     if (gx > 0x7FFFFFFF || gy > 65535) return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)gx, (unsigned)gy);
     if (form != 0) {
@@ -576,10 +659,10 @@ hipError_t launch_quantize(bool act, const void* x, int64_t rows, int64_t k, int
                            x, rows, k, ldx, A, B, r_min, r_max, q, e, lpr_log2, ts);
     else if (act && fp8)
         hipLaunchKernelGGL((quantize_kernel<true, true>), grid, dim3(kThreads), 0, stream, x,
-                           rows, k, ldx, A, B, r_min, r_max, q, e, lpr_log2, (int)tiled_scales);
+                           rows, k, ldx, A, B, r_min, r_max, q, e, lpr_log2, ts);
     else if (act)
         hipLaunchKernelGGL(quantize_kernel<true>, grid, dim3(kThreads), 0, stream, x, rows, k,
-                           ldx, A, B, r_min, r_max, q, e, lpr_log2, (int)tiled_scales);
+                           ldx, A, B, r_min, r_max, q, e, lpr_log2, ts);
     else
         hipLaunchKernelGGL(quantize_kernel<false>, grid, dim3(kThreads), 0, stream, x, rows,
                            k, ldx, A, B, r_min, r_max, q, e, lpr_log2, (int)tiled_scales);
