@@ -12,8 +12,9 @@ Inputs are resident in HBM before timing starts.  Every step uses the next of R 
 exceed the 256 MB Infinity Cache several times over; the measured rates are therefore HBM
 rates, not cache rates.  Kernel durations come from HIP events recorded on the stream the
 kernels are launched on: the timed steps run quantiser and GEMM in turn, and each kernel is
-then timed alone over the same number of back-to-back launches, so that its event interval
-holds nothing but its own executions.  The step time is wall clock around the timed steps.
+then timed alone over the same number of back-to-back launches, captured into a HIP graph
+and replayed, so that its event interval holds nothing but its own executions (and not the
+host's cost of enqueueing them).  The step time is wall clock around the timed steps.
 
 With --kv mxfp4|mxfp8 it measures the KV-cache side instead (slot-mapped cache writes of K
 and V rows, the query and attention-output transforms, the dequantisation of cache rows) on
@@ -140,6 +141,33 @@ def time_launches(stream, fn, first, K, R):
     return e0.elapsed_time(e1) * 1e-3 / K, (t1 - t0) / K
 
 
+def time_graph(stream, fn, first, K, R, reps=3):
+    """K launches of fn (fn(j, stream_handle) for set j = (first + i) % R) captured into one
+    HIP graph, replayed `reps` times on `stream`; returns the event-measured GPU time per
+    launch (seconds).  Replay takes the host's launch cost out of the interval, so small
+    kernels are timed by the GPU rather than by the Python loop that enqueues them."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=cs):
+        h = torch.cuda.current_stream().cuda_stream
+        for i in range(K):
+            if fn((first + i) % R, h):
+                raise RuntimeError("library call failed")
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        g.replay()                                   # untimed first replay
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) * 1e-3 / (K * reps)
+
+
 def measure(name, args):
     """Time one layer configuration; returns (record, layer)."""
     import numpy as np
@@ -216,9 +244,9 @@ def measure(name, args):
         def quant(x, S_, N_, ldx, a, b, r1, r2, xq, xe, lay, st):
             return bq.quantize_act_form_raw(x, S_, N_, ldx, fid, a, b, r1, r2, xq, xe, lay, st)
 
-    def launch_k1(j):
+    def launch_k1(j, s=sh):
         x, xq, xe, _, _, _ = ptr[j]
-        return quant(x, S, N, N, pA, pB, pr1, pr2, xq, xe, layout, sh)
+        return quant(x, S, N, N, pA, pB, pr1, pr2, xq, xe, layout, s)
 
     if epilogue != "f32":
         gemm_out = bq.gemm_w4a8_out_raw if w4a8 else bq.gemm_w4a4_out_raw
@@ -227,9 +255,9 @@ def measure(name, args):
         def gemm(xq, xe, wq, we, S_, N_, out_, y, lay, st):
             return gemm_out(xq, xe, wq, we, S_, N_, out_, y, bq.OUT_BF16, pres, lay, st)
 
-    def launch_k2(j):
+    def launch_k2(j, s=sh):
         _, xq, xe, wq, we, y = ptr[j]
-        return gemm(xq, xe, wq, we, S, N, out, y, layout, sh)
+        return gemm(xq, xe, wq, we, S, N, out, y, layout, s)
 
     def step(j):
         if launch_k1(j) | launch_k2(j):
@@ -251,10 +279,11 @@ def measure(name, args):
     K = args.steps
     t_step_ev, t_step_wall = timed(lambda j: step(j) or 0, args.warmup, K)
     ms_per_step = t_step_wall * 1e3
-    # per-kernel durations: the same launches, each kernel alone back to back, so that an
-    # event interval holds one kernel's executions and the dispatch gaps between them only
-    t_k1, _ = timed(launch_k1, args.warmup + K, K)
-    t_k2, _ = timed(launch_k2, args.warmup + 2 * K, K)
+    # per-kernel durations: the same launches, each kernel alone back to back in a captured
+    # graph, so that an event interval holds one kernel's executions and the dispatch gaps
+    # between them only
+    t_k1 = time_graph(stream, launch_k1, args.warmup + K, K, R)
+    t_k2 = time_graph(stream, launch_k2, args.warmup + 2 * K, K, R)
 
     if args.copy_calibration:
         # plain copy of known size, outside the timed region, for scaling HBM counters
@@ -438,27 +467,27 @@ def measure_kv(name, args):
     sh = stream.cuda_stream
     BF = bq.OUT_BF16
 
-    def write_k(j):
+    def write_k(j, s=sh):
         return bq.quantize_kv_raw(xks[j].data_ptr(), T, N, N, slots[j].data_ptr(), num_slots,
                                   fmt, dA.data_ptr(), dB.data_ptr(), rmin.data_ptr(),
-                                  rmax.data_ptr(), kq.data_ptr(), ke.data_ptr(), sh)
+                                  rmax.data_ptr(), kq.data_ptr(), ke.data_ptr(), s)
 
-    def write_v(j):
+    def write_v(j, s=sh):
         return bq.quantize_kv_raw(xvs[j].data_ptr(), T, N, N, slots[j].data_ptr(), num_slots,
                                   fmt, dAv.data_ptr(), dBv.data_ptr(), rmin.data_ptr(),
-                                  rmax.data_ptr(), vq.data_ptr(), ve.data_ptr(), sh)
+                                  rmax.data_ptr(), vq.data_ptr(), ve.data_ptr(), s)
 
-    def tq(j):
+    def tq(j, s=sh):
         return bq.transform_rows_raw(qs[j].data_ptr(), BF, T, Nq, Nq, dAq.data_ptr(),
-                                     dBq.data_ptr(), qts[j].data_ptr(), BF, sh)
+                                     dBq.data_ptr(), qts[j].data_ptr(), BF, s)
 
-    def to(j):
+    def to(j, s=sh):
         return bq.transform_rows_raw(os_[j].data_ptr(), BF, T, Nq, Nq, dAo.data_ptr(),
-                                     dBo.data_ptr(), ots[j].data_ptr(), BF, sh)
+                                     dBo.data_ptr(), ots[j].data_ptr(), BF, s)
 
-    def dq(j):
+    def dq(j, s=sh):
         return bq.dequantize_rows_raw(kq.data_ptr(), ke.data_ptr(), num_slots, N, fmt,
-                                      slots[j].data_ptr(), T, deq[j].data_ptr(), BF, sh)
+                                      slots[j].data_ptr(), T, deq[j].data_ptr(), BF, s)
 
     def step(j):
         return write_k(j) | write_v(j) | tq(j) | to(j)
@@ -472,9 +501,9 @@ def measure_kv(name, args):
     torch.cuda.synchronize()
     K = args.steps
     t_step_ev, t_step_wall = time_launches(stream, step, args.warmup, K, R)
-    t_kv, _ = time_launches(stream, write_k, args.warmup + K, K, R)
-    t_tr, _ = time_launches(stream, tq, args.warmup + 2 * K, K, R)
-    t_dq, _ = time_launches(stream, dq, args.warmup + 3 * K, K, R)
+    t_kv = time_graph(stream, write_k, args.warmup + K, K, R)
+    t_tr = time_graph(stream, tq, args.warmup + 2 * K, K, R)
+    t_dq = time_graph(stream, dq, args.warmup + 3 * K, K, R)
     assert bool(torch.isfinite(deq[0].float()).all().item()), "non-finite dequantised rows"
 
     def roof(kernel, b, t):
