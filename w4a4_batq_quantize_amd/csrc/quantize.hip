@@ -123,10 +123,6 @@ __device__ __forceinline__ BlockParams load_block_params(const float* __restrict
     return p;
 }
 
-// An empty asm that takes one value of each of the block's loads (its parameters and its
-// four 16-byte pieces of x): every one of them is issued before this point, so the lane
-// waits for one round trip instead of a chain (the compiler otherwise issues the parameter
-// loads after the transform that precedes their use).
 // A (8x8, wave-uniform) as four 16-dword scalar loads, taken whole by an empty asm so that
 // none of them is left until after the vector loads have completed.
 __device__ __forceinline__ void pin_uniform_a(const float* __restrict__ A)
@@ -136,15 +132,22 @@ __device__ __forceinline__ void pin_uniform_a(const float* __restrict__ A)
     asm volatile("" ::"s"(a[0]), "s"(a[1]), "s"(a[2]), "s"(a[3]));
 }
 
-template <bool kAct, int kForm>
+// An empty asm that takes one value of each of the block's loads (A, B_i, the ratios when
+// kRatios, and each 16-byte piece of x): every one of them is issued before this point, so
+// the lane waits for one round trip instead of a chain (the compiler otherwise issues some
+// loads after the arithmetic that precedes their use, and waits for them there).
+template <bool kBf16, bool kRatios>
 __device__ __forceinline__ void issue_together(const float* __restrict__ A, const BlockParams& p,
                                                const float (&x)[32])
 {
-    static_assert(kForm == 0, "GPK lane mapping only");
     pin_uniform_a(A);
-    if constexpr (kAct)
+    // x: one value of each 16-byte load (4 for bf16 rows, 8 for fp32 rows)
+    if constexpr (kBf16 && kRatios)
         asm volatile("" ::"v"(p.b[0].x), "v"(p.b[1].x), "v"(p.b[2].x), "v"(p.b[3].x),
                      "v"(p.rmin), "v"(p.rmax), "v"(x[0]), "v"(x[8]), "v"(x[16]), "v"(x[24]));
+    else if constexpr (kBf16)
+        asm volatile("" ::"v"(p.b[0].x), "v"(p.b[1].x), "v"(p.b[2].x), "v"(p.b[3].x),
+                     "v"(x[0]), "v"(x[8]), "v"(x[16]), "v"(x[24]));
     else
         asm volatile("" ::"v"(p.b[0].x), "v"(p.b[1].x), "v"(p.b[2].x), "v"(p.b[3].x),
                      "v"(x[0]), "v"(x[4]), "v"(x[8]), "v"(x[12]), "v"(x[16]), "v"(x[20]),
@@ -324,7 +327,7 @@ quantize_kernel(const void* __restrict__ xin, int64_t rows, int64_t k, int64_t l
     const BlockParams p = load_block_params<kAct, kForm>(B, r_min, r_max, blk);
     float x[32];
     load_block<kAct>(xin, row, ldx, blk, x);
-    if constexpr (kForm == 0) issue_together<kAct, kForm>(A, p, x);
+    if constexpr (kForm == 0) issue_together<kAct, kAct>(A, p, x);
     quantize_block<kAct, kFp8, kForm>(x, A, p, q, e, row, blk, k, tiled_scales);
 }
 
@@ -486,27 +489,12 @@ transform_rows_kernel(const void* __restrict__ xin, int64_t rows, int64_t k, int
                          (lane >> lpr_log2));
     const int64_t blk = (int64_t)blockIdx.y * 64 + (lane & ((1 << lpr_log2) - 1));
     if (row >= rows || blk >= k) return;
+    const BlockParams p = load_block_params<false, 0>(B, nullptr, nullptr, blk);
     float x[32];
-    if constexpr (kInBf16) {
-        load_bf16_block(static_cast<const uint16_t*>(xin) + row * ldx + 32 * blk, x);
-    } else {
-        const float4* xp = reinterpret_cast<const float4*>(static_cast<const float*>(xin) +
-                                                           row * ldx + 32 * blk);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const float4 v = xp[t];
-            x[4 * t] = v.x;
-            x[4 * t + 1] = v.y;
-            x[4 * t + 2] = v.z;
-            x[4 * t + 3] = v.w;
-        }
-    }
-    const float4* bp = reinterpret_cast<const float4*>(B + 16 * blk);
-    float4 b[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) b[t] = bp[t];
+    load_block<kInBf16>(xin, row, ldx, blk, x);
+    issue_together<kInBf16, false>(A, p, x);    // every load issued before the first use
     float y[32];
-    gpk_transform(x, A, b, y);
+    gpk_transform(x, A, p.b, y);
     const int64_t off = row * 32 * k + 32 * blk;
     if constexpr (kOutBf16) {
         uint4* yp = reinterpret_cast<uint4*>(static_cast<uint16_t*>(yout) + off);
@@ -552,15 +540,25 @@ dequantize_rows_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict_
 #pragma unroll
         for (int j = 0; j < 32; ++j) v[j] = 0.0f;
     } else {
+        // the scale byte and the codes are loaded together
         const uint32_t eb = e[src * k + blk];
+        uint4 c0, c1;
+        if constexpr (kFp8) {
+            const uint4* qp = reinterpret_cast<const uint4*>(q + src * 32 * k + 32 * blk);
+            c0 = qp[0];
+            c1 = qp[1];
+            asm volatile("" ::"v"(eb), "v"(c0.x), "v"(c1.x));
+        } else {
+            c0 = *reinterpret_cast<const uint4*>(q + src * 16 * k + 16 * blk);
+            c1 = c0;
+            asm volatile("" ::"v"(eb), "v"(c0.x));
+        }
         // 2^(eb - 127): the exponent field itself, the subnormal 2^-127 for eb = 0, NaN for
         // the E8M0 NaN byte 0xFF
         const float s = eb == 255u ? __uint_as_float(0x7FC00000u)
                         : eb       ? __uint_as_float(eb << 23)
                                    : __uint_as_float(0x00400000u);
         if constexpr (kFp8) {
-            const uint4* qp = reinterpret_cast<const uint4*>(q + src * 32 * k + 32 * blk);
-            const uint4 c0 = qp[0], c1 = qp[1];
             const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
             for (int j = 0; j < 32; ++j) {
@@ -573,8 +571,7 @@ dequantize_rows_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict_
                 v[j] = ((c & 0x80u) ? -mag : mag) * s;
             }
         } else {
-            const uint4 cw = *reinterpret_cast<const uint4*>(q + src * 16 * k + 16 * blk);
-            const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
+            const uint32_t w[4] = {c0.x, c0.y, c0.z, c0.w};
             // E2M1 magnitudes in halves: 0, 1, 2, 3, 4, 6, 8, 12
             constexpr uint32_t kHalves = 0xC8643210u;
 #pragma unroll
