@@ -86,10 +86,14 @@ __device__ __forceinline__ void tile_origin(int64_t tiles_o, int64_t tiles_s, in
 constexpr int kStageBlocks = 8;
 constexpr int kRowBytes = 16 * kStageBlocks;   // 128
 
-template <int BO_, int BS_, int WO_, int WS_, int NB_, bool TS_, int SB_ = 4>
+template <int BO_, int BS_, int WO_, int WS_, int NB_, bool TS_, int SB_ = 4, bool SW_ = false>
 struct DmaCfg {
     static constexpr int BO = BO_, BS = BS_, WO = WO_, WS = WS_, NB = NB_;
     static constexpr bool TS = TS_;   // scales in the MFMA-tiled layout (else row-major)
+    // SW: activations as the MFMA's row operand and weights as its column operand, so a
+    // lane's accumulator column is one output feature and a register row one token: each
+    // dword store of the epilogue writes 32 consecutive outputs (whole 128-byte lines)
+    static constexpr bool SW = SW_;
     static constexpr int SB = TS_ ? 4 : SB_;                        // scale DMA bytes per lane
     static constexpr int kWaves = WO * WS;
     static constexpr int kThreads = 64 * kWaves;
@@ -326,9 +330,14 @@ __device__ __forceinline__ void dma_mfma_frags(v16f (&acc)[C::TM][C::TN],
 #pragma unroll
         for (int b = 0; b < C::TN; ++b) {
             const v8i bv = {(int)f.b[b].x, (int)f.b[b].y, (int)f.b[b].z, (int)f.b[b].w, 0, 0, 0, 0};
-            acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                av, bv, acc[a][b], kFmtE2M1, kFmtE2M1, kSel, (int)wsc[kWord][a], kSel,
-                (int)xsc[kWord][b]);
+            if constexpr (C::SW)
+                acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    bv, av, acc[a][b], kFmtE2M1, kFmtE2M1, kSel, (int)xsc[kWord][b], kSel,
+                    (int)wsc[kWord][a]);
+            else
+                acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    av, bv, acc[a][b], kFmtE2M1, kFmtE2M1, kSel, (int)wsc[kWord][a], kSel,
+                    (int)xsc[kWord][b]);
         }
         // this row's share of the K-step's DMA slots
         __builtin_amdgcn_sched_barrier(0);
@@ -513,11 +522,71 @@ __device__ __forceinline__ void dma_pipeline_step(v16f (&acc)[C::TM][C::TN], uin
 // Store a consumer wave's TM x TN accumulator tiles: lane l of tile (a, b) holds, in its
 // register group g, y[s][o .. o+3] with s = 32b + l%32 and o = 32a + 8g + 4(l/32) relative to
 // the wave's origin.
+// One output through the epilogue (residual add, fp32 or bf16 store).
+__device__ __forceinline__ void epi_store1(const DmaArgs& p, float* __restrict__ y, int64_t s,
+                                           int64_t o, float v)
+{
+    const int64_t idx = s * p.out + o;
+    if (p.res) v += __uint_as_float((uint32_t)p.res[idx] << 16);
+    if (p.out_bf16)
+        reinterpret_cast<uint16_t*>(y)[idx] = (uint16_t)bf16_rne(v);
+    else
+        y[idx] = v;
+}
+
+// Store of the swapped orientation (C::SW): lane l of tile (a, b) holds, in register r,
+// y[s][o] with o = 32a + l%32 and s = 32b + 8(r/4) + 4(l/32) + r%4 relative to the wave's
+// origin; each store instruction writes two tokens' 32 consecutive outputs.
+template <class C>
+__device__ __forceinline__ void store_tile_sw(const v16f (&acc)[C::TM][C::TN], const DmaArgs& p,
+                                              float* __restrict__ y, int64_t o0, int64_t s0,
+                                              int wrow0, int xrow0, int lane, int nt_store)
+{
+    const int lr = lane & 31, lg = lane >> 5;
+    const bool interior = !p.res && !p.out_bf16 && o0 + C::BO <= p.out && s0 + C::BS <= p.S;
+    if (interior) {
+        float* base = y + (s0 + xrow0 + 4 * lg) * p.out + o0 + wrow0 + lr;
+#pragma unroll
+        for (int b = 0; b < C::TN; ++b) {
+#pragma unroll
+            for (int a = 0; a < C::TM; ++a) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float* d = base + (32 * b + 8 * (r >> 2) + (r & 3)) * p.out + 32 * a;
+                    if (nt_store)
+                        __builtin_nontemporal_store(acc[a][b][r], d);
+                    else
+                        *d = acc[a][b][r];
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int a = 0; a < C::TM; ++a) {
+        const int64_t o = o0 + wrow0 + 32 * a + lr;
+        if (o >= p.out) continue;
+#pragma unroll
+        for (int b = 0; b < C::TN; ++b) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t s = s0 + xrow0 + 32 * b + 8 * (r >> 2) + 4 * lg + (r & 3);
+                if (s < p.S) epi_store1(p, y, s, o, acc[a][b][r]);
+            }
+        }
+    }
+}
+
 template <class C>
 __device__ __forceinline__ void store_tile(const v16f (&acc)[C::TM][C::TN], const DmaArgs& p,
                                            float* __restrict__ y, int64_t o0, int64_t s0,
                                            int wrow0, int xrow0, int lane, int nt_store = 0)
 {
+    if constexpr (C::SW) {
+        store_tile_sw<C>(acc, p, y, o0, s0, wrow0, xrow0, lane, nt_store);
+        return;
+    }
     const int lr = lane & 31, lg = lane >> 5;
     if (p.res || p.out_bf16) {
         // epilogue with a residual and/or bf16 output
@@ -760,7 +829,7 @@ gemm_pc_kernel(DmaArgs p, float* __restrict__ y, int64_t tiles_o, int64_t tiles_
 }
 
 using CfgQ = DmaCfg<256, 128, 2, 2, 3, false>;    // 256 tiles for a 2048 x 4096 output
-using CfgQT = DmaCfg<256, 128, 2, 2, 3, true>;
+using CfgQT = DmaCfg<256, 128, 2, 2, 3, true, 4, true>;
 
 // =======================================================================================
 // gemm_generic_kernel: any N % 32 == 0, any alignment of the scale arrays
