@@ -1361,9 +1361,11 @@ __device__ __forceinline__ void w4a8_mfma(v16f (&acc)[w4a8::TM][w4a8::TN], const
         const v8i av = {(int)f.a[a].x, (int)f.a[a].y, (int)f.a[a].z, (int)f.a[a].w, 0, 0, 0, 0};
 #pragma unroll
         for (int b = 0; b < TN; ++b) {
+            // activations (E4M3) as the row operand, weights (E2M1) as the column operand:
+            // the swapped orientation of CfgW4A8 (line-wide epilogue stores)
             acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                av, f.b[b], acc[a][b], kFmtE2M1, kFmtE4M3, kSel, (int)wsc[kWord][a], kSel,
-                (int)xsc[kWord][b]);
+                f.b[b], av, acc[a][b], kFmtE4M3, kFmtE2M1, kSel, (int)xsc[kWord][b], kSel,
+                (int)wsc[kWord][a]);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -1431,7 +1433,7 @@ __device__ __forceinline__ void w4a8_stage(v16f (&acc)[w4a8::TM][w4a8::TN], cons
 }
 
 // Tile config for the shared epilogue (store_tile reads BO, BS, TM, TN only).
-using CfgW4A8 = DmaCfg<256, 128, 2, 2, 2, true>;
+using CfgW4A8 = DmaCfg<256, 128, 2, 2, 2, true, 4, true>;
 
 template <bool TS>
 __global__ void __launch_bounds__(64 * w4a8::kWaves)
