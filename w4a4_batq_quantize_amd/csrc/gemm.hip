@@ -540,7 +540,7 @@ __device__ __forceinline__ void epi_store1(const DmaArgs& p, float* __restrict__
 template <class C>
 __device__ __forceinline__ void store_tile_sw(const v16f (&acc)[C::TM][C::TN], const DmaArgs& p,
                                               float* __restrict__ y, int64_t o0, int64_t s0,
-                                              int wrow0, int xrow0, int lane, int nt_store)
+                                              int wrow0, int xrow0, int lane)
 {
     const int lr = lane & 31, lg = lane >> 5;
     const bool interior = !p.res && !p.out_bf16 && o0 + C::BO <= p.out && s0 + C::BS <= p.S;
@@ -552,11 +552,7 @@ __device__ __forceinline__ void store_tile_sw(const v16f (&acc)[C::TM][C::TN], c
             for (int a = 0; a < C::TM; ++a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    float* d = base + (32 * b + 8 * (r >> 2) + (r & 3)) * p.out + 32 * a;
-                    if (nt_store)
-                        __builtin_nontemporal_store(acc[a][b][r], d);
-                    else
-                        *d = acc[a][b][r];
+                    base[(32 * b + 8 * (r >> 2) + (r & 3)) * p.out + 32 * a] = acc[a][b][r];
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -581,10 +577,10 @@ __device__ __forceinline__ void store_tile_sw(const v16f (&acc)[C::TM][C::TN], c
 template <class C>
 __device__ __forceinline__ void store_tile(const v16f (&acc)[C::TM][C::TN], const DmaArgs& p,
                                            float* __restrict__ y, int64_t o0, int64_t s0,
-                                           int wrow0, int xrow0, int lane, int nt_store = 0)
+                                           int wrow0, int xrow0, int lane)
 {
     if constexpr (C::SW) {
-        store_tile_sw<C>(acc, p, y, o0, s0, wrow0, xrow0, lane, nt_store);
+        store_tile_sw<C>(acc, p, y, o0, s0, wrow0, xrow0, lane);
         return;
     }
     const int lr = lane & 31, lg = lane >> 5;
@@ -612,26 +608,8 @@ __device__ __forceinline__ void store_tile(const v16f (&acc)[C::TM][C::TN], cons
     const bool interior = (p.out & 3) == 0 && o0 + C::BO <= p.out && s0 + C::BS <= p.S;
     if (interior) {
         // whole tile inside the output: unconditional 16-byte stores, one 32x32 tile at a
-        // time (keeps the accumulator-to-VGPR copies short-lived).  Non-temporal stores when
-        // the launch's data outgrows the Infinity Cache, so the output stream does not evict
-        // the operands other tiles still read.
+        // time (keeps the accumulator-to-VGPR copies short-lived)
         float* base = y + (s0 + xrow0 + lr) * p.out + o0 + wrow0 + 4 * lg;
-        if (nt_store) {
-#pragma unroll
-            for (int b = 0; b < C::TN; ++b) {
-#pragma unroll
-                for (int a = 0; a < C::TM; ++a) {
-#pragma unroll
-                    for (int g = 0; g < 4; ++g)
-                        __builtin_nontemporal_store(
-                            v4f{acc[a][b][4 * g], acc[a][b][4 * g + 1], acc[a][b][4 * g + 2],
-                                acc[a][b][4 * g + 3]},
-                            reinterpret_cast<v4f*>(base + 32 * b * p.out + 32 * a + 8 * g));
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-            return;
-        }
 #pragma unroll
         for (int b = 0; b < C::TN; ++b) {
 #pragma unroll
@@ -736,7 +714,7 @@ gemm_dma_kernel(DmaArgs p, float* __restrict__ y, int64_t tiles_o, int64_t tiles
 // drain their LDS reads, lgkmcnt(0), before every barrier).
 template <class C>
 __global__ void __launch_bounds__(2 * C::kThreads)
-gemm_pc_kernel(DmaArgs p, float* __restrict__ y, int64_t tiles_o, int64_t tiles_s, int nt_store)
+gemm_pc_kernel(DmaArgs p, float* __restrict__ y, int64_t tiles_o, int64_t tiles_s)
 {
     constexpr int NB = C::NB;
     __shared__ __attribute__((aligned(16))) uint8_t lds0[C::kBufBytes];
@@ -825,10 +803,10 @@ gemm_pc_kernel(DmaArgs p, float* __restrict__ y, int64_t tiles_o, int64_t tiles_
             if (last == i)
                 pc_stage<C, false>(acc, bufs[i], bufs[i], f0, f1, sc, wrow0, xrow0, lane);
     }
-    store_tile<C>(acc, p, y, o0, s0, wrow0, xrow0, lane, nt_store);
+    store_tile<C>(acc, p, y, o0, s0, wrow0, xrow0, lane);
 }
 
-using CfgQ = DmaCfg<256, 128, 2, 2, 3, false>;    // 256 tiles for a 2048 x 4096 output
+using CfgQ = DmaCfg<256, 128, 2, 2, 3, false, 4, true>;    // 256 tiles for a 2048 x 4096 output
 using CfgQT = DmaCfg<256, 128, 2, 2, 3, true, 4, true>;
 
 // =======================================================================================
@@ -1437,8 +1415,7 @@ using CfgW4A8 = DmaCfg<256, 128, 2, 2, 2, true, 4, true>;
 
 template <bool TS>
 __global__ void __launch_bounds__(64 * w4a8::kWaves)
-gemm_w4a8_kernel(DmaArgs p, float* __restrict__ y, int64_t tiles_o, int64_t tiles_s,
-                 int nt_store)
+gemm_w4a8_kernel(DmaArgs p, float* __restrict__ y, int64_t tiles_o, int64_t tiles_s)
 {
     using namespace w4a8;
     __shared__ __attribute__((aligned(16))) uint8_t lds0[kBufBytes];
@@ -1477,7 +1454,7 @@ gemm_w4a8_kernel(DmaArgs p, float* __restrict__ y, int64_t tiles_o, int64_t tile
         // the trailing prefetch must land before the workgroup's LDS is released
         __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
     }
-    store_tile<CfgW4A8>(acc, p, y, o0, s0, wrow0, xrow0, lane, nt_store);
+    store_tile<CfgW4A8>(acc, p, y, o0, s0, wrow0, xrow0, lane);
 }
 
 }  // namespace
@@ -1518,15 +1495,9 @@ hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq,
         const int64_t tiles_s = (S + CfgQ::BS - 1) / CfgQ::BS;
         if (tiles_o * tiles_s > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
         const dim3 grid((unsigned)(tiles_o * tiles_s));
-        // output stores bypass the Infinity Cache (256 MB) when the operands alone take more
-        // than a quarter of it: they are re-read by later tile rounds and the output stream
-        // would evict them (measured: S=16384, N=12288 -> 4096, 134 MB of operands, 12%
-        // faster; 45-58 MB of operands, as for gate_up or N=4096, are slower that way)
-        constexpr int64_t kOperandBytesForNt = (int64_t)64 << 20;
-        const int nt = (S + out) * (N / 2 + N / 32) > kOperandBytesForNt ? 1 : 0;
         if (tiled_scales)
             hipLaunchKernelGGL(gemm_pc_kernel<CfgQT>, grid, dim3(2 * CfgQT::kThreads), 0,
-                               stream, p, y, tiles_o, tiles_s, nt);
+                               stream, p, y, tiles_o, tiles_s);
         else
             hipLaunchKernelGGL(gemm_dma_kernel<CfgQ>, grid, dim3(CfgQ::kThreads), 0, stream,
                                p, y, tiles_o, tiles_s);
@@ -1575,14 +1546,13 @@ hipError_t launch_gemm_w4a8(const uint8_t* xq8, const uint8_t* xe, const uint8_t
     const int64_t tiles_o = (out + w4a8::BO - 1) / w4a8::BO;
     const int64_t tiles_s = (S + w4a8::BS - 1) / w4a8::BS;
     if (tiles_o * tiles_s > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    const int nt = (S * 2 + out) * (N / 2 + N / 32) > (64LL << 20) ? 1 : 0;
     const dim3 grid((unsigned)(tiles_o * tiles_s)), block(64 * w4a8::kWaves);
     if (tiled_scales)
         hipLaunchKernelGGL(gemm_w4a8_kernel<true>, grid, block, 0, stream, p, y, tiles_o,
-                           tiles_s, nt);
+                           tiles_s);
     else
         hipLaunchKernelGGL(gemm_w4a8_kernel<false>, grid, block, 0, stream, p, y, tiles_o,
-                           tiles_s, nt);
+                           tiles_s);
     return hipGetLastError();
 }
 
