@@ -983,41 +983,60 @@ gemm_generic_kernel(DmaArgs p, int tiled, float* __restrict__ y, int64_t tiles_o
 // With S <= 64 the output is one or two 32-token columns and the work is reading the
 // weights once (0.53 B per weight element) at HBM speed; a 256 x 128 tile grid would leave
 // most of the chip idle.  Here a workgroup owns 32 output rows and all S tokens, and its
-// kSplit waves split the K range: each wave streams its part of the 32 weight rows (and the
-// tokens' codes, L2-resident) straight into registers through buffer loads, one stage
-// (8 blocks) ahead, and multiplies with the 32x32x64 scaled MFMA.  The kSplit partial
-// tiles are then summed through LDS in wave order (a fixed order: results do not depend on
+// kSplit waves split the K range.  Each wave streams its part of the 32 weight rows into a
+// two-slot LDS ring of its own by DMA, whole 128-byte lines per request (8 rows x 128 B per
+// instruction, the 16-byte chunks XOR-swizzled by row pair as in the tiled kernels), so
+// every line is requested once; the tokens' codes and the scales (L2-resident) go straight
+// into registers.  A stage's weight DMA and its token and scale loads are issued together,
+// two stages ahead of use, and a wave reads only its own slots, so its loop has no barrier.
+// It multiplies with the 32x32x64 scaled MFMA.  The kSplit partial tiles are then summed
+// through LDS (reusing the ring) in wave order (a fixed order: results do not depend on
 // timing) and wave (b, g) stores register group g of token column b.
-// waves per workgroup: 16 for one token column (68 VGPRs), 8 for two (registers)
+// waves per workgroup: 16 for one token column, 8 for two (registers)
 template <int TN>
 struct SkinnySplit {
     static constexpr int value = TN == 1 ? 16 : 8;
 };
 
+constexpr int kSkinnySlot = 32 * kRowBytes;                 // 32 weight rows x 128 B
+
 template <int TN, bool F8>
 struct SkinnyStage {
-    v4u w[4];                 // K-steps 0..3: 16 bytes of the lane's weight row
-    v4u x[TN][4][F8 ? 2 : 1]; // and of its token rows (E4M3: 32 bytes, two halves)
+    v4u x[TN][4][F8 ? 2 : 1]; // K-steps 0..3: the lane's token rows (E4M3: 32 bytes, two halves)
     uint2 ws;                 // scale bytes (tiled: .x only; row-major: both words)
     uint2 xs[TN];
 };
 
+// loads per stage issued by skinny_dma + skinny_load, in that order
+template <int TN, bool F8>
+constexpr int kSkinnyGroup = 4 + TN * 4 * (F8 ? 2 : 1) + 1 + TN;
+
+// The 32 weight rows of stage ks into `slot`: instruction q moves rows 8q..8q+7, lane L the
+// global chunk (L%8) ^ ((row/2)%8) of row 8q + L/8 into LDS row 8q + L/8, position L%8.
+__device__ __forceinline__ void skinny_dma(uint8_t* slot, const __amdgpu_buffer_rsrc_t& rw,
+                                           const uint32_t (&woff)[4], int ks)
+{
+#if defined(__HIP_DEVICE_COMPILE__)   // the LDS-load builtins exist for the device only
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t*)(slot + q * 1024), 16,
+                                                 woff[q], ks * kRowBytes, 0, 0);
+#endif
+}
+
 template <int TN, bool TS, bool F8>
 __device__ __forceinline__ void skinny_load(SkinnyStage<TN, F8>& st,
-                                            const __amdgpu_buffer_rsrc_t& rw,
                                             const __amdgpu_buffer_rsrc_t& rx,
                                             const __amdgpu_buffer_rsrc_t& rwe,
-                                            const __amdgpu_buffer_rsrc_t& rxe, uint32_t wrow,
+                                            const __amdgpu_buffer_rsrc_t& rxe,
                                             const uint32_t (&xrow)[TN], uint32_t wse,
                                             const uint32_t (&xse)[TN], int64_t k, int ks,
                                             int lg)
 {
-    const uint32_t rb = 16u * (uint32_t)k;                     // bytes per weight code row
     const uint32_t xrb = (F8 ? 32u : 16u) * (uint32_t)k;       // bytes per token code row
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const uint32_t c = (uint32_t)ks * kRowBytes + 16u * (2 * t + lg);
-        st.w[t] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(wrow * rb + c), 0, 0);
 #pragma unroll
         for (int b = 0; b < TN; ++b) {
             if constexpr (F8) {
@@ -1052,15 +1071,15 @@ __device__ __forceinline__ void skinny_load(SkinnyStage<TN, F8>& st,
 }
 
 template <int TN, bool TS, bool F8, int T>
-__device__ __forceinline__ void skinny_step(v16f (&acc)[TN], const SkinnyStage<TN, F8>& st,
-                                            int lg)
+__device__ __forceinline__ void skinny_step(v16f (&acc)[TN], const uint4& w,
+                                            const SkinnyStage<TN, F8>& st, int lg)
 {
     // tiled: byte T of the one dword; row-major: byte 2(T%2) of word T/2, pre-shifted so the
     // lane's half (block 2T + lane/32) sits in that byte
     constexpr int kSel = TS ? T : 2 * (T & 1);
     constexpr int kFmtX = F8 ? 0 : kFmtE2M1;                   // 0: E4M3
     const uint32_t wsc = TS ? st.ws.x : (((T >> 1) ? st.ws.y : st.ws.x) >> (8 * lg));
-    const v8i av = {(int)st.w[T].x, (int)st.w[T].y, (int)st.w[T].z, (int)st.w[T].w, 0, 0, 0, 0};
+    const v8i av = {(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
 #pragma unroll
     for (int b = 0; b < TN; ++b) {
         const uint32_t xsc = TS ? st.xs[b].x : (((T >> 1) ? st.xs[b].y : st.xs[b].x) >> (8 * lg));
@@ -1075,14 +1094,25 @@ __device__ __forceinline__ void skinny_step(v16f (&acc)[TN], const SkinnyStage<T
     }
 }
 
+// One stage out of an LDS slot: the four weight fragments (lane: row lr, K block 2T + lg)
+// are read first, then the MFMAs; every read has landed when this returns, so the slot may
+// be refilled.
 template <int TN, bool TS, bool F8>
-__device__ __forceinline__ void skinny_stage(v16f (&acc)[TN], const SkinnyStage<TN, F8>& st,
-                                             int lg)
+__device__ __forceinline__ void skinny_stage(v16f (&acc)[TN], const uint8_t* slot,
+                                             const SkinnyStage<TN, F8>& st, int lr, int lg)
 {
-    skinny_step<TN, TS, F8, 0>(acc, st, lg);
-    skinny_step<TN, TS, F8, 1>(acc, st, lg);
-    skinny_step<TN, TS, F8, 2>(acc, st, lg);
-    skinny_step<TN, TS, F8, 3>(acc, st, lg);
+    const uint8_t* row = slot + lr * kRowBytes;
+    const int key = (lr >> 1) & 7;
+    uint4 w[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        w[t] = *reinterpret_cast<const uint4*>(row + 16 * ((2 * t + lg) ^ key));
+    skinny_step<TN, TS, F8, 0>(acc, w[0], st, lg);
+    skinny_step<TN, TS, F8, 1>(acc, w[1], st, lg);
+    skinny_step<TN, TS, F8, 2>(acc, w[2], st, lg);
+    skinny_step<TN, TS, F8, 3>(acc, w[3], st, lg);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // F8: the tokens' codes are E4M3 (one byte per element, the W4A8 setting)
@@ -1092,7 +1122,11 @@ gemm_skinny_kernel(DmaArgs p, float* __restrict__ y)
 {
     constexpr int kSplit = SkinnySplit<TN>::value;
     static_assert(kSplit >= 4 * TN, "one storing wave per (token column, register group)");
-    __shared__ float red[kSplit][TN][16][64];
+    constexpr int kRingBytes = kSplit * 2 * kSkinnySlot;
+    constexpr int kRedBytes = kSplit * TN * 16 * 64 * 4;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kRingBytes > kRedBytes ? kRingBytes
+                                                                                : kRedBytes];
+    constexpr int kGroup = kSkinnyGroup<TN, F8>;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lr = lane & 31, lg = lane >> 5;
@@ -1121,28 +1155,57 @@ gemm_skinny_kernel(DmaArgs p, float* __restrict__ y)
     for (int b = 0; b < TN; ++b)
         xse[b] = TS ? (uint32_t)((xrow[b] >> 5) * k8 * 256 + (xrow[b] & 31) * 8 + 4 * lg)
                     : xrow[b] * (uint32_t)k;
+    // weight DMA offsets (stage 0) of this lane's four instructions
+    uint32_t woff[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int r = 8 * q + (lane >> 3);
+        const int64_t row = o0 + r < p.out ? o0 + r : p.out - 1;
+        woff[q] = (uint32_t)(row * 16 * k + 16 * ((lane & 7) ^ ((r >> 1) & 7)));
+    }
+    uint8_t* slot0 = smem + wave * 2 * kSkinnySlot;
+    uint8_t* slot1 = slot0 + kSkinnySlot;
 
     v16f acc[TN];
 #pragma unroll
     for (int b = 0; b < TN; ++b) acc[b] = v16f{};
     if (s0 < s1) {
-        SkinnyStage<TN, F8> cur, nxt;
-        skinny_load<TN, TS, F8>(cur, rw, rx, rwe, rxe, wrow, xrow, wse, xse, k, s0, lg);
-        int s = s0;
-        for (;;) {
-            const bool more = s + 1 < s1;
-            skinny_load<TN, TS, F8>(nxt, rw, rx, rwe, rxe, wrow, xrow, wse, xse, k,
-                                more ? s + 1 : s, lg);
-            skinny_stage<TN, TS, F8>(acc, cur, lg);
-            if (!more) break;
-            const bool more2 = s + 2 < s1;
-            skinny_load<TN, TS, F8>(cur, rw, rx, rwe, rxe, wrow, xrow, wse, xse, k,
-                                more2 ? s + 2 : s + 1, lg);
-            skinny_stage<TN, TS, F8>(acc, nxt, lg);
-            if (!more2) break;
-            s += 2;
+        // stage s0 + 2i in (slot0, st0), s0 + 2i + 1 in (slot1, st1); a stage's group is
+        // issued two stages ahead, so at most one other group is in flight at each wait
+        SkinnyStage<TN, F8> st0, st1;
+        skinny_dma(slot0, rw, woff, s0);
+        skinny_load<TN, TS, F8>(st0, rx, rwe, rxe, xrow, wse, xse, k, s0, lg);
+        if (s0 + 1 < s1) {
+            skinny_dma(slot1, rw, woff, s0 + 1);
+            skinny_load<TN, TS, F8>(st1, rx, rwe, rxe, xrow, wse, xse, k, s0 + 1, lg);
+        }
+        for (int s = s0;; s += 2) {
+            if (s + 1 < s1)
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm(kGroup, 15));
+            else
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+            skinny_stage<TN, TS, F8>(acc, slot0, st0, lr, lg);
+            if (s + 1 >= s1) break;
+            if (s + 2 < s1) {
+                skinny_dma(slot0, rw, woff, s + 2);
+                skinny_load<TN, TS, F8>(st0, rx, rwe, rxe, xrow, wse, xse, k, s + 2, lg);
+            }
+            if (s + 2 < s1)
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm(kGroup, 15));
+            else
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+            skinny_stage<TN, TS, F8>(acc, slot1, st1, lr, lg);
+            if (s + 2 >= s1) break;
+            if (s + 3 < s1) {
+                skinny_dma(slot1, rw, woff, s + 3);
+                skinny_load<TN, TS, F8>(st1, rx, rwe, rxe, xrow, wse, xse, k, s + 3, lg);
+            }
         }
     }
+    // every wave's DMA has landed (its last wait was vmcnt(0)); the ring becomes the
+    // reduction buffer once all waves are past their last read
+    __syncthreads();
+    float (*red)[TN][16][64] = reinterpret_cast<float (*)[TN][16][64]>(smem);
     // sum the kSplit partial tiles in wave order
 #pragma unroll
     for (int b = 0; b < TN; ++b)
@@ -1177,6 +1240,7 @@ gemm_skinny_kernel(DmaArgs p, float* __restrict__ y)
         }
     }
 }
+
 
 // =======================================================================================
 // gemm_w4a8_kernel<TS>: MXFP8 (E4M3) activations x MXFP4 weights, the W4A8 setting
