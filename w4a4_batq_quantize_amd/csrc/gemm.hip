@@ -992,24 +992,28 @@ gemm_generic_kernel(DmaArgs p, int tiled, float* __restrict__ y, int64_t tiles_o
 // It multiplies with the 32x32x64 scaled MFMA.  The kSplit partial tiles are then summed
 // through LDS (reusing the ring) in wave order (a fixed order: results do not depend on
 // timing) and wave (b, g) stores register group g of token column b.
-// waves per workgroup: 16 for one token column, 8 for two (registers)
-template <int TN>
+// Waves per workgroup.  XL: the token rows come through the LDS ring as well (two E2M1 token
+// columns: 64 rows of token codes per stage, twice the weight rows, would otherwise be
+// loaded as MFMA fragments, each line requested four times); the ring's size then allows
+// six waves.
+template <int TN, bool XL>
 struct SkinnySplit {
-    static constexpr int value = TN == 1 ? 16 : 8;
+    static constexpr int value = XL ? 6 : TN == 1 ? 16 : 8;
 };
 
 constexpr int kSkinnySlot = 32 * kRowBytes;                 // 32 weight rows x 128 B
 
-template <int TN, bool F8>
+template <int TN, bool F8, bool XL = false>
 struct SkinnyStage {
-    v4u x[TN][4][F8 ? 2 : 1]; // K-steps 0..3: the lane's token rows (E4M3: 32 bytes, two halves)
-    uint2 ws;                 // scale bytes (tiled: .x only; row-major: both words)
+    v4u x[XL ? 1 : TN][4][F8 ? 2 : 1]; // K-steps 0..3: the lane's token rows (E4M3: 32 bytes,
+                                       // two halves); unused with XL
+    uint2 ws;                          // scale bytes (tiled: .x only; row-major: both words)
     uint2 xs[TN];
 };
 
-// loads per stage issued by skinny_dma + skinny_load, in that order
-template <int TN, bool F8>
-constexpr int kSkinnyGroup = 4 + TN * 4 * (F8 ? 2 : 1) + 1 + TN;
+// loads per stage issued by skinny_dma (+ skinny_dma_x) + skinny_load, in that order
+template <int TN, bool F8, bool XL>
+constexpr int kSkinnyGroup = 4 + (XL ? 4 * TN : TN * 4 * (F8 ? 2 : 1)) + 1 + TN;
 
 // The 32 weight rows of stage ks into `slot`: instruction q moves rows 8q..8q+7, lane L the
 // global chunk (L%8) ^ ((row/2)%8) of row 8q + L/8 into LDS row 8q + L/8, position L%8.
@@ -1024,8 +1028,24 @@ __device__ __forceinline__ void skinny_dma(uint8_t* slot, const __amdgpu_buffer_
 #endif
 }
 
-template <int TN, bool TS, bool F8>
-__device__ __forceinline__ void skinny_load(SkinnyStage<TN, F8>& st,
+// The token rows of stage ks for XL (E2M1): column b's 32 rows into slot + b * 4096 with
+// the weight rows' layout and swizzle.
+template <int TN>
+__device__ __forceinline__ void skinny_dma_x(uint8_t* slot, const __amdgpu_buffer_rsrc_t& rx,
+                                             const uint32_t (&xoff)[TN][4], int ks)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+    for (int b = 0; b < TN; ++b)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(slot + b * 4096 + q * 1024),
+                                                     16, xoff[b][q], ks * kRowBytes, 0, 0);
+#endif
+}
+
+template <int TN, bool TS, bool F8, bool XL = false>
+__device__ __forceinline__ void skinny_load(SkinnyStage<TN, F8, XL>& st,
                                             const __amdgpu_buffer_rsrc_t& rx,
                                             const __amdgpu_buffer_rsrc_t& rwe,
                                             const __amdgpu_buffer_rsrc_t& rxe,
@@ -1038,7 +1058,7 @@ __device__ __forceinline__ void skinny_load(SkinnyStage<TN, F8>& st,
     for (int t = 0; t < 4; ++t) {
         const uint32_t c = (uint32_t)ks * kRowBytes + 16u * (2 * t + lg);
 #pragma unroll
-        for (int b = 0; b < TN; ++b) {
+        for (int b = 0; b < (XL ? 0 : TN); ++b) {
             if constexpr (F8) {
                 // E4M3 lane half h: chunks 4t + h and 4t + 2 + h of the 256-byte stage row
                 const uint32_t c8 = (uint32_t)ks * 2 * kRowBytes + 16u * (4 * t + lg);
@@ -1070,9 +1090,10 @@ __device__ __forceinline__ void skinny_load(SkinnyStage<TN, F8>& st,
     }
 }
 
-template <int TN, bool TS, bool F8, int T>
+template <int TN, bool TS, bool F8, bool XL, int T>
 __device__ __forceinline__ void skinny_step(v16f (&acc)[TN], const uint4& w,
-                                            const SkinnyStage<TN, F8>& st, int lg)
+                                            const uint4 (&xl)[TN],
+                                            const SkinnyStage<TN, F8, XL>& st, int lg)
 {
     // tiled: byte T of the one dword; row-major: byte 2(T%2) of word T/2, pre-shifted so the
     // lane's half (block 2T + lane/32) sits in that byte
@@ -1083,9 +1104,13 @@ __device__ __forceinline__ void skinny_step(v16f (&acc)[TN], const uint4& w,
 #pragma unroll
     for (int b = 0; b < TN; ++b) {
         const uint32_t xsc = TS ? st.xs[b].x : (((T >> 1) ? st.xs[b].y : st.xs[b].x) >> (8 * lg));
-        const v4u u = st.x[b][T][0];
+        v4u u;
+        if constexpr (XL)
+            u = v4u{xl[b].x, xl[b].y, xl[b].z, xl[b].w};
+        else
+            u = st.x[b][T][0];
         v8i bv = {(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
-        if constexpr (F8) {
+        if constexpr (F8 && !XL) {
             const v4u v = st.x[b][T][F8 ? 1 : 0];
             bv = v8i{(int)u.x, (int)u.y, (int)u.z, (int)u.w, (int)v.x, (int)v.y, (int)v.z, (int)v.w};
         }
@@ -1097,36 +1122,44 @@ __device__ __forceinline__ void skinny_step(v16f (&acc)[TN], const uint4& w,
 // One stage out of an LDS slot: the four weight fragments (lane: row lr, K block 2T + lg)
 // are read first, then the MFMAs; every read has landed when this returns, so the slot may
 // be refilled.
-template <int TN, bool TS, bool F8>
+template <int TN, bool TS, bool F8, bool XL>
 __device__ __forceinline__ void skinny_stage(v16f (&acc)[TN], const uint8_t* slot,
-                                             const SkinnyStage<TN, F8>& st, int lr, int lg)
+                                             const SkinnyStage<TN, F8, XL>& st, int lr, int lg)
 {
     const uint8_t* row = slot + lr * kRowBytes;
     const int key = (lr >> 1) & 7;
-    uint4 w[4];
+    uint4 w[4], x[4][TN];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 4; ++t) {
         w[t] = *reinterpret_cast<const uint4*>(row + 16 * ((2 * t + lg) ^ key));
-    skinny_step<TN, TS, F8, 0>(acc, w[0], st, lg);
-    skinny_step<TN, TS, F8, 1>(acc, w[1], st, lg);
-    skinny_step<TN, TS, F8, 2>(acc, w[2], st, lg);
-    skinny_step<TN, TS, F8, 3>(acc, w[3], st, lg);
+        if constexpr (XL) {
+#pragma unroll
+            for (int b = 0; b < TN; ++b)
+                x[t][b] = *reinterpret_cast<const uint4*>(row + kSkinnySlot + b * 4096 +
+                                                          16 * ((2 * t + lg) ^ key));
+        }
+    }
+    skinny_step<TN, TS, F8, XL, 0>(acc, w[0], x[0], st, lg);
+    skinny_step<TN, TS, F8, XL, 1>(acc, w[1], x[1], st, lg);
+    skinny_step<TN, TS, F8, XL, 2>(acc, w[2], x[2], st, lg);
+    skinny_step<TN, TS, F8, XL, 3>(acc, w[3], x[3], st, lg);
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
     __builtin_amdgcn_sched_barrier(0);
 }
 
 // F8: the tokens' codes are E4M3 (one byte per element, the W4A8 setting)
 template <int TN, bool TS, bool F8 = false>
-__global__ void __launch_bounds__(64 * SkinnySplit<TN>::value)
+__global__ void __launch_bounds__((64 * SkinnySplit<TN, TN == 2 && !F8>::value))
 gemm_skinny_kernel(DmaArgs p, float* __restrict__ y)
 {
-    constexpr int kSplit = SkinnySplit<TN>::value;
-    static_assert(kSplit >= 4 * TN, "one storing wave per (token column, register group)");
-    constexpr int kRingBytes = kSplit * 2 * kSkinnySlot;
+    constexpr bool XL = TN == 2 && !F8;
+    constexpr int kSplit = SkinnySplit<TN, XL>::value;
+    constexpr int kSlotBytes = kSkinnySlot * (XL ? 1 + TN : 1);   // weights (+ token rows)
+    constexpr int kRingBytes = kSplit * 2 * kSlotBytes;
     constexpr int kRedBytes = kSplit * TN * 16 * 64 * 4;
     __shared__ __attribute__((aligned(16))) uint8_t smem[kRingBytes > kRedBytes ? kRingBytes
                                                                                 : kRedBytes];
-    constexpr int kGroup = kSkinnyGroup<TN, F8>;
+    constexpr int kGroup = kSkinnyGroup<TN, F8, XL>;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lr = lane & 31, lg = lane >> 5;
@@ -1163,8 +1196,23 @@ gemm_skinny_kernel(DmaArgs p, float* __restrict__ y)
         const int64_t row = o0 + r < p.out ? o0 + r : p.out - 1;
         woff[q] = (uint32_t)(row * 16 * k + 16 * ((lane & 7) ^ ((r >> 1) & 7)));
     }
-    uint8_t* slot0 = smem + wave * 2 * kSkinnySlot;
-    uint8_t* slot1 = slot0 + kSkinnySlot;
+    // token-row DMA offsets (XL): column b, instruction q, as the weights'
+    uint32_t xoff[TN][4];
+#pragma unroll
+    for (int b = 0; b < TN; ++b)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = 8 * q + (lane >> 3);
+            const int64_t row = 32 * b + r < p.S ? 32 * b + r : p.S - 1;
+            xoff[b][q] = (uint32_t)(row * 16 * k + 16 * ((lane & 7) ^ ((r >> 1) & 7)));
+        }
+    uint8_t* slot0 = smem + wave * 2 * kSlotBytes;
+    uint8_t* slot1 = slot0 + kSlotBytes;
+    auto issue = [&](uint8_t* slot, SkinnyStage<TN, F8, XL>& st, int ks) {
+        skinny_dma(slot, rw, woff, ks);
+        if constexpr (XL) skinny_dma_x<TN>(slot + kSkinnySlot, rx, xoff, ks);
+        skinny_load<TN, TS, F8, XL>(st, rx, rwe, rxe, xrow, wse, xse, k, ks, lg);
+    };
 
     v16f acc[TN];
 #pragma unroll
@@ -1172,34 +1220,24 @@ gemm_skinny_kernel(DmaArgs p, float* __restrict__ y)
     if (s0 < s1) {
         // stage s0 + 2i in (slot0, st0), s0 + 2i + 1 in (slot1, st1); a stage's group is
         // issued two stages ahead, so at most one other group is in flight at each wait
-        SkinnyStage<TN, F8> st0, st1;
-        skinny_dma(slot0, rw, woff, s0);
-        skinny_load<TN, TS, F8>(st0, rx, rwe, rxe, xrow, wse, xse, k, s0, lg);
-        if (s0 + 1 < s1) {
-            skinny_dma(slot1, rw, woff, s0 + 1);
-            skinny_load<TN, TS, F8>(st1, rx, rwe, rxe, xrow, wse, xse, k, s0 + 1, lg);
-        }
+        SkinnyStage<TN, F8, XL> st0, st1;
+        issue(slot0, st0, s0);
+        if (s0 + 1 < s1) issue(slot1, st1, s0 + 1);
         for (int s = s0;; s += 2) {
             if (s + 1 < s1)
                 __builtin_amdgcn_s_waitcnt(waitcnt_imm(kGroup, 15));
             else
                 __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
-            skinny_stage<TN, TS, F8>(acc, slot0, st0, lr, lg);
+            skinny_stage<TN, TS, F8, XL>(acc, slot0, st0, lr, lg);
             if (s + 1 >= s1) break;
-            if (s + 2 < s1) {
-                skinny_dma(slot0, rw, woff, s + 2);
-                skinny_load<TN, TS, F8>(st0, rx, rwe, rxe, xrow, wse, xse, k, s + 2, lg);
-            }
+            if (s + 2 < s1) issue(slot0, st0, s + 2);
             if (s + 2 < s1)
                 __builtin_amdgcn_s_waitcnt(waitcnt_imm(kGroup, 15));
             else
                 __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
-            skinny_stage<TN, TS, F8>(acc, slot1, st1, lr, lg);
+            skinny_stage<TN, TS, F8, XL>(acc, slot1, st1, lr, lg);
             if (s + 2 >= s1) break;
-            if (s + 3 < s1) {
-                skinny_dma(slot1, rw, woff, s + 3);
-                skinny_load<TN, TS, F8>(st1, rx, rwe, rxe, xrow, wse, xse, k, s + 3, lg);
-            }
+            if (s + 3 < s1) issue(slot1, st1, s + 3);
         }
     }
     // every wave's DMA has landed (its last wait was vmcnt(0)); the ring becomes the
@@ -1212,8 +1250,9 @@ gemm_skinny_kernel(DmaArgs p, float* __restrict__ y)
 #pragma unroll
         for (int r = 0; r < 16; ++r) red[wave][b][r][lane] = acc[b][r];
     __syncthreads();
-    if (wave < 4 * TN) {
-        const int b = wave / 4, g = wave % 4;
+    // (token column b, register group g) pairs, kSplit waves taking them in turn
+    for (int bg = wave; bg < 4 * TN; bg += kSplit) {
+        const int b = bg / 4, g = bg % 4;
         float v[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -1540,13 +1579,13 @@ hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq,
         if (tiles_o > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
         const dim3 grid((unsigned)tiles_o);
         if (S <= 32) {
-            const dim3 block(64 * SkinnySplit<1>::value);
+            const dim3 block(64 * SkinnySplit<1, false>::value);
             if (tiled_scales)
                 hipLaunchKernelGGL((gemm_skinny_kernel<1, true>), grid, block, 0, stream, p, y);
             else
                 hipLaunchKernelGGL((gemm_skinny_kernel<1, false>), grid, block, 0, stream, p, y);
         } else {
-            const dim3 block(64 * SkinnySplit<2>::value);
+            const dim3 block(64 * SkinnySplit<2, true>::value);    // E2M1 tokens via LDS
             if (tiled_scales)
                 hipLaunchKernelGGL((gemm_skinny_kernel<2, true>), grid, block, 0, stream, p, y);
             else
@@ -1593,13 +1632,13 @@ hipError_t launch_gemm_w4a8(const uint8_t* xq8, const uint8_t* xe, const uint8_t
         if (tiles_w > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
         const dim3 grid((unsigned)tiles_w);
         if (S <= 32) {
-            const dim3 block(64 * SkinnySplit<1>::value);
+            const dim3 block(64 * SkinnySplit<1, false>::value);
             if (tiled_scales)
                 hipLaunchKernelGGL((gemm_skinny_kernel<1, true, true>), grid, block, 0, stream, p, y);
             else
                 hipLaunchKernelGGL((gemm_skinny_kernel<1, false, true>), grid, block, 0, stream, p, y);
         } else {
-            const dim3 block(64 * SkinnySplit<2>::value);
+            const dim3 block(64 * SkinnySplit<2, false>::value);
             if (tiled_scales)
                 hipLaunchKernelGGL((gemm_skinny_kernel<2, true, true>), grid, block, 0, stream, p, y);
             else
