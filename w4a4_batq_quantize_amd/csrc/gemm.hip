@@ -992,16 +992,25 @@ gemm_generic_kernel(DmaArgs p, int tiled, float* __restrict__ y, int64_t tiles_o
 // It multiplies with the 32x32x64 scaled MFMA.  The kSplit partial tiles are then summed
 // through LDS (reusing the ring) in wave order (a fixed order: results do not depend on
 // timing) and wave (b, g) stores register group g of token column b.
-// Waves per workgroup.  XL: the token rows come through the LDS ring as well (two E2M1 token
-// columns: 64 rows of token codes per stage, twice the weight rows, would otherwise be
-// loaded as MFMA fragments, each line requested four times); the ring's size then allows
-// six waves.
-template <int TN, bool XL>
-struct SkinnySplit {
-    static constexpr int value = XL ? 6 : TN == 1 ? 16 : 8;
+constexpr int kSkinnySlotW = 32 * kRowBytes;                // 32 weight rows x 128 B
+
+// Configuration per token-column count and token format.  XL: the token rows come through
+// the LDS ring as well (loaded as MFMA fragments each line is requested four times, and
+// with many distinct token rows their bytes outweigh the weights'); the waves are then as
+// many as the ring's slots allow in LDS.
+template <int TN, bool F8>
+struct SkinnyCfg {
+    // measured: through LDS for two token columns and for E4M3 tokens; one E2M1 column
+    // (at most 32 distinct, mostly repeated rows) is 1-2% faster as direct fragment loads
+    static constexpr bool XL = TN == 2 || F8;
+    static constexpr int kXBytes = 32 * kRowBytes * (F8 ? 2 : 1);      // token rows / column
+    static constexpr int kSlot = kSkinnySlotW + (XL ? TN * kXBytes : 0);
+    static constexpr int kFit = (160 * 1024) / (2 * kSlot);
+    static constexpr int kMaxWaves = TN == 1 ? 16 : 8;
+    static constexpr int waves = !XL ? kMaxWaves : (kFit < kMaxWaves ? kFit : kMaxWaves);
+    static_assert(waves >= 2 && 2 * kSlot * waves <= 160 * 1024, "ring in LDS");
 };
 
-constexpr int kSkinnySlot = 32 * kRowBytes;                 // 32 weight rows x 128 B
 
 template <int TN, bool F8, bool XL = false>
 struct SkinnyStage {
@@ -1013,7 +1022,7 @@ struct SkinnyStage {
 
 // loads per stage issued by skinny_dma (+ skinny_dma_x) + skinny_load, in that order
 template <int TN, bool F8, bool XL>
-constexpr int kSkinnyGroup = 4 + (XL ? 4 * TN : TN * 4 * (F8 ? 2 : 1)) + 1 + TN;
+constexpr int kSkinnyGroup = 4 + TN * 4 * (F8 ? 2 : 1) + 1 + TN;
 
 // The 32 weight rows of stage ks into `slot`: instruction q moves rows 8q..8q+7, lane L the
 // global chunk (L%8) ^ ((row/2)%8) of row 8q + L/8 into LDS row 8q + L/8, position L%8.
@@ -1028,19 +1037,22 @@ __device__ __forceinline__ void skinny_dma(uint8_t* slot, const __amdgpu_buffer_
 #endif
 }
 
-// The token rows of stage ks for XL (E2M1): column b's 32 rows into slot + b * 4096 with
-// the weight rows' layout and swizzle.
-template <int TN>
+// The token rows of stage ks for XL: column b's 32 rows into slot + b * kXBytes.  E2M1:
+// 128-byte rows, as the weights (8 rows per instruction, chunk key (row/2)%8); E4M3:
+// 256-byte rows, 4 rows per instruction, the 16 chunks keyed by row%16.
+template <int TN, bool F8>
 __device__ __forceinline__ void skinny_dma_x(uint8_t* slot, const __amdgpu_buffer_rsrc_t& rx,
-                                             const uint32_t (&xoff)[TN][4], int ks)
+                                             const uint32_t (&xoff)[TN][F8 ? 8 : 4], int ks)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
+    constexpr int kXBytes = 32 * kRowBytes * (F8 ? 2 : 1);
 #pragma unroll
     for (int b = 0; b < TN; ++b)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(slot + b * 4096 + q * 1024),
-                                                     16, xoff[b][q], ks * kRowBytes, 0, 0);
+        for (int q = 0; q < (F8 ? 8 : 4); ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rx, (lds_void_t*)(slot + b * kXBytes + q * 1024), 16, xoff[b][q],
+                ks * kRowBytes * (F8 ? 2 : 1), 0, 0);
 #endif
 }
 
@@ -1092,7 +1104,7 @@ __device__ __forceinline__ void skinny_load(SkinnyStage<TN, F8, XL>& st,
 
 template <int TN, bool TS, bool F8, bool XL, int T>
 __device__ __forceinline__ void skinny_step(v16f (&acc)[TN], const uint4& w,
-                                            const uint4 (&xl)[TN],
+                                            const uint4 (&xl)[TN][F8 ? 2 : 1],
                                             const SkinnyStage<TN, F8, XL>& st, int lg)
 {
     // tiled: byte T of the one dword; row-major: byte 2(T%2) of word T/2, pre-shifted so the
@@ -1106,12 +1118,13 @@ __device__ __forceinline__ void skinny_step(v16f (&acc)[TN], const uint4& w,
         const uint32_t xsc = TS ? st.xs[b].x : (((T >> 1) ? st.xs[b].y : st.xs[b].x) >> (8 * lg));
         v4u u;
         if constexpr (XL)
-            u = v4u{xl[b].x, xl[b].y, xl[b].z, xl[b].w};
+            u = v4u{xl[b][0].x, xl[b][0].y, xl[b][0].z, xl[b][0].w};
         else
             u = st.x[b][T][0];
         v8i bv = {(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
-        if constexpr (F8 && !XL) {
-            const v4u v = st.x[b][T][F8 ? 1 : 0];
+        if constexpr (F8) {
+            const uint4 h = xl[b][F8 ? 1 : 0];
+            const v4u v = XL ? v4u{h.x, h.y, h.z, h.w} : st.x[b][T][F8 ? 1 : 0];
             bv = v8i{(int)u.x, (int)u.y, (int)u.z, (int)u.w, (int)v.x, (int)v.y, (int)v.z, (int)v.w};
         }
         acc[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
@@ -1128,15 +1141,26 @@ __device__ __forceinline__ void skinny_stage(v16f (&acc)[TN], const uint8_t* slo
 {
     const uint8_t* row = slot + lr * kRowBytes;
     const int key = (lr >> 1) & 7;
-    uint4 w[4], x[4][TN];
+    constexpr int kXBytes = 32 * kRowBytes * (F8 ? 2 : 1);
+    uint4 w[4], x[4][TN][F8 ? 2 : 1];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         w[t] = *reinterpret_cast<const uint4*>(row + 16 * ((2 * t + lg) ^ key));
         if constexpr (XL) {
 #pragma unroll
-            for (int b = 0; b < TN; ++b)
-                x[t][b] = *reinterpret_cast<const uint4*>(row + kSkinnySlot + b * 4096 +
-                                                          16 * ((2 * t + lg) ^ key));
+            for (int b = 0; b < TN; ++b) {
+                const uint8_t* xr = slot + kSkinnySlotW + b * kXBytes;
+                if constexpr (F8) {
+                    // E4M3 lane half h: chunks 4t + h and 4t + 2 + h of the 256-byte row
+                    const uint8_t* r8 = xr + lr * 2 * kRowBytes;
+                    x[t][b][0] = *reinterpret_cast<const uint4*>(r8 + 16 * ((4 * t + lg) ^ (lr & 15)));
+                    x[t][b][F8 ? 1 : 0] =
+                        *reinterpret_cast<const uint4*>(r8 + 16 * ((4 * t + 2 + lg) ^ (lr & 15)));
+                } else {
+                    x[t][b][0] = *reinterpret_cast<const uint4*>(xr + lr * kRowBytes +
+                                                                 16 * ((2 * t + lg) ^ key));
+                }
+            }
         }
     }
     skinny_step<TN, TS, F8, XL, 0>(acc, w[0], x[0], st, lg);
@@ -1149,12 +1173,12 @@ __device__ __forceinline__ void skinny_stage(v16f (&acc)[TN], const uint8_t* slo
 
 // F8: the tokens' codes are E4M3 (one byte per element, the W4A8 setting)
 template <int TN, bool TS, bool F8 = false>
-__global__ void __launch_bounds__((64 * SkinnySplit<TN, TN == 2 && !F8>::value))
+__global__ void __launch_bounds__((64 * SkinnyCfg<TN, F8>::waves))
 gemm_skinny_kernel(DmaArgs p, float* __restrict__ y)
 {
-    constexpr bool XL = TN == 2 && !F8;
-    constexpr int kSplit = SkinnySplit<TN, XL>::value;
-    constexpr int kSlotBytes = kSkinnySlot * (XL ? 1 + TN : 1);   // weights (+ token rows)
+    constexpr bool XL = SkinnyCfg<TN, F8>::XL;
+    constexpr int kSplit = SkinnyCfg<TN, F8>::waves;
+    constexpr int kSlotBytes = SkinnyCfg<TN, F8>::kSlot;          // weights (+ token rows)
     constexpr int kRingBytes = kSplit * 2 * kSlotBytes;
     constexpr int kRedBytes = kSplit * TN * 16 * 64 * 4;
     __shared__ __attribute__((aligned(16))) uint8_t smem[kRingBytes > kRedBytes ? kRingBytes
@@ -1196,21 +1220,22 @@ gemm_skinny_kernel(DmaArgs p, float* __restrict__ y)
         const int64_t row = o0 + r < p.out ? o0 + r : p.out - 1;
         woff[q] = (uint32_t)(row * 16 * k + 16 * ((lane & 7) ^ ((r >> 1) & 7)));
     }
-    // token-row DMA offsets (XL): column b, instruction q, as the weights'
-    uint32_t xoff[TN][4];
+    // token-row DMA offsets (XL): column b, instruction q
+    uint32_t xoff[TN][F8 ? 8 : 4];
 #pragma unroll
     for (int b = 0; b < TN; ++b)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int r = 8 * q + (lane >> 3);
+        for (int q = 0; q < (F8 ? 8 : 4); ++q) {
+            const int r = F8 ? 4 * q + (lane >> 4) : 8 * q + (lane >> 3);
             const int64_t row = 32 * b + r < p.S ? 32 * b + r : p.S - 1;
-            xoff[b][q] = (uint32_t)(row * 16 * k + 16 * ((lane & 7) ^ ((r >> 1) & 7)));
+            xoff[b][q] = F8 ? (uint32_t)(row * 32 * k + 16 * ((lane & 15) ^ (r & 15)))
+                            : (uint32_t)(row * 16 * k + 16 * ((lane & 7) ^ ((r >> 1) & 7)));
         }
     uint8_t* slot0 = smem + wave * 2 * kSlotBytes;
     uint8_t* slot1 = slot0 + kSlotBytes;
     auto issue = [&](uint8_t* slot, SkinnyStage<TN, F8, XL>& st, int ks) {
         skinny_dma(slot, rw, woff, ks);
-        if constexpr (XL) skinny_dma_x<TN>(slot + kSkinnySlot, rx, xoff, ks);
+        if constexpr (XL) skinny_dma_x<TN, F8>(slot + kSkinnySlotW, rx, xoff, ks);
         skinny_load<TN, TS, F8, XL>(st, rx, rwe, rxe, xrow, wse, xse, k, ks, lg);
     };
 
@@ -1579,13 +1604,13 @@ hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq,
         if (tiles_o > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
         const dim3 grid((unsigned)tiles_o);
         if (S <= 32) {
-            const dim3 block(64 * SkinnySplit<1, false>::value);
+            const dim3 block(64 * SkinnyCfg<1, false>::waves);
             if (tiled_scales)
                 hipLaunchKernelGGL((gemm_skinny_kernel<1, true>), grid, block, 0, stream, p, y);
             else
                 hipLaunchKernelGGL((gemm_skinny_kernel<1, false>), grid, block, 0, stream, p, y);
         } else {
-            const dim3 block(64 * SkinnySplit<2, true>::value);    // E2M1 tokens via LDS
+            const dim3 block(64 * SkinnyCfg<2, false>::waves);
             if (tiled_scales)
                 hipLaunchKernelGGL((gemm_skinny_kernel<2, true>), grid, block, 0, stream, p, y);
             else
@@ -1632,13 +1657,13 @@ hipError_t launch_gemm_w4a8(const uint8_t* xq8, const uint8_t* xe, const uint8_t
         if (tiles_w > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
         const dim3 grid((unsigned)tiles_w);
         if (S <= 32) {
-            const dim3 block(64 * SkinnySplit<1, false>::value);
+            const dim3 block(64 * SkinnyCfg<1, true>::waves);
             if (tiled_scales)
                 hipLaunchKernelGGL((gemm_skinny_kernel<1, true, true>), grid, block, 0, stream, p, y);
             else
                 hipLaunchKernelGGL((gemm_skinny_kernel<1, false, true>), grid, block, 0, stream, p, y);
         } else {
-            const dim3 block(64 * SkinnySplit<2, false>::value);
+            const dim3 block(64 * SkinnyCfg<2, true>::waves);
             if (tiled_scales)
                 hipLaunchKernelGGL((gemm_skinny_kernel<2, true, true>), grid, block, 0, stream, p, y);
             else
