@@ -20,8 +20,9 @@ hipError_t launch_quantize(bool act, const void* x, int64_t rows, int64_t k, int
                            const float* r_max, uint8_t* q, uint8_t* e, bool tiled_scales,
                            hipStream_t stream, bool fp8 = false, int form = 0);
 
-// RMSNorm (gamma fp32 [32k], eps) fused in front of the GPK activation quantiser; one wave
-// per row, k <= 512 (hipErrorNotSupported otherwise).
+// RMSNorm (gamma fp32 [32k], eps) fused in front of the GPK activation quantiser; 64, 128
+// or 256 threads per row (the padded block count, clamped), one or two blocks per thread,
+// k <= 512 (hipErrorNotSupported otherwise).
 hipError_t launch_rmsnorm_quantize(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx,
                                    const float* gamma, float eps, const float* A,
                                    const float* B, const float* r_min, const float* r_max,
