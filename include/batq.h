@@ -329,6 +329,32 @@ batq_status batq_dequantize_rows(const uint8_t* q, const uint8_t* e, int64_t src
                                  batq_kv_format fmt, const int64_t* index, int64_t rows,
                                  void* y, batq_out_type y_type, void* stream);
 
+/* Token count up to which batq_linear_w4a4 runs in one kernel. */
+#define BATQ_LINEAR_FUSED_TOKENS 4
+
+/*
+ * The online linear layer in one call: y = the W4A4 product of batq_quantize_act(x) with
+ * the prepared weights (gist.science summary, sections 2D and 4: activations transformed
+ * and clipped online, MXFP4 x MXFP4 product).  For 1 <= S <= BATQ_LINEAR_FUSED_TOKENS (and
+ * N/32 <= 512, N/32 % 8 == 0) one kernel does it: the few-token GEMM encodes the token rows
+ * itself, with the quantiser's arithmetic, so the codes are exactly batq_quantize_act's and
+ * y agrees with the two-call path within the GEMM's accumulation bound (its K split, and so
+ * its fp32 summation order, differs); xq / xe are then not used and may be NULL.  Otherwise
+ * the two calls run, with xq / xe as the caller's workspace for the activation codes and
+ * scales (sized as batq_quantize_act's q and e in `layout`).
+ *   x, S, N, ldx, A, B, r_min, r_max: as batq_quantize_act
+ *   wq, we, layout, out, y: as batq_gemm_w4a4 (y dev fp32 [S, out], 16-byte aligned)
+ *   xq, xe: dev workspace or NULL (see above; BATQ_ERR_NULL when needed and missing,
+ *           BATQ_ERR_UNSUPPORTED when the one-kernel path declines aligned-scale or size
+ *           limits and no workspace is given)
+ * Does not allocate or synchronise.
+ */
+batq_status batq_linear_w4a4(const uint16_t* x, int64_t S, int64_t N, int64_t ldx,
+                             const float* A, const float* B, const float* r_min,
+                             const float* r_max, const uint8_t* wq, const uint8_t* we,
+                             batq_scale_layout layout, int64_t out, float* y, uint8_t* xq,
+                             uint8_t* xe, void* stream);
+
 /*
  * Host: clip ratios r[i] = fp32(1 / (1 + exp(-alpha[i]))) evaluated in binary64 and rounded
  * once (daily-arxiv summary, clipping bullet: the sigmoid keeps each ratio in (0, 1);

@@ -1,7 +1,7 @@
 """The online calls captured into a HIP graph (as bench.py times them) and replayed: every
 replay, with eager work and synchronisations between replays, gives bit for bit the eager
 result (quantiser codes and scales, W4A4 and W4A8 GEMM outputs, KV cache rows, transformed
-rows)."""
+rows, the one-kernel linear layer)."""
 import numpy as np
 import pytest
 
@@ -44,6 +44,7 @@ def test_graph_replays_match_eager(bq):
     sq = torch.empty((3, N // 2), dtype=torch.uint8, device="cuda")
     se = torch.empty((bq.scale_bytes(3, N, T),), dtype=torch.uint8, device="cuda")
     ys = torch.empty((3, out), dtype=torch.float32, device="cuda")
+    yl = torch.empty_like(ys)
     cq = torch.zeros((300, N // 2), dtype=torch.uint8, device="cuda")
     ce = torch.zeros((300, N // 32), dtype=torch.uint8, device="cuda")
     tr = torch.empty((S, N), dtype=torch.bfloat16, device="cuda")
@@ -55,10 +56,11 @@ def test_graph_replays_match_eager(bq):
         bq.gemm_w4a8(xq8, xe8, wq, we, y=y8, layout=T)
         bq.quantize_act(xs, A, B, r1, r2, q=sq, e=se, layout=T)       # few-token GEMM
         bq.gemm_w4a4(sq, se, wq, we, y=ys, layout=T)
+        bq.linear_w4a4(xs, A, B, r1, r2, wq, we, layout=T, y=yl)     # one-kernel linear
         bq.quantize_kv(x, slots, bq.KV_MXFP4, A, B, r1, r2, cq, ce)
         bq.transform_rows(x, A, B, out_dtype=torch.bfloat16, y=tr)
 
-    outs = (xq, xe, y4, xq8, xe8, y8, sq, se, ys, cq, ce, tr)
+    outs = (xq, xe, y4, xq8, xe8, y8, sq, se, ys, yl, cq, ce, tr)
     # every output starts from zeros, here and before each replay: the bytes no call writes
     # (the tiled scale buffers' padding rows) then compare equal too
     for t in outs:
@@ -85,7 +87,7 @@ def test_graph_replays_match_eager(bq):
         g.replay()
         torch.cuda.synchronize()
         for name, got, want in zip(("xq", "xe", "y4", "xq8", "xe8", "y8", "sq", "se", "ys",
-                                    "cq", "ce", "tr"), outs, eager):
+                                    "yl", "cq", "ce", "tr"), outs, eager):
             assert torch.equal(got.view(torch.uint8) if got.dtype == torch.bfloat16 else got,
                                want.view(torch.uint8) if want.dtype == torch.bfloat16 else want), \
                 f"replay {rep}: {name}"

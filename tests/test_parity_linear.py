@@ -1,0 +1,98 @@
+"""GPU parity of batq_linear_w4a4, the linear layer in one call: for 1..4 tokens one kernel
+(the few-token GEMM encoding the token rows itself), otherwise quantiser + GEMM through the
+caller's workspace; both against the oracle's quantisation, weight preparation and fp64
+product within the GEMM's accumulation bound (1e-5 * sum|terms|)."""
+import numpy as np
+import pytest
+
+import workloads as wl
+from tests.gpu_util import (ORACLE_THREADS, assert_gemm_close, bf16_to_device, f32_to_device,
+                            to_host)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def bq():
+    import torch
+    import w4a4_batq_quantize_amd as bq
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    bq.lib()
+    return bq
+
+
+def run_linear(bq, L, layout, ldx=None):
+    import torch
+    S, N = L.x_bits.shape
+    wq, we = bq.prepare_weight(f32_to_device(L.W), L.A, L.B, layout=layout)
+    if ldx is not None and ldx != N:
+        wide = np.zeros((S, ldx), dtype=np.uint16)
+        wide[:, :N] = L.x_bits
+        wide[:, N:] = 0x7FC0                       # NaN padding: must never be read
+        x = bf16_to_device(wide)[:, :N]
+    else:
+        x = bf16_to_device(L.x_bits)
+    y = bq.linear_w4a4(x, f32_to_device(L.A), f32_to_device(L.B),
+                       f32_to_device(bq.clip_ratios(L.alpha_min)),
+                       f32_to_device(bq.clip_ratios(L.alpha_max)), wq, we, layout=layout)
+    torch.cuda.synchronize()
+    return to_host(y)
+
+
+def oracle_linear(orc, L):
+    rmin, rmax = orc.clip_ratio(L.alpha_min), orc.clip_ratio(L.alpha_max)
+    xq, xe = orc.quantize_act(L.x_bits, L.A, L.B, rmin, rmax, nthreads=ORACLE_THREADS)
+    wq, we = orc.prepare_weight(L.W, L.A, L.B, nthreads=ORACLE_THREADS)
+    return orc.gemm(xq, xe, wq, we, nthreads=ORACLE_THREADS)
+
+
+@pytest.mark.parametrize("tiled", [True, False])
+@pytest.mark.parametrize("S,N,out,ldx", [
+    (1, 256, 33, None),         # one stage, ragged out
+    (1, 12288, 4096, None),     # decode shape
+    (2, 4096, 300, 4104),       # strided rows
+    (3, 16384, 130, None),      # k = 512, the largest row of the one-kernel path
+    (4, 2048, 4096, None),
+    (4, 8192, 64, 8200),
+])
+def test_linear_one_kernel(bq, orc, S, N, out, ldx, tiled):
+    L = wl.make_layer(wl.custom("lin", S, N, out, seed=(101, S, N, out),
+                                outliers=("channels_uniform", 8, 20.0, 100.0)))
+    layout = bq.SCALES_MFMA_TILED if tiled else bq.SCALES_ROW_MAJOR
+    print(f"[linear one-kernel] S={S} N={N} out={out} tiled={tiled}", flush=True)
+    y = run_linear(bq, L, layout, ldx=ldx)
+    y_ref, t_ref = oracle_linear(orc, L)
+    assert_gemm_close(y, y_ref, t_ref, what=f"S={S} N={N} out={out} tiled={tiled}")
+
+
+@pytest.mark.parametrize("S,N,out", [
+    (5, 4096, 96),              # more tokens than the one-kernel path takes
+    (2, 16640, 64),             # k = 520 > 512
+    (3, 96, 40),                # k = 3: not a multiple of 8
+])
+def test_linear_two_steps(bq, orc, S, N, out):
+    L = wl.make_layer(wl.custom("lin2", S, N, out, seed=(102, S, N, out)))
+    y = run_linear(bq, L, bq.SCALES_MFMA_TILED)
+    y_ref, t_ref = oracle_linear(orc, L)
+    assert_gemm_close(y, y_ref, t_ref, what=f"two steps S={S} N={N} out={out}")
+
+
+def test_linear_one_kernel_matches_two_calls(bq):
+    """Same codes as batq_quantize_act (the quantiser's own arithmetic): the one-kernel output
+    and the two-call output differ only by the GEMM's fp32 summation order."""
+    import torch
+    L = wl.make_layer(wl.custom("lin3", 4, 4096, 512, seed=103))
+    T = bq.SCALES_MFMA_TILED
+    wq, we = bq.prepare_weight(f32_to_device(L.W), L.A, L.B, layout=T)
+    args = (bf16_to_device(L.x_bits), f32_to_device(L.A), f32_to_device(L.B),
+            f32_to_device(bq.clip_ratios(L.alpha_min)), f32_to_device(bq.clip_ratios(L.alpha_max)))
+    y1 = bq.linear_w4a4(*args, wq, we, layout=T)
+    xq, xe = bq.quantize_act(*args, layout=T)
+    y2 = bq.gemm_w4a4(xq, xe, wq, we, layout=T)
+    torch.cuda.synchronize()
+    a, b = to_host(y1).astype(np.float64), to_host(y2).astype(np.float64)
+    assert np.max(np.abs(a - b) / (np.abs(b) + 1e-3)) < 1e-4
+    # deterministic
+    y3 = bq.linear_w4a4(*args, wq, we, layout=T)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y3)

@@ -22,6 +22,7 @@
 #include <stdint.h>
 
 #include "internal.h"
+#include "mx_block.h"
 
 namespace batq {
 namespace {
@@ -1585,6 +1586,213 @@ gemm_w4a8_kernel(DmaArgs p, float* __restrict__ y, int64_t tiles_o, int64_t tile
     store_tile<CfgW4A8>(acc, p, y, o0, s0, wrow0, xrow0, lane);
 }
 
+// =======================================================================================
+// gemm_linear_skinny_kernel<TS>: the whole linear layer for at most four tokens
+// =======================================================================================
+//
+// With S <= 4 the activation quantiser is a launch of its own for a few hundred blocks; here
+// the few-token GEMM encodes the tokens itself.  Each workgroup (kLinWaves waves splitting
+// K, as gemm_skinny_kernel) first puts its waves' first two weight stages in flight, then
+// its lanes transform, clip and encode every block of the S token rows (mx::encode_block,
+// the quantiser's own arithmetic, so the codes are bit for bit batq_quantize_act's) into
+// a shared LDS buffer, and after a barrier streams the weights as gemm_skinny_kernel does,
+// taking the token fragments and scales from that buffer.  Every workgroup encodes the
+// same rows (S k blocks, at most three per lane): that costs VALU time the first weight
+// stages' latency mostly hides, and saves the quantiser's launch and the codes' round trip.
+constexpr int kLinTokens = 4, kLinWaves = 12, kLinMaxK = 512;
+
+template <bool TS>
+__global__ void __launch_bounds__(64 * kLinWaves)
+gemm_linear_skinny_kernel(DmaArgs p, const uint16_t* __restrict__ x, int64_t ldx,
+                          const float* __restrict__ A, const float* __restrict__ B,
+                          const float* __restrict__ r_min, const float* __restrict__ r_max,
+                          float* __restrict__ y)
+{
+    constexpr int kRingBytes = kLinWaves * 2 * kSkinnySlotW;
+    constexpr int kRowStride = kLinMaxK * 16 + 16;                // token code row in LDS
+    constexpr int kCodeBytes = kLinTokens * kRowStride;
+    constexpr int kRedBytes = kLinWaves * 16 * 64 * 4;
+    static_assert(kRedBytes <= kRingBytes, "reduction reuses the ring");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kRingBytes + kCodeBytes +
+                                                         kLinTokens * kLinMaxK];
+    uint8_t* xcode = smem + kRingBytes;
+    uint8_t* xscale = xcode + kCodeBytes;
+    constexpr int kGroup = 4 + 1;                                 // weight DMA + scale load
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lr = lane & 31, lg = lane >> 5;
+    const int64_t o0 = (int64_t)blockIdx.x * 32;
+    const int64_t k = p.k, S = p.S;
+    const int nst = (int)(k / kStageBlocks);
+    const int s0 = (int)((int64_t)wave * nst / kLinWaves);
+    const int s1 = (int)((int64_t)(wave + 1) * nst / kLinWaves);
+
+    const uint32_t wrow = (uint32_t)(o0 + lr < p.out ? o0 + lr : p.out - 1);
+    const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(p.wq, p.out * 16 * k);
+    const int64_t k8 = k / 8;
+    const __amdgpu_buffer_rsrc_t rwe =
+        buffer_rsrc(p.we, TS ? ((p.out + 31) / 32) * 256 * k8 : p.out * k);
+    const uint32_t wse = TS ? (uint32_t)((wrow >> 5) * k8 * 256 + (wrow & 31) * 8 + 4 * lg)
+                            : wrow * (uint32_t)k;
+    uint32_t woff[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int r = 8 * q + (lane >> 3);
+        const int64_t row = o0 + r < p.out ? o0 + r : p.out - 1;
+        woff[q] = (uint32_t)(row * 16 * k + 16 * ((lane & 7) ^ ((r >> 1) & 7)));
+    }
+    uint8_t* slot0 = smem + wave * 2 * kSkinnySlotW;
+    uint8_t* slot1 = slot0 + kSkinnySlotW;
+    // a stage's group: the weight DMA, then the lane's weight-scale load
+    auto issue = [&](uint8_t* slot, uint2& ws, int ks) {
+        skinny_dma(slot, rw, woff, ks);
+        if constexpr (TS) {
+            ws.x = __builtin_amdgcn_raw_buffer_load_b32(rwe, (int)(wse + (uint32_t)ks * 256u), 0, 0);
+        } else {
+            const v2u v = __builtin_amdgcn_raw_buffer_load_b64(
+                rwe, (int)(wse + (uint32_t)ks * kStageBlocks), 0, 0);
+            ws = make_uint2(v.x, v.y);
+        }
+    };
+    uint2 ws0 = make_uint2(0, 0), ws1 = make_uint2(0, 0);
+    if (s0 < s1) issue(slot0, ws0, s0);
+    if (s0 + 1 < s1) issue(slot1, ws1, s0 + 1);
+
+    // encode the S token rows into LDS: block q = t k + b, lanes of the workgroup in turn;
+    // every load of a lane's blocks is issued before the first is encoded
+    {
+        const int tid = threadIdx.x;
+        const int64_t nblk = S * k;
+        constexpr int kPer = (kLinTokens * kLinMaxK + 64 * kLinWaves - 1) / (64 * kLinWaves);
+        uint4 xv[kPer][4];
+        mx::BlockParams bp[kPer];
+#pragma unroll
+        for (int m = 0; m < kPer; ++m) {
+            const int64_t q = tid + (int64_t)m * 64 * kLinWaves;
+            if (q < nblk) {
+                const int64_t t = q / k, b = q - t * k;
+                bp[m] = mx::load_block_params<true, 0>(B, r_min, r_max, b);
+                const uint4* xp = reinterpret_cast<const uint4*>(x + t * ldx + 32 * b);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xv[m][i] = xp[i];
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < kPer; ++m) {
+            const int64_t q = tid + (int64_t)m * 64 * kLinWaves;
+            if (q < nblk) {
+                const int64_t t = q / k, b = q - t * k;
+                float xf[32];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t w4[4] = {xv[m][i].x, xv[m][i].y, xv[m][i].z, xv[m][i].w};
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        xf[8 * i + 2 * d] = mx::bf16_lo(w4[d]);
+                        xf[8 * i + 2 * d + 1] = mx::bf16_hi(w4[d]);
+                    }
+                }
+                const mx::BlockCode<false> c = mx::encode_block<true, false, 0>(xf, A, bp[m], b);
+                *reinterpret_cast<uint4*>(xcode + t * kRowStride + 16 * b) =
+                    make_uint4(c.w[0], c.w[1], c.w[2], c.w[3]);
+                // the group's 8 bytes in the MFMA-tiled order (block b at (b%2)*4 + (b%8)/2)
+                xscale[t * k + 8 * (b >> 3) + ((b & 1) << 2) + ((b & 7) >> 1)] = (uint8_t)c.ebyte;
+            }
+        }
+    }
+    __syncthreads();
+
+    const int xr = lr < S ? lr : (int)S - 1;                      // token row of this lane
+    const uint8_t* xrow = xcode + xr * kRowStride;
+    const uint8_t* xsrow = xscale + xr * k + 4 * lg;
+    v16f acc = v16f{};
+    auto stage = [&](const uint8_t* slot, const uint2& ws, int ks) {
+        const uint8_t* row = slot + lr * kRowBytes;
+        const int key = (lr >> 1) & 7;
+        uint4 w[4], xv[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            w[t] = *reinterpret_cast<const uint4*>(row + 16 * ((2 * t + lg) ^ key));
+            xv[t] = *reinterpret_cast<const uint4*>(xrow + 16 * (8 * ks + 2 * t + lg));
+        }
+        const uint32_t xsc = *reinterpret_cast<const uint32_t*>(xsrow + 8 * ks);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            // weight scale byte: tiled, byte t of the one dword; row-major, byte 2(t%2) of
+            // word t/2 pre-shifted by the lane's half; token scales: byte t (tiled order)
+            const uint32_t wsc = TS ? ws.x : (((t >> 1) ? ws.y : ws.x) >> (8 * lg));
+            const v8i av = {(int)w[t].x, (int)w[t].y, (int)w[t].z, (int)w[t].w, 0, 0, 0, 0};
+            const v8i bv = {(int)xv[t].x, (int)xv[t].y, (int)xv[t].z, (int)xv[t].w, 0, 0, 0, 0};
+            switch (t) {   // the byte selects are immediates
+            case 0:
+                acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    av, bv, acc, kFmtE2M1, kFmtE2M1, 0, (int)wsc, 0, (int)xsc);
+                break;
+            case 1:
+                acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    av, bv, acc, kFmtE2M1, kFmtE2M1, TS ? 1 : 2, (int)wsc, 1, (int)xsc);
+                break;
+            case 2:
+                acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    av, bv, acc, kFmtE2M1, kFmtE2M1, TS ? 2 : 0, (int)wsc, 2, (int)xsc);
+                break;
+            default:
+                acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    av, bv, acc, kFmtE2M1, kFmtE2M1, TS ? 3 : 2, (int)wsc, 3, (int)xsc);
+                break;
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    if (s0 < s1) {
+        for (int s = s0;; s += 2) {
+            if (s + 1 < s1)
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm(kGroup, 15));
+            else
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+            stage(slot0, ws0, s);
+            if (s + 1 >= s1) break;
+            if (s + 2 < s1) issue(slot0, ws0, s + 2);
+            if (s + 2 < s1)
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm(kGroup, 15));
+            else
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+            stage(slot1, ws1, s + 1);
+            if (s + 2 >= s1) break;
+            if (s + 3 < s1) issue(slot1, ws1, s + 3);
+        }
+    }
+    // the partial tiles summed through LDS (the ring, reused) in wave order
+    __syncthreads();
+    float (*red)[16][64] = reinterpret_cast<float (*)[16][64]>(smem);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[wave][r][lane] = acc[r];
+    __syncthreads();
+    if (wave < 4) {
+        const int g = wave;
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float t = red[0][4 * g + i][lane];
+#pragma unroll
+            for (int w = 1; w < kLinWaves; ++w) t += red[w][4 * g + i][lane];
+            v[i] = t;
+        }
+        const int64_t o = o0 + 8 * g + 4 * lg;
+        if (lr < S) {
+            float* dst = y + lr * p.out + o;
+            if ((p.out & 3) == 0 && o + 3 < p.out) {
+                *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (o + i < p.out) dst[i] = v[i];
+            }
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq,
@@ -1681,6 +1889,33 @@ hipError_t launch_gemm_w4a8(const uint8_t* xq8, const uint8_t* xe, const uint8_t
     else
         hipLaunchKernelGGL(gemm_w4a8_kernel<false>, grid, block, 0, stream, p, y, tiles_o,
                            tiles_s);
+    return hipGetLastError();
+}
+
+}  // namespace batq
+
+namespace batq {
+
+hipError_t launch_linear_skinny(const uint16_t* x, int64_t S, int64_t k, int64_t ldx,
+                                const float* A, const float* B, const float* r_min,
+                                const float* r_max, const uint8_t* wq, const uint8_t* we,
+                                bool tiled_scales, int64_t out, float* y, hipStream_t stream)
+{
+    if (S < 1 || S > kLinTokens || k < 1 || k > kLinMaxK || k % kStageBlocks != 0)
+        return hipErrorNotSupported;
+    const uintptr_t salign = tiled_scales ? 256 : 8;
+    if ((reinterpret_cast<uintptr_t>(we) % salign) != 0 || out * 16 * k >= (1LL << 32))
+        return hipErrorNotSupported;
+    const DmaArgs p{nullptr, nullptr, wq, we, S, k, out, nullptr, 0};
+    const int64_t tiles_o = (out + 31) / 32;
+    if (tiles_o > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)tiles_o), block(64 * kLinWaves);
+    if (tiled_scales)
+        hipLaunchKernelGGL(gemm_linear_skinny_kernel<true>, grid, block, 0, stream, p, x, ldx, A,
+                           B, r_min, r_max, y);
+    else
+        hipLaunchKernelGGL(gemm_linear_skinny_kernel<false>, grid, block, 0, stream, p, x, ldx,
+                           A, B, r_min, r_max, y);
     return hipGetLastError();
 }
 

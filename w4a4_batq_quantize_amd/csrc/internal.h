@@ -49,6 +49,14 @@ hipError_t launch_dequantize_rows(const uint8_t* q, const uint8_t* e, int64_t ro
                                   bool fp8, const int64_t* index, int64_t src_rows, void* y,
                                   bool y_bf16, hipStream_t stream);
 
+// The linear layer for 1 <= S <= 4 tokens in one kernel: the few-token GEMM encodes the
+// bf16 token rows itself (bit for bit launch_quantize's codes); k <= 512, k % 8 == 0;
+// hipErrorNotSupported outside that.
+hipError_t launch_linear_skinny(const uint16_t* x, int64_t S, int64_t k, int64_t ldx,
+                                const float* A, const float* B, const float* r_min,
+                                const float* r_max, const uint8_t* wq, const uint8_t* we,
+                                bool tiled_scales, int64_t out, float* y, hipStream_t stream);
+
 // MXFP4 x MXFP4 -> fp32 GEMM, y[S, out] = dq(x)[S, N] dq(w)[out, N]^T; both scale
 // arrays in the same layout (tiled_scales: MFMA-tiled, else row-major).
 // Epilogue (both GEMMs): res, when not null, is a bf16 [S, out] residual added in fp32;
