@@ -1042,17 +1042,17 @@ __device__ __forceinline__ void skinny_dma(uint8_t* slot, const __amdgpu_buffer_
 // 128-byte rows, as the weights (8 rows per instruction, chunk key (row/2)%8); E4M3:
 // 256-byte rows, 4 rows per instruction, the 16 chunks keyed by row%16.
 template <int TN, bool F8>
-__device__ __forceinline__ void skinny_dma_x(uint8_t* slot, const __amdgpu_buffer_rsrc_t& rx,
+__device__ __forceinline__ void skinny_dma_x(uint8_t* const (&xs)[TN],
+                                             const __amdgpu_buffer_rsrc_t& rx,
                                              const uint32_t (&xoff)[TN][F8 ? 8 : 4], int ks)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
-    constexpr int kXBytes = 32 * kRowBytes * (F8 ? 2 : 1);
 #pragma unroll
     for (int b = 0; b < TN; ++b)
 #pragma unroll
         for (int q = 0; q < (F8 ? 8 : 4); ++q)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rx, (lds_void_t*)(slot + b * kXBytes + q * 1024), 16, xoff[b][q],
+                rx, (lds_void_t*)(xs[b] + q * 1024), 16, xoff[b][q],
                 ks * kRowBytes * (F8 ? 2 : 1), 0, 0);
 #endif
 }
@@ -1138,11 +1138,11 @@ __device__ __forceinline__ void skinny_step(v16f (&acc)[TN], const uint4& w,
 // be refilled.
 template <int TN, bool TS, bool F8, bool XL>
 __device__ __forceinline__ void skinny_stage(v16f (&acc)[TN], const uint8_t* slot,
+                                             uint8_t* const (&xs)[TN],
                                              const SkinnyStage<TN, F8, XL>& st, int lr, int lg)
 {
     const uint8_t* row = slot + lr * kRowBytes;
     const int key = (lr >> 1) & 7;
-    constexpr int kXBytes = 32 * kRowBytes * (F8 ? 2 : 1);
     uint4 w[4], x[4][TN][F8 ? 2 : 1];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -1150,7 +1150,7 @@ __device__ __forceinline__ void skinny_stage(v16f (&acc)[TN], const uint8_t* slo
         if constexpr (XL) {
 #pragma unroll
             for (int b = 0; b < TN; ++b) {
-                const uint8_t* xr = slot + kSkinnySlotW + b * kXBytes;
+                const uint8_t* xr = xs[b];
                 if constexpr (F8) {
                     // E4M3 lane half h: chunks 4t + h and 4t + 2 + h of the 256-byte row
                     const uint8_t* r8 = xr + lr * 2 * kRowBytes;
@@ -1172,6 +1172,52 @@ __device__ __forceinline__ void skinny_stage(v16f (&acc)[TN], const uint8_t* slo
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// A wave's two-slot ring over its stages s0..s1-1: stage s0 + 2i in slot 0, s0 + 2i + 1 in
+// slot 1, each stage's group of loads issued two stages ahead.  The steady-state loop
+// refills both slots unconditionally and the last two or three stages are peeled, so that
+// every wait point sees the same loads in flight on every path into it: the compiler's own
+// waits (for the registers a group loads, and for the LDS its DMA writes, tracked per LDS
+// array) then match the explicit ones, where a conditional refill inside the loop made
+// them wait for everything in flight.  kPrimed: the caller has issued stages s0 and s0 + 1
+// (the second one a refetch into slot 1 when the wave has a single stage).
+template <int kGroup, bool kPrimed, class I0, class I1, class C0, class C1>
+__device__ __forceinline__ void ring_pipeline(int s0, int s1, I0&& issue0, I1&& issue1,
+                                              C0&& compute0, C1&& compute1)
+{
+    const int n = s1 - s0;
+    if (n <= 0) return;
+    if constexpr (!kPrimed) issue0(s0);
+    if (n == 1) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+        compute0(s0);
+        return;
+    }
+    if constexpr (!kPrimed) issue1(s0 + 1);
+    int s = s0;
+    for (; s + 3 < s1; s += 2) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(kGroup, 15));
+        compute0(s);
+        issue0(s + 2);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(kGroup, 15));
+        compute1(s + 1);
+        issue1(s + 3);
+    }
+    if (s + 2 < s1) {                     // three stages left
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(kGroup, 15));
+        compute0(s);
+        issue0(s + 2);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(kGroup, 15));
+        compute1(s + 1);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+        compute0(s + 2);
+    } else {                              // two stages left
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(kGroup, 15));
+        compute0(s);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+        compute1(s + 1);
+    }
+}
+
 // F8: the tokens' codes are E4M3 (one byte per element, the W4A8 setting)
 template <int TN, bool TS, bool F8 = false>
 __global__ void __launch_bounds__((64 * SkinnyCfg<TN, F8>::waves))
@@ -1179,11 +1225,20 @@ gemm_skinny_kernel(DmaArgs p, float* __restrict__ y)
 {
     constexpr bool XL = SkinnyCfg<TN, F8>::XL;
     constexpr int kSplit = SkinnyCfg<TN, F8>::waves;
-    constexpr int kSlotBytes = SkinnyCfg<TN, F8>::kSlot;          // weights (+ token rows)
-    constexpr int kRingBytes = kSplit * 2 * kSlotBytes;
-    constexpr int kRedBytes = kSplit * TN * 16 * 64 * 4;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kRingBytes > kRedBytes ? kRingBytes
-                                                                                : kRedBytes];
+    constexpr int kXBytes = SkinnyCfg<TN, F8>::kXBytes;             // token rows / column
+    constexpr int kRingBytes = kSplit * kSkinnySlotW;              // weight rows, one slot
+    constexpr int kXRing = XL ? kSplit * kXBytes : 16;             // token rows, one slot
+    static_assert(kSplit * 16 * 64 * 4 <= kRingBytes, "a column's reduction in one array");
+    static_assert(2 * (kRingBytes + TN * kXRing) <= 160 * 1024 || !XL, "ring in LDS");
+    // every region the DMA writes in an array of its own (weight rows of slot 0 and 1, token
+    // column b of slot 0 and 1): the compiler keeps one representative DMA per array and
+    // orders a read after the DMA into the same array, so a slot's reads do not wait for
+    // the other slot's refill
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kRingBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t ring1[kRingBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t x00[kXRing], x10[kXRing];
+    __shared__ __attribute__((aligned(16))) uint8_t x01[TN > 1 ? kXRing : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t x11[TN > 1 ? kXRing : 16];
     constexpr int kGroup = kSkinnyGroup<TN, F8, XL>;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -1232,59 +1287,59 @@ gemm_skinny_kernel(DmaArgs p, float* __restrict__ y)
             xoff[b][q] = F8 ? (uint32_t)(row * 32 * k + 16 * ((lane & 15) ^ (r & 15)))
                             : (uint32_t)(row * 16 * k + 16 * ((lane & 7) ^ ((r >> 1) & 7)));
         }
-    uint8_t* slot0 = smem + wave * 2 * kSlotBytes;
-    uint8_t* slot1 = slot0 + kSlotBytes;
-    auto issue = [&](uint8_t* slot, SkinnyStage<TN, F8, XL>& st, int ks) {
+    uint8_t* slot0 = smem + wave * kSkinnySlotW;
+    uint8_t* slot1 = ring1 + wave * kSkinnySlotW;
+    const int xw = XL ? wave * kXBytes : 0;
+    uint8_t* xs0[TN];
+    uint8_t* xs1[TN];
+    xs0[0] = x00 + xw;
+    xs1[0] = x10 + xw;
+    if constexpr (TN > 1) {
+        xs0[TN - 1] = x01 + xw;
+        xs1[TN - 1] = x11 + xw;
+    }
+    auto issue = [&](uint8_t* slot, uint8_t* const (&xs)[TN], SkinnyStage<TN, F8, XL>& st,
+                     int ks) {
         skinny_dma(slot, rw, woff, ks);
-        if constexpr (XL) skinny_dma_x<TN, F8>(slot + kSkinnySlotW, rx, xoff, ks);
+        if constexpr (XL) skinny_dma_x<TN, F8>(xs, rx, xoff, ks);
         skinny_load<TN, TS, F8, XL>(st, rx, rwe, rxe, xrow, wse, xse, k, ks, lg);
     };
 
     v16f acc[TN];
 #pragma unroll
     for (int b = 0; b < TN; ++b) acc[b] = v16f{};
-    if (s0 < s1) {
+    {
         // stage s0 + 2i in (slot0, st0), s0 + 2i + 1 in (slot1, st1); a stage's group is
         // issued two stages ahead, so at most one other group is in flight at each wait
         SkinnyStage<TN, F8, XL> st0, st1;
-        issue(slot0, st0, s0);
-        if (s0 + 1 < s1) issue(slot1, st1, s0 + 1);
-        for (int s = s0;; s += 2) {
-            if (s + 1 < s1)
-                __builtin_amdgcn_s_waitcnt(waitcnt_imm(kGroup, 15));
-            else
-                __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
-            skinny_stage<TN, TS, F8, XL>(acc, slot0, st0, lr, lg);
-            if (s + 1 >= s1) break;
-            if (s + 2 < s1) issue(slot0, st0, s + 2);
-            if (s + 2 < s1)
-                __builtin_amdgcn_s_waitcnt(waitcnt_imm(kGroup, 15));
-            else
-                __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
-            skinny_stage<TN, TS, F8, XL>(acc, slot1, st1, lr, lg);
-            if (s + 2 >= s1) break;
-            if (s + 3 < s1) issue(slot1, st1, s + 3);
-        }
+        ring_pipeline<kGroup, false>(
+            s0, s1, [&](int ks) { issue(slot0, xs0, st0, ks); },
+            [&](int ks) { issue(slot1, xs1, st1, ks); },
+            [&](int) { skinny_stage<TN, TS, F8, XL>(acc, slot0, xs0, st0, lr, lg); },
+            [&](int) { skinny_stage<TN, TS, F8, XL>(acc, slot1, xs1, st1, lr, lg); });
     }
-    // every wave's DMA has landed (its last wait was vmcnt(0)); the ring becomes the
-    // reduction buffer once all waves are past their last read
+    // every wave's DMA has landed (its last wait was vmcnt(0)); the weight arrays become the
+    // reduction buffers (token column b in slot b's) once all waves are past their last read
     __syncthreads();
-    float (*red)[TN][16][64] = reinterpret_cast<float (*)[TN][16][64]>(smem);
+    auto red = [&](int b) {
+        return reinterpret_cast<float (*)[16][64]>(b == 0 ? smem : ring1);
+    };
     // sum the kSplit partial tiles in wave order
 #pragma unroll
     for (int b = 0; b < TN; ++b)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) red[wave][b][r][lane] = acc[b][r];
+        for (int r = 0; r < 16; ++r) red(b)[wave][r][lane] = acc[b][r];
     __syncthreads();
     // (token column b, register group g) pairs, kSplit waves taking them in turn
     for (int bg = wave; bg < 4 * TN; bg += kSplit) {
         const int b = bg / 4, g = bg % 4;
+        float (*rb)[16][64] = red(b);
         float v[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float t = red[0][b][4 * g + i][lane];
+            float t = rb[0][4 * g + i][lane];
 #pragma unroll
-            for (int w = 1; w < kSplit; ++w) t += red[w][b][4 * g + i][lane];
+            for (int w = 1; w < kSplit; ++w) t += rb[w][4 * g + i][lane];
             v[i] = t;
         }
         const int64_t srow = 32 * b + lr;
@@ -1608,15 +1663,18 @@ gemm_linear_skinny_kernel(DmaArgs p, const uint16_t* __restrict__ x, int64_t ldx
                           const float* __restrict__ r_min, const float* __restrict__ r_max,
                           float* __restrict__ y)
 {
-    constexpr int kRingBytes = kLinWaves * 2 * kSkinnySlotW;
+    constexpr int kRingBytes = kLinWaves * kSkinnySlotW;           // one slot of each wave
     constexpr int kRowStride = kLinMaxK * 16 + 16;                // token code row in LDS
     constexpr int kCodeBytes = kLinTokens * kRowStride;
     constexpr int kRedBytes = kLinWaves * 16 * 64 * 4;
-    static_assert(kRedBytes <= kRingBytes, "reduction reuses the ring");
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kRingBytes + kCodeBytes +
-                                                         kLinTokens * kLinMaxK];
-    uint8_t* xcode = smem + kRingBytes;
-    uint8_t* xscale = xcode + kCodeBytes;
+    static_assert(kRedBytes <= kRingBytes, "reduction reuses the first slots");
+    // four arrays: the compiler orders an LDS access only after the DMA into the same array,
+    // so with each slot and the token buffers in arrays of their own, the encoder's stores
+    // and a slot's reads wait for that slot's DMA, not for the other slot's in flight
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kRingBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t ring1[kRingBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t xcode[kCodeBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t xscale[kLinTokens * kLinMaxK];
     constexpr int kGroup = 4 + 1;                                 // weight DMA + scale load
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -1641,8 +1699,8 @@ gemm_linear_skinny_kernel(DmaArgs p, const uint16_t* __restrict__ x, int64_t ldx
         const int64_t row = o0 + r < p.out ? o0 + r : p.out - 1;
         woff[q] = (uint32_t)(row * 16 * k + 16 * ((lane & 7) ^ ((r >> 1) & 7)));
     }
-    uint8_t* slot0 = smem + wave * 2 * kSkinnySlotW;
-    uint8_t* slot1 = slot0 + kSkinnySlotW;
+    uint8_t* slot0 = smem + wave * kSkinnySlotW;
+    uint8_t* slot1 = ring1 + wave * kSkinnySlotW;
     // a stage's group: the weight DMA, then the lane's weight-scale load
     auto issue = [&](uint8_t* slot, uint2& ws, int ks) {
         skinny_dma(slot, rw, woff, ks);
@@ -1655,33 +1713,38 @@ gemm_linear_skinny_kernel(DmaArgs p, const uint16_t* __restrict__ x, int64_t ldx
         }
     };
     uint2 ws0 = make_uint2(0, 0), ws1 = make_uint2(0, 0);
-    if (s0 < s1) issue(slot0, ws0, s0);
-    if (s0 + 1 < s1) issue(slot1, ws1, s0 + 1);
 
-    // encode the S token rows into LDS: block q = t k + b, lanes of the workgroup in turn;
-    // every load of a lane's blocks is issued before the first is encoded
+    // encode the S token rows into LDS: block q = t k + b, lanes of the workgroup in turn.
+    // The token loads go out before the first two weight stages: vector-memory loads retire
+    // in issue order, so the encoder then waits for its own rows only, and the weight
+    // stages stream in while it runs.
     {
-        const int tid = threadIdx.x;
-        const int64_t nblk = S * k;
+        const uint32_t tid = threadIdx.x, k32 = (uint32_t)k;
+        const uint32_t nblk = (uint32_t)(S * k);                  // at most 4 * 512
         constexpr int kPer = (kLinTokens * kLinMaxK + 64 * kLinWaves - 1) / (64 * kLinWaves);
         uint4 xv[kPer][4];
         mx::BlockParams bp[kPer];
 #pragma unroll
         for (int m = 0; m < kPer; ++m) {
-            const int64_t q = tid + (int64_t)m * 64 * kLinWaves;
+            const uint32_t q = tid + (uint32_t)m * 64 * kLinWaves;
             if (q < nblk) {
-                const int64_t t = q / k, b = q - t * k;
+                const uint32_t t = q / k32, b = q - t * k32;
                 bp[m] = mx::load_block_params<true, 0>(B, r_min, r_max, b);
                 const uint4* xp = reinterpret_cast<const uint4*>(x + t * ldx + 32 * b);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) xv[m][i] = xp[i];
             }
         }
+        // issued by every wave, so that the compiler's wait for the token rows counts the
+        // same ten younger loads on every path; a wave with fewer than two stages of its
+        // own refetches the last stage into a slot it never reads
+        issue(slot0, ws0, s0 < nst ? s0 : nst - 1);
+        issue(slot1, ws1, s0 + 1 < nst ? s0 + 1 : nst - 1);
 #pragma unroll
         for (int m = 0; m < kPer; ++m) {
-            const int64_t q = tid + (int64_t)m * 64 * kLinWaves;
+            const uint32_t q = tid + (uint32_t)m * 64 * kLinWaves;
             if (q < nblk) {
-                const int64_t t = q / k, b = q - t * k;
+                const uint32_t t = q / k32, b = q - t * k32;
                 float xf[32];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -1700,7 +1763,10 @@ gemm_linear_skinny_kernel(DmaArgs p, const uint16_t* __restrict__ x, int64_t ldx
             }
         }
     }
-    __syncthreads();
+    // the token buffers are complete once every wave's LDS stores have: a bare barrier after
+    // lgkmcnt(0), which leaves the weight stages in flight (the loop waits for them itself)
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    barrier_only();
 
     const int xr = lr < S ? lr : (int)S - 1;                      // token row of this lane
     const uint8_t* xrow = xcode + xr * kRowStride;
@@ -1745,25 +1811,12 @@ gemm_linear_skinny_kernel(DmaArgs p, const uint16_t* __restrict__ x, int64_t ldx
         __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
         __builtin_amdgcn_sched_barrier(0);
     };
-    if (s0 < s1) {
-        for (int s = s0;; s += 2) {
-            if (s + 1 < s1)
-                __builtin_amdgcn_s_waitcnt(waitcnt_imm(kGroup, 15));
-            else
-                __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
-            stage(slot0, ws0, s);
-            if (s + 1 >= s1) break;
-            if (s + 2 < s1) issue(slot0, ws0, s + 2);
-            if (s + 2 < s1)
-                __builtin_amdgcn_s_waitcnt(waitcnt_imm(kGroup, 15));
-            else
-                __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
-            stage(slot1, ws1, s + 1);
-            if (s + 2 >= s1) break;
-            if (s + 3 < s1) issue(slot1, ws1, s + 3);
-        }
-    }
-    // the partial tiles summed through LDS (the ring, reused) in wave order
+    ring_pipeline<kGroup, true>(
+        s0, s1, [&](int ks) { issue(slot0, ws0, ks); }, [&](int ks) { issue(slot1, ws1, ks); },
+        [&](int ks) { stage(slot0, ws0, ks); }, [&](int ks) { stage(slot1, ws1, ks); });
+    // the partial tiles summed through LDS (the ring, reused) in wave order, once every
+    // wave's stage DMA (the unused refetches included) has landed
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
     __syncthreads();
     float (*red)[16][64] = reinterpret_cast<float (*)[16][64]>(smem);
 #pragma unroll
