@@ -336,12 +336,15 @@ batq_status batq_dequantize_rows(const uint8_t* q, const uint8_t* e, int64_t src
  * The online linear layer in one call: y = the W4A4 product of batq_quantize_act(x) with
  * the prepared weights (gist.science summary, sections 2D and 4: activations transformed
  * and clipped online, MXFP4 x MXFP4 product).  For 1 <= S <= BATQ_LINEAR_FUSED_TOKENS (and
- * N/32 <= 512, N/32 % 8 == 0) one kernel does it: the few-token GEMM encodes the token rows
- * itself, with the quantiser's arithmetic, so the codes are exactly batq_quantize_act's and
- * y agrees with the two-call path within the GEMM's accumulation bound (its K split, and so
- * its fp32 summation order, differs); xq / xe are then not used and may be NULL.  Otherwise
- * the two calls run, with xq / xe as the caller's workspace for the activation codes and
- * scales (sized as batq_quantize_act's q and e in `layout`).
+ * N/32 <= 512, N/32 % 8 == 0) one kernel can do it: the few-token GEMM encodes the token
+ * rows itself, with the quantiser's arithmetic, so the codes are exactly
+ * batq_quantize_act's and y agrees with the two-call path within the GEMM's accumulation
+ * bound (its K split, and so its fp32 summation order, differs).  In that range xq / xe may
+ * be NULL, and the one kernel runs; when they are given, the library runs whichever of the
+ * two paths is faster for the shape (measured: the one kernel up to S * N/32 = 1024).
+ * Otherwise the two calls run, with xq / xe as the caller's workspace for the activation
+ * codes and scales (sized as batq_quantize_act's q and e in `layout`).  Either path gives
+ * the same result for the same inputs on every call.
  *   x, S, N, ldx, A, B, r_min, r_max: as batq_quantize_act
  *   wq, we, layout, out, y: as batq_gemm_w4a4 (y dev fp32 [S, out], 16-byte aligned)
  *   xq, xe: dev workspace or NULL (see above; BATQ_ERR_NULL when needed and missing,

@@ -56,6 +56,11 @@ CASES = [
     (33, 512, 258, False, False),
     (150, 2048, 260, True, True),
     (20, 1024, 300, True, True),
+    # at most 16 tokens: the 16-row few-token kernel, both layouts and both token formats
+    (5, 4096, 258, True, False),
+    (3, 2048, 130, False, False),
+    (7, 1024, 300, True, True),
+    (2, 512, 66, False, True),
 ]
 
 

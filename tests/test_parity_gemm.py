@@ -41,6 +41,31 @@ def test_gemm_random_operands_ragged(bq, orc, S, N, out):
     assert_gemm_close(y, y_ref, t_ref, what=f"S={S} N={N} out={out}")
 
 
+@pytest.mark.parametrize("tiled", [False, True])
+@pytest.mark.parametrize("S,N,out", [
+    # at most 16 tokens: the 16-row kernel (one K stage over eight waves; the longest K it
+    # takes, k = 512, with ragged out; a full round of workgroups; three rounds) and, past
+    # its dispatch rule, the 32-row kernel with the same token count (k = 384, out = 6144)
+    (1, 256, 17), (16, 256, 40), (2, 16384, 4100), (16, 4096, 4096), (1, 2048, 12290),
+    (9, 8192, 700), (5, 12288, 6144),
+])
+def test_gemm_few_tokens_both_layouts(bq, orc, S, N, out, tiled):
+    import torch
+    from tests.gpu_util import to_tiled_scales
+    xq, xe = wl.random_mxfp4(S, N, seed=(77, S, N, out))
+    wq, we = wl.random_mxfp4(out, N, seed=(78, S, N, out))
+    if tiled:
+        xe_d, we_d = to_tiled_scales(xe), to_tiled_scales(we)
+    else:
+        xe_d, we_d = xe, we
+    print(f"[gemm few tokens] S={S} N={N} out={out} tiled={tiled}", flush=True)
+    y = bq.gemm_w4a4(u8_to_device(xq), u8_to_device(xe_d), u8_to_device(wq), u8_to_device(we_d),
+                     layout=bq.SCALES_MFMA_TILED if tiled else bq.SCALES_ROW_MAJOR)
+    torch.cuda.synchronize()
+    y_ref, t_ref = orc.gemm(xq, xe, wq, we, nthreads=ORACLE_THREADS)
+    assert_gemm_close(to_host(y), y_ref, t_ref, what=f"S={S} N={N} out={out} tiled={tiled}")
+
+
 def test_gemm_zero_k_writes_zeros(bq):
     import torch
     y = torch.full((5, 7), 3.0, device="cuda")

@@ -21,7 +21,9 @@ def bq():
     return bq
 
 
-def run_linear(bq, L, layout, ldx=None):
+def run_linear(bq, L, layout, ldx=None, workspace=True):
+    """batq_linear_w4a4 on the layer; workspace=False calls the C entry with no workspace,
+    which takes the one-kernel path (the binding passes one and lets the library choose)."""
     import torch
     S, N = L.x_bits.shape
     wq, we = bq.prepare_weight(f32_to_device(L.W), L.A, L.B, layout=layout)
@@ -32,9 +34,19 @@ def run_linear(bq, L, layout, ldx=None):
         x = bf16_to_device(wide)[:, :N]
     else:
         x = bf16_to_device(L.x_bits)
-    y = bq.linear_w4a4(x, f32_to_device(L.A), f32_to_device(L.B),
-                       f32_to_device(bq.clip_ratios(L.alpha_min)),
-                       f32_to_device(bq.clip_ratios(L.alpha_max)), wq, we, layout=layout)
+    A, B = f32_to_device(L.A), f32_to_device(L.B)
+    r1 = f32_to_device(bq.clip_ratios(L.alpha_min))
+    r2 = f32_to_device(bq.clip_ratios(L.alpha_max))
+    if workspace:
+        y = bq.linear_w4a4(x, A, B, r1, r2, wq, we, layout=layout)
+    else:
+        out = wq.shape[0]
+        y = torch.empty((S, out), dtype=torch.float32, device="cuda")
+        st = bq.linear_w4a4_raw(x.data_ptr(), S, N, x.stride(0), A.data_ptr(), B.data_ptr(),
+                                r1.data_ptr(), r2.data_ptr(), wq.data_ptr(), we.data_ptr(), out,
+                                y.data_ptr(), 0, 0, layout=layout,
+                                stream=torch.cuda.current_stream().cuda_stream)
+        assert st == 0, bq.status_string(st)
     torch.cuda.synchronize()
     return to_host(y)
 
@@ -60,7 +72,7 @@ def test_linear_one_kernel(bq, orc, S, N, out, ldx, tiled):
                                 outliers=("channels_uniform", 8, 20.0, 100.0)))
     layout = bq.SCALES_MFMA_TILED if tiled else bq.SCALES_ROW_MAJOR
     print(f"[linear one-kernel] S={S} N={N} out={out} tiled={tiled}", flush=True)
-    y = run_linear(bq, L, layout, ldx=ldx)
+    y = run_linear(bq, L, layout, ldx=ldx, workspace=False)
     y_ref, t_ref = oracle_linear(orc, L)
     assert_gemm_close(y, y_ref, t_ref, what=f"S={S} N={N} out={out} tiled={tiled}")
 
@@ -75,6 +87,16 @@ def test_linear_two_steps(bq, orc, S, N, out):
     y = run_linear(bq, L, bq.SCALES_MFMA_TILED)
     y_ref, t_ref = oracle_linear(orc, L)
     assert_gemm_close(y, y_ref, t_ref, what=f"two steps S={S} N={N} out={out}")
+
+
+@pytest.mark.parametrize("S,N,out", [(1, 4096, 96), (3, 16384, 64), (4, 12288, 40)])
+def test_linear_with_workspace_either_path(bq, orc, S, N, out):
+    """With a workspace the library picks a path by shape (the one kernel, or the two calls
+    for larger S * k): the result is the oracle's within the bound either way."""
+    L = wl.make_layer(wl.custom("lin4", S, N, out, seed=(104, S, N, out)))
+    y = run_linear(bq, L, bq.SCALES_MFMA_TILED, workspace=True)
+    y_ref, t_ref = oracle_linear(orc, L)
+    assert_gemm_close(y, y_ref, t_ref, what=f"workspace S={S} N={N} out={out}")
 
 
 def test_linear_one_kernel_matches_two_calls(bq):

@@ -155,6 +155,24 @@ def test_gemm8_random_operands_ragged(bq, orc, S, N, out, tiled):
     assert_gemm_close(y[rows], y_hw, t_ref[rows], what=what + " (model)")
 
 
+@pytest.mark.parametrize("tiled", [False, True])
+@pytest.mark.parametrize("S,N,out", [
+    # at most 16 tokens: the 16-row kernel with E4M3 token fragments (one K stage; k = 512
+    # with ragged out; a full round) and, past its dispatch rule, the 32-row kernel
+    (1, 256, 17), (16, 4096, 1000), (3, 16384, 4100), (8, 12288, 6144), (4, 4096, 12300),
+])
+def test_gemm8_few_tokens(bq, orc, S, N, out, tiled):
+    xq8, xe = wl.random_mxfp8(S, N, seed=(79, S, N, out))
+    wq, we = wl.random_mxfp4(out, N, seed=(80, S, N, out))
+    print(f"[gemm8 few tokens] S={S} N={N} out={out} tiled={tiled}", flush=True)
+    y = gpu_gemm8(bq, xq8, xe, wq, we, tiled)
+    what = f"w4a8 few tokens S={S} N={N} out={out} tiled={tiled}"
+    y_ref, t_ref = orc.gemm_w4a8(xq8, xe, wq, we, nthreads=ORACLE_THREADS)
+    assert_gemm_close(y, y_ref, t_ref, rel=W4A8_REL, what=what)
+    y_hw = gemm_w4a8_mfma_model(xq8, xe, wq, we, rows=np.arange(S))
+    assert_gemm_close(y, y_hw, t_ref, what=what + " (model)")
+
+
 @pytest.mark.parametrize("S,N,out", [(33, 1024, 70), (130, 2048, 260)])
 def test_gemm8_narrow_scales(bq, orc, S, N, out):
     """Scales within a factor 32 of each other: every block contributes to every output, so

@@ -291,8 +291,9 @@ def gemm_w4a4(xq, xe, wq, we, y=None, layout=SCALES_ROW_MAJOR, stream=None):
 
 def linear_w4a4(x, A, B, r_min, r_max, wq, we, layout=SCALES_ROW_MAJOR, y=None, stream=None):
     """One pass of the online path through batq_linear_w4a4: quantise the activations and
-    multiply with the prepared weights (scales `we` in `layout`); one kernel for up to
-    LINEAR_FUSED_TOKENS tokens, else the two calls with a workspace allocated here."""
+    multiply with the prepared weights (scales `we` in `layout`).  A workspace for the
+    activation codes is allocated here and passed, so the library picks the faster of its
+    one-kernel path (up to LINEAR_FUSED_TOKENS tokens) and the two calls."""
     import torch
     assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
     S, N = x.shape
@@ -304,15 +305,11 @@ def linear_w4a4(x, A, B, r_min, r_max, wq, we, layout=SCALES_ROW_MAJOR, y=None, 
     if y is None:
         y = torch.empty((S, out), dtype=torch.float32, device=x.device)
     assert y.dtype == torch.float32 and y.shape == (S, out) and y.is_contiguous()
-    k = N // 32
-    xq = xe = None
-    if not (S <= LINEAR_FUSED_TOKENS and k <= 512 and k % 8 == 0):
-        xq = torch.empty((S, N // 2), dtype=torch.uint8, device=x.device)
-        xe = _scale_tensor(S, N, layout, x.device)
+    xq = torch.empty((S, N // 2), dtype=torch.uint8, device=x.device)
+    xe = _scale_tensor(S, N, layout, x.device)
     _check("batq_linear_w4a4", linear_w4a4_raw(
         _ptr(x), S, N, x.stride(0), _ptr(A), _ptr(B), _ptr(r_min), _ptr(r_max), _ptr(wq),
-        _ptr(we), out, _ptr(y), _ptr(xq) if xq is not None else 0,
-        _ptr(xe) if xe is not None else 0, layout, _stream(stream)))
+        _ptr(we), out, _ptr(y), _ptr(xq), _ptr(xe), layout, _stream(stream)))
     return y
 
 

@@ -194,9 +194,11 @@ BATQ_API batq_status batq_linear_w4a4(const uint16_t* x, int64_t S, int64_t N, i
     if (N == 0) return batq_gemm_w4a4(nullptr, nullptr, nullptr, nullptr, layout, S, 0, out, y,
                                       stream);
     const int64_t k = N / 32;
-    const bool fused = S <= BATQ_LINEAR_FUSED_TOKENS && k <= 512 && k % 8 == 0;
+    const bool can_fuse = S <= BATQ_LINEAR_FUSED_TOKENS && k <= 512 && k % 8 == 0;
     if (!y || !x || !A || !B || !r_min || !r_max || !wq || !we) return BATQ_ERR_NULL;
-    if (!fused && (!xq || !xe)) return BATQ_ERR_NULL;
+    if (!can_fuse && (!xq || !xe)) return BATQ_ERR_NULL;
+    // with a workspace, the one kernel where it measured faster than the two calls
+    const bool fused = can_fuse && (!xq || !xe || S * k <= 1024);
     if (ldx < N || mul_overflows(S, ldx) || mul_overflows(S, out) || mul_overflows(out, N))
         return BATQ_ERR_SHAPE;
     if (ldx % 8 != 0 || !aligned(x, 16) || !aligned(B, 16) || !aligned(y, 16) ||

@@ -1846,6 +1846,201 @@ gemm_linear_skinny_kernel(DmaArgs p, const uint16_t* __restrict__ x, int64_t ldx
     }
 }
 
+// =======================================================================================
+// gemm_skinny16_kernel<TS, F8>: at most 16 tokens, 16 output rows per workgroup
+// =======================================================================================
+//
+// The few-token GEMM is weight streaming, and its time is the HBM round trips of each
+// workgroup's weight panel.  With 32 output rows per workgroup an out = 4096 layer has 128
+// workgroups (half the CUs) and, at N = 12288, a panel (196 KB) larger than LDS, so part of
+// it waits for a slot to free: a second round trip.  Here a workgroup owns 16 output rows
+// (the 16x16x128 scaled MFMA: lane l holds row l%16 and K block l/16 of a 128-element
+// K-step), so out = 4096 gives 256 workgroups, and the whole panel (16 rows x 16 k bytes, at
+// most 128 KB up to k = 512) is requested at once: each of the kS16Waves waves issues the
+// LDS DMA of every stage of its K range together with its token fragments and scales, waits
+// once, and multiplies.  The partial tiles are summed through LDS in wave order.  Tokens
+// (at most 16) are one MFMA column, loaded as fragments straight into registers: E2M1 16
+// bytes per lane (K block l/16); E4M3 32 bytes, lane group g holding elements 16g..16g+15
+// of the K-step's first half and of its second half (16-byte units g and 4 + g of the
+// 128-byte K-step row), the E4M3 operand layout of the 32x32x64 form extended to four
+// lane groups; a lane's scale byte belongs to K block l/16 either way.
+constexpr int kS16Rows = 16, kS16Waves = 8, kS16MaxK = 512, kS16MaxTokens = 16;
+constexpr int kS16Stage = kS16Rows * kRowBytes;               // one 128-byte line per row
+constexpr int kS16Per = kS16MaxK / kStageBlocks / kS16Waves;  // stages per wave, at most
+
+// dynamic LDS bytes of a launch: the panel, or the reduction buffer if that is larger
+inline size_t s16_lds_bytes(int64_t k)
+{
+    const size_t panel = (size_t)(k / kStageBlocks) * kS16Stage;
+    const size_t red = (size_t)kS16Waves * 4 * 64 * 4;
+    return panel > red ? panel : red;
+}
+
+// Whether the 16-row kernel takes a few-token GEMM (S <= 16, k <= 512).  A workgroup's
+// time is about one round trip of its panel (the 32-row kernel's: one or two, its panel
+// beyond 128 KB from k = 384 on), so the counts of workgroup rounds decide: rounds =
+// ceil(workgroups / (CUs x workgroups per CU)), bounded for the 16-row kernel by the
+// panel's LDS and by registers (one for E4M3 tokens, 162 VGPRs x 8 waves; two for E2M1),
+// one 32-row workgroup per CU.  Measured on S = 1, 8, N = 4096..16384, out = 4096..12288:
+// no more rounds than the 32-row grid is faster (up to 32%, out = 4096 and 12288 at short
+// K) but for a few 5% cases; more rounds is 5-13% slower, except at three rounds or more
+// (out = 12288): 7-14% faster with E2M1 tokens, 9-15% with one E4M3 token (3-4% slower
+// with eight, whose 32-byte rows every workgroup reads again).
+constexpr int kNumCUs = 256;                                  // MI355X
+inline bool use_skinny16(int64_t S, int64_t k, int64_t out, bool f8)
+{
+    if (S > kS16MaxTokens || k > kS16MaxK) return false;
+    const int64_t by_lds = (int64_t)((160 * 1024) / s16_lds_bytes(k));
+    const int64_t per_cu = by_lds < (f8 ? 1 : 2) ? by_lds : (f8 ? 1 : 2);
+    const int64_t tiles = (out + kS16Rows - 1) / kS16Rows;
+    const int64_t rounds = (tiles + kNumCUs * per_cu - 1) / (kNumCUs * per_cu);
+    const int64_t rounds32 = ((out + 31) / 32 + kNumCUs - 1) / kNumCUs;
+    return rounds <= rounds32 || (rounds >= 3 && (!f8 || S <= 4));
+}
+
+template <bool TS, bool F8>
+__global__ void __launch_bounds__(64 * kS16Waves)
+gemm_skinny16_kernel(DmaArgs p, float* __restrict__ y)
+{
+    // dynamic LDS: the panel of this launch's K (k / 8 stages of 2 KB, at least the 8 KB of
+    // the reduction), so that several workgroups share a CU when K is short
+    extern __shared__ __attribute__((aligned(16))) uint8_t panel[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lr = lane & 15, lg = lane >> 4;
+    const int64_t o0 = (int64_t)blockIdx.x * kS16Rows;
+    const int64_t k = p.k, k8 = k / 8;
+    const int nst = (int)(k / kStageBlocks);
+    const int s0 = wave * nst / kS16Waves, n = (wave + 1) * nst / kS16Waves - s0;
+
+    const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(p.wq, p.out * 16 * k);
+    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(p.xq, p.S * (F8 ? 32 : 16) * k);
+    const __amdgpu_buffer_rsrc_t rwe =
+        buffer_rsrc(p.we, TS ? ((p.out + 31) / 32) * 256 * k8 : p.out * k);
+    const __amdgpu_buffer_rsrc_t rxe =
+        buffer_rsrc(p.xe, TS ? ((p.S + 31) / 32) * 256 * k8 : p.S * k);
+    // DMA: instruction q moves rows 8q..8q+7, lane L the global chunk (L%8) ^ ((row/2)%8) of
+    // row 8q + L/8 into position L%8 of that row's 128 bytes (rows past `out` clamped)
+    uint32_t woff[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int r = 8 * q + (lane >> 3);
+        const int64_t row = o0 + r < p.out ? o0 + r : p.out - 1;
+        woff[q] = (uint32_t)(row * 16 * k + 16 * ((lane & 7) ^ ((r >> 1) & 7)));
+    }
+    const uint32_t wrow = (uint32_t)(o0 + lr < p.out ? o0 + lr : p.out - 1);
+    const uint32_t xrow = (uint32_t)(lr < p.S ? lr : p.S - 1);
+    // scales of stage 0: tiled, the dword of the row's 8 bytes that holds blocks with the
+    // lane's parity (blocks 4j + lg of the stage sit at byte 4 (lg%2) + 2j + lg/2);
+    // row-major, the row's 8 bytes of the stage (block 4j + lg at byte 4j + lg)
+    const uint32_t wse = TS ? (uint32_t)((wrow >> 5) * k8 * 256 + (wrow & 31) * 8 + 4 * (lg & 1))
+                            : wrow * (uint32_t)k;
+    const uint32_t xse = TS ? (uint32_t)((xrow >> 5) * k8 * 256 + (xrow & 31) * 8 + 4 * (lg & 1))
+                            : xrow * (uint32_t)k;
+    const uint32_t xrb = (F8 ? 32u : 16u) * (uint32_t)k;          // token code row bytes
+
+    v4u xf[kS16Per][2][F8 ? 2 : 1];
+    uint2 ws[kS16Per], xs[kS16Per];
+#pragma unroll
+    for (int i = 0; i < kS16Per; ++i) {
+        if (i < n) {
+            const int ks = s0 + i;
+#if defined(__HIP_DEVICE_COMPILE__)   // the LDS-load builtins exist for the device only
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rw, (lds_void_t*)(panel + ks * kS16Stage + q * 1024), 16, woff[q],
+                    ks * kRowBytes, 0, 0);
+#endif
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                if constexpr (F8) {
+                    const uint32_t c = xrow * xrb + (uint32_t)ks * 256u + 128u * j + 16u * lg;
+                    xf[i][j][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)c, 0, 0);
+                    xf[i][j][F8 ? 1 : 0] =
+                        __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(c + 64), 0, 0);
+                } else {
+                    const uint32_t c = xrow * xrb + (uint32_t)ks * kRowBytes + 64u * j + 16u * lg;
+                    xf[i][j][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)c, 0, 0);
+                }
+            }
+            if constexpr (TS) {
+                ws[i].x = __builtin_amdgcn_raw_buffer_load_b32(rwe, (int)(wse + (uint32_t)ks * 256u), 0, 0);
+                xs[i].x = __builtin_amdgcn_raw_buffer_load_b32(rxe, (int)(xse + (uint32_t)ks * 256u), 0, 0);
+            } else {
+                const v2u a = __builtin_amdgcn_raw_buffer_load_b64(rwe, (int)(wse + (uint32_t)ks * 8u), 0, 0);
+                const v2u b = __builtin_amdgcn_raw_buffer_load_b64(rxe, (int)(xse + (uint32_t)ks * 8u), 0, 0);
+                ws[i] = make_uint2(a.x, a.y);
+                xs[i] = make_uint2(b.x, b.y);
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+
+    v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+    const int key = (lr >> 1) & 7;
+#pragma unroll
+    for (int i = 0; i < kS16Per; ++i) {
+        if (i < n) {
+            const uint8_t* row = panel + (s0 + i) * kS16Stage + lr * kRowBytes;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const uint4 a = *reinterpret_cast<const uint4*>(row + 16 * ((4 * j + lg) ^ key));
+                const v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+                const v4u u = xf[i][j][0];
+                v8i bv = {(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
+                if constexpr (F8) {
+                    const v4u v = xf[i][j][F8 ? 1 : 0];
+                    bv = v8i{(int)u.x, (int)u.y, (int)u.z, (int)u.w, (int)v.x, (int)v.y, (int)v.z, (int)v.w};
+                }
+                // tiled: byte 2j of the dword pre-shifted by the lane's lg/2; row-major: byte
+                // 0 of word j pre-shifted by lg
+                const uint32_t wsc = TS ? ws[i].x >> (8 * (lg >> 1)) : (j ? ws[i].y : ws[i].x) >> (8 * lg);
+                const uint32_t xsc = TS ? xs[i].x >> (8 * (lg >> 1)) : (j ? xs[i].y : xs[i].x) >> (8 * lg);
+                if (j == 0)
+                    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        av, bv, acc, kFmtE2M1, F8 ? 0 : kFmtE2M1, 0, (int)wsc, 0, (int)xsc);
+                else
+                    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        av, bv, acc, kFmtE2M1, F8 ? 0 : kFmtE2M1, TS ? 2 : 0, (int)wsc,
+                        TS ? 2 : 0, (int)xsc);
+            }
+        }
+    }
+
+    // the partial tiles summed through LDS (the panel, reused) in wave order
+    __syncthreads();
+    float (*red)[4][64] = reinterpret_cast<float (*)[4][64]>(panel);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][i][lane] = acc[i];
+    __syncthreads();
+    if (wave == 0) {
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float t = red[0][i][lane];
+#pragma unroll
+            for (int w = 1; w < kS16Waves; ++w) t += red[w][i][lane];
+            v[i] = t;
+        }
+        const int64_t o = o0 + 4 * lg;
+        if (lr < p.S && (p.res || p.out_bf16)) {
+            if (o < p.out)
+                epi_store4(p, y, lr, o, v[0], v[1], v[2], v[3],
+                           (int)(p.out - o < 4 ? p.out - o : 4), (p.out & 3) == 0);
+        } else if (lr < p.S) {
+            float* dst = y + lr * p.out + o;
+            if ((p.out & 3) == 0 && o + 3 < p.out) {
+                *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (o + i < p.out) dst[i] = v[i];
+            }
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq,
@@ -1859,6 +2054,19 @@ hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq,
                         (reinterpret_cast<uintptr_t>(xe) % salign) == 0 &&
                         (reinterpret_cast<uintptr_t>(we) % salign) == 0 &&
                         S * 16 * p.k < (1LL << 32) && out * 16 * p.k < (1LL << 32);
+    if (dma_ok && use_skinny16(S, p.k, out, false)) {
+        // at most 16 tokens: 16-row workgroups, the whole weight panel requested at once
+        const int64_t tiles_o = (out + kS16Rows - 1) / kS16Rows;
+        if (tiles_o > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+        const size_t lds = s16_lds_bytes(p.k);
+        if (tiled_scales)
+            hipLaunchKernelGGL((gemm_skinny16_kernel<true, false>), dim3((unsigned)tiles_o),
+                               dim3(64 * kS16Waves), lds, stream, p, y);
+        else
+            hipLaunchKernelGGL((gemm_skinny16_kernel<false, false>), dim3((unsigned)tiles_o),
+                               dim3(64 * kS16Waves), lds, stream, p, y);
+        return hipGetLastError();
+    }
     if (dma_ok && S <= 64) {
         // few tokens: weight streaming, K split across the waves of a 32-row workgroup
         const int64_t tiles_o = (out + 31) / 32;
@@ -1912,6 +2120,19 @@ hipError_t launch_gemm_w4a8(const uint8_t* xq8, const uint8_t* xe, const uint8_t
         return hipErrorNotSupported;
     const bool s8 = (reinterpret_cast<uintptr_t>(xe) % 8) == 0 &&
                     (reinterpret_cast<uintptr_t>(we) % 8) == 0;
+    if (use_skinny16(S, p.k, out, true) && (tiled_scales || s8)) {
+        // at most 16 tokens: 16-row workgroups with E4M3 token fragments
+        const int64_t tiles_o = (out + kS16Rows - 1) / kS16Rows;
+        if (tiles_o > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+        const size_t lds = s16_lds_bytes(p.k);
+        if (tiled_scales)
+            hipLaunchKernelGGL((gemm_skinny16_kernel<true, true>), dim3((unsigned)tiles_o),
+                               dim3(64 * kS16Waves), lds, stream, p, y);
+        else
+            hipLaunchKernelGGL((gemm_skinny16_kernel<false, true>), dim3((unsigned)tiles_o),
+                               dim3(64 * kS16Waves), lds, stream, p, y);
+        return hipGetLastError();
+    }
     if (S <= 64 && (tiled_scales || s8)) {
         // few tokens: the weight-streaming kernel with E4M3 token codes
         const int64_t tiles_w = (out + 31) / 32;
