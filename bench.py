@@ -374,7 +374,7 @@ def measure(name, args):
         # fp32 outputs (the factors and ratios are a few KB)
         b_lin = S * N * 2 + out * (N // 2 + k) + 4 * S * out
         rec["linear_one_kernel"] = {
-            "kernel": "gemm_linear_skinny_kernel (transform + clip + MXFP4 of the token rows "
+            "kernel": "gemm_linear16_kernel (transform + clip + MXFP4 of the token rows "
                       "inside the few-token GEMM)",
             "avg_us": round(t_lin * 1e6, 3), "two_kernels_us": round((t_k1 + t_k2) * 1e6, 3),
             "bound": "hbm", "achieved": round(b_lin / t_lin / 1e9, 1), "peak": HBM_PEAK_GBS,

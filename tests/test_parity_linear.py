@@ -89,10 +89,14 @@ def test_linear_two_steps(bq, orc, S, N, out):
     assert_gemm_close(y, y_ref, t_ref, what=f"two steps S={S} N={N} out={out}")
 
 
-@pytest.mark.parametrize("S,N,out", [(1, 4096, 96), (3, 16384, 64), (4, 12288, 40)])
+@pytest.mark.parametrize("S,N,out", [
+    (1, 4096, 96), (3, 16384, 64),        # one kernel
+    (4, 12288, 2064), (2, 16384, 6200),   # two calls: S k ceil(out/16) beyond 196608
+])
 def test_linear_with_workspace_either_path(bq, orc, S, N, out):
     """With a workspace the library picks a path by shape (the one kernel, or the two calls
-    for larger S * k): the result is the oracle's within the bound either way."""
+    when the token encoding all its workgroups repeat grows large): the result is the
+    oracle's within the bound either way."""
     L = wl.make_layer(wl.custom("lin4", S, N, out, seed=(104, S, N, out)))
     y = run_linear(bq, L, bq.SCALES_MFMA_TILED, workspace=True)
     y_ref, t_ref = oracle_linear(orc, L)

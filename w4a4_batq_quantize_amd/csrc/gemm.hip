@@ -2041,6 +2041,173 @@ gemm_skinny16_kernel(DmaArgs p, float* __restrict__ y)
     }
 }
 
+// =======================================================================================
+// gemm_linear16_kernel<TS, NPER>: the layer in one kernel on 16-row workgroups
+// =======================================================================================
+//
+// gemm_skinny16_kernel's structure (16 output rows per workgroup, 16x16x128 scaled MFMA, the
+// whole weight panel in flight at once) with the token rows encoded in the kernel, as
+// gemm_linear_skinny_kernel does: the lanes' token loads go out first, then every wave's
+// weight stages (NPER each; a wave past the last stage refetches it into a scratch slot, so
+// every wave issues the same loads and the wait before the encoder counts them exactly),
+// then the lanes encode the S k blocks into LDS while the panel streams in.  The token
+// buffers are static arrays, apart from the dynamic panel, so the encoder's stores do not
+// wait for the weight DMA.  Token fragments and scales then come from LDS (scale bytes in
+// plain order, one per lane).  S k <= kLin16MaxSK, so that panel and buffers fit in LDS.
+constexpr int kLin16MaxSK = 1536;
+
+template <bool TS, int NPER>
+__global__ void __launch_bounds__(64 * kS16Waves)
+gemm_linear16_kernel(DmaArgs p, const uint16_t* __restrict__ x, int64_t ldx,
+                     const float* __restrict__ A, const float* __restrict__ B,
+                     const float* __restrict__ r_min, const float* __restrict__ r_max,
+                     float* __restrict__ y)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t xcode[kLin16MaxSK * 16];
+    __shared__ __attribute__((aligned(16))) uint8_t xscale[kLin16MaxSK];
+    extern __shared__ __attribute__((aligned(16))) uint8_t panel[];   // nst stages + scratch
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lr = lane & 15, lg = lane >> 4;
+    const int64_t o0 = (int64_t)blockIdx.x * kS16Rows;
+    const int64_t k = p.k, k8 = k / 8, S = p.S;
+    const int nst = (int)(k / kStageBlocks);
+    const int s0 = wave * NPER;
+
+    const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(p.wq, p.out * 16 * k);
+    const __amdgpu_buffer_rsrc_t rwe =
+        buffer_rsrc(p.we, TS ? ((p.out + 31) / 32) * 256 * k8 : p.out * k);
+    // 32-bit offsets (out * 16 k < 2^32): a 64-bit product truncated here made the compiler
+    // read a register still being loaded as its unused high half, a wait ahead of the DMA
+    uint32_t woff[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int r = 8 * q + (lane >> 3);
+        const uint32_t row = (uint32_t)(o0 + r < p.out ? o0 + r : p.out - 1);
+        woff[q] = row * (uint32_t)(16 * k) + 16u * ((lane & 7) ^ ((r >> 1) & 7));
+    }
+    const uint32_t wrow = (uint32_t)(o0 + lr < p.out ? o0 + lr : p.out - 1);
+    const uint32_t wse = TS ? (uint32_t)((wrow >> 5) * k8 * 256 + (wrow & 31) * 8 + 4 * (lg & 1))
+                            : wrow * (uint32_t)k;
+
+    // token loads first: block q = t k + b, lanes of the workgroup in turn
+    constexpr int kPer = (kLin16MaxSK + 64 * kS16Waves - 1) / (64 * kS16Waves);
+    const uint32_t tid = threadIdx.x, k32 = (uint32_t)k, nblk = (uint32_t)(S * k);
+    uint4 xv[kPer][4];
+    mx::BlockParams bp[kPer];
+#pragma unroll
+    for (int m = 0; m < kPer; ++m) {
+        const uint32_t q = tid + (uint32_t)m * 64 * kS16Waves;
+        if (q < nblk) {
+            const uint32_t t = q / k32, b = q - t * k32;
+            bp[m] = mx::load_block_params<true, 0>(B, r_min, r_max, b);
+            const uint4* xp = reinterpret_cast<const uint4*>(x + t * ldx + 32 * b);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xv[m][i] = xp[i];
+        }
+    }
+    // then the wave's NPER weight stages (past the last stage: a refetch into the scratch slot)
+    uint2 ws[NPER];
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) {
+        const int ks = s0 + i < nst ? s0 + i : nst - 1;
+        uint8_t* dst = panel + (s0 + i < nst ? ks : nst) * kS16Stage;
+#if defined(__HIP_DEVICE_COMPILE__)   // the LDS-load builtins exist for the device only
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t*)(dst + q * 1024), 16,
+                                                     woff[q], ks * kRowBytes, 0, 0);
+#endif
+        if constexpr (TS) {
+            ws[i].x = __builtin_amdgcn_raw_buffer_load_b32(rwe, (int)(wse + (uint32_t)ks * 256u), 0, 0);
+        } else {
+            const v2u a = __builtin_amdgcn_raw_buffer_load_b64(rwe, (int)(wse + (uint32_t)ks * 8u), 0, 0);
+            ws[i] = make_uint2(a.x, a.y);
+        }
+    }
+    // encode the token blocks into LDS (codes row-major, scale bytes in plain order)
+#pragma unroll
+    for (int m = 0; m < kPer; ++m) {
+        const uint32_t q = tid + (uint32_t)m * 64 * kS16Waves;
+        if (q < nblk) {
+            const uint32_t t = q / k32, b = q - t * k32;
+            float xf[32];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t w4[4] = {xv[m][i].x, xv[m][i].y, xv[m][i].z, xv[m][i].w};
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    xf[8 * i + 2 * d] = mx::bf16_lo(w4[d]);
+                    xf[8 * i + 2 * d + 1] = mx::bf16_hi(w4[d]);
+                }
+            }
+            const mx::BlockCode<false> c = mx::encode_block<true, false, 0>(xf, A, bp[m], b);
+            *reinterpret_cast<uint4*>(xcode + 16 * q) = make_uint4(c.w[0], c.w[1], c.w[2], c.w[3]);
+            xscale[q] = (uint8_t)c.ebyte;
+        }
+    }
+    // the token buffers are complete once every wave's LDS stores have; the weight stages
+    // stay in flight across the barrier, and each wave then waits for its own
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    barrier_only();
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+
+    const uint32_t xr = (uint32_t)(lr < S ? lr : S - 1);
+    const uint8_t* xrow = xcode + 16 * xr * k32;
+    const uint8_t* xsrow = xscale + xr * k32;
+    v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+    const int key = (lr >> 1) & 7;
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) {
+        if (s0 + i < nst) {
+            const int ks = s0 + i;
+            const uint8_t* row = panel + ks * kS16Stage + lr * kRowBytes;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int blk = 8 * ks + 4 * j + lg;
+                const uint4 a = *reinterpret_cast<const uint4*>(row + 16 * ((4 * j + lg) ^ key));
+                const uint4 u = *reinterpret_cast<const uint4*>(xrow + 16 * blk);
+                const v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+                const v8i bv = {(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
+                const uint32_t wsc = TS ? ws[i].x >> (8 * (lg >> 1)) : (j ? ws[i].y : ws[i].x) >> (8 * lg);
+                const uint32_t xsc = xsrow[blk];
+                if (j == 0)
+                    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        av, bv, acc, kFmtE2M1, kFmtE2M1, 0, (int)wsc, 0, (int)xsc);
+                else
+                    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        av, bv, acc, kFmtE2M1, kFmtE2M1, TS ? 2 : 0, (int)wsc, 0, (int)xsc);
+            }
+        }
+    }
+
+    // the partial tiles summed through LDS (the panel, reused) in wave order
+    __syncthreads();
+    float (*red)[4][64] = reinterpret_cast<float (*)[4][64]>(panel);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][i][lane] = acc[i];
+    __syncthreads();
+    if (wave == 0 && lr < S) {
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float t = red[0][i][lane];
+#pragma unroll
+            for (int w = 1; w < kS16Waves; ++w) t += red[w][i][lane];
+            v[i] = t;
+        }
+        const int64_t o = o0 + 4 * lg;
+        float* dst = y + lr * p.out + o;
+        if ((p.out & 3) == 0 && o + 3 < p.out) {
+            *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (o + i < p.out) dst[i] = v[i];
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq,
@@ -2170,6 +2337,37 @@ hipError_t launch_gemm_w4a8(const uint8_t* xq8, const uint8_t* xe, const uint8_t
 
 namespace batq {
 
+template <bool TS, int NPER>
+static void launch_linear16_n(const DmaArgs& p, const uint16_t* x, int64_t ldx, const float* A,
+                              const float* B, const float* r_min, const float* r_max, float* y,
+                              hipStream_t stream)
+{
+    const int64_t tiles = (p.out + kS16Rows - 1) / kS16Rows;
+    const size_t panel = (size_t)(p.k / kStageBlocks + 1) * kS16Stage;   // + the scratch slot
+    const size_t red = (size_t)kS16Waves * 4 * 64 * 4;
+    hipLaunchKernelGGL((gemm_linear16_kernel<TS, NPER>), dim3((unsigned)tiles),
+                       dim3(64 * kS16Waves), panel > red ? panel : red, stream, p, x, ldx, A, B,
+                       r_min, r_max, y);
+}
+
+template <bool TS>
+static void launch_linear16(const DmaArgs& p, const uint16_t* x, int64_t ldx, const float* A,
+                            const float* B, const float* r_min, const float* r_max, float* y,
+                            hipStream_t stream)
+{
+    const int nper = (int)((p.k / kStageBlocks + kS16Waves - 1) / kS16Waves);
+    switch (nper) {
+    case 1: launch_linear16_n<TS, 1>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
+    case 2: launch_linear16_n<TS, 2>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
+    case 3: launch_linear16_n<TS, 3>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
+    case 4: launch_linear16_n<TS, 4>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
+    case 5: launch_linear16_n<TS, 5>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
+    case 6: launch_linear16_n<TS, 6>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
+    case 7: launch_linear16_n<TS, 7>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
+    default: launch_linear16_n<TS, 8>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
+    }
+}
+
 hipError_t launch_linear_skinny(const uint16_t* x, int64_t S, int64_t k, int64_t ldx,
                                 const float* A, const float* B, const float* r_min,
                                 const float* r_max, const uint8_t* wq, const uint8_t* we,
@@ -2181,6 +2379,15 @@ hipError_t launch_linear_skinny(const uint16_t* x, int64_t S, int64_t k, int64_t
     if ((reinterpret_cast<uintptr_t>(we) % salign) != 0 || out * 16 * k >= (1LL << 32))
         return hipErrorNotSupported;
     const DmaArgs p{nullptr, nullptr, wq, we, S, k, out, nullptr, 0};
+    if (S * k <= kLin16MaxSK && k <= kS16MaxK) {
+        // 16-row workgroups, the whole panel in flight
+        if ((out + kS16Rows - 1) / kS16Rows > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+        if (tiled_scales)
+            launch_linear16<true>(p, x, ldx, A, B, r_min, r_max, y, stream);
+        else
+            launch_linear16<false>(p, x, ldx, A, B, r_min, r_max, y, stream);
+        return hipGetLastError();
+    }
     const int64_t tiles_o = (out + 31) / 32;
     if (tiles_o > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)tiles_o), block(64 * kLinWaves);
