@@ -49,6 +49,22 @@ constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 1
 // needs is established by the explicit s_waitcnt placed before it.
 __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
+// K rotation of a tile when the grid has more tiles than CUs: the tile starts its K loop at
+// stage (weight tile + token tile) mod nst and wraps.  Tiles that share an operand tile then
+// request its stages at different times, so most of their requests find the lines a
+// neighbour has already brought into L2, where with every tile in step each request waits
+// for the same fill.  Measured on the producer/consumer kernel: gate_up and the S = 16384
+// prefills 4-7% faster; with a single round of tiles (q_proj, down_proj) no gain, so it is
+// off there (and in the W4A8 kernel, whose waves issue the DMA between their MFMAs, it
+// gained 2-3% on those shapes and cost 3% on the single-round ones).  Any order sums the
+// same terms (within the accumulation bound), and the rotation is fixed per tile.
+__device__ __forceinline__ int64_t k_rotation(int64_t tiles_o, int64_t tiles_s, int64_t o0,
+                                              int64_t s0, int64_t BO, int64_t BS, int64_t nst)
+{
+    if (nst == 0 || tiles_o * tiles_s <= 256) return 0;
+    return (o0 / BO + s0 / BS) % nst;
+}
+
 // Tile numbering: when the tile count divides evenly, each XCD (own L2) receives a
 // contiguous run of tiles; within the run, groups of `group_o` weight tiles are swept
 // across the activation tiles so neighbouring workgroups share operands.
@@ -736,8 +752,11 @@ gemm_pc_kernel(DmaArgs p, float* __restrict__ y, int64_t tiles_o, int64_t tiles_
         const int pw = wave - C::kWaves;
         DmaPlan<C> pl;
         dma_plan<C>(pl, p, o0, s0, pw, lane);
+        const int64_t rot = k_rotation(tiles_o, tiles_s, o0, s0, C::BO, C::BS, nst);
+        auto phys = [&](int64_t ks) { const int64_t t = ks + rot; return t >= nst ? t - nst : t; };
 #pragma unroll
-        for (int i = 0; i < NB - 1; ++i) dma_stage<C>(bufs[i], pl, p, i < nst ? i : nst - 1, pw);
+        for (int i = 0; i < NB - 1; ++i)
+            dma_stage<C>(bufs[i], pl, p, phys(i < nst ? i : nst - 1), pw);
         const int64_t nfull = nst - nst % NB;
         int64_t s = 0;
         for (; s < nfull; s += NB) {
@@ -746,7 +765,8 @@ gemm_pc_kernel(DmaArgs p, float* __restrict__ y, int64_t tiles_o, int64_t tiles_
                 __builtin_amdgcn_s_waitcnt(waitcnt_imm(C::kDmaPerStage * (NB - 2), 0));
                 barrier_only();
                 const int64_t ahead = s + i + NB - 1;
-                dma_stage<C>(bufs[(i + NB - 1) % NB], pl, p, ahead < nst ? ahead : nst - 1, pw);
+                dma_stage<C>(bufs[(i + NB - 1) % NB], pl, p, phys(ahead < nst ? ahead : nst - 1),
+                             pw);
             }
         }
 #pragma unroll
@@ -755,7 +775,8 @@ gemm_pc_kernel(DmaArgs p, float* __restrict__ y, int64_t tiles_o, int64_t tiles_
                 __builtin_amdgcn_s_waitcnt(waitcnt_imm(C::kDmaPerStage * (NB - 2), 0));
                 barrier_only();
                 const int64_t ahead = s + i + NB - 1;
-                dma_stage<C>(bufs[(i + NB - 1) % NB], pl, p, ahead < nst ? ahead : nst - 1, pw);
+                dma_stage<C>(bufs[(i + NB - 1) % NB], pl, p, phys(ahead < nst ? ahead : nst - 1),
+                             pw);
             }
         // the trailing prefetches must land before the workgroup's LDS is released
         __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
@@ -1914,6 +1935,7 @@ gemm_skinny16_kernel(DmaArgs p, float* __restrict__ y)
     const int s0 = wave * nst / kS16Waves, n = (wave + 1) * nst / kS16Waves - s0;
 
     const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(p.wq, p.out * 16 * k);
+    (void)rw;                                   // used by the device-only LDS loads
     const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(p.xq, p.S * (F8 ? 32 : 16) * k);
     const __amdgpu_buffer_rsrc_t rwe =
         buffer_rsrc(p.we, TS ? ((p.out + 31) / 32) * 256 * k8 : p.out * k);
@@ -2075,6 +2097,7 @@ gemm_linear16_kernel(DmaArgs p, const uint16_t* __restrict__ x, int64_t ldx,
     const int s0 = wave * NPER;
 
     const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(p.wq, p.out * 16 * k);
+    (void)rw;                                   // used by the device-only LDS loads
     const __amdgpu_buffer_rsrc_t rwe =
         buffer_rsrc(p.we, TS ? ((p.out + 31) / 32) * 256 * k8 : p.out * k);
     // 32-bit offsets (out * 16 k < 2^32): a 64-bit product truncated here made the compiler
@@ -2112,6 +2135,7 @@ gemm_linear16_kernel(DmaArgs p, const uint16_t* __restrict__ x, int64_t ldx,
     for (int i = 0; i < NPER; ++i) {
         const int ks = s0 + i < nst ? s0 + i : nst - 1;
         uint8_t* dst = panel + (s0 + i < nst ? ks : nst) * kS16Stage;
+        (void)dst;
 #if defined(__HIP_DEVICE_COMPILE__)   // the LDS-load builtins exist for the device only
 #pragma unroll
         for (int q = 0; q < 2; ++q)
