@@ -287,12 +287,13 @@ def measure(name, args):
     # at most four tokens the layer also runs as one kernel (batq_linear_w4a4): timed the
     # same way, for the record beside the two kernels (same outputs)
     t_lin = None
-    if (not w4a8 and form == "gpk" and not rms and epilogue == "f32"
-            and S <= bq.LINEAR_FUSED_TOKENS and k % 8 == 0 and k <= 512):
+    if (form == "gpk" and not rms and epilogue == "f32" and S <= bq.LINEAR_FUSED_TOKENS
+            and k % 8 == 0 and k <= 512 and (not w4a8 or S * k <= bq.LINEAR_W4A8_FUSED_BLOCKS)):
+        lin = bq.linear_w4a8_raw if w4a8 else bq.linear_w4a4_raw
+
         def launch_lin(j, s=sh):
             x, _, _, wq, we, y = ptr[j]
-            return bq.linear_w4a4_raw(x, S, N, N, pA, pB, pr1, pr2, wq, we, out, y, 0, 0,
-                                      layout, s)
+            return lin(x, S, N, N, pA, pB, pr1, pr2, wq, we, out, y, 0, 0, layout, s)
         t_lin = time_graph(stream, launch_lin, args.warmup + 3 * K, K, R)
 
     if args.copy_calibration:
@@ -374,8 +375,9 @@ def measure(name, args):
         # fp32 outputs (the factors and ratios are a few KB)
         b_lin = S * N * 2 + out * (N // 2 + k) + 4 * S * out
         rec["linear_one_kernel"] = {
-            "kernel": "gemm_linear16_kernel (transform + clip + MXFP4 of the token rows "
-                      "inside the few-token GEMM)",
+            "kernel": "gemm_linear16_kernel (transform + clip + "
+                      + ("MXFP8" if w4a8 else "MXFP4") + " of the token rows inside the "
+                      "few-token GEMM)",
             "avg_us": round(t_lin * 1e6, 3), "two_kernels_us": round((t_k1 + t_k2) * 1e6, 3),
             "bound": "hbm", "achieved": round(b_lin / t_lin / 1e9, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(b_lin / t_lin / 1e9 / HBM_PEAK_GBS, 4),

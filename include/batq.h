@@ -359,6 +359,35 @@ batq_status batq_linear_w4a4(const uint16_t* x, int64_t S, int64_t N, int64_t ld
                              batq_scale_layout layout, int64_t out, float* y, uint8_t* xq,
                              uint8_t* xe, void* stream);
 
+/* Largest S * N/32 the one-kernel W4A8 layer takes (its MXFP8 token codes live in LDS). */
+#define BATQ_LINEAR_W4A8_FUSED_BLOCKS 768
+
+/*
+ * The W4A8 linear layer in one call: y = the W4A8 product of batq_quantize_act_mxfp8(x)
+ * with the prepared MXFP4 weights (gist.science summary, section 4: the W4A8KV16 setting,
+ * activations transformed and clipped online as in W4A4, then MXFP8).  For
+ * 1 <= S <= BATQ_LINEAR_FUSED_TOKENS with S * N/32 <= BATQ_LINEAR_W4A8_FUSED_BLOCKS (and
+ * N/32 % 8 == 0) one kernel can do it: the few-token W4A8 GEMM encodes the token rows to
+ * MXFP8 itself with the quantiser's arithmetic, so the codes are exactly
+ * batq_quantize_act_mxfp8's and y has batq_gemm_w4a8's accuracy.  In that range the one
+ * kernel runs and xq8 / xe are not used (it measured faster than the two calls on every
+ * shape it takes; they may be NULL).  Otherwise batq_quantize_act_mxfp8 then
+ * batq_gemm_w4a8 run, with xq8 (dev u8 [S, N]) / xe (sized as that call's e in `layout`) as
+ * the caller's workspace.  The same inputs give the same result on every call.
+ *   x, S, N, ldx, A, B, r_min, r_max: as batq_quantize_act_mxfp8
+ *   wq, we, layout, out, y: as batq_gemm_w4a8 (N % 256 == 0, else BATQ_ERR_UNSUPPORTED;
+ *           y dev fp32 [S, out], 16-byte aligned)
+ *   xq8, xe: dev workspace or NULL (BATQ_ERR_NULL when needed and missing,
+ *           BATQ_ERR_UNSUPPORTED when the one-kernel path declines aligned-scale or size
+ *           limits and no workspace is given)
+ * Does not allocate or synchronise.
+ */
+batq_status batq_linear_w4a8(const uint16_t* x, int64_t S, int64_t N, int64_t ldx,
+                             const float* A, const float* B, const float* r_min,
+                             const float* r_max, const uint8_t* wq, const uint8_t* we,
+                             batq_scale_layout layout, int64_t out, float* y, uint8_t* xq8,
+                             uint8_t* xe, void* stream);
+
 /*
  * Host: clip ratios r[i] = fp32(1 / (1 + exp(-alpha[i]))) evaluated in binary64 and rounded
  * once (daily-arxiv summary, clipping bullet: the sigmoid keeps each ratio in (0, 1);

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_entry_point(bq):
                             "batq_gemm_w4a4_out", "batq_gemm_w4a8_out",
                             "batq_quantize_act_rmsnorm", "batq_quantize_kv",
                             "batq_transform_rows", "batq_dequantize_rows",
-                            "batq_linear_w4a4"])
+                            "batq_linear_w4a4", "batq_linear_w4a8"])
     L = ctypes.CDLL(bq.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -211,6 +211,21 @@ def test_linear_argument_errors(bq):
     assert f(D, 4, 256, 256, D, D, D, D, D, D, 8, 0) == NULL                # y
     assert f(D, 5, 256, 256, D, D, D, D, D, D, 8, D) == NULL                # workspace needed
     assert f(D, 2, 32 * 520, 32 * 520, D, D, D, D, D, D, 8, D) == NULL      # k > 512: too
+    assert f(D, 4, 256, 200, D, D, D, D, D, D, 8, D) == SHAPE               # ldx < N
+    assert f(D, 4, 256, 260, D, D, D, D, D, D, 8, D) == ALIGN               # ldx % 8
+    assert f(D, 4, 256, 256, D, D + 4, D, D, D, D, 8, D) == ALIGN           # B
+    assert f(D, 4, 256, 256, D, D, D, D, D, D, 8, D, layout=7) == UNSUPPORTED
+
+
+def test_linear_w4a8_argument_errors(bq):
+    f = bq.linear_w4a8_raw
+    # (x, S, N, ldx, A, B, r_min, r_max, wq, we, out, y, xq8, xe)
+    assert f(D, 4, 48, 64, D, D, D, D, D, D, 8, D) == SHAPE                # N % 32
+    assert f(0, 0, 256, 256, 0, 0, 0, 0, 0, 0, 8, 0) == OK                  # no tokens
+    assert f(D, 4, 256, 256, D, D, D, D, D, D, 8, 0) == NULL                # y
+    assert f(D, 5, 256, 256, D, D, D, D, D, D, 8, D) == NULL                # workspace needed
+    assert f(D, 4, 32 * 256, 32 * 256, D, D, D, D, D, D, 8, D) == NULL      # S k > 768: too
+    assert f(D, 2, 32 * 520, 32 * 520, D, D, D, D, D, D, 8, D) == NULL      # k > 512
     assert f(D, 4, 256, 200, D, D, D, D, D, D, 8, D) == SHAPE               # ldx < N
     assert f(D, 4, 256, 260, D, D, D, D, D, D, 8, D) == ALIGN               # ldx % 8
     assert f(D, 4, 256, 256, D, D + 4, D, D, D, D, 8, D) == ALIGN           # B

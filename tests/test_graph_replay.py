@@ -45,6 +45,7 @@ def test_graph_replays_match_eager(bq):
     se = torch.empty((bq.scale_bytes(3, N, T),), dtype=torch.uint8, device="cuda")
     ys = torch.empty((3, out), dtype=torch.float32, device="cuda")
     yl = torch.empty_like(ys)
+    yl8 = torch.empty_like(ys)
     cq = torch.zeros((300, N // 2), dtype=torch.uint8, device="cuda")
     ce = torch.zeros((300, N // 32), dtype=torch.uint8, device="cuda")
     tr = torch.empty((S, N), dtype=torch.bfloat16, device="cuda")
@@ -57,10 +58,11 @@ def test_graph_replays_match_eager(bq):
         bq.quantize_act(xs, A, B, r1, r2, q=sq, e=se, layout=T)       # few-token GEMM
         bq.gemm_w4a4(sq, se, wq, we, y=ys, layout=T)
         bq.linear_w4a4(xs, A, B, r1, r2, wq, we, layout=T, y=yl)     # one-kernel linear
+        bq.linear_w4a8(xs, A, B, r1, r2, wq, we, layout=T, y=yl8)    # and its W4A8 form
         bq.quantize_kv(x, slots, bq.KV_MXFP4, A, B, r1, r2, cq, ce)
         bq.transform_rows(x, A, B, out_dtype=torch.bfloat16, y=tr)
 
-    outs = (xq, xe, y4, xq8, xe8, y8, sq, se, ys, yl, cq, ce, tr)
+    outs = (xq, xe, y4, xq8, xe8, y8, sq, se, ys, yl, yl8, cq, ce, tr)
     # every output starts from zeros, here and before each replay: the bytes no call writes
     # (the tiled scale buffers' padding rows) then compare equal too
     for t in outs:
@@ -87,7 +89,7 @@ def test_graph_replays_match_eager(bq):
         g.replay()
         torch.cuda.synchronize()
         for name, got, want in zip(("xq", "xe", "y4", "xq8", "xe8", "y8", "sq", "se", "ys",
-                                    "yl", "cq", "ce", "tr"), outs, eager):
+                                    "yl", "yl8", "cq", "ce", "tr"), outs, eager):
             assert torch.equal(got.view(torch.uint8) if got.dtype == torch.bfloat16 else got,
                                want.view(torch.uint8) if want.dtype == torch.bfloat16 else want), \
                 f"replay {rep}: {name}"

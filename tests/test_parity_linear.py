@@ -1,7 +1,8 @@
-"""GPU parity of batq_linear_w4a4, the linear layer in one call: for 1..4 tokens one kernel
-(the few-token GEMM encoding the token rows itself), otherwise quantiser + GEMM through the
-caller's workspace; both against the oracle's quantisation, weight preparation and fp64
-product within the GEMM's accumulation bound (1e-5 * sum|terms|)."""
+"""GPU parity of batq_linear_w4a4 and batq_linear_w4a8, the linear layer in one call: for 1..4
+tokens one kernel (the few-token GEMM encoding the token rows itself), otherwise quantiser +
+GEMM through the caller's workspace; against the oracle's quantisation, weight preparation
+and fp64 product within the GEMM's accumulation bound (1e-5 * sum|terms|; W4A8 with the
+hardware's product truncation added, and against the truncation model within 1e-5)."""
 import numpy as np
 import pytest
 
@@ -122,3 +123,70 @@ def test_linear_one_kernel_matches_two_calls(bq):
     y3 = bq.linear_w4a4(*args, wq, we, layout=T)
     torch.cuda.synchronize()
     assert torch.equal(y1, y3)
+
+
+# ----------------------------------------------------------------------------------------
+# W4A8: MXFP8 token rows
+# ----------------------------------------------------------------------------------------
+
+def run_linear8(bq, L, layout, workspace=True):
+    import torch
+    S, N = L.x_bits.shape
+    wq, we = bq.prepare_weight(f32_to_device(L.W), L.A, L.B, layout=layout)
+    x = bf16_to_device(L.x_bits)
+    A, B = f32_to_device(L.A), f32_to_device(L.B)
+    r1 = f32_to_device(bq.clip_ratios(L.alpha_min))
+    r2 = f32_to_device(bq.clip_ratios(L.alpha_max))
+    if workspace:
+        y = bq.linear_w4a8(x, A, B, r1, r2, wq, we, layout=layout)
+    else:
+        out = wq.shape[0]
+        y = torch.empty((S, out), dtype=torch.float32, device="cuda")
+        st = bq.linear_w4a8_raw(x.data_ptr(), S, N, x.stride(0), A.data_ptr(), B.data_ptr(),
+                                r1.data_ptr(), r2.data_ptr(), wq.data_ptr(), we.data_ptr(), out,
+                                y.data_ptr(), 0, 0, layout=layout,
+                                stream=torch.cuda.current_stream().cuda_stream)
+        assert st == 0, bq.status_string(st)
+    torch.cuda.synchronize()
+    return to_host(y)
+
+
+def check_linear8(orc, L, y, what):
+    from tests.mfma_fp8_model import HW_TRUNCATION_REL, gemm_w4a8_mfma_model
+    rmin, rmax = orc.clip_ratio(L.alpha_min), orc.clip_ratio(L.alpha_max)
+    xq8, xe = orc.quantize_act_fp8(L.x_bits, L.A, L.B, rmin, rmax, nthreads=ORACLE_THREADS)
+    wq, we = orc.prepare_weight(L.W, L.A, L.B, nthreads=ORACLE_THREADS)
+    y_ref, t_ref = orc.gemm_w4a8(xq8, xe, wq, we, nthreads=ORACLE_THREADS)
+    assert_gemm_close(y, y_ref, t_ref, rel=HW_TRUNCATION_REL + 1e-5, what=what)
+    y_hw = gemm_w4a8_mfma_model(xq8, xe, wq, we, rows=np.arange(y.shape[0]))
+    assert_gemm_close(y, y_hw, t_ref, what=what + " (model)")
+
+
+@pytest.mark.parametrize("tiled", [True, False])
+@pytest.mark.parametrize("S,N,out", [
+    (1, 256, 33),               # one stage, ragged out
+    (1, 16384, 4100),           # k = 512 (S k = 512)
+    (2, 12288, 300),            # S k = 768, the largest the one kernel takes
+    (3, 8192, 130),
+    (4, 6144, 4096),            # S k = 768
+])
+def test_linear8_one_kernel(bq, orc, S, N, out, tiled):
+    L = wl.make_layer(wl.custom("lin8", S, N, out, seed=(111, S, N, out),
+                                outliers=("channels_uniform", 8, 20.0, 100.0)))
+    layout = bq.SCALES_MFMA_TILED if tiled else bq.SCALES_ROW_MAJOR
+    print(f"[linear8 one-kernel] S={S} N={N} out={out} tiled={tiled}", flush=True)
+    y = run_linear8(bq, L, layout, workspace=False)
+    check_linear8(orc, L, y, f"w4a8 one kernel S={S} N={N} out={out} tiled={tiled}")
+
+
+@pytest.mark.parametrize("S,N,out", [
+    (5, 4096, 96),              # more tokens than the one kernel takes
+    (4, 8192, 64),              # S k = 1024 > 768
+    (4, 4096, 12300),           # one kernel, the workspace unused
+    (1, 2048, 40),
+])
+def test_linear8_with_workspace(bq, orc, S, N, out):
+    L = wl.make_layer(wl.custom("lin8w", S, N, out, seed=(112, S, N, out)))
+    y = run_linear8(bq, L, bq.SCALES_MFMA_TILED, workspace=True)
+    check_linear8(orc, L, y, f"w4a8 workspace S={S} N={N} out={out}")
+

@@ -35,6 +35,7 @@ SIGNATURES = {
     "batq_transform_rows": [_P, _I, _I64, _I64, _I64, _P, _P, _P, _I, _P],
     "batq_dequantize_rows": [_P, _P, _I64, _I64, _I, _P, _I64, _P, _I, _P],
     "batq_linear_w4a4": [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _I, _I64, _P, _P, _P, _P],
+    "batq_linear_w4a8": [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _I, _I64, _P, _P, _P, _P],
     "batq_clip_ratios": [_P, _I64, _P],
     "batq_weight_factors": [_P, _P, _I64, _P, _P],
     "batq_status_string": [_I],
@@ -48,6 +49,7 @@ SCALES_MFMA_TILED = 1
 
 # batq_linear_w4a4 runs in one kernel up to this many tokens (BATQ_LINEAR_FUSED_TOKENS)
 LINEAR_FUSED_TOKENS = 4
+LINEAR_W4A8_FUSED_BLOCKS = 768
 
 # Element types (batq_out_type) of GEMM outputs and of transformed / dequantised rows.
 OUT_F32 = 0
@@ -162,6 +164,12 @@ def quantize_act_rmsnorm_raw(x, S, N, ldx, gamma, eps, A, B, r_min, r_max, q, e,
 def linear_w4a4_raw(x, S, N, ldx, A, B, r_min, r_max, wq, we, out, y, xq=0, xe=0,
                     layout=SCALES_ROW_MAJOR, stream=0) -> int:
     return lib().batq_linear_w4a4(x, S, N, ldx, A, B, r_min, r_max, wq, we, layout, out, y, xq,
+                                  xe, stream)
+
+
+def linear_w4a8_raw(x, S, N, ldx, A, B, r_min, r_max, wq, we, out, y, xq8=0, xe=0,
+                    layout=SCALES_ROW_MAJOR, stream=0) -> int:
+    return lib().batq_linear_w4a8(x, S, N, ldx, A, B, r_min, r_max, wq, we, layout, out, y, xq8,
                                   xe, stream)
 
 
@@ -352,11 +360,33 @@ def gemm_w4a8(xq8, xe, wq, we, y=None, layout=SCALES_ROW_MAJOR, stream=None):
     return y
 
 
-def linear_w4a8(x, A, B, r_min, r_max, wq, we, layout=SCALES_ROW_MAJOR, stream=None):
-    """The W4A8 pass: MXFP8 activations, then the W4A8 GEMM against the prepared MXFP4
-    weights (scales `we` in `layout`)."""
-    xq8, xe = quantize_act_mxfp8(x, A, B, r_min, r_max, layout=layout, stream=stream)
-    return gemm_w4a8(xq8, xe, wq, we, layout=layout, stream=stream)
+def linear_w4a8(x, A, B, r_min, r_max, wq, we, layout=SCALES_ROW_MAJOR, y=None, stream=None):
+    """The W4A8 layer through batq_linear_w4a8: transform, clip and MXFP8 of the activations,
+    then the W4A8 product with the prepared weights (scales `we` in `layout`): one kernel up
+    to LINEAR_FUSED_TOKENS tokens and LINEAR_W4A8_FUSED_BLOCKS token blocks, else the two
+    calls with a workspace allocated here."""
+    import torch
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    S, N = x.shape
+    out = wq.shape[0]
+    assert wq.dtype == torch.uint8 and wq.is_contiguous() and wq.shape[1] * 2 == N
+    assert we.dtype == torch.uint8 and we.is_contiguous() and we.numel() == scale_bytes(out, N, layout)
+    for t in (A, B, r_min, r_max):
+        assert t.dtype == torch.float32 and t.is_contiguous()
+    if y is None:
+        y = torch.empty((S, out), dtype=torch.float32, device=x.device)
+    assert y.dtype == torch.float32 and y.shape == (S, out) and y.is_contiguous()
+    k = N // 32
+    xq8 = xe = None
+    if not (S <= LINEAR_FUSED_TOKENS and k <= 512 and k % 8 == 0
+            and S * k <= LINEAR_W4A8_FUSED_BLOCKS):
+        xq8 = torch.empty((S, N), dtype=torch.uint8, device=x.device)
+        xe = _scale_tensor(S, N, layout, x.device)
+    _check("batq_linear_w4a8", linear_w4a8_raw(
+        _ptr(x), S, N, x.stride(0), _ptr(A), _ptr(B), _ptr(r_min), _ptr(r_max), _ptr(wq),
+        _ptr(we), out, _ptr(y), _ptr(xq8) if xq8 is not None else 0,
+        _ptr(xe) if xe is not None else 0, layout, _stream(stream)))
+    return y
 
 
 # ---------------------------------------------------------------------------------------

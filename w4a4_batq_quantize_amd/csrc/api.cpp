@@ -220,6 +220,42 @@ BATQ_API batq_status batq_linear_w4a4(const uint16_t* x, int64_t S, int64_t N, i
     return batq_gemm_w4a4(xq, xe, wq, we, layout, S, N, out, y, stream);
 }
 
+BATQ_API batq_status batq_linear_w4a8(const uint16_t* x, int64_t S, int64_t N, int64_t ldx,
+                                      const float* A, const float* B, const float* r_min,
+                                      const float* r_max, const uint8_t* wq, const uint8_t* we,
+                                      batq_scale_layout layout, int64_t out, float* y,
+                                      uint8_t* xq8, uint8_t* xe, void* stream)
+{
+    if (S < 0 || N < 0 || out < 0 || N % 32 != 0) return BATQ_ERR_SHAPE;
+    if (S == 0 || out == 0) return BATQ_OK;
+    if (!valid_layout(layout)) return BATQ_ERR_UNSUPPORTED;
+    if (N == 0) return batq_gemm_w4a8(nullptr, nullptr, nullptr, nullptr, layout, S, 0, out, y,
+                                      stream);
+    const int64_t k = N / 32;
+    const bool can_fuse = S <= BATQ_LINEAR_FUSED_TOKENS && k <= 512 && k % 8 == 0 &&
+                          S * k <= BATQ_LINEAR_W4A8_FUSED_BLOCKS;
+    if (!y || !x || !A || !B || !r_min || !r_max || !wq || !we) return BATQ_ERR_NULL;
+    if (!can_fuse && (!xq8 || !xe)) return BATQ_ERR_NULL;
+    if (ldx < N || mul_overflows(S, ldx) || mul_overflows(S, out) || mul_overflows(out, N))
+        return BATQ_ERR_SHAPE;
+    if (ldx % 8 != 0 || !aligned(x, 16) || !aligned(B, 16) || !aligned(y, 16) ||
+        !aligned(wq, 16) || !aligned(A, 4) || !aligned(r_min, 4) || !aligned(r_max, 4))
+        return BATQ_ERR_ALIGN;
+    // the one kernel wherever it applies: measured faster than the two calls on every
+    // shape it takes (its token rows are at most 768 blocks)
+    if (can_fuse) {
+        const hipError_t err = batq::launch_linear16_w4a8(
+            x, S, k, ldx, A, B, r_min, r_max, wq, we, layout == BATQ_SCALES_MFMA_TILED, out, y,
+            as_stream(stream));
+        if (err != hipErrorNotSupported) return from_hip(err);
+        if (!xq8 || !xe) return BATQ_ERR_UNSUPPORTED;
+    }
+    const batq_status st =
+        batq_quantize_act_mxfp8(x, S, N, ldx, A, B, r_min, r_max, xq8, xe, layout, stream);
+    if (st != BATQ_OK) return st;
+    return batq_gemm_w4a8(xq8, xe, wq, we, layout, S, N, out, y, stream);
+}
+
 BATQ_API batq_status batq_quantize_act_mxfp8(const uint16_t* x, int64_t S, int64_t N,
                                              int64_t ldx, const float* A, const float* B,
                                              const float* r_min, const float* r_max,

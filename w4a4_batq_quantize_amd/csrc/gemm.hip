@@ -2076,17 +2076,21 @@ gemm_skinny16_kernel(DmaArgs p, float* __restrict__ y)
 // buffers are static arrays, apart from the dynamic panel, so the encoder's stores do not
 // wait for the weight DMA.  Token fragments and scales then come from LDS (scale bytes in
 // plain order, one per lane).  S k <= kLin16MaxSK, so that panel and buffers fit in LDS.
-constexpr int kLin16MaxSK = 1536;
+// F8: the tokens encoded to MXFP8 (E4M3, 32 bytes per block: the W4A8 layer), fragments in
+// gemm_skinny16_kernel's E4M3 lane layout, S k <= kLin16MaxSK8.
+constexpr int kLin16MaxSK = 1536, kLin16MaxSK8 = 768;
 
-template <bool TS, int NPER>
+template <bool TS, int NPER, bool F8 = false>
 __global__ void __launch_bounds__(64 * kS16Waves)
 gemm_linear16_kernel(DmaArgs p, const uint16_t* __restrict__ x, int64_t ldx,
                      const float* __restrict__ A, const float* __restrict__ B,
                      const float* __restrict__ r_min, const float* __restrict__ r_max,
                      float* __restrict__ y)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t xcode[kLin16MaxSK * 16];
-    __shared__ __attribute__((aligned(16))) uint8_t xscale[kLin16MaxSK];
+    constexpr int kMaxSK = F8 ? kLin16MaxSK8 : kLin16MaxSK;
+    constexpr int kCB = F8 ? 32 : 16;                             // code bytes per block
+    __shared__ __attribute__((aligned(16))) uint8_t xcode[kMaxSK * kCB];
+    __shared__ __attribute__((aligned(16))) uint8_t xscale[kMaxSK];
     extern __shared__ __attribute__((aligned(16))) uint8_t panel[];   // nst stages + scratch
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -2114,7 +2118,7 @@ gemm_linear16_kernel(DmaArgs p, const uint16_t* __restrict__ x, int64_t ldx,
                             : wrow * (uint32_t)k;
 
     // token loads first: block q = t k + b, lanes of the workgroup in turn
-    constexpr int kPer = (kLin16MaxSK + 64 * kS16Waves - 1) / (64 * kS16Waves);
+    constexpr int kPer = (kMaxSK + 64 * kS16Waves - 1) / (64 * kS16Waves);
     const uint32_t tid = threadIdx.x, k32 = (uint32_t)k, nblk = (uint32_t)(S * k);
     uint4 xv[kPer][4];
     mx::BlockParams bp[kPer];
@@ -2165,8 +2169,11 @@ gemm_linear16_kernel(DmaArgs p, const uint16_t* __restrict__ x, int64_t ldx,
                     xf[8 * i + 2 * d + 1] = mx::bf16_hi(w4[d]);
                 }
             }
-            const mx::BlockCode<false> c = mx::encode_block<true, false, 0>(xf, A, bp[m], b);
-            *reinterpret_cast<uint4*>(xcode + 16 * q) = make_uint4(c.w[0], c.w[1], c.w[2], c.w[3]);
+            const mx::BlockCode<F8> c = mx::encode_block<true, F8, 0>(xf, A, bp[m], b);
+            *reinterpret_cast<uint4*>(xcode + kCB * q) = make_uint4(c.w[0], c.w[1], c.w[2], c.w[3]);
+            if constexpr (F8)
+                *reinterpret_cast<uint4*>(xcode + kCB * q + 16) =
+                    make_uint4(c.w[F8 ? 4 : 0], c.w[F8 ? 5 : 1], c.w[F8 ? 6 : 2], c.w[F8 ? 7 : 3]);
             xscale[q] = (uint8_t)c.ebyte;
         }
     }
@@ -2177,7 +2184,7 @@ gemm_linear16_kernel(DmaArgs p, const uint16_t* __restrict__ x, int64_t ldx,
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
 
     const uint32_t xr = (uint32_t)(lr < S ? lr : S - 1);
-    const uint8_t* xrow = xcode + 16 * xr * k32;
+    const uint8_t* xrow = xcode + kCB * xr * k32;
     const uint8_t* xsrow = xscale + xr * k32;
     v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
     const int key = (lr >> 1) & 7;
@@ -2190,17 +2197,27 @@ gemm_linear16_kernel(DmaArgs p, const uint16_t* __restrict__ x, int64_t ldx,
             for (int j = 0; j < 2; ++j) {
                 const int blk = 8 * ks + 4 * j + lg;
                 const uint4 a = *reinterpret_cast<const uint4*>(row + 16 * ((4 * j + lg) ^ key));
-                const uint4 u = *reinterpret_cast<const uint4*>(xrow + 16 * blk);
                 const v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
-                const v8i bv = {(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
+                v8i bv;
+                if constexpr (F8) {
+                    // E4M3 lane group g: 16-byte units g and 4 + g of the K-step's 128 bytes
+                    const uint8_t* kr = xrow + kCB * (8 * ks + 4 * j);
+                    const uint4 u = *reinterpret_cast<const uint4*>(kr + 16 * lg);
+                    const uint4 v = *reinterpret_cast<const uint4*>(kr + 64 + 16 * lg);
+                    bv = v8i{(int)u.x, (int)u.y, (int)u.z, (int)u.w, (int)v.x, (int)v.y, (int)v.z, (int)v.w};
+                } else {
+                    const uint4 u = *reinterpret_cast<const uint4*>(xrow + kCB * blk);
+                    bv = v8i{(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
+                }
                 const uint32_t wsc = TS ? ws[i].x >> (8 * (lg >> 1)) : (j ? ws[i].y : ws[i].x) >> (8 * lg);
                 const uint32_t xsc = xsrow[blk];
+                constexpr int kFmtX = F8 ? 0 : kFmtE2M1;
                 if (j == 0)
                     acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        av, bv, acc, kFmtE2M1, kFmtE2M1, 0, (int)wsc, 0, (int)xsc);
+                        av, bv, acc, kFmtE2M1, kFmtX, 0, (int)wsc, 0, (int)xsc);
                 else
                     acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        av, bv, acc, kFmtE2M1, kFmtE2M1, TS ? 2 : 0, (int)wsc, 0, (int)xsc);
+                        av, bv, acc, kFmtE2M1, kFmtX, TS ? 2 : 0, (int)wsc, 0, (int)xsc);
             }
         }
     }
@@ -2361,7 +2378,7 @@ hipError_t launch_gemm_w4a8(const uint8_t* xq8, const uint8_t* xe, const uint8_t
 
 namespace batq {
 
-template <bool TS, int NPER>
+template <bool TS, int NPER, bool F8>
 static void launch_linear16_n(const DmaArgs& p, const uint16_t* x, int64_t ldx, const float* A,
                               const float* B, const float* r_min, const float* r_max, float* y,
                               hipStream_t stream)
@@ -2369,26 +2386,26 @@ static void launch_linear16_n(const DmaArgs& p, const uint16_t* x, int64_t ldx, 
     const int64_t tiles = (p.out + kS16Rows - 1) / kS16Rows;
     const size_t panel = (size_t)(p.k / kStageBlocks + 1) * kS16Stage;   // + the scratch slot
     const size_t red = (size_t)kS16Waves * 4 * 64 * 4;
-    hipLaunchKernelGGL((gemm_linear16_kernel<TS, NPER>), dim3((unsigned)tiles),
+    hipLaunchKernelGGL((gemm_linear16_kernel<TS, NPER, F8>), dim3((unsigned)tiles),
                        dim3(64 * kS16Waves), panel > red ? panel : red, stream, p, x, ldx, A, B,
                        r_min, r_max, y);
 }
 
-template <bool TS>
+template <bool TS, bool F8>
 static void launch_linear16(const DmaArgs& p, const uint16_t* x, int64_t ldx, const float* A,
                             const float* B, const float* r_min, const float* r_max, float* y,
                             hipStream_t stream)
 {
     const int nper = (int)((p.k / kStageBlocks + kS16Waves - 1) / kS16Waves);
     switch (nper) {
-    case 1: launch_linear16_n<TS, 1>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
-    case 2: launch_linear16_n<TS, 2>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
-    case 3: launch_linear16_n<TS, 3>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
-    case 4: launch_linear16_n<TS, 4>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
-    case 5: launch_linear16_n<TS, 5>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
-    case 6: launch_linear16_n<TS, 6>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
-    case 7: launch_linear16_n<TS, 7>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
-    default: launch_linear16_n<TS, 8>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
+    case 1: launch_linear16_n<TS, 1, F8>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
+    case 2: launch_linear16_n<TS, 2, F8>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
+    case 3: launch_linear16_n<TS, 3, F8>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
+    case 4: launch_linear16_n<TS, 4, F8>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
+    case 5: launch_linear16_n<TS, 5, F8>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
+    case 6: launch_linear16_n<TS, 6, F8>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
+    case 7: launch_linear16_n<TS, 7, F8>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
+    default: launch_linear16_n<TS, 8, F8>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
     }
 }
 
@@ -2407,9 +2424,9 @@ hipError_t launch_linear_skinny(const uint16_t* x, int64_t S, int64_t k, int64_t
         // 16-row workgroups, the whole panel in flight
         if ((out + kS16Rows - 1) / kS16Rows > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
         if (tiled_scales)
-            launch_linear16<true>(p, x, ldx, A, B, r_min, r_max, y, stream);
+            launch_linear16<true, false>(p, x, ldx, A, B, r_min, r_max, y, stream);
         else
-            launch_linear16<false>(p, x, ldx, A, B, r_min, r_max, y, stream);
+            launch_linear16<false, false>(p, x, ldx, A, B, r_min, r_max, y, stream);
         return hipGetLastError();
     }
     const int64_t tiles_o = (out + 31) / 32;
@@ -2421,6 +2438,26 @@ hipError_t launch_linear_skinny(const uint16_t* x, int64_t S, int64_t k, int64_t
     else
         hipLaunchKernelGGL(gemm_linear_skinny_kernel<false>, grid, block, 0, stream, p, x, ldx,
                            A, B, r_min, r_max, y);
+    return hipGetLastError();
+}
+
+hipError_t launch_linear16_w4a8(const uint16_t* x, int64_t S, int64_t k, int64_t ldx,
+                                const float* A, const float* B, const float* r_min,
+                                const float* r_max, const uint8_t* wq, const uint8_t* we,
+                                bool tiled_scales, int64_t out, float* y, hipStream_t stream)
+{
+    if (S < 1 || S > kLinTokens || k < 1 || k > kS16MaxK || k % kStageBlocks != 0 ||
+        S * k > kLin16MaxSK8)
+        return hipErrorNotSupported;
+    const uintptr_t salign = tiled_scales ? 256 : 8;
+    if ((reinterpret_cast<uintptr_t>(we) % salign) != 0 || out * 16 * k >= (1LL << 32))
+        return hipErrorNotSupported;
+    if ((out + kS16Rows - 1) / kS16Rows > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    const DmaArgs p{nullptr, nullptr, wq, we, S, k, out, nullptr, 0};
+    if (tiled_scales)
+        launch_linear16<true, true>(p, x, ldx, A, B, r_min, r_max, y, stream);
+    else
+        launch_linear16<false, true>(p, x, ldx, A, B, r_min, r_max, y, stream);
     return hipGetLastError();
 }
 

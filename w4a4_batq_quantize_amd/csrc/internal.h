@@ -57,6 +57,14 @@ hipError_t launch_linear_skinny(const uint16_t* x, int64_t S, int64_t k, int64_t
                                 const float* r_max, const uint8_t* wq, const uint8_t* we,
                                 bool tiled_scales, int64_t out, float* y, hipStream_t stream);
 
+// The W4A8 layer for at most four tokens in one kernel (MXFP8 token rows encoded in the
+// 16-row few-token W4A8 GEMM); hipErrorNotSupported outside S <= 4, k <= 512, k % 8 == 0,
+// S k <= 768, the scale alignment or the 32-bit weight offsets.
+hipError_t launch_linear16_w4a8(const uint16_t* x, int64_t S, int64_t k, int64_t ldx,
+                                const float* A, const float* B, const float* r_min,
+                                const float* r_max, const uint8_t* wq, const uint8_t* we,
+                                bool tiled_scales, int64_t out, float* y, hipStream_t stream);
+
 // MXFP4 x MXFP4 -> fp32 GEMM, y[S, out] = dq(x)[S, N] dq(w)[out, N]^T; both scale
 // arrays in the same layout (tiled_scales: MFMA-tiled, else row-major).
 // Epilogue (both GEMMs): res, when not null, is a bf16 [S, out] residual added in fp32;
