@@ -577,7 +577,7 @@ def main():
     ap.add_argument("--config", default="q_proj")
     ap.add_argument("--rotate-bytes", type=float, default=2.0e9,
                     help="total bytes of the rotated buffer sets")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=16.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for counter scaling)")
