@@ -48,6 +48,8 @@ def test_gemm_random_operands_ragged(bq, orc, S, N, out):
     # its dispatch rule, the 32-row kernel with the same token count (k = 384, out = 6144)
     (1, 256, 17), (16, 256, 40), (2, 16384, 4100), (16, 4096, 4096), (1, 2048, 12290),
     (9, 8192, 700), (5, 12288, 6144),
+    # 33..64 tokens: two token halves per 32-row tile (out <= 4096) or the two-column kernel
+    (40, 2048, 4100), (64, 1024, 4096), (33, 1024, 4200), (64, 512, 8200),
 ])
 def test_gemm_few_tokens_both_layouts(bq, orc, S, N, out, tiled):
     import torch

@@ -160,6 +160,8 @@ def test_gemm8_random_operands_ragged(bq, orc, S, N, out, tiled):
     # at most 16 tokens: the 16-row kernel with E4M3 token fragments (one K stage; k = 512
     # with ragged out; a full round) and, past its dispatch rule, the 32-row kernel
     (1, 256, 17), (16, 4096, 1000), (3, 16384, 4100), (8, 12288, 6144), (4, 4096, 12300),
+    # 33..64 tokens: two token halves per tile (out <= 4096) or the two-column kernel
+    (40, 2048, 4096), (64, 1024, 300), (33, 1024, 4200),
 ])
 def test_gemm8_few_tokens(bq, orc, S, N, out, tiled):
     xq8, xe = wl.random_mxfp8(S, N, seed=(79, S, N, out))

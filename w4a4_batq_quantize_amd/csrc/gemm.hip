@@ -1264,7 +1264,17 @@ gemm_skinny_kernel(DmaArgs p, float* __restrict__ y)
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lr = lane & 31, lg = lane >> 5;
-    const int64_t o0 = (int64_t)blockIdx.x * 32;
+    // more than 32 tokens with one token column: two workgroups per 32-row tile, one per
+    // 32-token half, the pair on one XCD (workgroup i runs on XCD i % 8) so that both read
+    // the tile's weight lines from the same L2
+    int64_t tile = blockIdx.x, tb = 0;
+    if (TN == 1 && p.S > 32) {
+        const int64_t g = (int64_t)blockIdx.x >> 4, r = blockIdx.x & 15;
+        tile = g * 8 + (r & 7);
+        tb = 32 * (r >> 3);
+        if (tile * 32 >= p.out) return;                   // the grid is rounded up to 16
+    }
+    const int64_t o0 = tile * 32;
     const int64_t k = p.k;
     const int nst = (int)(k / kStageBlocks);
     const int s0 = (int)((int64_t)wave * nst / kSplit), s1 = (int)((int64_t)(wave + 1) * nst / kSplit);
@@ -1273,7 +1283,8 @@ gemm_skinny_kernel(DmaArgs p, float* __restrict__ y)
     const uint32_t wrow = (uint32_t)(o0 + lr < p.out ? o0 + lr : p.out - 1);
     uint32_t xrow[TN];
 #pragma unroll
-    for (int b = 0; b < TN; ++b) xrow[b] = (uint32_t)(32 * b + lr < p.S ? 32 * b + lr : p.S - 1);
+    for (int b = 0; b < TN; ++b)
+        xrow[b] = (uint32_t)(tb + 32 * b + lr < p.S ? tb + 32 * b + lr : p.S - 1);
     const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(p.wq, p.out * 16 * k);
     const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(p.xq, p.S * (F8 ? 32 : 16) * k);
     const int64_t k8 = k / 8;
@@ -1304,7 +1315,7 @@ gemm_skinny_kernel(DmaArgs p, float* __restrict__ y)
 #pragma unroll
         for (int q = 0; q < (F8 ? 8 : 4); ++q) {
             const int r = F8 ? 4 * q + (lane >> 4) : 8 * q + (lane >> 3);
-            const int64_t row = 32 * b + r < p.S ? 32 * b + r : p.S - 1;
+            const int64_t row = tb + 32 * b + r < p.S ? tb + 32 * b + r : p.S - 1;
             xoff[b][q] = F8 ? (uint32_t)(row * 32 * k + 16 * ((lane & 15) ^ (r & 15)))
                             : (uint32_t)(row * 16 * k + 16 * ((lane & 7) ^ ((r >> 1) & 7)));
         }
@@ -1363,7 +1374,7 @@ gemm_skinny_kernel(DmaArgs p, float* __restrict__ y)
             for (int w = 1; w < kSplit; ++w) t += rb[w][4 * g + i][lane];
             v[i] = t;
         }
-        const int64_t srow = 32 * b + lr;
+        const int64_t srow = tb + 32 * b + lr;
         const int64_t o = o0 + 8 * g + 4 * lg;
         if (srow < p.S && (p.res || p.out_bf16)) {
             if (o < p.out)
@@ -1908,6 +1919,16 @@ inline size_t s16_lds_bytes(int64_t k)
 // (out = 12288): 7-14% faster with E2M1 tokens, 9-15% with one E4M3 token (3-4% slower
 // with eight, whose 32-byte rows every workgroup reads again).
 constexpr int kNumCUs = 256;                                  // MI355X
+
+// 33..64 tokens: the one-column 32-row kernel on two token halves per tile when the doubled
+// grid still fits in one round of workgroups (out <= 4096), else the two-column kernel.
+// Measured (S = 33, 48, 64; N = 4096, 12288): at out = 4096 the halves are 8-13% faster with
+// E2M1 tokens and 20-30% with E4M3 (16 waves instead of 6 or 4, all CUs); at out = 12288
+// they take two rounds instead of one and are up to 24% slower (E2M1).
+inline bool skinny_halves(int64_t S, int64_t tiles32)
+{
+    return S > 32 && 2 * tiles32 <= kNumCUs;
+}
 inline bool use_skinny16(int64_t S, int64_t k, int64_t out, bool f8)
 {
     if (S > kS16MaxTokens || k > kS16MaxK) return false;
@@ -2278,14 +2299,17 @@ hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq,
     if (dma_ok && S <= 64) {
         // few tokens: weight streaming, K split across the waves of a 32-row workgroup
         const int64_t tiles_o = (out + 31) / 32;
-        if (tiles_o > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+        if (tiles_o > 0x7FFFFFFF / 2) return hipErrorInvalidConfiguration;
         const dim3 grid((unsigned)tiles_o);
-        if (S <= 32) {
+        if (S <= 32 || skinny_halves(S, tiles_o)) {
+            // one token column; 33..64 tokens as two halves per tile (the grid rounded up
+            // to whole groups of 8 tiles)
+            const dim3 grid1((unsigned)(S <= 32 ? tiles_o : (tiles_o + 7) / 8 * 16));
             const dim3 block(64 * SkinnyCfg<1, false>::waves);
             if (tiled_scales)
-                hipLaunchKernelGGL((gemm_skinny_kernel<1, true>), grid, block, 0, stream, p, y);
+                hipLaunchKernelGGL((gemm_skinny_kernel<1, true>), grid1, block, 0, stream, p, y);
             else
-                hipLaunchKernelGGL((gemm_skinny_kernel<1, false>), grid, block, 0, stream, p, y);
+                hipLaunchKernelGGL((gemm_skinny_kernel<1, false>), grid1, block, 0, stream, p, y);
         } else {
             const dim3 block(64 * SkinnyCfg<2, false>::waves);
             if (tiled_scales)
@@ -2344,14 +2368,15 @@ hipError_t launch_gemm_w4a8(const uint8_t* xq8, const uint8_t* xe, const uint8_t
     if (S <= 64 && (tiled_scales || s8)) {
         // few tokens: the weight-streaming kernel with E4M3 token codes
         const int64_t tiles_w = (out + 31) / 32;
-        if (tiles_w > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+        if (tiles_w > 0x7FFFFFFF / 2) return hipErrorInvalidConfiguration;
         const dim3 grid((unsigned)tiles_w);
-        if (S <= 32) {
+        if (S <= 32 || skinny_halves(S, tiles_w)) {
+            const dim3 grid1((unsigned)(S <= 32 ? tiles_w : (tiles_w + 7) / 8 * 16));
             const dim3 block(64 * SkinnyCfg<1, true>::waves);
             if (tiled_scales)
-                hipLaunchKernelGGL((gemm_skinny_kernel<1, true, true>), grid, block, 0, stream, p, y);
+                hipLaunchKernelGGL((gemm_skinny_kernel<1, true, true>), grid1, block, 0, stream, p, y);
             else
-                hipLaunchKernelGGL((gemm_skinny_kernel<1, false, true>), grid, block, 0, stream, p, y);
+                hipLaunchKernelGGL((gemm_skinny_kernel<1, false, true>), grid1, block, 0, stream, p, y);
         } else {
             const dim3 block(64 * SkinnyCfg<2, true>::waves);
             if (tiled_scales)
