@@ -212,12 +212,13 @@ def sample_rows(S):
 
 
 @pytest.mark.parametrize("tiled", [False, True])
-@pytest.mark.parametrize("name", ["tiny", "q_proj", "down_proj", "sweep_s8_n4096",
-                                  "sweep_s16384_n12288"])
+@pytest.mark.parametrize("name", ["tiny", "q_proj", "down_proj", "sweep_s1_n12288",
+                                  "sweep_s8_n4096", "sweep_s16384_n12288"])
 def test_linear_w4a8_end_to_end(bq, orc, name, tiled):
-    """Seeded layer -> HIP MXFP8 quantise + HIP weight prep + HIP W4A8 GEMM, against the
-    oracle's MXFP8 quantisation, weight preparation and fp64 W4A8 product on sampled token
-    rows (every output column of those rows)."""
+    """Seeded layer -> HIP weight prep + batq_linear_w4a8 (one kernel for the one-token
+    decode layer, else HIP MXFP8 quantise + HIP W4A8 GEMM), against the oracle's MXFP8
+    quantisation, weight preparation and fp64 W4A8 product on sampled token rows (every
+    output column of those rows)."""
     import torch
     L = wl.make_layer(name)
     S, N, out = L.cfg.S, L.cfg.N, L.cfg.out
