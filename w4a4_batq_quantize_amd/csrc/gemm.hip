@@ -1,23 +1,28 @@
-// MXFP4 x MXFP4 -> fp32 GEMM on gfx950 scaled MFMA (the W4A4 linear layer).
+// MXFP4 x MXFP4 (and E2M1 x E4M3) -> fp32 GEMMs on gfx950 scaled MFMA: the product of the
+// W4A4 (W4A8) linear layer, and the layer in one kernel for a few tokens.
 //
-// y[s][o] = sum_n dq(x)[s][n] dq(w)[o][n] with dq = e2m1(code) * 2^(e-127) per 32-element
-// block.  The contraction runs on the scaled MFMA instructions with both operands in E2M1
-// (format code 4): each lane supplies 32 consecutive K values (16 bytes) of one row together
-// with the E8M0 scale of exactly that 32-element block, so MX blocks map onto lanes one to
-// one and the block scales are applied inside the instruction.
+// y[s][o] = sum_n dq(x)[s][n] dq(w)[o][n] with dq = code value * 2^(e-127) per 32-element
+// block.  The contraction runs on the scaled MFMA instructions: each lane supplies the K
+// values of one MX block of one row (16 bytes of E2M1, or 32 bytes of E4M3 gathered as the
+// instruction lays them out) together with the E8M0 scale of exactly that block, so blocks
+// map onto lanes one to one and the block scales are applied inside the instruction.
 //
-// The MFMA row operand is the weight tile (out dimension) and the column operand the
-// activation tile (token dimension), so every group of four accumulator registers is four
-// consecutive output features of one token: one 16-byte store into row-major y.
-//
-// Two kernels:
-//  - gemm_dma_kernel, for N % 256 == 0 with 8-byte-aligned scale arrays (all the layer
-//    shapes of interest): V_MFMA_SCALE_F32_32X32X64_F8F6F4 (on gfx950 the FP4 32x32x64
-//    form runs at twice the rate of the FP4 16x16x128 form, measured), operands moved
-//    HBM/L2 -> LDS by global_load_lds_dwordx4 without passing through registers, three LDS
-//    stages in flight;
+// Kernels, by token count S (the launchers below choose):
+//  - gemm_pc_kernel / gemm_dma_kernel (S > 64; MFMA-tiled / row-major scales):
+//    V_MFMA_SCALE_F32_32X32X64_F8F6F4 on 256 (out) x 128 (token) tiles, operands moved
+//    HBM/L2 -> LDS by buffer_load ... lds without passing through registers, three LDS
+//    stages; producer waves issue the DMA and consumer waves the MFMAs in the first;
+//  - gemm_w4a8_kernel (S > 64, E4M3 tokens): the same tile shape and DMA with mixed formats;
+//  - gemm_skinny16_kernel (S <= 16, by a workgroup-rounds rule) and gemm_skinny_kernel
+//    (S <= 64 otherwise): weight streaming, 16 or 32 output rows per workgroup and K split
+//    across its waves;
+//  - gemm_linear16_kernel / gemm_linear_skinny_kernel: the few-token GEMM that encodes its
+//    token rows itself (the whole layer in one kernel, S <= 4);
 //  - gemm_generic_kernel for any other N (ragged K) or alignment: the 16x16x128 form with
 //    register-staged, bounds-checked loads.
+// In the tiled kernels the activation tile is the MFMA row operand and the weight tile the
+// column operand, so a lane's accumulators are one output feature of 16 tokens and every
+// dword store instruction writes whole 128-byte lines of y.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
