@@ -340,9 +340,10 @@ batq_status batq_dequantize_rows(const uint8_t* q, const uint8_t* e, int64_t src
  * rows itself, with the quantiser's arithmetic, so the codes are exactly
  * batq_quantize_act's and y agrees with the two-call path within the GEMM's accumulation
  * bound (its K split, and so its fp32 summation order, differs).  In that range xq / xe may
- * be NULL, and the one kernel runs; when they are given, the library runs whichever of the
- * two paths is faster for the shape (measured: the one kernel while S * N/32 <= 1536 and
- * S * N/32 * ceil(out / 16) <= 196608, the token blocks all its workgroups encode).
+ * be NULL, and the one kernel runs.  When they are given, the library runs whichever of the
+ * two paths is faster for the shape (measured: the one kernel while S <= 16,
+ * S * N/32 <= 1536 and S * N/32 * ceil(out / 16) <= 196608, the token blocks all its
+ * workgroups encode), also for 4 < S <= 16.
  * Otherwise the two calls run, with xq / xe as the caller's workspace for the activation
  * codes and scales (sized as batq_quantize_act's q and e in `layout`).  Either path gives
  * the same result for the same inputs on every call.

@@ -92,7 +92,9 @@ def test_linear_two_steps(bq, orc, S, N, out):
 
 @pytest.mark.parametrize("S,N,out", [
     (1, 4096, 96), (3, 16384, 64),        # one kernel
+    (5, 4096, 96), (16, 1024, 130),       # one kernel for more than 4 tokens (small S k)
     (4, 12288, 2064), (2, 16384, 6200),   # two calls: S k ceil(out/16) beyond 196608
+    (8, 4096, 4096),                      # two calls: S k ceil(out/16) = 262144
 ])
 def test_linear_with_workspace_either_path(bq, orc, S, N, out):
     """With a workspace the library picks a path by shape (the one kernel, or the two calls

@@ -197,10 +197,12 @@ BATQ_API batq_status batq_linear_w4a4(const uint16_t* x, int64_t S, int64_t N, i
     const bool can_fuse = S <= BATQ_LINEAR_FUSED_TOKENS && k <= 512 && k % 8 == 0;
     if (!y || !x || !A || !B || !r_min || !r_max || !wq || !we) return BATQ_ERR_NULL;
     if (!can_fuse && (!xq || !xe)) return BATQ_ERR_NULL;
-    // with a workspace, the one kernel where it measured faster than the two calls: every
-    // 16-row workgroup encodes the S k token blocks, so the total encoding work decides
-    const bool fused =
-        can_fuse && (!xq || !xe || (S * k <= 1536 && S * k * ((out + 15) / 16) <= 196608));
+    // with a workspace, the one kernel where it measured faster than the two calls (up to
+    // 16 tokens on 16-row workgroups): every workgroup encodes the S k token blocks, so the
+    // total encoding work decides
+    const bool small = S <= 16 && k <= 512 && k % 8 == 0 && S * k <= 1536 &&
+                       S * k * ((out + 15) / 16) <= 196608;
+    const bool fused = (can_fuse && (!xq || !xe)) || small;
     if (ldx < N || mul_overflows(S, ldx) || mul_overflows(S, out) || mul_overflows(out, N))
         return BATQ_ERR_SHAPE;
     if (ldx % 8 != 0 || !aligned(x, 16) || !aligned(B, 16) || !aligned(y, 16) ||

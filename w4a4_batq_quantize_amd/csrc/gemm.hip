@@ -2444,7 +2444,9 @@ hipError_t launch_linear_skinny(const uint16_t* x, int64_t S, int64_t k, int64_t
                                 const float* r_max, const uint8_t* wq, const uint8_t* we,
                                 bool tiled_scales, int64_t out, float* y, hipStream_t stream)
 {
-    if (S < 1 || S > kLinTokens || k < 1 || k > kLinMaxK || k % kStageBlocks != 0)
+    // up to 4 tokens any k <= 512; up to 16 (one MFMA token column) on 16-row workgroups
+    if (S < 1 || S > kS16MaxTokens || k < 1 || k > kLinMaxK || k % kStageBlocks != 0 ||
+        (S > kLinTokens && S * k > kLin16MaxSK))
         return hipErrorNotSupported;
     const uintptr_t salign = tiled_scales ? 256 : 8;
     if ((reinterpret_cast<uintptr_t>(we) % salign) != 0 || out * 16 * k >= (1LL << 32))
