@@ -2103,11 +2103,13 @@ gemm_skinny16_kernel(DmaArgs p, float* __restrict__ y)
 // wait for the weight DMA.  Token fragments and scales then come from LDS (scale bytes in
 // plain order, one per lane).  S k <= kLin16MaxSK, so that panel and buffers fit in LDS.
 // F8: the tokens encoded to MXFP8 (E4M3, 32 bytes per block: the W4A8 layer), fragments in
-// gemm_skinny16_kernel's E4M3 lane layout, S k <= kLin16MaxSK8.
+// gemm_skinny16_kernel's E4M3 lane layout, S k <= kLin16MaxSK8.  W: waves per workgroup
+// (16 when one round of workgroups covers `out`: the encoding is spread over twice the
+// lanes, measured 7-9% faster there; 8 otherwise, where 16 measured 3-7% slower).
 constexpr int kLin16MaxSK = 1536, kLin16MaxSK8 = 768;
 
-template <bool TS, int NPER, bool F8 = false>
-__global__ void __launch_bounds__(64 * kS16Waves)
+template <bool TS, int NPER, bool F8 = false, int W = kS16Waves>
+__global__ void __launch_bounds__(64 * W)
 gemm_linear16_kernel(DmaArgs p, const uint16_t* __restrict__ x, int64_t ldx,
                      const float* __restrict__ A, const float* __restrict__ B,
                      const float* __restrict__ r_min, const float* __restrict__ r_max,
@@ -2144,13 +2146,13 @@ gemm_linear16_kernel(DmaArgs p, const uint16_t* __restrict__ x, int64_t ldx,
                             : wrow * (uint32_t)k;
 
     // token loads first: block q = t k + b, lanes of the workgroup in turn
-    constexpr int kPer = (kMaxSK + 64 * kS16Waves - 1) / (64 * kS16Waves);
+    constexpr int kPer = (kMaxSK + 64 * W - 1) / (64 * W);
     const uint32_t tid = threadIdx.x, k32 = (uint32_t)k, nblk = (uint32_t)(S * k);
     uint4 xv[kPer][4];
     mx::BlockParams bp[kPer];
 #pragma unroll
     for (int m = 0; m < kPer; ++m) {
-        const uint32_t q = tid + (uint32_t)m * 64 * kS16Waves;
+        const uint32_t q = tid + (uint32_t)m * 64 * W;
         if (q < nblk) {
             const uint32_t t = q / k32, b = q - t * k32;
             bp[m] = mx::load_block_params<true, 0>(B, r_min, r_max, b);
@@ -2182,7 +2184,7 @@ gemm_linear16_kernel(DmaArgs p, const uint16_t* __restrict__ x, int64_t ldx,
     // encode the token blocks into LDS (codes row-major, scale bytes in plain order)
 #pragma unroll
     for (int m = 0; m < kPer; ++m) {
-        const uint32_t q = tid + (uint32_t)m * 64 * kS16Waves;
+        const uint32_t q = tid + (uint32_t)m * 64 * W;
         if (q < nblk) {
             const uint32_t t = q / k32, b = q - t * k32;
             float xf[32];
@@ -2260,7 +2262,7 @@ gemm_linear16_kernel(DmaArgs p, const uint16_t* __restrict__ x, int64_t ldx,
         for (int i = 0; i < 4; ++i) {
             float t = red[0][i][lane];
 #pragma unroll
-            for (int w = 1; w < kS16Waves; ++w) t += red[w][i][lane];
+            for (int w = 1; w < W; ++w) t += red[w][i][lane];
             v[i] = t;
         }
         const int64_t o = o0 + 4 * lg;
@@ -2408,34 +2410,42 @@ hipError_t launch_gemm_w4a8(const uint8_t* xq8, const uint8_t* xe, const uint8_t
 
 namespace batq {
 
-template <bool TS, int NPER, bool F8>
+template <bool TS, int NPER, bool F8, int W>
 static void launch_linear16_n(const DmaArgs& p, const uint16_t* x, int64_t ldx, const float* A,
                               const float* B, const float* r_min, const float* r_max, float* y,
                               hipStream_t stream)
 {
     const int64_t tiles = (p.out + kS16Rows - 1) / kS16Rows;
     const size_t panel = (size_t)(p.k / kStageBlocks + 1) * kS16Stage;   // + the scratch slot
-    const size_t red = (size_t)kS16Waves * 4 * 64 * 4;
-    hipLaunchKernelGGL((gemm_linear16_kernel<TS, NPER, F8>), dim3((unsigned)tiles),
-                       dim3(64 * kS16Waves), panel > red ? panel : red, stream, p, x, ldx, A, B,
-                       r_min, r_max, y);
+    const size_t red = (size_t)W * 4 * 64 * 4;
+    hipLaunchKernelGGL((gemm_linear16_kernel<TS, NPER, F8, W>), dim3((unsigned)tiles),
+                       dim3(64 * W), panel > red ? panel : red, stream, p, x, ldx, A, B, r_min,
+                       r_max, y);
 }
 
-template <bool TS, bool F8>
+template <bool TS, bool F8, int W = kS16Waves>
 static void launch_linear16(const DmaArgs& p, const uint16_t* x, int64_t ldx, const float* A,
                             const float* B, const float* r_min, const float* r_max, float* y,
                             hipStream_t stream)
 {
-    const int nper = (int)((p.k / kStageBlocks + kS16Waves - 1) / kS16Waves);
+    // stages per wave: at most kS16MaxK / 8 / W (8 with 8 waves, 4 with 16)
+    constexpr int kMaxPer = kS16MaxK / kStageBlocks / W;
+    const int nper = (int)((p.k / kStageBlocks + W - 1) / W);
     switch (nper) {
-    case 1: launch_linear16_n<TS, 1, F8>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
-    case 2: launch_linear16_n<TS, 2, F8>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
-    case 3: launch_linear16_n<TS, 3, F8>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
-    case 4: launch_linear16_n<TS, 4, F8>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
-    case 5: launch_linear16_n<TS, 5, F8>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
-    case 6: launch_linear16_n<TS, 6, F8>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
-    case 7: launch_linear16_n<TS, 7, F8>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
-    default: launch_linear16_n<TS, 8, F8>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
+    case 1: launch_linear16_n<TS, 1, F8, W>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
+    case 2: launch_linear16_n<TS, 2, F8, W>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
+    case 3: launch_linear16_n<TS, 3, F8, W>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
+    case 4: launch_linear16_n<TS, 4, F8, W>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
+    default:
+        if constexpr (kMaxPer > 4) {
+            switch (nper) {
+            case 5: launch_linear16_n<TS, 5, F8, W>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
+            case 6: launch_linear16_n<TS, 6, F8, W>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
+            case 7: launch_linear16_n<TS, 7, F8, W>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
+            default: launch_linear16_n<TS, kMaxPer, F8, W>(p, x, ldx, A, B, r_min, r_max, y, stream); break;
+            }
+        }
+        break;
     }
 }
 
@@ -2455,10 +2465,15 @@ hipError_t launch_linear_skinny(const uint16_t* x, int64_t S, int64_t k, int64_t
     if (S * k <= kLin16MaxSK && k <= kS16MaxK) {
         // 16-row workgroups, the whole panel in flight
         if ((out + kS16Rows - 1) / kS16Rows > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-        if (tiled_scales)
-            launch_linear16<true, false>(p, x, ldx, A, B, r_min, r_max, y, stream);
-        else
-            launch_linear16<false, false>(p, x, ldx, A, B, r_min, r_max, y, stream);
+        // 16 waves when one round of workgroups covers out
+        const bool wide = (out + kS16Rows - 1) / kS16Rows <= kNumCUs;
+        if (tiled_scales) {
+            if (wide) launch_linear16<true, false, 16>(p, x, ldx, A, B, r_min, r_max, y, stream);
+            else launch_linear16<true, false>(p, x, ldx, A, B, r_min, r_max, y, stream);
+        } else {
+            if (wide) launch_linear16<false, false, 16>(p, x, ldx, A, B, r_min, r_max, y, stream);
+            else launch_linear16<false, false>(p, x, ldx, A, B, r_min, r_max, y, stream);
+        }
         return hipGetLastError();
     }
     const int64_t tiles_o = (out + 31) / 32;
