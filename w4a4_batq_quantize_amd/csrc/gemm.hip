@@ -2104,8 +2104,9 @@ gemm_skinny16_kernel(DmaArgs p, float* __restrict__ y)
 // plain order, one per lane).  S k <= kLin16MaxSK, so that panel and buffers fit in LDS.
 // F8: the tokens encoded to MXFP8 (E4M3, 32 bytes per block: the W4A8 layer), fragments in
 // gemm_skinny16_kernel's E4M3 lane layout, S k <= kLin16MaxSK8.  W: waves per workgroup
-// (16 when one round of workgroups covers `out`: the encoding is spread over twice the
-// lanes, measured 7-9% faster there; 8 otherwise, where 16 measured 3-7% slower).
+// (E2M1 tokens: 16 when one round of workgroups covers `out`, the encoding spread over
+// twice the lanes, measured 7-9% faster there, and 8 otherwise, where 16 measured 3-7%
+// slower; E4M3 tokens: 8, where 16 measured up to 25% slower).
 constexpr int kLin16MaxSK = 1536, kLin16MaxSK8 = 768;
 
 template <bool TS, int NPER, bool F8 = false, int W = kS16Waves>
