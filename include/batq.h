@@ -83,7 +83,7 @@ typedef enum batq_status {
     BATQ_ERR_NULL = 1,        /* a required pointer is NULL                                  */
     BATQ_ERR_SHAPE = 2,       /* negative size, N not a multiple of 32, ldx < N, or overflow */
     BATQ_ERR_ALIGN = 3,       /* a pointer or stride breaks the alignment stated below       */
-    BATQ_ERR_UNSUPPORTED = 4, /* valid for the format but beyond this build's limits         */
+    BATQ_ERR_UNSUPPORTED = 4, /* valid for the format but beyond the library's limits        */
     BATQ_ERR_SINGULAR = 5,    /* a GPK factor is not invertible                              */
     BATQ_ERR_HIP = 6          /* the HIP runtime reported an error (launch, copy, alloc)     */
 } batq_status;

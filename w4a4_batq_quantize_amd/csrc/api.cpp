@@ -86,7 +86,7 @@ BATQ_API const char* batq_status_string(batq_status status)
         case BATQ_ERR_NULL: return "BATQ_ERR_NULL: a required pointer is NULL";
         case BATQ_ERR_SHAPE: return "BATQ_ERR_SHAPE: invalid size";
         case BATQ_ERR_ALIGN: return "BATQ_ERR_ALIGN: misaligned pointer or stride";
-        case BATQ_ERR_UNSUPPORTED: return "BATQ_ERR_UNSUPPORTED: beyond this build's limits";
+        case BATQ_ERR_UNSUPPORTED: return "BATQ_ERR_UNSUPPORTED: valid for the format but beyond the library's limits";
         case BATQ_ERR_SINGULAR: return "BATQ_ERR_SINGULAR: a GPK factor is not invertible";
         case BATQ_ERR_HIP: return "BATQ_ERR_HIP: HIP runtime error";
     }
