@@ -3,9 +3,10 @@
 
 One step is one pass of the whole online path over one batch of synthetic input: the fused
 transform + clip + MXFP4 quantiser (K1) on the bf16 activations, then the MXFP4 x MXFP4
-scaled-MFMA GEMM (K2) against weights prepared offline.  Default workload: the
-q_proj-shaped layer S=2048 tokens, N=4096 in-features, out=4096 (Qwen3-8B shape), seeded
-synthetic data.
+scaled-MFMA GEMM (K2) against weights prepared offline.  Default workload: the largest
+layer configuration, the S=16384-token prefill through a down_proj-shaped layer (N=12288
+in-features, out=4096; Qwen3-8B shape), seeded synthetic data; the q_proj-shaped layer
+(S=2048, N=4096, out=4096) is timed beside it as a secondary record.
 
 Inputs are resident in HBM before timing starts.  Every step uses the next of R buffer sets
 (activations, codes, scales, prepared weights, output), with R chosen so the sets together
@@ -85,13 +86,29 @@ def measured_traffic(kernel: str, workload: str):
         return None
 
 
-def cpu_baseline(L, seconds, w4a8=False):
-    """The oracle as it stands, on a bounded sample of token rows of the same layer:
-    quantise the sampled rows and compute every output of those rows."""
+def host_cpu():
+    """The host's CPU model and logical core count, and the cores this process may use."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return model, os.cpu_count() or 1, max(1, usable or 1)
+
+
+def cpu_baseline(L, seconds, w4a8=False, runs=3):
+    """The oracle as it stands (plain C, OpenMP over token rows) on every core this process
+    may use, on a bounded sample of token rows of the same layer: quantise the sampled rows
+    and compute every output of those rows.  The sample is sized by a short probe so that
+    one run takes about `seconds`; the median of `runs` runs is reported."""
     import numpy as np
     from oracle import oracle
 
-    threads = max(1, min(16, os.cpu_count() or 1))
+    model, nproc, threads = host_cpu()
     S, N, out = L.cfg.S, L.cfg.N, L.cfg.out
     r1, r2 = oracle.clip_ratio(L.alpha_min), oracle.clip_ratio(L.alpha_max)
     wq, we = oracle.prepare_weight(L.W, L.A, L.B, nthreads=threads)   # offline, untimed
@@ -109,17 +126,22 @@ def cpu_baseline(L, seconds, w4a8=False):
     probe = min(S, threads)
     tq, tg = run(probe)
     rows = int(min(S, max(probe, probe * seconds / max(tq + tg, 1e-6))))
-    tq, tg = run(rows)
+    times = sorted((run(rows) for _ in range(runs)), key=lambda t: t[0] + t[1])
+    tq, tg = times[len(times) // 2]
     return {
         "value": round(k1_bytes(rows, N, 1.0 if w4a8 else 0.5) / tq / 1e9, 4),
         "unit": "GB/s",
         "gemm_value": round(k2_flops(rows, N, out) / tg / 1e12, 6),
         "gemm_unit": "TFLOP/s",
         "seconds": round(tq + tg, 2),
+        "runs": runs,
         "cores": threads,
+        "host_logical_cores": nproc,
+        "cpu_model": model,
         "kind": "oracle",
-        "sample": f"{rows} of {S} token rows: quantise them and compute all {out} outputs "
-                  f"of each (plain C oracle, OpenMP over rows)",
+        "sample": f"{rows} of {S} token rows (evenly spaced): quantise them and compute all "
+                  f"{out} outputs of each; plain C oracle, OpenMP over rows on {threads} "
+                  f"threads; median of {runs} runs",
     }
 
 
@@ -574,10 +596,15 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="q_proj")
+    ap.add_argument("--config", default="sweep_s16384_n12288",
+                    help="layer configuration (default: the S=16384 prefill, N=12288 -> 4096)")
+    ap.add_argument("--also", default="q_proj",
+                    help="a second configuration timed after the first and reported under "
+                         "'secondary' (kernel times and rooflines only); 'none' to skip")
     ap.add_argument("--rotate-bytes", type=float, default=2.0e9,
                     help="total bytes of the rotated buffer sets")
-    ap.add_argument("--cpu-seconds", type=float, default=16.0)
+    ap.add_argument("--cpu-seconds", type=float, default=6.0,
+                    help="target length of one CPU-baseline run (three runs are made)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for counter scaling)")
@@ -603,7 +630,8 @@ def main():
         sys.exit(2)
 
     if args.kv:
-        name = "kv_prefill" if args.config == "q_proj" else args.config
+        import workloads as wl
+        name = args.config if args.config in wl.KV_CONFIGS else "kv_prefill"
         rec, L, fmt = measure_kv(name, args)
         if not args.no_cpu_baseline:
             rec["cpu_baseline"] = cpu_baseline_kv(L, fmt, args.cpu_seconds)
@@ -616,6 +644,12 @@ def main():
             print(json.dumps(rec), flush=True)
         return
     rec, L = measure(args.config, args)
+    if args.also and args.also != "none" and args.also != args.config:
+        rec2, _ = measure(args.also, args)
+        rec["secondary"] = {k: rec2[k] for k in ("config", "kernel_us", "step_gpu_us",
+                                                 "gemm", "roofline_kernels")}
+        rec["secondary"]["value"] = rec2["value"]
+        rec["secondary"]["unit"] = rec2["unit"]
     if not args.no_cpu_baseline:
         if args.form == "gpk" and not args.rmsnorm:
             rec["cpu_baseline"] = cpu_baseline(L, args.cpu_seconds, args.precision == "w4a8")

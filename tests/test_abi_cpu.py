@@ -303,3 +303,53 @@ def test_tiled_scale_layout_definition():
     import w4a4_batq_quantize_amd as bq
     assert bq.scale_bytes(17, 4096, bq.SCALES_MFMA_TILED) == tiled_scale_bytes(17, 128)
     assert bq.scale_bytes(17, 4096, bq.SCALES_ROW_MAJOR) == 17 * 128
+
+
+def test_torch_wrappers_check_operands_before_any_launch(bq, monkeypatch):
+    """The torch-level wrappers check every operand's type, element count and device before
+    they reach the C ABI (which sees raw pointers only): a wrong size raises here, on the
+    host, and no library call is made."""
+    import torch
+    calls = []
+    monkeypatch.setattr(bq._binding, "lib", lambda: calls.append(1) or None)
+    S, N, out = 4, 256, 64
+    k = N // 32
+    x = torch.zeros((S, N), dtype=torch.bfloat16)
+    A, B = torch.eye(8), torch.eye(4).repeat(k, 1, 1).contiguous()
+    r = torch.ones(k)
+    bad = [
+        lambda: bq.quantize_act(x, A, B[:-1].contiguous(), r, r),                   # short B
+        lambda: bq.quantize_act(x, A, B, r[:-1], r),                                # short ratios
+        lambda: bq.quantize_act(x, A, B, r, r, e=torch.empty(S * k - 1, dtype=torch.uint8)),
+        lambda: bq.quantize_act(x, A, B, r, r, q=torch.empty((S, N // 2 - 1), dtype=torch.uint8)),
+        lambda: bq.quantize_act(x, A.double(), B, r, r),                            # dtype
+        lambda: bq.quantize_act(x, A.to("meta"), B, r, r),                          # device
+        lambda: bq.quantize_act_mxfp8(x, A, B, r, r, q8=torch.empty((S, N // 2), dtype=torch.uint8)),
+        lambda: bq.quantize_act_rmsnorm(x, torch.ones(N - 1), 1e-6, A, B, r, r),
+    ]
+    xq = torch.zeros((S, N // 2), dtype=torch.uint8)
+    xe = torch.zeros((S, k), dtype=torch.uint8)
+    wq = torch.zeros((out, N // 2), dtype=torch.uint8)
+    we = torch.zeros((out, k), dtype=torch.uint8)
+    bad += [
+        lambda: bq.gemm_w4a4(xq, xe, wq, we[:-1]),                                   # short we
+        lambda: bq.gemm_w4a4(xq, xe[:, :-1].contiguous(), wq, we),
+        lambda: bq.gemm_w4a4(xq, xe, wq, we, y=torch.empty((S, out - 1))),
+        lambda: bq.gemm_w4a4(xq, torch.zeros(S * k, dtype=torch.uint8), wq, we,
+                             layout=bq.SCALES_MFMA_TILED),              # tiled scales are padded
+        lambda: bq.gemm_w4a8(xq, xe, wq, we),                                       # E4M3 rows are N bytes
+        lambda: bq.linear_w4a4(x, A, B, r, r, wq, we[:-1]),
+        lambda: bq.linear_w4a4(x, A, B, r, r, wq, we, workspace=(xq[:-1], xe)),
+        lambda: bq.linear_w4a8(x, A, B, r, r, wq, we, workspace=(xq, xe)),          # xq8 is [S, N]
+        lambda: bq.gemm_out(xq, xe, wq, we, residual=torch.zeros((S, out + 1), dtype=torch.bfloat16)),
+        lambda: bq.transform_rows(x, A, B[:-1].contiguous()),
+        lambda: bq.quantize_kv(x, torch.zeros(S - 1, dtype=torch.int64), bq.KV_MXFP4, A, B, r, r,
+                               torch.zeros((8, N // 2), dtype=torch.uint8),
+                               torch.zeros((8, k), dtype=torch.uint8)),
+        lambda: bq.dequantize_rows(torch.zeros((8, N // 2), dtype=torch.uint8),
+                                   torch.zeros((8, k - 1), dtype=torch.uint8), bq.KV_MXFP4),
+    ]
+    for i, f in enumerate(bad):
+        with pytest.raises(AssertionError):
+            f()
+        assert not calls, f"case {i} reached the library"

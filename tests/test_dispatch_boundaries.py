@@ -33,20 +33,28 @@ GEMM_CASES = [
 ]
 
 
+# scale bytes of the random operands: 35 octaves, or 5 (every block then matters to every
+# output at the 1e-5 sum|terms| bound)
+SCALES = {"wide": (110, 145), "narrow": (125, 130)}
+
+
+@pytest.mark.parametrize("scales", list(SCALES))
 @pytest.mark.parametrize("w4a8", [False, True])
 @pytest.mark.parametrize("S,N,out", GEMM_CASES)
-def test_gemm_dispatch_boundaries(bq, orc, S, N, out, w4a8):
+def test_gemm_dispatch_boundaries(bq, orc, S, N, out, w4a8, scales):
     import torch
     seed = (121, S, N, out, int(w4a8))
-    xq, xe = (wl.random_mxfp8 if w4a8 else wl.random_mxfp4)(S, N, seed=seed)
-    wq, we = wl.random_mxfp4(out, N, seed=seed + (1,))
-    print(f"[dispatch gemm] S={S} N={N} out={out} w4a8={w4a8}", flush=True)
+    lo, hi = SCALES[scales]
+    xq, xe = (wl.random_mxfp8 if w4a8 else wl.random_mxfp4)(S, N, seed=seed, scale_lo=lo,
+                                                           scale_hi=hi)
+    wq, we = wl.random_mxfp4(out, N, seed=seed + (1,), scale_lo=lo, scale_hi=hi)
+    print(f"[dispatch gemm] S={S} N={N} out={out} w4a8={w4a8} scales={scales}", flush=True)
     f = bq.gemm_w4a8 if w4a8 else bq.gemm_w4a4
     y = f(u8_to_device(xq), u8_to_device(to_tiled_scales(xe)), u8_to_device(wq),
           u8_to_device(to_tiled_scales(we)), layout=bq.SCALES_MFMA_TILED)
     torch.cuda.synchronize()
     y = to_host(y)
-    what = f"S={S} N={N} out={out} w4a8={w4a8}"
+    what = f"S={S} N={N} out={out} w4a8={w4a8} scales={scales}"
     if w4a8:
         y_ref, t_ref = orc.gemm_w4a8(xq, xe, wq, we, nthreads=ORACLE_THREADS)
         assert_gemm_close(y, y_ref, t_ref, rel=HW_TRUNCATION_REL + 1e-5, what=what)

@@ -68,3 +68,34 @@ def test_fused_quantiser_is_rmsnorm_then_the_pinned_quantiser(orc):
     xh, _ = orc.rmsnorm(L.x_bits, gamma, 1e-6)
     q2, e2 = orc.clip_quantize_f32(orc.transform_f32(xh, L.A, L.B), rmin, rmax)
     assert np.array_equal(q, q2) and np.array_equal(e, e2)
+
+
+@pytest.mark.parametrize("squares,T_halving,T_sequential", [
+    # block sums of squares chosen so that fp32 rounding depends on the order of the additions
+    # (2^24 + 1 is a tie between 2^24 and 2^24 + 2 and rounds to the even 2^24; 2^24 + 3 a
+    # tie between 2^24 + 2 and 2^24 + 4, which is the even one):
+    #   halving (t[b] += t[b + h], h = K/2 .. 1), eight blocks:
+    #     h=4: 2^24+1 -> 2^24, 2, 2, 2;  h=2: 2^24+2, 4;  h=1: 2^24+6
+    #   sequential: every +1 onto 2^24 is a tie that rounds back to 2^24
+    ([2 ** 24, 1, 1, 1, 1, 1, 1, 1], 2 ** 24 + 6, 2 ** 24),
+    # six blocks, padded to eight with zero sums:
+    #     h=4: 2^24+1 -> 2^24, 1+1 = 2, 1, 1;  h=2: 2^24+1 -> 2^24, 3;  h=1: 2^24+3 -> 2^24+4
+    ([2 ** 24, 1, 1, 1, 1, 1], 2 ** 24 + 4, 2 ** 24),
+])
+def test_block_sums_are_added_by_halving(orc, squares, T_halving, T_sequential):
+    """The order in which the per-block sums of squares are added is part of the stated
+    arithmetic (halving over the zero-padded power-of-two count).  Rows whose sum rounds
+    differently under another order pin it: the expected scale is worked out by hand from
+    the sum above, then through fp32 division, square root and reciprocal (IEEE, correctly
+    rounded: numpy's float32 operations)."""
+    k = len(squares)
+    N = 32 * k
+    x = np.zeros((1, N), dtype=np.float32)
+    for b, sq in enumerate(squares):
+        x[0, 32 * b] = np.sqrt(sq)                   # one element per block: 2^12 or 1
+    _, r = orc.rmsnorm(bf16(x), np.ones(N, np.float32), 0.0)
+    f = np.float32
+    expect = f(1) / np.sqrt(f(T_halving) / f(N))
+    other = f(1) / np.sqrt(f(T_sequential) / f(N))
+    assert expect != other
+    assert r[0] == expect

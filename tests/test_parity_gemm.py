@@ -9,6 +9,12 @@ from tests.gpu_util import (ORACLE_THREADS, assert_gemm_close, bf16_to_device,
 
 pytestmark = pytest.mark.gpu
 
+# Scale bytes of the random operands: "wide" spans 35 octaves per operand (the sum |terms| of
+# an output is then set by its few largest-scale blocks), "narrow" 5 octaves, so that every
+# block's contribution is far above the 1e-5 sum|terms| bound and a misread code fragment or
+# scale byte anywhere shows.
+SCALES = {"wide": (110, 145), "narrow": (125, 130)}
+
 
 @pytest.fixture(scope="module")
 def bq():
@@ -26,6 +32,7 @@ def gpu_gemm(bq, xq, xe, wq, we):
     return to_host(y)
 
 
+@pytest.mark.parametrize("scales", list(SCALES))
 @pytest.mark.parametrize("S,N,out", [
     (1, 32, 1), (3, 96, 5), (17, 4096, 100), (129, 4192, 300), (200, 256, 257),
     (64, 12288, 64), (128, 4096, 128), (256, 1024, 384), (300, 640, 20),
@@ -33,14 +40,16 @@ def gpu_gemm(bq, xq, xe, wq, we):
     # shorter than the number of waves splitting K
     (45, 2048, 77), (64, 256, 33), (1, 8192, 4100), (32, 512, 96), (33, 1536, 1),
 ])
-def test_gemm_random_operands_ragged(bq, orc, S, N, out):
-    xq, xe = wl.random_mxfp4(S, N, seed=(7, S, N, out))
-    wq, we = wl.random_mxfp4(out, N, seed=(8, S, N, out))
+def test_gemm_random_operands_ragged(bq, orc, S, N, out, scales):
+    lo, hi = SCALES[scales]
+    xq, xe = wl.random_mxfp4(S, N, seed=(7, S, N, out), scale_lo=lo, scale_hi=hi)
+    wq, we = wl.random_mxfp4(out, N, seed=(8, S, N, out), scale_lo=lo, scale_hi=hi)
     y = gpu_gemm(bq, xq, xe, wq, we)
     y_ref, t_ref = orc.gemm(xq, xe, wq, we, nthreads=ORACLE_THREADS)
-    assert_gemm_close(y, y_ref, t_ref, what=f"S={S} N={N} out={out}")
+    assert_gemm_close(y, y_ref, t_ref, what=f"S={S} N={N} out={out} scales={scales}")
 
 
+@pytest.mark.parametrize("scales", list(SCALES))
 @pytest.mark.parametrize("tiled", [False, True])
 @pytest.mark.parametrize("S,N,out", [
     # at most 16 tokens: the 16-row kernel (one K stage over eight waves; the longest K it
@@ -51,21 +60,23 @@ def test_gemm_random_operands_ragged(bq, orc, S, N, out):
     # 33..64 tokens: two token halves per 32-row tile (out <= 4096) or the two-column kernel
     (40, 2048, 4100), (64, 1024, 4096), (33, 1024, 4200), (64, 512, 8200),
 ])
-def test_gemm_few_tokens_both_layouts(bq, orc, S, N, out, tiled):
+def test_gemm_few_tokens_both_layouts(bq, orc, S, N, out, tiled, scales):
     import torch
     from tests.gpu_util import to_tiled_scales
-    xq, xe = wl.random_mxfp4(S, N, seed=(77, S, N, out))
-    wq, we = wl.random_mxfp4(out, N, seed=(78, S, N, out))
+    lo, hi = SCALES[scales]
+    xq, xe = wl.random_mxfp4(S, N, seed=(77, S, N, out), scale_lo=lo, scale_hi=hi)
+    wq, we = wl.random_mxfp4(out, N, seed=(78, S, N, out), scale_lo=lo, scale_hi=hi)
     if tiled:
         xe_d, we_d = to_tiled_scales(xe), to_tiled_scales(we)
     else:
         xe_d, we_d = xe, we
-    print(f"[gemm few tokens] S={S} N={N} out={out} tiled={tiled}", flush=True)
+    print(f"[gemm few tokens] S={S} N={N} out={out} tiled={tiled} scales={scales}", flush=True)
     y = bq.gemm_w4a4(u8_to_device(xq), u8_to_device(xe_d), u8_to_device(wq), u8_to_device(we_d),
                      layout=bq.SCALES_MFMA_TILED if tiled else bq.SCALES_ROW_MAJOR)
     torch.cuda.synchronize()
     y_ref, t_ref = orc.gemm(xq, xe, wq, we, nthreads=ORACLE_THREADS)
-    assert_gemm_close(to_host(y), y_ref, t_ref, what=f"S={S} N={N} out={out} tiled={tiled}")
+    assert_gemm_close(to_host(y), y_ref, t_ref,
+                      what=f"S={S} N={N} out={out} tiled={tiled} scales={scales}")
 
 
 def test_gemm_zero_k_writes_zeros(bq):
@@ -122,21 +133,23 @@ def test_linear_end_to_end(bq, orc, name):
 # MFMA-tiled scale layout (padding bytes are E8M0 NaN: any use would poison a result)
 # ----------------------------------------------------------------------------------------
 
+@pytest.mark.parametrize("scales", list(SCALES))
 @pytest.mark.parametrize("S,N,out", [
     (1, 32, 1), (17, 4096, 100), (129, 4192, 300), (64, 12288, 64), (128, 4096, 128),
     (256, 1024, 384), (300, 2048, 520), (33, 256, 36),
     (50, 1024, 130), (2, 512, 31), (63, 4096, 64),
 ])
-def test_gemm_random_operands_tiled_scales(bq, orc, S, N, out):
+def test_gemm_random_operands_tiled_scales(bq, orc, S, N, out, scales):
     import torch
     from tests.gpu_util import to_tiled_scales
-    xq, xe = wl.random_mxfp4(S, N, seed=(17, S, N, out))
-    wq, we = wl.random_mxfp4(out, N, seed=(18, S, N, out))
+    lo, hi = SCALES[scales]
+    xq, xe = wl.random_mxfp4(S, N, seed=(17, S, N, out), scale_lo=lo, scale_hi=hi)
+    wq, we = wl.random_mxfp4(out, N, seed=(18, S, N, out), scale_lo=lo, scale_hi=hi)
     y = bq.gemm_w4a4(u8_to_device(xq), u8_to_device(to_tiled_scales(xe)), u8_to_device(wq),
                      u8_to_device(to_tiled_scales(we)), layout=bq.SCALES_MFMA_TILED)
     torch.cuda.synchronize()
     y_ref, t_ref = orc.gemm(xq, xe, wq, we, nthreads=ORACLE_THREADS)
-    assert_gemm_close(to_host(y), y_ref, t_ref, what=f"tiled S={S} N={N} out={out}")
+    assert_gemm_close(to_host(y), y_ref, t_ref, what=f"tiled S={S} N={N} out={out} {scales}")
 
 
 @pytest.mark.parametrize("name", ["q_proj", "gate_up", "down_proj", "sweep_s1_n12288",

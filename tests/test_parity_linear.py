@@ -24,7 +24,8 @@ def bq():
 
 def run_linear(bq, L, layout, ldx=None, workspace=True):
     """batq_linear_w4a4 on the layer; workspace=False calls the C entry with no workspace,
-    which takes the one-kernel path (the binding passes one and lets the library choose)."""
+    which takes the one-kernel path; workspace=True passes one and lets the library
+    choose."""
     import torch
     S, N = L.x_bits.shape
     wq, we = bq.prepare_weight(f32_to_device(L.W), L.A, L.B, layout=layout)
@@ -39,7 +40,10 @@ def run_linear(bq, L, layout, ldx=None, workspace=True):
     r1 = f32_to_device(bq.clip_ratios(L.alpha_min))
     r2 = f32_to_device(bq.clip_ratios(L.alpha_max))
     if workspace:
-        y = bq.linear_w4a4(x, A, B, r1, r2, wq, we, layout=layout)
+        # the caller's workspace: the library chooses between the one kernel and two calls
+        xq = torch.empty((S, N // 2), dtype=torch.uint8, device="cuda")
+        xe = torch.empty((bq.scale_bytes(S, N, layout),), dtype=torch.uint8, device="cuda")
+        y = bq.linear_w4a4(x, A, B, r1, r2, wq, we, layout=layout, workspace=(xq, xe))
     else:
         out = wq.shape[0]
         y = torch.empty((S, out), dtype=torch.float32, device="cuda")
@@ -76,6 +80,33 @@ def test_linear_one_kernel(bq, orc, S, N, out, ldx, tiled):
     y = run_linear(bq, L, layout, ldx=ldx, workspace=False)
     y_ref, t_ref = oracle_linear(orc, L)
     assert_gemm_close(y, y_ref, t_ref, what=f"S={S} N={N} out={out} tiled={tiled}")
+
+
+@pytest.mark.parametrize("tiled", [True, False])
+@pytest.mark.parametrize("S,N,out", [
+    (1, 4096, 12288),           # decode gate/up shape: 768 workgroups, 8 waves, 1 stage each
+    (3, 16384, 4112),           # 257 workgroups: 8 waves with 8 stages each (k = 512)
+    (1, 12288, 4112),           # 8 waves with 6 stages each (k = 384)
+])
+def test_linear_one_kernel_eight_waves(bq, orc, S, N, out, tiled):
+    """The one-kernel layer takes 16 waves when one round of 16-row workgroups covers out
+    (ceil(out/16) <= 256 CUs) and 8 otherwise: these shapes are on the 8-wave side, with no
+    workspace, across the per-wave stage counts."""
+    L = wl.make_layer(wl.custom("lin8w", S, N, out, seed=(105, S, N, out)))
+    layout = bq.SCALES_MFMA_TILED if tiled else bq.SCALES_ROW_MAJOR
+    print(f"[linear one-kernel 8 waves] S={S} N={N} out={out} tiled={tiled}", flush=True)
+    y = run_linear(bq, L, layout, workspace=False)
+    y_ref, t_ref = oracle_linear(orc, L)
+    assert_gemm_close(y, y_ref, t_ref, what=f"8 waves S={S} N={N} out={out} tiled={tiled}")
+
+
+def test_linear_workspace_one_kernel_wide_out(bq, orc):
+    """With a workspace, S = 1, N = 4096, out = 12288 still takes the one kernel (S k
+    ceil(out/16) = 98304 is within the rule) on its 8-wave side."""
+    L = wl.make_layer(wl.custom("lin8ws", 1, 4096, 12288, seed=106))
+    y = run_linear(bq, L, bq.SCALES_MFMA_TILED, workspace=True)
+    y_ref, t_ref = oracle_linear(orc, L)
+    assert_gemm_close(y, y_ref, t_ref, what="workspace one kernel out=12288")
 
 
 @pytest.mark.parametrize("S,N,out", [

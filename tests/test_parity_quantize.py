@@ -81,7 +81,7 @@ def test_act_parity_prefill_sampled_rows(bq, orc, name):
     (37, 4192, 4256, 3),     # k=131: ragged against 64-block waves, padded rows
     (130, 2048, 2048, 4),    # several rows per wave and ragged row count
     (5, 64 * 32 * 3 + 32, 6208, 5),   # k=193
-    # shapes large enough for the row-group kernels (2 and 4 rows per lane), ragged tails
+    # larger shapes: many rounds of waves, ragged row counts and block counts, padded rows
     (2047, 4096, 4104, 6),
     (1025, 4160, 4160, 7),   # k=130
     (2049, 12288, 12288, 8),

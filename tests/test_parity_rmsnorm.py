@@ -101,3 +101,43 @@ def test_rmsnorm_quantize_edge_rows(bq, orc):
     q, e = run(bq, L, gamma, 0.0)
     q_ref, e_ref, zero = oracle(orc, L, gamma, 0.0)
     assert_codes_equal(q, e, q_ref, e_ref, zero, what="edge eps=0")
+
+
+@pytest.mark.parametrize("squares,T_halving,T_sequential", [
+    ([2 ** 24, 1, 1, 1, 1, 1, 1, 1], 2 ** 24 + 6, 2 ** 24),
+    ([2 ** 24, 1, 1, 1, 1, 1], 2 ** 24 + 4, 2 ** 24),
+])
+def test_rmsnorm_block_sum_order_on_gpu(bq, orc, squares, T_halving, T_sequential):
+    """The rows of the oracle's order pin (block sums of squares whose fp32 total depends on
+    the order of the additions), with identity factors and unit ratios, and gamma of one
+    element set so that its code is 4 under the halving order's scale r and 6 under the
+    sequential order's: the code then shows which order the kernel used."""
+    import torch
+    k = len(squares)
+    N = 32 * k
+    x = np.zeros((1, N), dtype=np.float32)
+    for b, sq in enumerate(squares):
+        x[0, 32 * b] = np.sqrt(sq)
+    f = np.float32
+    r_h = f(1) / np.sqrt(f(T_halving) / f(N))
+    r_s = f(1) / np.sqrt(f(T_sequential) / f(N))
+    # gamma for element 32 (x = 1, alone in its block, so its scaled value lies in [4, 8)):
+    # the fp32 nearest to 5 / r_h, nudged until r_h * gamma rounds to exactly 5 (a tie,
+    # which rounds to the even code: value 4) while r_s * gamma rounds above 5 (value 6)
+    g = f(5.0 / float(r_h))
+    for _ in range(8):
+        if f(r_h * g) == f(5) and f(r_s * g) > f(5):
+            break
+        g = np.nextafter(g, f(np.inf) if f(r_h * g) < f(5) else f(0))
+    assert f(r_h * g) == f(5) and f(r_s * g) > f(5), "no separating gamma"
+    gamma = np.ones(N, np.float32)
+    gamma[32] = g
+    L = wl.make_layer(wl.custom("rms-order", 1, N, 8, seed=10), with_weight=False)
+    L.x_bits = wl.f32_to_bf16_bits(x)
+    L.A = np.eye(8, dtype=np.float32)
+    L.B = np.tile(np.eye(4, dtype=np.float32), (k, 1, 1))
+    L.alpha_min = L.alpha_max = np.full(k, 30.0, np.float32)     # sigmoid(30) = 1 in fp32
+    q, e = run(bq, L, gamma, 0.0)
+    q_ref, e_ref, zero = oracle(orc, L, gamma, 0.0)
+    assert (q_ref[0, 16] & 0xF) == 6                            # value 4 (the halving order)
+    assert_codes_equal(q, e, q_ref, e_ref, zero, what=f"rmsnorm order k={k}")

@@ -235,6 +235,34 @@ def _ptr(t) -> int:
     return t.data_ptr()
 
 
+def _req(t, name, dtype, numel, device, contiguous=True):
+    """Argument check before any launch: the C ABI sees raw pointers only, so a tensor of the
+    wrong type, size or device would make a kernel read or write outside it."""
+    assert t is not None, f"{name} is required"
+    assert t.dtype == dtype, f"{name}: dtype {t.dtype}, expected {dtype}"
+    assert t.numel() == numel, f"{name}: {t.numel()} elements, expected {numel}"
+    assert t.device == device, f"{name} is on {t.device}, expected {device}"
+    if contiguous:
+        assert t.is_contiguous(), f"{name} must be contiguous"
+
+
+def _req_act(x):
+    """bf16 activations [S, N] with unit column stride and N a multiple of 32."""
+    import torch
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1, \
+        "x must be a bf16 [S, N] tensor with unit column stride"
+    assert x.shape[1] % 32 == 0, "N must be a multiple of 32"
+    return x.shape[0], x.shape[1]
+
+
+def _req_gpk(A, B, r_min, r_max, k, device):
+    import torch
+    _req(A, "A", torch.float32, 64, device)
+    _req(B, "B", torch.float32, 16 * k, device)
+    _req(r_min, "r_min", torch.float32, k, device)
+    _req(r_max, "r_max", torch.float32, k, device)
+
+
 def _scale_tensor(rows, N, layout, device):
     import torch
     if layout == SCALES_ROW_MAJOR:
@@ -248,15 +276,14 @@ def quantize_act(x, A, B, r_min, r_max, q=None, e=None, layout=SCALES_ROW_MAJOR,
     uint8 [S, N/2] and the scales: uint8 [S, N/32] row-major, or a flat uint8 buffer in the
     MFMA-tiled layout."""
     import torch
-    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
-    S, N = x.shape
+    S, N = _req_act(x)
     if q is None:
         q = torch.empty((S, N // 2), dtype=torch.uint8, device=x.device)
     if e is None:
         e = _scale_tensor(S, N, layout, x.device)
-    for t, dt in ((A, torch.float32), (B, torch.float32), (r_min, torch.float32),
-                  (r_max, torch.float32)):
-        assert t.dtype == dt and t.is_contiguous()
+    _req_gpk(A, B, r_min, r_max, N // 32, x.device)
+    _req(q, "q", torch.uint8, S * (N // 2), x.device)
+    _req(e, "e", torch.uint8, scale_bytes(S, N, layout), x.device)
     _check("batq_quantize_act", quantize_act_raw(
         _ptr(x), S, N, x.stride(0), _ptr(A), _ptr(B), _ptr(r_min), _ptr(r_max), _ptr(q),
         _ptr(e), layout, _stream(stream)))
@@ -286,38 +313,52 @@ def gemm_w4a4(xq, xe, wq, we, y=None, layout=SCALES_ROW_MAJOR, stream=None):
     import torch
     S, N = xq.shape[0], xq.shape[1] * 2
     out = wq.shape[0]
-    for t in (xq, xe, wq, we):
-        assert t.dtype == torch.uint8 and t.is_contiguous()
-    assert wq.shape[1] * 2 == N
-    assert xe.numel() == scale_bytes(S, N, layout) and we.numel() == scale_bytes(out, N, layout)
+    dev = xq.device
+    _req(xq, "xq", torch.uint8, S * (N // 2), dev)
+    _req(xe, "xe", torch.uint8, scale_bytes(S, N, layout), dev)
+    _req(wq, "wq", torch.uint8, out * (N // 2), dev)
+    _req(we, "we", torch.uint8, scale_bytes(out, N, layout), dev)
     if y is None:
-        y = torch.empty((S, out), dtype=torch.float32, device=xq.device)
+        y = torch.empty((S, out), dtype=torch.float32, device=dev)
+    _req(y, "y", torch.float32, S * out, dev)
     _check("batq_gemm_w4a4", gemm_w4a4_raw(_ptr(xq), _ptr(xe), _ptr(wq), _ptr(we), S, N, out,
                                            _ptr(y), layout, _stream(stream)))
     return y
 
 
-def linear_w4a4(x, A, B, r_min, r_max, wq, we, layout=SCALES_ROW_MAJOR, y=None, stream=None):
+def linear_w4a4(x, A, B, r_min, r_max, wq, we, layout=SCALES_ROW_MAJOR, y=None,
+                workspace=None, stream=None):
     """One pass of the online path through batq_linear_w4a4: quantise the activations and
-    multiply with the prepared weights (scales `we` in `layout`).  A workspace for the
-    activation codes is allocated here and passed, so the library picks the faster of its
-    one-kernel path (up to LINEAR_FUSED_TOKENS tokens) and the two calls."""
+    multiply with the prepared weights (scales `we` in `layout`).
+
+    `workspace` is the caller's (xq uint8 [S, N/2], xe scales of S x N in `layout`): given
+    it, the library picks the faster of its one-kernel path and the two calls.  Without it,
+    shapes the one kernel takes (at most LINEAR_FUSED_TOKENS tokens, N/32 a multiple of 8
+    up to 512) run with no workspace at all; any other shape gets one allocated here."""
     import torch
-    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
-    S, N = x.shape
+    S, N = _req_act(x)
     out = wq.shape[0]
-    assert wq.dtype == torch.uint8 and wq.is_contiguous() and wq.shape[1] * 2 == N
-    assert we.dtype == torch.uint8 and we.is_contiguous() and we.numel() == scale_bytes(out, N, layout)
-    for t in (A, B, r_min, r_max):
-        assert t.dtype == torch.float32 and t.is_contiguous()
+    dev = x.device
+    k = N // 32
+    _req_gpk(A, B, r_min, r_max, k, dev)
+    _req(wq, "wq", torch.uint8, out * (N // 2), dev)
+    _req(we, "we", torch.uint8, scale_bytes(out, N, layout), dev)
     if y is None:
-        y = torch.empty((S, out), dtype=torch.float32, device=x.device)
-    assert y.dtype == torch.float32 and y.shape == (S, out) and y.is_contiguous()
-    xq = torch.empty((S, N // 2), dtype=torch.uint8, device=x.device)
-    xe = _scale_tensor(S, N, layout, x.device)
+        y = torch.empty((S, out), dtype=torch.float32, device=dev)
+    _req(y, "y", torch.float32, S * out, dev)
+    if workspace is not None:
+        xq, xe = workspace
+        _req(xq, "workspace xq", torch.uint8, S * (N // 2), dev)
+        _req(xe, "workspace xe", torch.uint8, scale_bytes(S, N, layout), dev)
+    elif S <= LINEAR_FUSED_TOKENS and k <= 512 and k % 8 == 0:
+        xq = xe = None
+    else:
+        xq = torch.empty((S, N // 2), dtype=torch.uint8, device=dev)
+        xe = _scale_tensor(S, N, layout, dev)
     _check("batq_linear_w4a4", linear_w4a4_raw(
         _ptr(x), S, N, x.stride(0), _ptr(A), _ptr(B), _ptr(r_min), _ptr(r_max), _ptr(wq),
-        _ptr(we), out, _ptr(y), _ptr(xq), _ptr(xe), layout, _stream(stream)))
+        _ptr(we), out, _ptr(y), _ptr(xq) if xq is not None else 0,
+        _ptr(xe) if xe is not None else 0, layout, _stream(stream)))
     return y
 
 
@@ -330,14 +371,14 @@ def quantize_act_mxfp8(x, A, B, r_min, r_max, q8=None, e=None, layout=SCALES_ROW
     """Fused transform + clip + MXFP8 of bf16 activations x [S, N].  Returns the E4M3 codes
     uint8 [S, N] and the scales (as quantize_act)."""
     import torch
-    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
-    S, N = x.shape
+    S, N = _req_act(x)
     if q8 is None:
         q8 = torch.empty((S, N), dtype=torch.uint8, device=x.device)
     if e is None:
         e = _scale_tensor(S, N, layout, x.device)
-    for t in (A, B, r_min, r_max):
-        assert t.dtype == torch.float32 and t.is_contiguous()
+    _req_gpk(A, B, r_min, r_max, N // 32, x.device)
+    _req(q8, "q8", torch.uint8, S * N, x.device)
+    _req(e, "e", torch.uint8, scale_bytes(S, N, layout), x.device)
     _check("batq_quantize_act_mxfp8", quantize_act_mxfp8_raw(
         _ptr(x), S, N, x.stride(0), _ptr(A), _ptr(B), _ptr(r_min), _ptr(r_max), _ptr(q8),
         _ptr(e), layout, _stream(stream)))
@@ -349,39 +390,47 @@ def gemm_w4a8(xq8, xe, wq, we, y=None, layout=SCALES_ROW_MAJOR, stream=None):
     import torch
     S, N = xq8.shape
     out = wq.shape[0]
-    for t in (xq8, xe, wq, we):
-        assert t.dtype == torch.uint8 and t.is_contiguous()
-    assert wq.shape[1] * 2 == N
-    assert xe.numel() == scale_bytes(S, N, layout) and we.numel() == scale_bytes(out, N, layout)
+    dev = xq8.device
+    _req(xq8, "xq8", torch.uint8, S * N, dev)
+    _req(xe, "xe", torch.uint8, scale_bytes(S, N, layout), dev)
+    _req(wq, "wq", torch.uint8, out * (N // 2), dev)
+    _req(we, "we", torch.uint8, scale_bytes(out, N, layout), dev)
     if y is None:
-        y = torch.empty((S, out), dtype=torch.float32, device=xq8.device)
+        y = torch.empty((S, out), dtype=torch.float32, device=dev)
+    _req(y, "y", torch.float32, S * out, dev)
     _check("batq_gemm_w4a8", gemm_w4a8_raw(_ptr(xq8), _ptr(xe), _ptr(wq), _ptr(we), S, N, out,
                                            _ptr(y), layout, _stream(stream)))
     return y
 
 
-def linear_w4a8(x, A, B, r_min, r_max, wq, we, layout=SCALES_ROW_MAJOR, y=None, stream=None):
+def linear_w4a8(x, A, B, r_min, r_max, wq, we, layout=SCALES_ROW_MAJOR, y=None,
+                workspace=None, stream=None):
     """The W4A8 layer through batq_linear_w4a8: transform, clip and MXFP8 of the activations,
     then the W4A8 product with the prepared weights (scales `we` in `layout`): one kernel up
     to LINEAR_FUSED_TOKENS tokens and LINEAR_W4A8_FUSED_BLOCKS token blocks, else the two
-    calls with a workspace allocated here."""
+    calls through `workspace` (the caller's (xq8 uint8 [S, N], xe scales), or one allocated
+    here when none is given)."""
     import torch
-    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
-    S, N = x.shape
+    S, N = _req_act(x)
     out = wq.shape[0]
-    assert wq.dtype == torch.uint8 and wq.is_contiguous() and wq.shape[1] * 2 == N
-    assert we.dtype == torch.uint8 and we.is_contiguous() and we.numel() == scale_bytes(out, N, layout)
-    for t in (A, B, r_min, r_max):
-        assert t.dtype == torch.float32 and t.is_contiguous()
-    if y is None:
-        y = torch.empty((S, out), dtype=torch.float32, device=x.device)
-    assert y.dtype == torch.float32 and y.shape == (S, out) and y.is_contiguous()
+    dev = x.device
     k = N // 32
-    xq8 = xe = None
-    if not (S <= LINEAR_FUSED_TOKENS and k <= 512 and k % 8 == 0
-            and S * k <= LINEAR_W4A8_FUSED_BLOCKS):
-        xq8 = torch.empty((S, N), dtype=torch.uint8, device=x.device)
-        xe = _scale_tensor(S, N, layout, x.device)
+    _req_gpk(A, B, r_min, r_max, k, dev)
+    _req(wq, "wq", torch.uint8, out * (N // 2), dev)
+    _req(we, "we", torch.uint8, scale_bytes(out, N, layout), dev)
+    if y is None:
+        y = torch.empty((S, out), dtype=torch.float32, device=dev)
+    _req(y, "y", torch.float32, S * out, dev)
+    if workspace is not None:
+        xq8, xe = workspace
+        _req(xq8, "workspace xq8", torch.uint8, S * N, dev)
+        _req(xe, "workspace xe", torch.uint8, scale_bytes(S, N, layout), dev)
+    elif (S <= LINEAR_FUSED_TOKENS and k <= 512 and k % 8 == 0
+          and S * k <= LINEAR_W4A8_FUSED_BLOCKS):
+        xq8 = xe = None
+    else:
+        xq8 = torch.empty((S, N), dtype=torch.uint8, device=dev)
+        xe = _scale_tensor(S, N, layout, dev)
     _check("batq_linear_w4a8", linear_w4a8_raw(
         _ptr(x), S, N, x.stride(0), _ptr(A), _ptr(B), _ptr(r_min), _ptr(r_max), _ptr(wq),
         _ptr(we), out, _ptr(y), _ptr(xq8) if xq8 is not None else 0,
@@ -399,14 +448,21 @@ def quantize_act_form(x, form, F0, F1, r_min, r_max, q=None, e=None, layout=SCAL
     device fp32: GPK A [8,8] / B [k,4,4]; KRONECKER A [k,8,8] / B [k,4,4]; FULL P [k,32,32] /
     None."""
     import torch
-    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
-    S, N = x.shape
+    S, N = _req_act(x)
+    k = N // 32
+    dev = x.device
     if q is None:
-        q = torch.empty((S, N // 2), dtype=torch.uint8, device=x.device)
+        q = torch.empty((S, N // 2), dtype=torch.uint8, device=dev)
     if e is None:
-        e = _scale_tensor(S, N, layout, x.device)
-    for t in (F0, r_min, r_max) + ((F1,) if F1 is not None else ()):
-        assert t.dtype == torch.float32 and t.is_contiguous()
+        e = _scale_tensor(S, N, layout, dev)
+    f0n = {TRANSFORM_GPK: 64, TRANSFORM_KRONECKER: 64 * k, TRANSFORM_FULL: 1024 * k}[form]
+    _req(F0, "F0", torch.float32, f0n, dev)
+    if form != TRANSFORM_FULL:
+        _req(F1, "F1", torch.float32, 16 * k, dev)
+    _req(r_min, "r_min", torch.float32, k, dev)
+    _req(r_max, "r_max", torch.float32, k, dev)
+    _req(q, "q", torch.uint8, S * (N // 2), dev)
+    _req(e, "e", torch.uint8, scale_bytes(S, N, layout), dev)
     _check("batq_quantize_act_form", quantize_act_form_raw(
         _ptr(x), S, N, x.stride(0), form, _ptr(F0), _ptr(F1) if F1 is not None else 0,
         _ptr(r_min), _ptr(r_max), _ptr(q), _ptr(e), layout, _stream(stream)))
@@ -444,16 +500,16 @@ def gemm_out(xq, xe, wq, we, out_dtype=None, residual=None, y=None, layout=SCALE
     S = xq.shape[0]
     N = xq.shape[1] if w4a8 else xq.shape[1] * 2
     out = wq.shape[0]
-    for t in (xq, xe, wq, we):
-        assert t.dtype == torch.uint8 and t.is_contiguous()
-    assert wq.shape[1] * 2 == N
-    assert xe.numel() == scale_bytes(S, N, layout) and we.numel() == scale_bytes(out, N, layout)
+    dev = xq.device
+    _req(xq, "xq", torch.uint8, S * (N if w4a8 else N // 2), dev)
+    _req(xe, "xe", torch.uint8, scale_bytes(S, N, layout), dev)
+    _req(wq, "wq", torch.uint8, out * (N // 2), dev)
+    _req(we, "we", torch.uint8, scale_bytes(out, N, layout), dev)
     if residual is not None:
-        assert residual.dtype == torch.bfloat16 and residual.shape == (S, out)
-        assert residual.is_contiguous()
+        _req(residual, "residual", torch.bfloat16, S * out, dev)
     if y is None:
-        y = torch.empty((S, out), dtype=out_dtype, device=xq.device)
-    assert y.dtype == out_dtype and y.shape == (S, out) and y.is_contiguous()
+        y = torch.empty((S, out), dtype=out_dtype, device=dev)
+    _req(y, "y", out_dtype, S * out, dev)
     yt = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32
     fn, raw = (("batq_gemm_w4a8_out", gemm_w4a8_out_raw) if w4a8 else
                ("batq_gemm_w4a4_out", gemm_w4a4_out_raw))
@@ -471,14 +527,15 @@ def quantize_act_rmsnorm(x, gamma, eps, A, B, r_min, r_max, q=None, e=None,
     """RMSNorm (gamma fp32 [N] on the device, eps) + transform + clip + MXFP4 of bf16
     activations x [S, N]; returns the codes and scales as quantize_act."""
     import torch
-    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
-    S, N = x.shape
+    S, N = _req_act(x)
     if q is None:
         q = torch.empty((S, N // 2), dtype=torch.uint8, device=x.device)
     if e is None:
         e = _scale_tensor(S, N, layout, x.device)
-    for t in (gamma, A, B, r_min, r_max):
-        assert t.dtype == torch.float32 and t.is_contiguous()
+    _req(gamma, "gamma", torch.float32, N, x.device)
+    _req_gpk(A, B, r_min, r_max, N // 32, x.device)
+    _req(q, "q", torch.uint8, S * (N // 2), x.device)
+    _req(e, "e", torch.uint8, scale_bytes(S, N, layout), x.device)
     _check("batq_quantize_act_rmsnorm", quantize_act_rmsnorm_raw(
         _ptr(x), S, N, x.stride(0), _ptr(gamma), float(eps), _ptr(A), _ptr(B), _ptr(r_min),
         _ptr(r_max), _ptr(q), _ptr(e), layout, _stream(stream)))
@@ -495,16 +552,13 @@ def quantize_kv(x, slots, fmt, A, B, r_min, r_max, cache_q, cache_e, stream=None
     (KV_MXFP4) or [num_slots, N] (KV_MXFP8), cache_e uint8 [num_slots, N/32]; updated in
     place."""
     import torch
-    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
-    T, N = x.shape
+    T, N = _req_act(x)
+    dev = x.device
     num_slots = cache_q.shape[0]
-    assert slots.dtype == torch.int64 and slots.is_contiguous() and slots.numel() == T
-    assert cache_q.dtype == torch.uint8 and cache_q.is_contiguous()
-    assert cache_e.dtype == torch.uint8 and cache_e.is_contiguous()
-    assert cache_q.shape == (num_slots, N // 2 if fmt == KV_MXFP4 else N)
-    assert cache_e.shape == (num_slots, N // 32)
-    for t in (A, B, r_min, r_max):
-        assert t.dtype == torch.float32 and t.is_contiguous()
+    _req(slots, "slots", torch.int64, T, dev)
+    _req(cache_q, "cache_q", torch.uint8, num_slots * (N // 2 if fmt == KV_MXFP4 else N), dev)
+    _req(cache_e, "cache_e", torch.uint8, num_slots * (N // 32), dev)
+    _req_gpk(A, B, r_min, r_max, N // 32, dev)
     _check("batq_quantize_kv", quantize_kv_raw(
         _ptr(x), T, N, x.stride(0), _ptr(slots), num_slots, fmt, _ptr(A), _ptr(B), _ptr(r_min),
         _ptr(r_max), _ptr(cache_q), _ptr(cache_e), _stream(stream)))
@@ -523,12 +577,13 @@ def transform_rows(x, A, B, out_dtype=None, y=None, stream=None):
     import torch
     assert x.dim() == 2 and x.stride(1) == 1
     rows, N = x.shape
+    assert N % 32 == 0, "N must be a multiple of 32"
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     if y is None:
         y = torch.empty((rows, N), dtype=out_dtype, device=x.device)
-    assert y.dtype == out_dtype and y.shape == (rows, N) and y.is_contiguous()
-    for t in (A, B):
-        assert t.dtype == torch.float32 and t.is_contiguous()
+    _req(y, "y", out_dtype, rows * N, x.device)
+    _req(A, "A", torch.float32, 64, x.device)
+    _req(B, "B", torch.float32, 16 * (N // 32), x.device)
     _check("batq_transform_rows", transform_rows_raw(
         _ptr(x), _elem_type(x.dtype), rows, N, x.stride(0), _ptr(A), _ptr(B), _ptr(y),
         _elem_type(out_dtype), _stream(stream)))
@@ -539,18 +594,20 @@ def dequantize_rows(cache_q, cache_e, fmt, index=None, out_dtype=None, y=None, s
     """Cache rows (all, or those listed in the int64 index) back to fp32 (default) or bf16
     [rows, N]; an index entry outside the cache gives a zero row."""
     import torch
+    assert cache_q.dim() == 2
     src_rows = cache_q.shape[0]
     N = cache_q.shape[1] * 2 if fmt == KV_MXFP4 else cache_q.shape[1]
-    assert cache_q.dtype == torch.uint8 and cache_q.is_contiguous()
-    assert cache_e.dtype == torch.uint8 and cache_e.is_contiguous()
-    assert cache_e.shape == (src_rows, N // 32)
+    assert N % 32 == 0, "N must be a multiple of 32"
+    dev = cache_q.device
+    _req(cache_q, "cache_q", torch.uint8, cache_q.numel(), dev)
+    _req(cache_e, "cache_e", torch.uint8, src_rows * (N // 32), dev)
     if index is not None:
-        assert index.dtype == torch.int64 and index.is_contiguous()
+        _req(index, "index", torch.int64, index.numel(), dev)
     rows = src_rows if index is None else index.numel()
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     if y is None:
-        y = torch.empty((rows, N), dtype=out_dtype, device=cache_q.device)
-    assert y.dtype == out_dtype and y.shape == (rows, N) and y.is_contiguous()
+        y = torch.empty((rows, N), dtype=out_dtype, device=dev)
+    _req(y, "y", out_dtype, rows * N, dev)
     _check("batq_dequantize_rows", dequantize_rows_raw(
         _ptr(cache_q), _ptr(cache_e), src_rows, N, fmt, _ptr(index) if index is not None else 0,
         rows, _ptr(y), _elem_type(out_dtype), _stream(stream)))
