@@ -337,8 +337,11 @@ def measure(name, args):
     k2_ai = k2_flops(S, N, out) / b2
     k2_roof = min(peak, k2_ai * HBM_PEAK_GBS / 1e3)
     k1_name = "quantize_kernel_mxfp8" if w4a8 else "quantize_kernel"
+    big = (not w4a8 and epilogue == "f32" and k % 32 == 0
+           and ((S + 255) // 256) * ((out + 255) // 256) >= 512)
     k2_name = ("gemm_w4a8_kernel" if w4a8 else
-               "gemm_skinny_kernel" if S <= 64 else "gemm_pc_kernel")
+               "gemm_skinny_kernel" if S <= 64 else
+               "gemm_big_kernel" if big else "gemm_pc_kernel")
     tr1 = measured_traffic(k1_name, L.cfg.name) if form == "gpk" and not rms else None
     tr2 = measured_traffic(k2_name, L.cfg.name) if epilogue == "f32" else None
     roof_k1 = {"kernel": f"{k1_name} (fused BAT+clip+{'MXFP8' if w4a8 else 'MXFP4'}"

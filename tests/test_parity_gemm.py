@@ -173,3 +173,34 @@ def test_linear_end_to_end_tiled_scales(bq, orc, name):
     wq_ref, we_ref = orc.prepare_weight(L.W, L.A, L.B, nthreads=ORACLE_THREADS)
     y_ref, t_ref = orc.gemm(xq_ref, xe_ref, wq_ref, we_ref, nthreads=ORACLE_THREADS)
     assert_gemm_close(y[rows], y_ref, t_ref, what=f"{name} tiled")
+
+
+# ----------------------------------------------------------------------------------------
+# persistent 256 x 256 big-tile kernel (MFMA-tiled scales, N % 1024 == 0, >= 512 tiles)
+# ----------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("scales", list(SCALES))
+@pytest.mark.parametrize("S,N,out", [
+    (8192, 4096, 4096),          # exactly 512 tiles: two per workgroup
+    (4133, 1024, 8292),          # ragged tokens and outputs (17 x 33 tiles), K = 8 stages
+    (16384, 2048, 8192),         # 2048 tiles: eight per workgroup
+    (2048, 3072, 24576 + 40),    # gate/up-like, ragged out, K = 24 stages
+])
+def test_gemm_big_tiles(bq, orc, S, N, out, scales):
+    """Sampled token rows (every output of each) against the oracle: the rows at every tile
+    edge, the ragged tail and a spread through the middle."""
+    import torch
+    from tests.gpu_util import to_tiled_scales
+    lo, hi = SCALES[scales]
+    xq, xe = wl.random_mxfp4(S, N, seed=(91, S, N, out), scale_lo=lo, scale_hi=hi)
+    wq, we = wl.random_mxfp4(out, N, seed=(92, S, N, out), scale_lo=lo, scale_hi=hi)
+    print(f"[gemm big tiles] S={S} N={N} out={out} scales={scales}", flush=True)
+    y = bq.gemm_w4a4(u8_to_device(xq), u8_to_device(to_tiled_scales(xe)), u8_to_device(wq),
+                     u8_to_device(to_tiled_scales(we)), layout=bq.SCALES_MFMA_TILED)
+    torch.cuda.synchronize()
+    y = to_host(y)
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, 255, 256, 257, S // 2, S - 2, S - 1],
+                                     np.arange(13, S, max(1, S // 24))]))
+    rows = rows[rows < S]
+    y_ref, t_ref = orc.gemm(xq, xe, wq, we, rows=rows, nthreads=ORACLE_THREADS)
+    assert_gemm_close(y[rows], y_ref, t_ref, what=f"big S={S} N={N} out={out} {scales}")

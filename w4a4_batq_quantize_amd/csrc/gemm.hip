@@ -26,6 +26,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 #include "internal.h"
 #include "mx_block.h"
 
@@ -831,6 +833,483 @@ gemm_pc_kernel(DmaArgs p, float* __restrict__ y, int64_t tiles_o, int64_t tiles_
                 pc_stage<C, false>(acc, bufs[i], bufs[i], f0, f1, sc, wrow0, xrow0, lane);
     }
     store_tile<C>(acc, p, y, o0, s0, wrow0, xrow0, lane);
+}
+
+// =======================================================================================
+// gemm_big_kernel<WO, WS>: persistent 256 x 256 tiles, every wave streams and multiplies
+// =======================================================================================
+//
+// For grids of several rounds of tiles.  A 256 x 256 tile moves half the operand bytes per
+// flop of a 256 x 128 one (512 rows per K element for 2 x 256 x 256 flops).  One workgroup
+// per CU walks its tiles in turn (tile b, b + grid, ...), and the stage DMA runs on from one
+// tile into the next, so a tile's first stages arrive while the previous one finishes and
+// its output stores drain under the next tile's matrix-core work (measured with in-kernel
+// timestamps: a tile's first stage waited ~6 us for its data and its stores took ~3.5-6 us
+// when every tile began and ended in a round of its own).
+//
+// K stages are 128 elements (64 code bytes per operand row: a whole 64-byte request per
+// row).  Four stage buffers of 32 KB are all in flight while the matrix cores work from
+// registers: after the barrier that ends stage s the buffer of stage s is refilled with
+// stage s + 4 (of this tile or the next), so stages s+1 .. s+4 are in flight during stage s.
+// The scales come as whole 256-byte units of the MFMA-tiled layout (one 32-row panel x 8
+// blocks: two stages) into a ring of four 4 KB unit buffers, issued with the even stage's
+// codes.
+//
+// LDS layout of a code buffer: tile rows 0..255 weights, 256..511 tokens, 64 bytes each; the
+// 16-byte chunk c of row r sits at slot c ^ ((r / 4) % 4).  gfx950's LDS serves a
+// ds_read_b128 16 lanes at a time from 64 banks (256 bytes): the 16 lanes reading rows
+// r..r+15 (r a multiple of 16) at one chunk then hit 16 distinct 16-byte bank groups (4
+// rows per bank row x 4 slots); measured conflict-free (the same rate as contiguous reads).
+// The DMA writes 64 lanes x 16 bytes contiguously (16 rows per instruction), lane l
+// fetching chunk (l % 4) ^ ((row / 4) % 4) of row l / 4.  Lane offsets are the same for
+// every tile; the tile's first row enters as the instruction's uniform offset, and rows past
+// the end of an operand read zeros (the buffer descriptor's size), which no stored output
+// uses.
+//
+// Waves: WO x WS, each owning (256/WO) x (256/WS) outputs as TM x TN 32 x 32 MFMA tiles (the
+// activation tile is the MFMA row operand: line-wide epilogue stores as in the tiled
+// kernels above).  Each K-step issues its MFMAs one at a time with the memory instructions
+// of the wave in between (the next K-step's fragments; after the stage's barrier, the DMA
+// of stage s+4 and the next stage's scales and fragments).
+namespace big {
+constexpr int BO = 256, BS = 256;
+constexpr int kRowB = 64;                        // code bytes per operand row per stage
+constexpr int kRows = BO + BS;
+constexpr int kCodeBytes = kRows * kRowB;        // 32 KB
+constexpr int kPanels = kRows / 32;              // 16 scale panels
+constexpr int kUnitBytes = kPanels * 256;        // 4 KB: the scales of two stages
+constexpr int NB = 4;                            // code buffers (stages s+1..s+4 in flight)
+constexpr int NSC = 4;                           // scale unit buffers
+}  // namespace big
+
+template <int WO_, int WS_, bool ROT_ = true, int GO_ = 4>
+struct BigCfg {
+    static constexpr int WO = WO_, WS = WS_;
+    static constexpr bool kRotate = ROT_;        // K rotation of the tiles (see k_rotation)
+    static constexpr int kGroupO = GO_;          // weight tiles per XCD sweep (see tile_origin)
+    static constexpr int BO = big::BO, BS = big::BS;
+    static constexpr bool SW = true, TS = true;
+    static constexpr int kWaves = WO * WS, kThreads = 64 * kWaves;
+    static constexpr int TM = BO / WO / 32, TN = BS / WS / 32;
+    static constexpr int kCodeDma = big::kCodeBytes / 1024 / kWaves;   // per wave per stage
+    static constexpr int kScaleDma = big::kPanels / kWaves;            // per wave per unit
+    // this wave's DMA instructions of two consecutive stages (exactly one of them even)
+    static constexpr int kWait = 2 * kCodeDma + kScaleDma;
+    static_assert(kCodeDma >= 1 && kScaleDma >= 1 && kWaves * kScaleDma == big::kPanels, "split");
+    static_assert(BO % (WO * 32) == 0 && BS % (WS * 32) == 0, "tiles");
+    static_assert(big::NB * big::kCodeBytes + big::NSC * big::kUnitBytes <= 160 * 1024, "LDS");
+    // a wave streams weight rows only or token rows only
+    static_assert((BO / 16) % kCodeDma == 0 && (BO / 32) % kScaleDma == 0, "weight waves");
+};
+
+// This wave's DMA: its operand (weights or tokens), the lane offsets of its instructions
+// (the same for every tile), and the operand's bytes per row and per 32-row scale panel.
+struct BigPlan {
+    __amdgpu_buffer_rsrc_t code, scale;
+    uint32_t code_off[8];                        // per DMA instruction
+    uint32_t scale_off[4];                       // per unit instruction
+    uint32_t row_bytes, panel_bytes;             // 16 k, 32 k
+    bool weights;
+};
+
+template <class C>
+__device__ __forceinline__ void big_plan(BigPlan& pl, const DmaArgs& p, int wave, int lane)
+{
+    const bool w = wave * C::kCodeDma * 16 < C::BO;
+    const int64_t rows = w ? p.out : p.S;
+    const int tile0 = w ? 0 : C::BO;
+    pl.weights = w;
+    pl.code = buffer_rsrc(w ? p.wq : p.xq, rows * 16 * p.k);
+    pl.scale = buffer_rsrc(w ? p.we : p.xe, ((rows + 31) / 32) * 32 * p.k);
+    pl.row_bytes = (uint32_t)(16 * p.k);
+    pl.panel_bytes = (uint32_t)(32 * p.k);
+#pragma unroll
+    for (int i = 0; i < C::kCodeDma; ++i) {
+        const int r = (wave * C::kCodeDma + i) * 16 + (lane >> 2) - tile0;   // operand row in tile
+        const int c = (lane & 3) ^ ((r >> 2) & 3);
+        pl.code_off[i] = (uint32_t)r * pl.row_bytes + 16u * (uint32_t)c;
+    }
+#pragma unroll
+    for (int j = 0; j < C::kScaleDma; ++j) {
+        const int panel = (wave * C::kScaleDma + j) - tile0 / 32;
+        pl.scale_off[j] = (uint32_t)panel * pl.panel_bytes + 4u * (uint32_t)lane;
+    }
+}
+
+// A tile as the DMA sees it: the uniform byte offsets of this wave's operand rows, and the
+// K rotation of the tile's stages (even).
+struct BigTile {
+    uint32_t code_base, scale_base;
+    int rot;
+};
+
+template <class C>
+__device__ __forceinline__ BigTile big_tile(const BigPlan& pl, int64_t o0, int64_t s0, int rot)
+{
+    const uint32_t first = (uint32_t)(pl.weights ? o0 : s0);
+    return BigTile{(uint32_t)__builtin_amdgcn_readfirstlane((int)(first * pl.row_bytes)),
+                   (uint32_t)__builtin_amdgcn_readfirstlane((int)((first / 32) * pl.panel_bytes)),
+                   __builtin_amdgcn_readfirstlane(rot)};
+}
+
+// The LDS of the big-tile kernel: four code buffers and four scale-unit buffers, each an
+// array of its own (the compiler orders an LDS read only after DMA into the same array).
+__shared__ __attribute__((aligned(16))) uint8_t big_c0[big::kCodeBytes];
+__shared__ __attribute__((aligned(16))) uint8_t big_c1[big::kCodeBytes];
+__shared__ __attribute__((aligned(16))) uint8_t big_c2[big::kCodeBytes];
+__shared__ __attribute__((aligned(16))) uint8_t big_c3[big::kCodeBytes];
+__shared__ __attribute__((aligned(16))) uint8_t big_u0[big::kUnitBytes];
+__shared__ __attribute__((aligned(16))) uint8_t big_u1[big::kUnitBytes];
+__shared__ __attribute__((aligned(16))) uint8_t big_u2[big::kUnitBytes];
+__shared__ __attribute__((aligned(16))) uint8_t big_u3[big::kUnitBytes];
+
+template <int I>
+__device__ __forceinline__ uint8_t* big_code()
+{
+    if constexpr (I % 4 == 0) return big_c0;
+    else if constexpr (I % 4 == 1) return big_c1;
+    else if constexpr (I % 4 == 2) return big_c2;
+    else return big_c3;
+}
+
+template <int I>
+__device__ __forceinline__ uint8_t* big_unit()
+{
+    if constexpr (I % 4 == 0) return big_u0;
+    else if constexpr (I % 4 == 1) return big_u1;
+    else if constexpr (I % 4 == 2) return big_u2;
+    else return big_u3;
+}
+
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1 (unrolled, i a constant).
+template <class F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>)
+{
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f)
+{
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// The DMA of one stage, I = its index in its group of 8 (code buffer I % 4; with the unit
+// of the stage pair when I is even): this wave's instructions, unit first, one call per
+// instruction d = 0 .. count-1, so that the caller can spread them between MFMAs.
+template <class C, int I>
+struct BigDma {
+    static constexpr int kScale = (I & 1) == 0 ? C::kScaleDma : 0;
+    static constexpr int kCount = kScale + C::kCodeDma;
+    template <int D>
+    __device__ __forceinline__ static void issue(const BigPlan& pl, const BigTile& t, int ph,
+                                                 int wave)
+    {
+#if defined(__HIP_DEVICE_COMPILE__)
+        // the wave's byte offset in the buffer, made opaque here so that the compiler forms
+        // each instruction's LDS address when it is issued instead of keeping one register per
+        // buffer and instruction alive across the loop (that ran out of scalar registers)
+        uint32_t woff = (uint32_t)wave;
+        asm volatile("" : "+s"(woff));
+        if constexpr (D < kScale) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                pl.scale, (lds_void_t*)(big_unit<I / 2>() + (woff * C::kScaleDma + D) * 256), 4,
+                pl.scale_off[D], (int)(t.scale_base + (uint32_t)(ph / 2) * 256u), 0, 0);
+        } else if constexpr (D < kCount) {
+            constexpr int c = D - kScale;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                pl.code, (lds_void_t*)(big_code<I>() + (woff * C::kCodeDma + c) * 1024), 16,
+                pl.code_off[c], (int)(t.code_base + (uint32_t)ph * big::kRowB), 0, 0);
+        }
+#endif
+    }
+};
+
+template <int TM, int TN>
+struct BigFrags {
+    uint4 a[TM];      // weight fragments
+    uint4 b[TN];      // token fragments
+};
+
+template <int TM, int TN>
+struct BigScales {
+    uint32_t w[TM], x[TN];
+};
+
+// Fragment P of K-step T in the order the MFMAs consume them: weight 0, tokens 0..TN-1,
+// weights 1..TM-1.
+template <class C, int T, int P>
+__device__ __forceinline__ void big_frag_piece(BigFrags<C::TM, C::TN>& f, const uint8_t* buf,
+                                               int wrow0, int xrow0, int lr, int lg)
+{
+    const uint32_t slot = 16u * (uint32_t)((2 * T + lg) ^ ((lr >> 2) & 3));
+    if constexpr (P >= 1 && P <= C::TN) {
+        constexpr int b = P - 1;
+        f.b[b] = *reinterpret_cast<const uint4*>(buf + (C::BO + xrow0 + 32 * b + lr) * big::kRowB +
+                                                 slot);
+    } else {
+        constexpr int a = P == 0 ? 0 : P - C::TN;
+        f.a[a] = *reinterpret_cast<const uint4*>(buf + (wrow0 + 32 * a + lr) * big::kRowB + slot);
+    }
+}
+
+// Scale dword R of a unit buffer for this lane: weights 0..TM-1, then tokens 0..TN-1 (the
+// lane's dword of its row's 8 bytes: byte b selects the unit's K-step b).
+template <class C, int R>
+__device__ __forceinline__ void big_scale_piece(BigScales<C::TM, C::TN>& sc, const uint8_t* u,
+                                                int wrow0, int xrow0, int lr, int lg)
+{
+    if constexpr (R < C::TM)
+        sc.w[R] = *reinterpret_cast<const uint32_t*>(u + (wrow0 / 32 + R) * 256 + lr * 8 + 4 * lg);
+    else
+        sc.x[R - C::TM] = *reinterpret_cast<const uint32_t*>(
+            u + ((C::BO + xrow0) / 32 + R - C::TM) * 256 + lr * 8 + 4 * lg);
+}
+
+// The TM x TN MFMAs of one K-step (SEL = the K-step's byte in the scale dwords), each
+// followed by extra(i): the memory instructions issued in the matrix cores' shadow, one
+// slot per MFMA, in a fixed order (scheduling fences around every piece).
+template <class C, int SEL, class X>
+__device__ __forceinline__ void big_kstep(v16f (&acc)[C::TM][C::TN],
+                                          const BigFrags<C::TM, C::TN>& f,
+                                          const BigScales<C::TM, C::TN>& sc, X&& extra)
+{
+    static_for<C::TM * C::TN>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        constexpr int a = i / C::TN, b = i % C::TN;
+        const v8i av = {(int)f.a[a].x, (int)f.a[a].y, (int)f.a[a].z, (int)f.a[a].w, 0, 0, 0, 0};
+        const v8i bv = {(int)f.b[b].x, (int)f.b[b].y, (int)f.b[b].z, (int)f.b[b].w, 0, 0, 0, 0};
+        acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            bv, av, acc[a][b], kFmtE2M1, kFmtE2M1, SEL, (int)sc.x[b], SEL, (int)sc.w[a]);
+        __builtin_amdgcn_sched_barrier(0);
+        extra(ic);
+        __builtin_amdgcn_sched_barrier(0);
+    });
+}
+
+struct BigWave {
+    int wave, wrow0, xrow0, lr, lg;
+};
+
+// Stage s = 8 g + I of a tile (I a compile-time index: code buffer I % 4, unit buffer
+// (I / 2) % 4, scale bytes 2 (I % 2) and 2 (I % 2) + 1).  On entry f0 holds (or is loading)
+// K-step 0 of stage s and sc its unit's scales.  K-step 0 reads K-step 1's fragments in its
+// shadow.  K-step 1 takes, after its first MFMA, the wait for stage s+1 and the barrier (every
+// wave has then read all of stage s, and all of stage s+1 has landed), then issues the DMA
+// of the stage 4 ahead into stage s's buffer (`nt`, at physical stage `ph`: of this tile, the
+// next, or, past the last, a refetch into a buffer never read again so that every wait
+// counts the same) and reads the next stage's scales and K-step 0 fragments, all between its
+// MFMAs (after the last stage of all, reads of a buffer whose contents are not used).
+template <class C, int I>
+__device__ __forceinline__ void big_stage(v16f (&acc)[C::TM][C::TN], const BigPlan& pl,
+                                          const BigWave& wv, const BigTile& nt, int ph,
+                                          BigFrags<C::TM, C::TN>& f0,
+                                          BigFrags<C::TM, C::TN>& f1,
+                                          BigScales<C::TM, C::TN>& sc)
+{
+    constexpr int kSel = 2 * (I & 1);
+    constexpr int kPieces = C::TM + C::TN;
+    constexpr int kSlots = C::TM * C::TN;
+    static_assert(kPieces <= kSlots, "one fragment per MFMA slot");
+    big_kstep<C, kSel>(acc, f0, sc, [&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i < kPieces)
+            big_frag_piece<C, 1, i>(f1, big_code<I>(), wv.wrow0, wv.xrow0, wv.lr, wv.lg);
+    });
+    BigScales<C::TM, C::TN> sn = sc;
+    constexpr int J = (I + 1) % 8;                       // index of stage s+1
+    constexpr bool kNewUnit = (J & 1) == 0;
+    using D = BigDma<C, (I + 4) % 8>;
+    constexpr int kReads = kPieces + (kNewUnit ? kPieces : 0);
+    static_assert(2 * (kSlots - 1) >= D::kCount, "DMA slots");
+    static_assert(2 * (kSlots - 1) >= kReads, "read slots");
+    big_kstep<C, kSel + 1>(acc, f1, sc, [&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        {
+            if constexpr (i == 0) {
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm(C::kWait, 0));
+                barrier_only();
+            }
+            // slots 1.. : two DMA instructions and two reads per slot
+            static_for<2>([&](auto jc) {
+                constexpr int d = 2 * (i - 1) + decltype(jc)::value;
+                if constexpr (i >= 1) D::template issue<d>(pl, nt, ph, wv.wave);
+            });
+            static_for<2>([&](auto jc) {
+                constexpr int r = 2 * (i - 1) + decltype(jc)::value;
+                if constexpr (i >= 1 && r < kReads) {
+                    if constexpr (kNewUnit && r < kPieces)
+                        big_scale_piece<C, r>(sn, big_unit<J / 2>(), wv.wrow0, wv.xrow0, wv.lr,
+                                              wv.lg);
+                    else
+                        big_frag_piece<C, 0, kNewUnit ? r - kPieces : r>(
+                            f0, big_code<J>(), wv.wrow0, wv.xrow0, wv.lr, wv.lg);
+                }
+            });
+        }
+    });
+    sc = sn;
+}
+
+// Tile number i of the launch: XCD-aware order (as tile_origin does for one round per
+// workgroup), so that the 32 tiles an XCD runs at once share operand rows.
+template <int64_t group_o>
+__device__ __forceinline__ void big_tile_origin(int64_t i, int64_t tiles_o, int64_t tiles_s,
+                                                int64_t& o0, int64_t& s0)
+{
+    const int64_t total = tiles_o * tiles_s;
+    int64_t id = i;
+    if (total % kXcds == 0) id = (id % kXcds) * (total / kXcds) + id / kXcds;
+    const int64_t span = group_o * tiles_s;
+    const int64_t first_o = (id / span) * group_o;
+    const int64_t gsize = tiles_o - first_o < group_o ? tiles_o - first_o : group_o;
+    const int64_t rem = id % span;
+    o0 = (first_o + rem % gsize) * big::BO;
+    s0 = (rem / gsize) * big::BS;
+}
+
+// fp32 output of a wave's TM x TN accumulator tiles: lane l of tile (a, b) holds, in register
+// r, y[s][o] with o = 32a + l%32 and s = 32b + 8(r/4) + 4(l/32) + r%4 relative to the wave's
+// origin; each store instruction writes two tokens' 32 consecutive outputs.
+template <int TM, int TN>
+__device__ __forceinline__ void big_store(const v16f (&acc)[TM][TN], const DmaArgs& p,
+                                          float* __restrict__ y, int64_t o0, int64_t s0,
+                                          const BigWave& wv, int lane)
+{
+    const int lr = lane & 31, lg = lane >> 5;
+    const int64_t ob = o0 + wv.wrow0 + lr, sb = s0 + wv.xrow0 + 4 * lg;
+    float* base = y + sb * p.out + ob;
+    if (o0 + big::BO <= p.out && s0 + big::BS <= p.S) {
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+#pragma unroll
+            for (int a = 0; a < TM; ++a) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    base[(32 * b + 8 * (r >> 2) + (r & 3)) * p.out + 32 * a] = acc[a][b][r];
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        return;
+    }
+#pragma unroll
+    for (int b = 0; b < TN; ++b)
+#pragma unroll
+        for (int a = 0; a < TM; ++a)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t ds = 32 * b + 8 * (r >> 2) + (r & 3);
+                if (ob + 32 * a < p.out && sb + ds < p.S)
+                    base[ds * p.out + 32 * a] = acc[a][b][r];
+            }
+}
+
+template <class C>
+__global__ void __launch_bounds__(C::kThreads)
+gemm_big_kernel(DmaArgs p, float* __restrict__ y, int64_t tiles_o, int64_t tiles_s)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const BigWave wv{wave, (wave / C::WS) * (C::BO / C::WO), (wave % C::WS) * (C::BS / C::WS),
+                     lane & 31, lane >> 5};
+    const int64_t ntiles = tiles_o * tiles_s;
+    const int nst = (int)(p.k / 4);              // 128-element stages, a multiple of 8 (> 0)
+    const int64_t grid = gridDim.x;
+    BigPlan pl;
+    big_plan<C>(pl, p, wave, lane);
+    auto tile_of = [&](int64_t t, int64_t& o0, int64_t& s0) {
+        big_tile_origin<C::kGroupO>(t, tiles_o, tiles_s, o0, s0);
+        return big_tile<C>(pl, o0, s0,
+                           C::kRotate ? 2 * (int)k_rotation(tiles_o, tiles_s, o0, s0, C::BO, C::BS,
+                                                            nst / 2)
+                                      : 0);
+    };
+    int64_t t = blockIdx.x;                      // this workgroup's tiles: t, t + grid, ...
+    int64_t o0, s0;
+    BigTile cur = tile_of(t, o0, s0);
+    // the first tile's stages 0..3
+    static_for<4>([&](auto ic) {
+        constexpr int I = decltype(ic)::value;
+        const int ph = I + cur.rot < nst ? I + cur.rot : I + cur.rot - nst;
+        static_for<BigDma<C, I>::kCount>([&](auto dc) {
+            BigDma<C, I>::template issue<decltype(dc)::value>(pl, cur, ph, wave);
+        });
+    });
+    // stage 0: this wave's part once stages 1..3 remain in flight, then all of it
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(C::kWait + C::kCodeDma, 0));
+    barrier_only();
+    BigFrags<C::TM, C::TN> f0, f1;
+    BigScales<C::TM, C::TN> sc;
+    static_for<C::TM + C::TN>([&](auto rc) {
+        big_scale_piece<C, decltype(rc)::value>(sc, big_unit<0>(), wv.wrow0, wv.xrow0, wv.lr, wv.lg);
+    });
+    static_for<C::TM + C::TN>([&](auto rc) {
+        big_frag_piece<C, 0, decltype(rc)::value>(f0, big_code<0>(), wv.wrow0, wv.xrow0, wv.lr,
+                                                  wv.lg);
+    });
+
+    v16f acc[C::TM][C::TN];
+#pragma unroll
+    for (int a = 0; a < C::TM; ++a)
+#pragma unroll
+        for (int b = 0; b < C::TN; ++b) acc[a][b] = v16f{};
+    const int64_t my_tiles = (ntiles - t + grid - 1) / grid;
+    for (int64_t it = 0; it < my_tiles; ++it) {
+        const bool has_next = it + 1 < my_tiles;
+        int64_t o1 = o0, s1 = s0;
+        const BigTile nxt = has_next ? tile_of(t + grid, o1, s1) : cur;
+        // the DMA target of stage s is stage s + 4 of this tile (all but the last group's
+        // second half), else stage s + 4 - nst of the next tile, else (past the last tile)
+        // this tile's last stage again, into a buffer that is never read
+        int s = 0;
+        for (; s < nst - 8; s += 8) {
+            static_for<8>([&](auto ic) {
+                constexpr int I = decltype(ic)::value;
+                const int q = s + I + 4 + cur.rot;
+                big_stage<C, I>(acc, pl, wv, cur, q >= nst ? q - nst : q, f0, f1, sc);
+            });
+        }
+        static_for<4>([&](auto ic) {
+            constexpr int I = decltype(ic)::value;
+            const int q = s + I + 4 + cur.rot;
+            big_stage<C, I>(acc, pl, wv, cur, q >= nst ? q - nst : q, f0, f1, sc);
+        });
+        const int last = nst - 1 + cur.rot >= nst ? cur.rot - 1 : nst - 1 + cur.rot;
+        static_for<4>([&](auto ic) {
+            constexpr int I = 4 + decltype(ic)::value;
+            const int q = I - 4 + nxt.rot;
+            big_stage<C, I>(acc, pl, wv, nxt, has_next ? (q >= nst ? q - nst : q) : last, f0, f1,
+                            sc);
+        });
+        big_store(acc, p, y, o0, s0, wv, lane);
+#pragma unroll
+        for (int a = 0; a < C::TM; ++a)
+#pragma unroll
+            for (int b = 0; b < C::TN; ++b) acc[a][b] = v16f{};
+        t += grid;
+        o0 = o1;
+        s0 = s1;
+        cur = nxt;
+    }
+    // the trailing refetches must land before the workgroup's LDS is released
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+}
+
+// 256 x 256 tiles, 8 waves of 128 x 64 outputs each (the 4-wave 128 x 128 split measured
+// 1-9% slower on every shape tried)
+using CfgBig = BigCfg<2, 4>;
+
+// Whether the persistent big-tile kernel takes a GEMM: MFMA-tiled scales, fp32 output with no
+// residual, N a multiple of 1024 (whole groups of 8 stages), and at least two rounds of its
+// tiles.  Measured against the 256 x 128 producer/consumer kernel (graph-timed, rotated
+// buffers, best of two): S = 16384, N = 12288, out = 4096 (1024 tiles) 428 -> 418 us;
+// S = 16384, N = 4096 (1024 tiles) 192 -> 177 us; S = 2048, N = 4096, out = 24576 (768
+// tiles) 138 -> 133 us; with 128 tiles (q_proj, down_proj: half the CUs idle) 26 -> 40 us and
+// 58 -> 94 us, which is what the round count excludes.
+inline bool use_big(int64_t S, int64_t k, int64_t out, bool tiled, const uint16_t* res,
+                    bool out_bf16)
+{
+    if (!tiled || res || out_bf16 || k % 32 != 0 || k == 0) return false;
+    const int64_t tiles = ((S + 255) / 256) * ((out + 255) / 256);
+    return tiles >= 2 * 256;                        // two rounds on MI355X's 256 CUs
 }
 
 using CfgQ = DmaCfg<256, 128, 2, 2, 3, false, 4, true>;    // 256 tiles for a 2048 x 4096 output
@@ -2325,6 +2804,15 @@ hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq,
             else
                 hipLaunchKernelGGL((gemm_skinny_kernel<2, false>), grid, block, 0, stream, p, y);
         }
+        return hipGetLastError();
+    }
+    if (dma_ok && use_big(S, p.k, out, tiled_scales, res, out_bf16)) {
+        // several rounds of 256 x 256 tiles: the persistent big-tile kernel
+        const int64_t tiles_o = (out + CfgBig::BO - 1) / CfgBig::BO;
+        const int64_t tiles_s = (S + CfgBig::BS - 1) / CfgBig::BS;
+        const int64_t grid = tiles_o * tiles_s < kNumCUs ? tiles_o * tiles_s : kNumCUs;
+        hipLaunchKernelGGL(gemm_big_kernel<CfgBig>, dim3((unsigned)grid),
+                           dim3(CfgBig::kThreads), 0, stream, p, y, tiles_o, tiles_s);
         return hipGetLastError();
     }
     if (dma_ok) {
