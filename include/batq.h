@@ -13,7 +13,8 @@
  * Conventions for every entry point:
  *  - Sizes are int64_t.  "dev" pointers are device (HBM) memory owned by the caller (for
  *    example torch tensors); "host" pointers are ordinary host memory.  The library keeps
- *    no pointer after a call returns and holds no global mutable state.
+ *    no pointer after a call returns and holds no global mutable state, except the fixed
+ *    device scratch of batq_linear_w4a4_noalloc.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Device work is
  *    enqueued on it and the call returns without waiting, unless noted.  Results are valid
  *    once the stream reaches the work.
@@ -85,7 +86,8 @@ typedef enum batq_status {
     BATQ_ERR_ALIGN = 3,       /* a pointer or stride breaks the alignment stated below       */
     BATQ_ERR_UNSUPPORTED = 4, /* valid for the format but beyond the library's limits        */
     BATQ_ERR_SINGULAR = 5,    /* a GPK factor is not invertible                              */
-    BATQ_ERR_HIP = 6          /* the HIP runtime reported an error (launch, copy, alloc)     */
+    BATQ_ERR_HIP = 6,         /* the HIP runtime reported an error (launch, copy, alloc)     */
+    BATQ_ERR_TOO_LARGE = 7    /* the input exceeds batq_linear_w4a4_noalloc's fixed scratch  */
 } batq_status;
 
 /*
@@ -359,6 +361,31 @@ batq_status batq_linear_w4a4(const uint16_t* x, int64_t S, int64_t N, int64_t ld
                              const float* r_max, const uint8_t* wq, const uint8_t* we,
                              batq_scale_layout layout, int64_t out, float* y, uint8_t* xq,
                              uint8_t* xe, void* stream);
+
+/* Bytes of batq_linear_w4a4_noalloc's device scratch (activation codes and scales). */
+#define BATQ_NOALLOC_SCRATCH_BYTES (64LL << 20)
+
+/*
+ * batq_linear_w4a4 for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same layer and the same
+ * kernels as batq_linear_w4a4 given a workspace (the result is identical), with the
+ * activation codes and scales kept in a fixed device array of BATQ_NOALLOC_SCRATCH_BYTES
+ * that the library owns: every GPU it runs on holds one until the process ends, and every
+ * call on that GPU shares it (and leaves its contents behind).
+ *   arguments: as batq_linear_w4a4 without xq / xe; `stream` must belong to the current
+ *              device
+ *   Needs round_up(S * N/2, 256) + the scale bytes of S x N in `layout` <= the scratch size,
+ *   else BATQ_ERR_TOO_LARGE (checked before any HIP call; e.g. S = 16384 fits up to
+ *   N = 7680 in the MFMA-tiled layout, S = 2048 up to N = 61440).  The first call on a device looks up the device
+ *   address of its scratch (a HIP call, no allocation).
+ * Calls that overlap on one GPU (other streams, other threads) race on the scratch: order
+ * them.  Does not allocate or synchronise.
+ */
+batq_status batq_linear_w4a4_noalloc(const uint16_t* x, int64_t S, int64_t N, int64_t ldx,
+                                     const float* A, const float* B, const float* r_min,
+                                     const float* r_max, const uint8_t* wq, const uint8_t* we,
+                                     batq_scale_layout layout, int64_t out, float* y,
+                                     void* stream);
 
 /* Largest S * N/32 the one-kernel W4A8 layer takes (its MXFP8 token codes live in LDS). */
 #define BATQ_LINEAR_W4A8_FUSED_BLOCKS 768

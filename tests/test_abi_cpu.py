@@ -11,7 +11,7 @@ import pytest
 import workloads as wl
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-OK, NULL, SHAPE, ALIGN, UNSUPPORTED, SINGULAR, HIP = range(7)
+OK, NULL, SHAPE, ALIGN, UNSUPPORTED, SINGULAR, HIP, TOO_LARGE = range(8)
 
 # plausible, aligned device addresses; validation must fail before anything dereferences them
 D = 1 << 40
@@ -39,7 +39,8 @@ def test_library_exports_every_declared_entry_point(bq):
                             "batq_gemm_w4a4_out", "batq_gemm_w4a8_out",
                             "batq_quantize_act_rmsnorm", "batq_quantize_kv",
                             "batq_transform_rows", "batq_dequantize_rows",
-                            "batq_linear_w4a4", "batq_linear_w4a8"])
+                            "batq_linear_w4a4", "batq_linear_w4a8",
+                            "batq_linear_w4a4_noalloc"])
     L = ctypes.CDLL(bq.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -215,6 +216,28 @@ def test_linear_argument_errors(bq):
     assert f(D, 4, 256, 260, D, D, D, D, D, D, 8, D) == ALIGN               # ldx % 8
     assert f(D, 4, 256, 256, D, D + 4, D, D, D, D, 8, D) == ALIGN           # B
     assert f(D, 4, 256, 256, D, D, D, D, D, D, 8, D, layout=7) == UNSUPPORTED
+
+
+def test_linear_noalloc_argument_errors(bq):
+    """Every check runs before the first HIP call (which looks up the device scratch), so
+    these return on a host without a GPU; beyond the 64 MiB scratch: BATQ_ERR_TOO_LARGE."""
+    f = bq.linear_w4a4_noalloc_raw
+    T = bq.SCALES_MFMA_TILED
+    # (x, S, N, ldx, A, B, r_min, r_max, wq, we, out, y)
+    assert f(D, 4, 48, 64, D, D, D, D, D, D, 8, D) == SHAPE                # N % 32
+    assert f(0, 0, 256, 256, 0, 0, 0, 0, 0, 0, 8, 0) == OK                  # no tokens
+    assert f(D, 4, 256, 256, D, D, D, D, D, D, 8, 0) == NULL                # y
+    assert f(D, 4, 256, 256, D, D, D, D, D, 0, 8, D) == NULL                # we
+    assert f(D, 4, 256, 200, D, D, D, D, D, D, 8, D) == SHAPE               # ldx < N
+    assert f(D, 4, 256, 260, D, D, D, D, D, D, 8, D) == ALIGN               # ldx % 8
+    assert f(D, 4, 256, 256, D, D + 4, D, D, D, D, 8, D) == ALIGN           # B
+    assert f(D, 4, 256, 256, D, D, D, D, D, D, 8, D, layout=7) == UNSUPPORTED
+    # 16384 x 12288: 96 MiB of codes
+    assert f(D, 16384, 12288, 12288, D, D, D, D, D, D, 8, D, layout=T) == TOO_LARGE
+    # the boundary: 16384 tokens, N = 7680 fits the tiled layout (60 MiB + 3.75 MiB), 7936 not
+    fits = lambda n: (16384 * n // 2 + 255) // 256 * 256 + bq.scale_bytes(16384, n, T)
+    assert fits(7680) <= bq.NOALLOC_SCRATCH_BYTES < fits(7936)
+    assert f(D, 16384, 7936, 7936, D, D, D, D, D, D, 8, D, layout=T) == TOO_LARGE
 
 
 def test_linear_w4a8_argument_errors(bq):

@@ -15,7 +15,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libbatq.so")
 
 STATUS = {0: "BATQ_OK", 1: "BATQ_ERR_NULL", 2: "BATQ_ERR_SHAPE", 3: "BATQ_ERR_ALIGN",
-          4: "BATQ_ERR_UNSUPPORTED", 5: "BATQ_ERR_SINGULAR", 6: "BATQ_ERR_HIP"}
+          4: "BATQ_ERR_UNSUPPORTED", 5: "BATQ_ERR_SINGULAR", 6: "BATQ_ERR_HIP",
+          7: "BATQ_ERR_TOO_LARGE"}
 
 # Every exported entry point and its ctypes signature (the names of include/batq.h).
 _P, _I64, _I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
@@ -36,6 +37,7 @@ SIGNATURES = {
     "batq_dequantize_rows": [_P, _P, _I64, _I64, _I, _P, _I64, _P, _I, _P],
     "batq_linear_w4a4": [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _I, _I64, _P, _P, _P, _P],
     "batq_linear_w4a8": [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _I, _I64, _P, _P, _P, _P],
+    "batq_linear_w4a4_noalloc": [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _I, _I64, _P, _P],
     "batq_clip_ratios": [_P, _I64, _P],
     "batq_weight_factors": [_P, _P, _I64, _P, _P],
     "batq_status_string": [_I],
@@ -46,6 +48,9 @@ SIGNATURES = {
 # the GEMM consumes them (32-row x 8-block units of 256 bytes).
 SCALES_ROW_MAJOR = 0
 SCALES_MFMA_TILED = 1
+
+# bytes of batq_linear_w4a4_noalloc's device scratch (BATQ_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # batq_linear_w4a4 runs in one kernel up to this many tokens (BATQ_LINEAR_FUSED_TOKENS)
 LINEAR_FUSED_TOKENS = 4
@@ -165,6 +170,12 @@ def linear_w4a4_raw(x, S, N, ldx, A, B, r_min, r_max, wq, we, out, y, xq=0, xe=0
                     layout=SCALES_ROW_MAJOR, stream=0) -> int:
     return lib().batq_linear_w4a4(x, S, N, ldx, A, B, r_min, r_max, wq, we, layout, out, y, xq,
                                   xe, stream)
+
+
+def linear_w4a4_noalloc_raw(x, S, N, ldx, A, B, r_min, r_max, wq, we, out, y,
+                            layout=SCALES_ROW_MAJOR, stream=0) -> int:
+    return lib().batq_linear_w4a4_noalloc(x, S, N, ldx, A, B, r_min, r_max, wq, we, layout, out,
+                                          y, stream)
 
 
 def linear_w4a8_raw(x, S, N, ldx, A, B, r_min, r_max, wq, we, out, y, xq8=0, xe=0,

@@ -89,6 +89,7 @@ BATQ_API const char* batq_status_string(batq_status status)
         case BATQ_ERR_UNSUPPORTED: return "BATQ_ERR_UNSUPPORTED: valid for the format but beyond the library's limits";
         case BATQ_ERR_SINGULAR: return "BATQ_ERR_SINGULAR: a GPK factor is not invertible";
         case BATQ_ERR_HIP: return "BATQ_ERR_HIP: HIP runtime error";
+        case BATQ_ERR_TOO_LARGE: return "BATQ_ERR_TOO_LARGE: the activation codes and scales exceed the no-allocation entry point's 64 MiB scratch";
     }
     return "unknown batq_status";
 }
@@ -220,6 +221,40 @@ BATQ_API batq_status batq_linear_w4a4(const uint16_t* x, int64_t S, int64_t N, i
         batq_quantize_act(x, S, N, ldx, A, B, r_min, r_max, xq, xe, layout, stream);
     if (st != BATQ_OK) return st;
     return batq_gemm_w4a4(xq, xe, wq, we, layout, S, N, out, y, stream);
+}
+
+BATQ_API batq_status batq_linear_w4a4_noalloc(const uint16_t* x, int64_t S, int64_t N,
+                                              int64_t ldx, const float* A, const float* B,
+                                              const float* r_min, const float* r_max,
+                                              const uint8_t* wq, const uint8_t* we,
+                                              batq_scale_layout layout, int64_t out, float* y,
+                                              void* stream)
+{
+    if (S < 0 || N < 0 || out < 0 || N % 32 != 0) return BATQ_ERR_SHAPE;
+    if (S == 0 || out == 0) return BATQ_OK;
+    if (!valid_layout(layout)) return BATQ_ERR_UNSUPPORTED;
+    if (N == 0) return batq_gemm_w4a4(nullptr, nullptr, nullptr, nullptr, layout, S, 0, out, y,
+                                      stream);
+    if (!y || !x || !A || !B || !r_min || !r_max || !wq || !we) return BATQ_ERR_NULL;
+    if (ldx < N || mul_overflows(S, ldx) || mul_overflows(S, out) || mul_overflows(out, N))
+        return BATQ_ERR_SHAPE;
+    if (ldx % 8 != 0 || !aligned(x, 16) || !aligned(B, 16) || !aligned(y, 16) ||
+        !aligned(wq, 16) || !aligned(A, 4) || !aligned(r_min, 4) || !aligned(r_max, 4))
+        return BATQ_ERR_ALIGN;
+    const int64_t k = N / 32;
+    if (mul_overflows(S, k)) return BATQ_ERR_SHAPE;
+    // codes, then the scales from the next 256-byte boundary (the tiled layout's alignment)
+    const int64_t code_span = (S * (N / 2) + 255) / 256 * 256;
+    const int64_t scale_span = layout == BATQ_SCALES_MFMA_TILED
+                                   ? ((S + 31) / 32) * 32 * ((k + 7) / 8) * 8
+                                   : S * k;
+    if (code_span > batq::kNoAllocScratchBytes ||
+        scale_span > batq::kNoAllocScratchBytes - code_span)
+        return BATQ_ERR_TOO_LARGE;
+    uint8_t* scratch = nullptr;
+    if (batq::noalloc_scratch(&scratch) != hipSuccess) return BATQ_ERR_HIP;
+    return batq_linear_w4a4(x, S, N, ldx, A, B, r_min, r_max, wq, we, layout, out, y, scratch,
+                            scratch + code_span, stream);
 }
 
 BATQ_API batq_status batq_linear_w4a8(const uint16_t* x, int64_t S, int64_t N, int64_t ldx,

@@ -26,6 +26,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <utility>
 
 #include "internal.h"
@@ -2995,6 +2996,44 @@ hipError_t launch_linear16_w4a8(const uint16_t* x, int64_t S, int64_t k, int64_t
     else
         launch_linear16<false, true>(p, x, ldx, A, B, r_min, r_max, y, stream);
     return hipGetLastError();
+}
+
+}  // namespace batq
+
+// =======================================================================================
+// Device scratch of the no-allocation linear layer (batq_linear_w4a4_noalloc)
+// =======================================================================================
+namespace batq {
+namespace {
+
+// The activation codes and scales of batq_linear_w4a4_noalloc.  Every GPU the library runs
+// on holds its own copy (loaded with the code object) until the process ends.  In host code
+// this name stands for a host-side shadow, not device memory: the device address comes from
+// hipGetSymbolAddress, once per device, and only that address reaches kernels and copies.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+uint8_t* g_scratch_ptr[kMaxDevices];
+
+}  // namespace
+
+hipError_t noalloc_scratch(uint8_t** ptr)
+{
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        // first use on this device, with the device current: its copy's address
+        void* p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return err;
+        g_scratch_ptr[dev] = static_cast<uint8_t*>(p);
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 }  // namespace batq

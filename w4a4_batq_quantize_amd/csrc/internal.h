@@ -82,4 +82,10 @@ hipError_t launch_gemm_w4a8(const uint8_t* xq8, const uint8_t* xe, const uint8_t
                             int64_t out, float* y, hipStream_t stream,
                             const uint16_t* res = nullptr, bool out_bf16 = false);
 
+// The no-allocation linear layer's device scratch: activation codes, then (from the next
+// 256-byte boundary) their scales.  noalloc_scratch gives the current device's copy (its
+// address is looked up once per device, with the device current).
+constexpr int64_t kNoAllocScratchBytes = 64LL << 20;
+hipError_t noalloc_scratch(uint8_t** ptr);
+
 }  // namespace batq
