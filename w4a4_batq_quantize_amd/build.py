@@ -51,7 +51,9 @@ def build(verbose: bool = False) -> str:
               "-c", os.path.join(CSRC, src), "-o", obj], verbose)
         objs.append(obj)
     tmp = LIB + ".tmp"
-    _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    # (every symbol resolved at link time: a kernel whose host stub is missing fails here)
+    _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,--no-undefined", *objs, "-o", tmp],
+         verbose)
     os.replace(tmp, LIB)
     return LIB
 
