@@ -177,8 +177,11 @@ batq_status batq_quantize_act_mxfp8(const uint16_t* x, int64_t S, int64_t N, int
 /*
  * W4A8 GEMM: y[s][o] = sum_n dq8(xq8)[s][n] * dq(wq)[o][n] with dq8(code, e) =
  * e4m3(code) * 2^(e-127) and dq as in batq_gemm_w4a4 (the W4A8 setting of the gist.science
- * summary, section 4), on gfx950 scaled MFMA (E2M1 weights x E4M3 activations) with fp32
- * accumulation.  Each 32-element block product is exact; sums across blocks round in fp32.
+ * summary, section 4).  Both operands are dequantised to bf16 on the GPU -- exact for
+ * activation scale bytes 9..246 (every byte batq_quantize_act_mxfp8 writes for a block whose
+ * largest magnitude is at least 2^-110) and for every weight scale batq_prepare_weight
+ * writes -- and multiplied on gfx950's bf16 MFMA with fp32 accumulation: the products are
+ * exact and the sums round in fp32 (within 1e-5 of sum|terms| of the exact product).
  *
  *   xq8, xe  dev  activation codes [S, N] (16-byte aligned) and scales (4-byte aligned)
  *   wq, we   dev  weight codes [out, N/2] (16-byte aligned) and scales (4-byte aligned),

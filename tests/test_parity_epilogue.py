@@ -67,7 +67,6 @@ CASES = [
 @pytest.mark.parametrize("S,N,out,tiled,w4a8", CASES)
 def test_epilogue_bf16_and_residual(bq, orc, S, N, out, tiled, w4a8):
     import torch
-    from tests.mfma_fp8_model import HW_TRUNCATION_REL
     seed = (71, S, N, out, int(w4a8))
     if w4a8:
         xq, xe = wl.random_mxfp8(S, N, seed=seed, scale_lo=120, scale_hi=134)
@@ -81,7 +80,7 @@ def test_epilogue_bf16_and_residual(bq, orc, S, N, out, tiled, w4a8):
     y32 = run(bq, xq, xe, wq, we, tiled, w4a8, torch.float32, None)
     gemm = orc.gemm_w4a8 if w4a8 else orc.gemm
     y_ref, t_ref = gemm(xq, xe, wq, we, nthreads=ORACLE_THREADS)
-    rel = (HW_TRUNCATION_REL + 1e-5) if w4a8 else 1e-5
+    rel = 1e-5
     what = f"S={S} N={N} out={out} tiled={tiled} w4a8={w4a8}"
 
     for dtype, res in ((torch.bfloat16, None), (torch.bfloat16, res_bits),

@@ -190,8 +190,14 @@ def identity_weights(bq, N, e, layout):
     return W, wq, we
 
 
+# The W4A8 product dequantises the E4M3 codes to bf16, exact for scale bytes 9..246, so the
+# MXFP8 encoder is read back through it at bytes of that range (the quantiser alone is
+# checked at 0, 1, 127 and 246 above); 9 puts the smallest E4M3 value on bf16's subnormals.
+SCALE_BYTES_FP8_PRODUCT = [9, 10, 127, 246]
+
+
 @pytest.mark.parametrize("fp8,e", [(False, e) for e in SCALE_BYTES_FP4] +
-                         [(True, e) for e in SCALE_BYTES_FP8])
+                         [(True, e) for e in SCALE_BYTES_FP8_PRODUCT])
 def test_one_kernel_layer_ties(bq, orc, e, fp8):
     """The encoders inside the one-kernel layers (at most four tokens, no workspace), read
     back through an identity product: y equals the oracle's code values exactly."""

@@ -1,18 +1,20 @@
-// MXFP4 x MXFP4 (and E2M1 x E4M3) -> fp32 GEMMs on gfx950 scaled MFMA: the product of the
+// MXFP4 x MXFP4 (and E2M1 x E4M3) -> fp32 GEMMs on gfx950 matrix cores: the product of the
 // W4A4 (W4A8) linear layer, and the layer in one kernel for a few tokens.
 //
 // y[s][o] = sum_n dq(x)[s][n] dq(w)[o][n] with dq = code value * 2^(e-127) per 32-element
-// block.  The contraction runs on the scaled MFMA instructions: each lane supplies the K
-// values of one MX block of one row (16 bytes of E2M1, or 32 bytes of E4M3 gathered as the
-// instruction lays them out) together with the E8M0 scale of exactly that block, so blocks
-// map onto lanes one to one and the block scales are applied inside the instruction.
+// block.  W4A4: the contraction runs on the scaled MFMA instructions: each lane supplies the
+// K values of one MX block of one row (16 bytes of E2M1) together with the E8M0 scale of
+// exactly that block, so blocks map onto lanes one to one and the block scales are applied
+// inside the instruction.  W4A8: the same lane-to-block mapping, but both operands are
+// dequantised to bf16 in registers and multiplied on the bf16 MFMAs, which (unlike the scaled
+// MFMA with an E4M3 operand) return the product to within fp32 summation rounding.
 //
 // Kernels, by token count S (the launchers below choose):
 //  - gemm_pc_kernel / gemm_dma_kernel (S > 64; MFMA-tiled / row-major scales):
 //    V_MFMA_SCALE_F32_32X32X64_F8F6F4 on 256 (out) x 128 (token) tiles, operands moved
 //    HBM/L2 -> LDS by buffer_load ... lds without passing through registers, three LDS
 //    stages; producer waves issue the DMA and consumer waves the MFMAs in the first;
-//  - gemm_w4a8_kernel (S > 64, E4M3 tokens): the same tile shape and DMA with mixed formats;
+//  - gemm_w4a8_kernel (S > 64, E4M3 tokens): the same tile shape and DMA, bf16 MFMAs;
 //  - gemm_skinny16_kernel (S <= 16, by a workgroup-rounds rule) and gemm_skinny_kernel
 //    (S <= 64 otherwise): weight streaming, 16 or 32 output rows per workgroup and K split
 //    across its waves;
@@ -47,6 +49,86 @@ typedef __attribute__((address_space(1))) void gbl_void_t;
 constexpr int kThreads = 256;
 constexpr int kFmtE2M1 = 4;
 constexpr int kXcds = 8;
+
+// ---------------------------------------------------------------------------------------
+// W4A8 products, exactly
+// ---------------------------------------------------------------------------------------
+//
+// The scaled MFMA with an E4M3 operand does not return the exact product: measured on
+// gfx950, it forms the products of each group of 8 consecutive K positions aligned to the
+// largest of them and truncates them to 2^(E-13) (E that product's exponent sum), so a
+// product more than 9 octaves below its group's largest is cut (448 + 31 * 2^-6 comes out as
+// 448).  The W4A8 kernels therefore dequantise both operands to bf16 -- an E4M3 or E2M1 value
+// times its E8M0 scale is exact in bf16 for activation scale bytes 9..246 and weight scale
+// bytes 0..252, which covers every scale the quantisers produce from finite inputs above
+// 2^-110 -- and multiply them on the bf16 MFMAs, whose products are exact and whose sums
+// stayed within 1.3e-6 of the sum of |terms| in every measured case (wide and narrow scales,
+// 64 to 12288 K positions).  Each lane converts the 8 elements one bf16 MFMA takes from the
+// MX block it holds, so the MFMAs of one scaled step cover the same K positions on both
+// operands, in a different order (the sum is invariant to it).
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// E8M0 byte as the scale operand of the scaled conversions (they read its exponent field)
+__device__ __forceinline__ float e8m0_operand(uint32_t byte) { return __uint_as_float(byte << 23); }
+
+// elements 8q .. 8q + 7 of an E2M1 block (16 bytes) times 2^(s - 127), as bf16
+__device__ __forceinline__ v8bf dequant_e2m1_bf16(const v4u& c, int q, float s)
+{
+    const uint32_t w = c[q];
+    const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0);
+    const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1);
+    const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2);
+    const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3);
+    return v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// elements 8q .. 8q + 7 of an E4M3 block (32 bytes) times 2^(s - 127), as bf16
+__device__ __forceinline__ v8bf dequant_e4m3_bf16(const v8i& c, int q, float s)
+{
+    const uint32_t w0 = (uint32_t)c[2 * q], w1 = (uint32_t)c[2 * q + 1];
+    const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, false);
+    const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, true);
+    const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, false);
+    const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, true);
+    return v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+
+// acc (32 x 32) += the 64-position K-step whose block the lane holds (16 bytes of E2M1 codes
+// w, 32 bytes of E4M3 codes x, their scale bytes): four bf16 MFMAs.  kWeightsA: the weights
+// are the row operand (A) of the instruction, else the tokens are.
+template <bool kWeightsA>
+__device__ __forceinline__ v16f w4a8_step32(v16f acc, const v4u& w, const v8i& x, uint32_t wbyte,
+                                            uint32_t xbyte)
+{
+    const float sw = e8m0_operand(wbyte & 0xFFu), sx = e8m0_operand(xbyte & 0xFFu);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const v8bf a = dequant_e2m1_bf16(w, q, sw), b = dequant_e4m3_bf16(x, q, sx);
+        acc = kWeightsA ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0)
+                        : __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, acc, 0, 0, 0);
+        // (one MFMA's conversions at a time: they run while the previous MFMA does, and the
+        // bf16 operands do not all stay live)
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    return acc;
+}
+
+// acc (16 x 16, weights as the row operand) += the 128-position K-step whose block the lane
+// holds: four bf16 16x16x32 MFMAs
+__device__ __forceinline__ v4f w4a8_step16(v4f acc, const v4u& w, const v8i& x, uint32_t wbyte,
+                                           uint32_t xbyte)
+{
+    const float sw = e8m0_operand(wbyte & 0xFFu), sx = e8m0_operand(xbyte & 0xFFu);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dequant_e2m1_bf16(w, q, sw),
+                                                       dequant_e4m3_bf16(x, q, sx), acc, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    return acc;
+}
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8])
 constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
@@ -1579,12 +1661,13 @@ __device__ __forceinline__ void skinny_load(SkinnyStage<TN, F8, XL>& st,
 #pragma unroll
         for (int b = 0; b < (XL ? 0 : TN); ++b) {
             if constexpr (F8) {
-                // E4M3 lane half h: chunks 4t + h and 4t + 2 + h of the 256-byte stage row
-                const uint32_t c8 = (uint32_t)ks * 2 * kRowBytes + 16u * (4 * t + lg);
+                // E4M3 lane half h: block 2t + h, chunks 4t + 2h and 4t + 2h + 1 of the
+                // 256-byte stage row
+                const uint32_t c8 = (uint32_t)ks * 2 * kRowBytes + 16u * (4 * t + 2 * lg);
                 st.x[b][t][0] =
                     __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(xrow[b] * xrb + c8), 0, 0);
                 st.x[b][t][1] =
-                    __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(xrow[b] * xrb + c8 + 32), 0, 0);
+                    __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(xrow[b] * xrb + c8 + 16), 0, 0);
             } else {
                 st.x[b][t][0] =
                     __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(xrow[b] * xrb + c), 0, 0);
@@ -1617,7 +1700,6 @@ __device__ __forceinline__ void skinny_step(v16f (&acc)[TN], const uint4& w,
     // tiled: byte T of the one dword; row-major: byte 2(T%2) of word T/2, pre-shifted so the
     // lane's half (block 2T + lane/32) sits in that byte
     constexpr int kSel = TS ? T : 2 * (T & 1);
-    constexpr int kFmtX = F8 ? 0 : kFmtE2M1;                   // 0: E4M3
     const uint32_t wsc = TS ? st.ws.x : (((T >> 1) ? st.ws.y : st.ws.x) >> (8 * lg));
     const v8i av = {(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
 #pragma unroll
@@ -1628,14 +1710,18 @@ __device__ __forceinline__ void skinny_step(v16f (&acc)[TN], const uint4& w,
             u = v4u{xl[b][0].x, xl[b][0].y, xl[b][0].z, xl[b][0].w};
         else
             u = st.x[b][T][0];
-        v8i bv = {(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
         if constexpr (F8) {
             const uint4 h = xl[b][F8 ? 1 : 0];
             const v4u v = XL ? v4u{h.x, h.y, h.z, h.w} : st.x[b][T][F8 ? 1 : 0];
-            bv = v8i{(int)u.x, (int)u.y, (int)u.z, (int)u.w, (int)v.x, (int)v.y, (int)v.z, (int)v.w};
+            const v8i bv = {(int)u.x, (int)u.y, (int)u.z, (int)u.w,
+                            (int)v.x, (int)v.y, (int)v.z, (int)v.w};
+            acc[b] = w4a8_step32<true>(acc[b], v4u{w.x, w.y, w.z, w.w}, bv, wsc >> (8 * kSel),
+                                       xsc >> (8 * kSel));
+        } else {
+            const v8i bv = {(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
+            acc[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                av, bv, acc[b], kFmtE2M1, kFmtE2M1, kSel, (int)wsc, kSel, (int)xsc);
         }
-        acc[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            av, bv, acc[b], kFmtE2M1, kFmtX, kSel, (int)wsc, kSel, (int)xsc);
     }
 }
 
@@ -1658,11 +1744,13 @@ __device__ __forceinline__ void skinny_stage(v16f (&acc)[TN], const uint8_t* slo
             for (int b = 0; b < TN; ++b) {
                 const uint8_t* xr = xs[b];
                 if constexpr (F8) {
-                    // E4M3 lane half h: chunks 4t + h and 4t + 2 + h of the 256-byte row
+                    // E4M3 lane half h: block 2t + h, chunks 4t + 2h and 4t + 2h + 1 of the
+                    // 256-byte row
                     const uint8_t* r8 = xr + lr * 2 * kRowBytes;
-                    x[t][b][0] = *reinterpret_cast<const uint4*>(r8 + 16 * ((4 * t + lg) ^ (lr & 15)));
-                    x[t][b][F8 ? 1 : 0] =
-                        *reinterpret_cast<const uint4*>(r8 + 16 * ((4 * t + 2 + lg) ^ (lr & 15)));
+                    x[t][b][0] =
+                        *reinterpret_cast<const uint4*>(r8 + 16 * ((4 * t + 2 * lg) ^ (lr & 15)));
+                    x[t][b][F8 ? 1 : 0] = *reinterpret_cast<const uint4*>(
+                        r8 + 16 * ((4 * t + 2 * lg + 1) ^ (lr & 15)));
                 } else {
                     x[t][b][0] = *reinterpret_cast<const uint4*>(xr + lr * kRowBytes +
                                                                  16 * ((2 * t + lg) ^ key));
@@ -1883,12 +1971,11 @@ gemm_skinny_kernel(DmaArgs p, float* __restrict__ y)
 // gemm_w4a8_kernel<TS>: MXFP8 (E4M3) activations x MXFP4 weights, the W4A8 setting
 // =======================================================================================
 //
-// The scaled 32x32x64 MFMA with mixed operand formats: weights E2M1 (format 4, 16 bytes per
-// lane: lane half h holds block h of the K-step), activations E4M3 (format 0, 32 bytes per
-// lane, which hold the same K positions as the E2M1 lanes only as 16-byte halves of both
-// blocks: measured on gfx950, each scale applies to one 32-element K block).  Tile
-// 256 (out) x 128 (tokens), four waves (2 x 2, each 4 x 2 MFMA tiles) at one wave per SIMD,
-// so the 8-dword activation fragments and the accumulators fit in registers; each wave
+// Both operands dequantised to bf16 in registers and multiplied on the 32x32x16 bf16 MFMA
+// (exact products, see w4a8_step32): per 64-position K-step, lane half h holds block h of the
+// step in both operands, and four bf16 MFMAs cover it.  Tile 256 (out) x 128 (tokens), four
+// waves (2 x 2, each 4 x 2 MFMA tiles) at one wave per SIMD, so the 8-dword activation
+// fragments, their bf16 forms and the accumulators fit in registers; each wave
 // issues its quarter of the next stage's DMA between the MFMA rows of the current stage,
 // two stages in LDS, one barrier per stage.  A stage is 8
 // blocks: 256 weight rows of 128 bytes, 128 activation rows of 256 bytes, then the scale
@@ -2000,18 +2087,18 @@ struct W4A8Frags {
     v8i b[w4a8::TN];       // 32 bytes of the lane's token row
 };
 
+// Fragments of K-step T (the step's two blocks: lane half h holds block 2T + h): the 16 bytes
+// of the block in the lane's weight row and all 32 bytes of it in the lane's token row
+// (16-byte chunks 4T + 2h and 4T + 2h + 1 of the 256-byte stage row).
 template <int T>
-__device__ __forceinline__ void w4a8_frags(W4A8Frags& f, const uint8_t* buf, int wrow0,
-                                           int xrow0, int lr, int lg)
+__device__ __forceinline__ void w4a8_frags(W4A8Frags& f, const uint8_t* buf, int wrow0, int xrow0,
+                                           int lr, int lg)
 {
     using namespace w4a8;
     const int lr7 = (lr >> 1) & 7, lr15 = lr & 15;
     const uint32_t wpos = 16u * (uint32_t)((2 * T + lg) ^ lr7);
-    // E4M3 operand: lane half h holds elements [16h, 16h+16) of both blocks of the K-step
-    // (bytes 0-15 from block 2T, bytes 16-31 from block 2T+1), i.e. 16-byte chunks 4T + h
-    // and 4T + 2 + h of the stage row; the scale of lane half h still belongs to block 2T+h
-    const uint32_t x0 = 16u * (uint32_t)((4 * T + lg) ^ lr15);
-    const uint32_t x1 = 16u * (uint32_t)((4 * T + 2 + lg) ^ lr15);
+    const uint32_t x0 = 16u * (uint32_t)((4 * T + 2 * lg) ^ lr15);
+    const uint32_t x1 = 16u * (uint32_t)((4 * T + 2 * lg + 1) ^ lr15);
 #pragma unroll
     for (int a = 0; a < TM; ++a)
         f.a[a] = *reinterpret_cast<const v4u*>(buf + (wrow0 + 32 * a + lr) * kRowBytes + wpos);
@@ -2032,20 +2119,28 @@ __device__ __forceinline__ void w4a8_mfma(v16f (&acc)[w4a8::TM][w4a8::TN], const
 {
     constexpr int kSlots = (w4a8::kDma + 3) / 4;   // DMA instructions per K-step
     using namespace w4a8;
-    constexpr int kFmtE4M3 = 0;
+    // byte kSel of word kWord of the lane's scale dwords: block 2T + half of its row
     constexpr int kSel = TS ? T : 2 * (T & 1);
     constexpr int kWord = TS ? 0 : T >> 1;
+    v8bf xv[TN][4];
+#pragma unroll
+    for (int b = 0; b < TN; ++b) {
+        const float sx = e8m0_operand((xsc[kWord][b] >> (8 * kSel)) & 0xFFu);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xv[b][q] = dequant_e4m3_bf16(f.b[b], q, sx);
+    }
 #pragma unroll
     for (int a = 0; a < TM; ++a) {
-        const v8i av = {(int)f.a[a].x, (int)f.a[a].y, (int)f.a[a].z, (int)f.a[a].w, 0, 0, 0, 0};
+        const float sw = e8m0_operand((wsc[kWord][a] >> (8 * kSel)) & 0xFFu);
+        v8bf wv[4];
 #pragma unroll
-        for (int b = 0; b < TN; ++b) {
-            // activations (E4M3) as the row operand, weights (E2M1) as the column operand:
-            // the swapped orientation of CfgW4A8 (line-wide epilogue stores)
-            acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                f.b[b], av, acc[a][b], kFmtE4M3, kFmtE2M1, kSel, (int)xsc[kWord][b], kSel,
-                (int)wsc[kWord][a]);
-        }
+        for (int q = 0; q < 4; ++q) wv[q] = dequant_e2m1_bf16(f.a[a], q, sw);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int b = 0; b < TN; ++b)
+                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xv[b][q], wv[q], acc[a][b],
+                                                                    0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int d = a * kSlots / TM; d < (a + 1) * kSlots / TM; ++d) dma(T * kSlots + d);
@@ -2377,10 +2472,8 @@ gemm_linear_skinny_kernel(DmaArgs p, const uint16_t* __restrict__ x, int64_t ldx
 // LDS DMA of every stage of its K range together with its token fragments and scales, waits
 // once, and multiplies.  The partial tiles are summed through LDS in wave order.  Tokens
 // (at most 16) are one MFMA column, loaded as fragments straight into registers: E2M1 16
-// bytes per lane (K block l/16); E4M3 32 bytes, lane group g holding elements 16g..16g+15
-// of the K-step's first half and of its second half (16-byte units g and 4 + g of the
-// 128-byte K-step row), the E4M3 operand layout of the 32x32x64 form extended to four
-// lane groups; a lane's scale byte belongs to K block l/16 either way.
+// bytes per lane (K block l/16); E4M3 the whole 32-byte block l/16, multiplied as four
+// bf16 16x16x32 MFMAs (w4a8_step16); a lane's scale byte belongs to K block l/16 either way.
 constexpr int kS16Rows = 16, kS16Waves = 8, kS16MaxK = 512, kS16MaxTokens = 16;
 constexpr int kS16Stage = kS16Rows * kRowBytes;               // one 128-byte line per row
 constexpr int kS16Per = kS16MaxK / kStageBlocks / kS16Waves;  // stages per wave, at most
@@ -2483,10 +2576,11 @@ gemm_skinny16_kernel(DmaArgs p, float* __restrict__ y)
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 if constexpr (F8) {
-                    const uint32_t c = xrow * xrb + (uint32_t)ks * 256u + 128u * j + 16u * lg;
+                    // E4M3 lane group g: all 32 bytes of block 4j + g of the stage
+                    const uint32_t c = xrow * xrb + (uint32_t)ks * 256u + 128u * j + 32u * lg;
                     xf[i][j][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)c, 0, 0);
                     xf[i][j][F8 ? 1 : 0] =
-                        __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(c + 64), 0, 0);
+                        __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(c + 16), 0, 0);
                 } else {
                     const uint32_t c = xrow * xrb + (uint32_t)ks * kRowBytes + 64u * j + 16u * lg;
                     xf[i][j][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)c, 0, 0);
@@ -2516,22 +2610,26 @@ gemm_skinny16_kernel(DmaArgs p, float* __restrict__ y)
                 const uint4 a = *reinterpret_cast<const uint4*>(row + 16 * ((4 * j + lg) ^ key));
                 const v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
                 const v4u u = xf[i][j][0];
-                v8i bv = {(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
-                if constexpr (F8) {
-                    const v4u v = xf[i][j][F8 ? 1 : 0];
-                    bv = v8i{(int)u.x, (int)u.y, (int)u.z, (int)u.w, (int)v.x, (int)v.y, (int)v.z, (int)v.w};
-                }
                 // tiled: byte 2j of the dword pre-shifted by the lane's lg/2; row-major: byte
                 // 0 of word j pre-shifted by lg
                 const uint32_t wsc = TS ? ws[i].x >> (8 * (lg >> 1)) : (j ? ws[i].y : ws[i].x) >> (8 * lg);
                 const uint32_t xsc = TS ? xs[i].x >> (8 * (lg >> 1)) : (j ? xs[i].y : xs[i].x) >> (8 * lg);
-                if (j == 0)
-                    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        av, bv, acc, kFmtE2M1, F8 ? 0 : kFmtE2M1, 0, (int)wsc, 0, (int)xsc);
-                else
-                    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        av, bv, acc, kFmtE2M1, F8 ? 0 : kFmtE2M1, TS ? 2 : 0, (int)wsc,
-                        TS ? 2 : 0, (int)xsc);
+                if constexpr (F8) {
+                    const v4u v = xf[i][j][F8 ? 1 : 0];
+                    const v8i bv = {(int)u.x, (int)u.y, (int)u.z, (int)u.w,
+                                    (int)v.x, (int)v.y, (int)v.z, (int)v.w};
+                    const int sel = (j && TS) ? 16 : 0;
+                    acc = w4a8_step16(acc, v4u{a.x, a.y, a.z, a.w}, bv, wsc >> sel, xsc >> sel);
+                } else {
+                    const v8i bv = {(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
+                    if (j == 0)
+                        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            av, bv, acc, kFmtE2M1, kFmtE2M1, 0, (int)wsc, 0, (int)xsc);
+                    else
+                        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            av, bv, acc, kFmtE2M1, kFmtE2M1, TS ? 2 : 0, (int)wsc, TS ? 2 : 0,
+                            (int)xsc);
+                }
             }
         }
     }
@@ -2582,8 +2680,8 @@ gemm_skinny16_kernel(DmaArgs p, float* __restrict__ y)
 // buffers are static arrays, apart from the dynamic panel, so the encoder's stores do not
 // wait for the weight DMA.  Token fragments and scales then come from LDS (scale bytes in
 // plain order, one per lane).  S k <= kLin16MaxSK, so that panel and buffers fit in LDS.
-// F8: the tokens encoded to MXFP8 (E4M3, 32 bytes per block: the W4A8 layer), fragments in
-// gemm_skinny16_kernel's E4M3 lane layout, S k <= kLin16MaxSK8.  W: waves per workgroup
+// F8: the tokens encoded to MXFP8 (E4M3, 32 bytes per block: the W4A8 layer), lane group g
+// taking block 4j + g whole as in gemm_skinny16_kernel, S k <= kLin16MaxSK8.  W: waves per workgroup
 // (E2M1 tokens: 16 when one round of workgroups covers `out`, the encoding spread over
 // twice the lanes, measured 7-9% faster there, and 8 otherwise, where 16 measured 3-7%
 // slower; E4M3 tokens: 8, where 16 measured up to 25% slower).
@@ -2707,26 +2805,27 @@ gemm_linear16_kernel(DmaArgs p, const uint16_t* __restrict__ x, int64_t ldx,
                 const int blk = 8 * ks + 4 * j + lg;
                 const uint4 a = *reinterpret_cast<const uint4*>(row + 16 * ((4 * j + lg) ^ key));
                 const v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
-                v8i bv;
-                if constexpr (F8) {
-                    // E4M3 lane group g: 16-byte units g and 4 + g of the K-step's 128 bytes
-                    const uint8_t* kr = xrow + kCB * (8 * ks + 4 * j);
-                    const uint4 u = *reinterpret_cast<const uint4*>(kr + 16 * lg);
-                    const uint4 v = *reinterpret_cast<const uint4*>(kr + 64 + 16 * lg);
-                    bv = v8i{(int)u.x, (int)u.y, (int)u.z, (int)u.w, (int)v.x, (int)v.y, (int)v.z, (int)v.w};
-                } else {
-                    const uint4 u = *reinterpret_cast<const uint4*>(xrow + kCB * blk);
-                    bv = v8i{(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
-                }
                 const uint32_t wsc = TS ? ws[i].x >> (8 * (lg >> 1)) : (j ? ws[i].y : ws[i].x) >> (8 * lg);
                 const uint32_t xsc = xsrow[blk];
-                constexpr int kFmtX = F8 ? 0 : kFmtE2M1;
-                if (j == 0)
-                    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        av, bv, acc, kFmtE2M1, kFmtX, 0, (int)wsc, 0, (int)xsc);
-                else
-                    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        av, bv, acc, kFmtE2M1, kFmtX, TS ? 2 : 0, (int)wsc, 0, (int)xsc);
+                if constexpr (F8) {
+                    // E4M3 lane group g: all 32 bytes of block 4j + g of the K-step
+                    const uint8_t* kb = xrow + kCB * blk;
+                    const uint4 u = *reinterpret_cast<const uint4*>(kb);
+                    const uint4 v = *reinterpret_cast<const uint4*>(kb + 16);
+                    const v8i bv = {(int)u.x, (int)u.y, (int)u.z, (int)u.w,
+                                    (int)v.x, (int)v.y, (int)v.z, (int)v.w};
+                    acc = w4a8_step16(acc, v4u{a.x, a.y, a.z, a.w}, bv,
+                                      wsc >> ((j && TS) ? 16 : 0), xsc);
+                } else {
+                    const uint4 u = *reinterpret_cast<const uint4*>(xrow + kCB * blk);
+                    const v8i bv = {(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
+                    if (j == 0)
+                        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            av, bv, acc, kFmtE2M1, kFmtE2M1, 0, (int)wsc, 0, (int)xsc);
+                    else
+                        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            av, bv, acc, kFmtE2M1, kFmtE2M1, TS ? 2 : 0, (int)wsc, 0, (int)xsc);
+                }
             }
         }
     }
