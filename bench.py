@@ -411,6 +411,79 @@ def measure(name, args):
     return rec, L
 
 
+def measure_gemm_data(name, args):
+    """The W4A4 GEMM alone on one layer shape with three operand contents: the layer's own
+    codes (quantised activations, prepared weights), uniformly random code bytes, and all-zero
+    codes, every one with the layer's scale bytes.  Same kernel, same launches, same bytes
+    moved; only the values differ.  Returns one record with the three graph-timed durations."""
+    import numpy as np
+    import torch
+
+    import w4a4_batq_quantize_amd as bq
+    import workloads as wl
+
+    L = wl.make_layer(name)
+    S, N, out = L.cfg.S, L.cfg.N, L.cfg.out
+    k = N // 32
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    layout = bq.SCALES_MFMA_TILED
+    A = torch.from_numpy(L.A).to(dev)
+    B = torch.from_numpy(L.B).to(dev)
+    rmin = torch.from_numpy(bq.clip_ratios(L.alpha_min)).to(dev)
+    rmax = torch.from_numpy(bq.clip_ratios(L.alpha_max)).to(dev)
+    wq0, we0 = bq.prepare_weight(torch.from_numpy(L.W).to(dev), L.A, L.B, layout=layout)
+    x0 = torch.from_numpy(L.x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    xq0, xe0 = bq.quantize_act(x0, A, B, rmin, rmax, layout=layout)
+    del x0
+    torch.cuda.synchronize()
+    per_set = S * (N // 2 + k) + out * (N // 2 + k) + 4 * S * out
+    R = min(64, max(2, math.ceil(args.rotate_bytes / per_set)))
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+
+    def codes(kind, like):
+        if kind == "layer":
+            return like.clone()
+        if kind == "zero":
+            return torch.zeros_like(like)
+        return torch.randint(0, 256, like.shape, dtype=torch.int32, device=dev,
+                             generator=g).to(torch.uint8)
+
+    stream = torch.cuda.current_stream()
+    times = {}
+    for kind in ("layer", "random", "zero"):
+        sets = [(codes(kind, xq0), xe0.clone(), codes(kind, wq0), we0.clone(),
+                 torch.empty((S, out), dtype=torch.float32, device=dev)) for _ in range(R)]
+
+        def launch(j, st, sets=sets):
+            xq, xe, wq, we, y = sets[j]
+            return bq.gemm_w4a4_raw(xq.data_ptr(), xe.data_ptr(), wq.data_ptr(), we.data_ptr(),
+                                    S, N, out, y.data_ptr(), layout, st)
+        for j in range(R):                      # warm-up, untimed
+            if launch(j, stream.cuda_stream):
+                raise RuntimeError("library call failed")
+        torch.cuda.synchronize()
+        times[kind] = time_graph(stream, launch, 0, args.steps, R)
+        del sets
+        torch.cuda.empty_cache()
+    flops = k2_flops(S, N, out)
+    return {
+        "metric": "W4A4 MXFP4 GEMM time by operand contents (same kernel, shape and bytes)",
+        "unit": "us",
+        "config": {"workload": f"{name}: S={S} N={N} out={out}", "S": S, "N": N, "out": out,
+                   "rotated_buffer_sets": R, "scale_layout": "mfma_tiled",
+                   "operands": {"layer": "the layer's quantised activations and prepared "
+                                         "weights",
+                                "random": "uniformly random code bytes, the layer's scales",
+                                "zero": "all-zero code bytes, the layer's scales"}},
+        "steps": args.steps,
+        "gemm_us": {kd: round(t * 1e6, 3) for kd, t in times.items()},
+        "gemm_tflops": {kd: round(flops / t / 1e12, 1) for kd, t in times.items()},
+        "peak_tflops": FP4_PEAK_TFLOPS,
+    }
+
+
 # KV-cache side of attention with a transformed, quantised cache (W4A8KV8 / W4A8KV4), on the
 # evaluated 8B model's attention shape: 8 kv heads x head dim 128, 32 query heads (GQA 4).
 KV_HEADS, HEAD_DIM, GQA_GROUP = 8, 128, 4
@@ -627,6 +700,9 @@ def main():
                          "or kv_decode)")
     ap.add_argument("--all", action="store_true",
                     help="measure every layer configuration, one JSON line each (no CPU baseline)")
+    ap.add_argument("--gemm-data", action="store_true",
+                    help="time the W4A4 GEMM alone on the layer's codes, random codes and "
+                         "all-zero codes (the dependence of its speed on operand values)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: the path runs on one GPU; --gpus must be 1",
@@ -640,6 +716,9 @@ def main():
         if not args.no_cpu_baseline:
             rec["cpu_baseline"] = cpu_baseline_kv(L, fmt, args.cpu_seconds)
         print(json.dumps(rec), flush=True)
+        return
+    if args.gemm_data:
+        print(json.dumps(measure_gemm_data(args.config, args)), flush=True)
         return
     if args.all:
         import workloads as wl

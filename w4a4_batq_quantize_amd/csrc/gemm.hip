@@ -643,7 +643,10 @@ __device__ __forceinline__ void epi_store1(const DmaArgs& p, float* __restrict__
 
 // Store of the swapped orientation (C::SW): lane l of tile (a, b) holds, in register r,
 // y[s][o] with o = 32a + l%32 and s = 32b + 8(r/4) + 4(l/32) + r%4 relative to the wave's
-// origin; each store instruction writes two tokens' 32 consecutive outputs.
+// origin; each store instruction writes two tokens' 32 consecutive outputs.  Interior tiles
+// store with the non-temporal hint: the output is written once and never read back here, so
+// it should not displace operand lines that other tiles still read from the caches
+// (graph-timed on one box: q_proj 25.5 -> 23.7 us, down_proj 58.9 -> 56.6 us).
 template <class C>
 __device__ __forceinline__ void store_tile_sw(const v16f (&acc)[C::TM][C::TN], const DmaArgs& p,
                                               float* __restrict__ y, int64_t o0, int64_t s0,
@@ -659,7 +662,8 @@ __device__ __forceinline__ void store_tile_sw(const v16f (&acc)[C::TM][C::TN], c
             for (int a = 0; a < C::TM; ++a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    base[(32 * b + 8 * (r >> 2) + (r & 3)) * p.out + 32 * a] = acc[a][b][r];
+                    __builtin_nontemporal_store(
+                        acc[a][b][r], &base[(32 * b + 8 * (r >> 2) + (r & 3)) * p.out + 32 * a]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -1252,7 +1256,8 @@ __device__ __forceinline__ void big_tile_origin(int64_t i, int64_t tiles_o, int6
 
 // fp32 output of a wave's TM x TN accumulator tiles: lane l of tile (a, b) holds, in register
 // r, y[s][o] with o = 32a + l%32 and s = 32b + 8(r/4) + 4(l/32) + r%4 relative to the wave's
-// origin; each store instruction writes two tokens' 32 consecutive outputs.
+// origin; each store instruction writes two tokens' 32 consecutive outputs, non-temporal as
+// in store_tile_sw (S = 16384: N = 12288 397 -> 392 us, N = 4096 155 -> 146 us).
 template <int TM, int TN>
 __device__ __forceinline__ void big_store(const v16f (&acc)[TM][TN], const DmaArgs& p,
                                           float* __restrict__ y, int64_t o0, int64_t s0,
@@ -1268,7 +1273,8 @@ __device__ __forceinline__ void big_store(const v16f (&acc)[TM][TN], const DmaAr
             for (int a = 0; a < TM; ++a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    base[(32 * b + 8 * (r >> 2) + (r & 3)) * p.out + 32 * a] = acc[a][b][r];
+                    __builtin_nontemporal_store(
+                        acc[a][b][r], &base[(32 * b + 8 * (r >> 2) + (r & 3)) * p.out + 32 * a]);
                 __builtin_amdgcn_sched_barrier(0);
             }
         return;
