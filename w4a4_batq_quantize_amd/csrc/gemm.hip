@@ -939,8 +939,10 @@ gemm_pc_kernel(DmaArgs p, float* __restrict__ y, int64_t tiles_o, int64_t tiles_
 // registers: after the barrier that ends stage s the buffer of stage s is refilled with
 // stage s + 4 (of this tile or the next), so stages s+1 .. s+4 are in flight during stage s.
 // The scales come as whole 256-byte units of the MFMA-tiled layout (one 32-row panel x 8
-// blocks: two stages) into a ring of four 4 KB unit buffers, issued with the even stage's
-// codes.
+// blocks: two stages) into a ring of four 4 KB unit buffers.  Every fourth stage each wave
+// issues one 1 KB instruction (four panels of one unit, 16 bytes per lane): waves 0-3 the
+// stage's unit, waves 4-7 the next one.  Sixteen 4-byte-per-lane instructions per unit, the
+// form before this one, held the matrix cores back measurably more than four of these.
 //
 // LDS layout of a code buffer: tile rows 0..255 weights, 256..511 tokens, 64 bytes each; the
 // 16-byte chunk c of row r sits at slot c ^ ((r / 4) % 4).  gfx950's LDS serves a
@@ -979,14 +981,17 @@ struct BigCfg {
     static constexpr int kWaves = WO * WS, kThreads = 64 * kWaves;
     static constexpr int TM = BO / WO / 32, TN = BS / WS / 32;
     static constexpr int kCodeDma = big::kCodeBytes / 1024 / kWaves;   // per wave per stage
-    static constexpr int kScaleDma = big::kPanels / kWaves;            // per wave per unit
-    // this wave's DMA instructions of two consecutive stages (exactly one of them even)
-    static constexpr int kWait = 2 * kCodeDma + kScaleDma;
-    static_assert(kCodeDma >= 1 && kScaleDma >= 1 && kWaves * kScaleDma == big::kPanels, "split");
+    // this wave's DMA instructions of stage t: its code share, and with every fourth stage
+    // one 1 KB instruction of scales
+    static constexpr int count(int t) { return kCodeDma + (t % 4 == 0 ? 1 : 0); }
+    // the wait in stage I (its index in a group of 8): stages I+2 and I+3 stay in flight
+    static constexpr int wait(int I) { return count(I + 2) + count(I + 3); }
+    // two units of 16 panels x 256 bytes per four stages: one 1 KB instruction per wave
+    static_assert(kCodeDma >= 1 && kWaves == 8 && 2 * big::kUnitBytes == kWaves * 1024, "split");
     static_assert(BO % (WO * 32) == 0 && BS % (WS * 32) == 0, "tiles");
     static_assert(big::NB * big::kCodeBytes + big::NSC * big::kUnitBytes <= 160 * 1024, "LDS");
     // a wave streams weight rows only or token rows only
-    static_assert((BO / 16) % kCodeDma == 0 && (BO / 32) % kScaleDma == 0, "weight waves");
+    static_assert((BO / 16) % kCodeDma == 0 && BO / 32 == 8, "weight waves");
 };
 
 // This wave's DMA: its operand (weights or tokens), the lane offsets of its instructions
@@ -994,9 +999,10 @@ struct BigCfg {
 struct BigPlan {
     __amdgpu_buffer_rsrc_t code, scale;
     uint32_t code_off[8];                        // per DMA instruction
-    uint32_t scale_off[4];                       // per unit instruction
+    uint32_t scale_off;                          // the scale instruction
     uint32_t row_bytes, panel_bytes;             // 16 k, 32 k
-    bool weights;
+    int nst;                                     // stages per tile
+    bool weights, sweights;                      // code rows / scale panels of the weights
 };
 
 template <class C>
@@ -1007,20 +1013,22 @@ __device__ __forceinline__ void big_plan(BigPlan& pl, const DmaArgs& p, int wave
     const int tile0 = w ? 0 : C::BO;
     pl.weights = w;
     pl.code = buffer_rsrc(w ? p.wq : p.xq, rows * 16 * p.k);
-    pl.scale = buffer_rsrc(w ? p.we : p.xe, ((rows + 31) / 32) * 32 * p.k);
+    // scale instruction of wave v: panels 4 ((v % 4) % 2) .. + 3 of the weights (v % 4 < 2) or
+    // of the tokens, lanes 16 j .. 16 j + 15 carrying panel + j, 16 bytes each
+    const bool sw = (wave & 3) < 2;
+    pl.sweights = sw;
+    pl.scale = buffer_rsrc(sw ? p.we : p.xe, (((sw ? p.out : p.S) + 31) / 32) * 32 * p.k);
     pl.row_bytes = (uint32_t)(16 * p.k);
     pl.panel_bytes = (uint32_t)(32 * p.k);
+    pl.nst = (int)(p.k / 4);
 #pragma unroll
     for (int i = 0; i < C::kCodeDma; ++i) {
         const int r = (wave * C::kCodeDma + i) * 16 + (lane >> 2) - tile0;   // operand row in tile
         const int c = (lane & 3) ^ ((r >> 2) & 3);
         pl.code_off[i] = (uint32_t)r * pl.row_bytes + 16u * (uint32_t)c;
     }
-#pragma unroll
-    for (int j = 0; j < C::kScaleDma; ++j) {
-        const int panel = (wave * C::kScaleDma + j) - tile0 / 32;
-        pl.scale_off[j] = (uint32_t)panel * pl.panel_bytes + 4u * (uint32_t)lane;
-    }
+    pl.scale_off = (uint32_t)(4 * (wave & 1) + (lane >> 4)) * pl.panel_bytes +
+                   16u * (uint32_t)(lane & 15);
 }
 
 // A tile as the DMA sees it: the uniform byte offsets of this wave's operand rows, and the
@@ -1034,8 +1042,9 @@ template <class C>
 __device__ __forceinline__ BigTile big_tile(const BigPlan& pl, int64_t o0, int64_t s0, int rot)
 {
     const uint32_t first = (uint32_t)(pl.weights ? o0 : s0);
+    const uint32_t sfirst = (uint32_t)(pl.sweights ? o0 : s0);
     return BigTile{(uint32_t)__builtin_amdgcn_readfirstlane((int)(first * pl.row_bytes)),
-                   (uint32_t)__builtin_amdgcn_readfirstlane((int)((first / 32) * pl.panel_bytes)),
+                   (uint32_t)__builtin_amdgcn_readfirstlane((int)((sfirst / 32) * pl.panel_bytes)),
                    __builtin_amdgcn_readfirstlane(rot)};
 }
 
@@ -1080,13 +1089,14 @@ __device__ __forceinline__ void static_for(F&& f)
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// The DMA of one stage, I = its index in its group of 8 (code buffer I % 4; with the unit
-// of the stage pair when I is even): this wave's instructions, unit first, one call per
-// instruction d = 0 .. count-1, so that the caller can spread them between MFMAs.
+// The DMA of one stage, I = its index in its group of 8 (code buffer I % 4; when I % 4 == 0
+// also the scales of stages I .. I+3: unit I/2 from waves 0-3, unit I/2 + 1 from waves 4-7):
+// this wave's instructions, scales first, one call per instruction d = 0 .. count-1, so that
+// the caller can spread them between MFMAs.
 template <class C, int I>
 struct BigDma {
-    static constexpr int kScale = (I & 1) == 0 ? C::kScaleDma : 0;
-    static constexpr int kCount = kScale + C::kCodeDma;
+    static constexpr int kScale = I % 4 == 0 ? 1 : 0;
+    static constexpr int kCount = C::count(I);
     template <int D>
     __device__ __forceinline__ static void issue(const BigPlan& pl, const BigTile& t, int ph,
                                                  int wave)
@@ -1098,9 +1108,18 @@ struct BigDma {
         uint32_t woff = (uint32_t)wave;
         asm volatile("" : "+s"(woff));
         if constexpr (D < kScale) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                pl.scale, (lds_void_t*)(big_unit<I / 2>() + (woff * C::kScaleDma + D) * 256), 4,
-                pl.scale_off[D], (int)(t.scale_base + (uint32_t)(ph / 2) * 256u), 0, 0);
+            // waves 4-7 carry the next unit (stages ph + 2, ph + 3, wrapping with the K
+            // rotation); each wave's four panels land at panel (v % 4) * 4 of the unit
+            const int ph2 = ph + 2 < pl.nst ? ph + 2 : ph + 2 - pl.nst;
+            const uint32_t woff4 = (woff & 3u) * 1024u;
+            if (wave < 4)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    pl.scale, (lds_void_t*)(big_unit<I / 2>() + woff4), 16, pl.scale_off,
+                    (int)(t.scale_base + (uint32_t)(ph / 2) * 256u), 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    pl.scale, (lds_void_t*)(big_unit<I / 2 + 1>() + woff4), 16, pl.scale_off,
+                    (int)(t.scale_base + (uint32_t)(ph2 / 2) * 256u), 0, 0);
         } else if constexpr (D < kCount) {
             constexpr int c = D - kScale;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -1213,7 +1232,7 @@ __device__ __forceinline__ void big_stage(v16f (&acc)[C::TM][C::TN], const BigPl
         constexpr int i = decltype(ic)::value;
         {
             if constexpr (i == 0) {
-                __builtin_amdgcn_s_waitcnt(waitcnt_imm(C::kWait, 0));
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm(C::wait(I), 0));
                 barrier_only();
             }
             // slots 1.. : two DMA instructions and two reads per slot
@@ -1323,7 +1342,7 @@ gemm_big_kernel(DmaArgs p, float* __restrict__ y, int64_t tiles_o, int64_t tiles
         });
     });
     // stage 0: this wave's part once stages 1..3 remain in flight, then all of it
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(C::kWait + C::kCodeDma, 0));
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(C::count(1) + C::count(2) + C::count(3), 0));
     barrier_only();
     BigFrags<C::TM, C::TN> f0, f1;
     BigScales<C::TM, C::TN> sc;
