@@ -411,11 +411,13 @@ def measure(name, args):
     return rec, L
 
 
-def measure_gemm_data(name, args):
-    """The W4A4 GEMM alone on one layer shape with three operand contents: the layer's own
-    codes (quantised activations, prepared weights), uniformly random code bytes, and all-zero
-    codes, every one with the layer's scale bytes.  Same kernel, same launches, same bytes
-    moved; only the values differ.  Returns one record with the three graph-timed durations."""
+def measure_data_dependence(name, args):
+    """Each kernel of the W4A4 path alone on one layer shape with three operand contents.
+    GEMM: the layer's own codes (quantised activations, prepared weights), uniformly random
+    code bytes, and all-zero codes, every one with the layer's scale bytes.  Quantiser: the
+    layer's bf16 activations, N(0,1) activations, and all-zero activations.  Same kernels,
+    same launches, same bytes moved; only the values differ.  Returns one record with the
+    graph-timed durations."""
     import numpy as np
     import torch
 
@@ -435,7 +437,6 @@ def measure_gemm_data(name, args):
     wq0, we0 = bq.prepare_weight(torch.from_numpy(L.W).to(dev), L.A, L.B, layout=layout)
     x0 = torch.from_numpy(L.x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
     xq0, xe0 = bq.quantize_act(x0, A, B, rmin, rmax, layout=layout)
-    del x0
     torch.cuda.synchronize()
     per_set = S * (N // 2 + k) + out * (N // 2 + k) + 4 * S * out
     R = min(64, max(2, math.ceil(args.rotate_bytes / per_set)))
@@ -467,9 +468,33 @@ def measure_gemm_data(name, args):
         times[kind] = time_graph(stream, launch, 0, args.steps, R)
         del sets
         torch.cuda.empty_cache()
+    # the quantiser on the layer's activations, N(0,1) activations and zeros
+    R1 = min(64, max(2, math.ceil(args.rotate_bytes / (S * N * 2 + S * (N // 2 + k)))))
+    qtimes = {}
+    for kind in ("layer", "random", "zero"):
+        if kind == "layer":
+            xs = [x0.clone() for _ in range(R1)]
+        elif kind == "random":
+            xs = [torch.randn((S, N), device=dev, generator=g).to(torch.bfloat16)
+                  for _ in range(R1)]
+        else:
+            xs = [torch.zeros((S, N), dtype=torch.bfloat16, device=dev) for _ in range(R1)]
+        qs = [(torch.empty_like(xq0), torch.empty_like(xe0)) for _ in range(R1)]
+
+        def launch_q(j, st, xs=xs, qs=qs):
+            return bq.quantize_act_raw(xs[j].data_ptr(), S, N, N, A.data_ptr(), B.data_ptr(),
+                                       rmin.data_ptr(), rmax.data_ptr(), qs[j][0].data_ptr(),
+                                       qs[j][1].data_ptr(), layout, st)
+        for j in range(R1):
+            if launch_q(j, stream.cuda_stream):
+                raise RuntimeError("library call failed")
+        torch.cuda.synchronize()
+        qtimes[kind] = time_graph(stream, launch_q, 0, args.steps, R1)
+        del xs, qs
+        torch.cuda.empty_cache()
     flops = k2_flops(S, N, out)
     return {
-        "metric": "W4A4 MXFP4 GEMM time by operand contents (same kernel, shape and bytes)",
+        "metric": "W4A4 path kernel times by operand contents (same kernels, shapes and bytes)",
         "unit": "us",
         "config": {"workload": f"{name}: S={S} N={N} out={out}", "S": S, "N": N, "out": out,
                    "rotated_buffer_sets": R, "scale_layout": "mfma_tiled",
@@ -481,6 +506,10 @@ def measure_gemm_data(name, args):
         "gemm_us": {kd: round(t * 1e6, 3) for kd, t in times.items()},
         "gemm_tflops": {kd: round(flops / t / 1e12, 1) for kd, t in times.items()},
         "peak_tflops": FP4_PEAK_TFLOPS,
+        "quantize_us": {kd: round(t * 1e6, 3) for kd, t in qtimes.items()},
+        "quantize_gbs": {kd: round(k1_bytes(S, N) / t / 1e9, 1) for kd, t in qtimes.items()},
+        "quantize_operands": {"layer": "the layer's bf16 activations",
+                              "random": "N(0,1) bf16 activations", "zero": "all-zero activations"},
     }
 
 
@@ -700,9 +729,10 @@ def main():
                          "or kv_decode)")
     ap.add_argument("--all", action="store_true",
                     help="measure every layer configuration, one JSON line each (no CPU baseline)")
-    ap.add_argument("--gemm-data", action="store_true",
-                    help="time the W4A4 GEMM alone on the layer's codes, random codes and "
-                         "all-zero codes (the dependence of its speed on operand values)")
+    ap.add_argument("--data-dependence", action="store_true",
+                    help="time the quantiser and the W4A4 GEMM alone on the layer's operands, "
+                         "random operands and all-zero operands (the dependence of their speed "
+                         "on the values)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: the path runs on one GPU; --gpus must be 1",
@@ -717,8 +747,8 @@ def main():
             rec["cpu_baseline"] = cpu_baseline_kv(L, fmt, args.cpu_seconds)
         print(json.dumps(rec), flush=True)
         return
-    if args.gemm_data:
-        print(json.dumps(measure_gemm_data(args.config, args)), flush=True)
+    if args.data_dependence:
+        print(json.dumps(measure_data_dependence(args.config, args)), flush=True)
         return
     if args.all:
         import workloads as wl
