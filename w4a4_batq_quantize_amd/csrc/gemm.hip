@@ -14,7 +14,11 @@
 //    V_MFMA_SCALE_F32_32X32X64_F8F6F4 on 256 (out) x 128 (token) tiles, operands moved
 //    HBM/L2 -> LDS by buffer_load ... lds without passing through registers, three LDS
 //    stages; producer waves issue the DMA and consumer waves the MFMAs in the first;
-//  - gemm_w4a8_kernel (S > 64, E4M3 tokens): the same tile shape and DMA, bf16 MFMAs;
+//  - gemm_big_kernel (two or more rounds of 256 x 256 tiles, MFMA-tiled scales, fp32
+//    output without residual): persistent workgroups whose waves all stream and multiply,
+//    256-element K stages moved as whole 128-byte lines, the stage DMA running on from one
+//    tile into the next;
+//  - gemm_w4a8_kernel (S > 64, E4M3 tokens): the 256 x 128 tile and DMA, bf16 MFMAs;
 //  - gemm_skinny16_kernel (S <= 16, by a workgroup-rounds rule) and gemm_skinny_kernel
 //    (S <= 64 otherwise): weight streaming, 16 or 32 output rows per workgroup and K split
 //    across its waves;
@@ -934,41 +938,36 @@ gemm_pc_kernel(DmaArgs p, float* __restrict__ y, int64_t tiles_o, int64_t tiles_
 // timestamps: a tile's first stage waited ~6 us for its data and its stores took ~3.5-6 us
 // when every tile began and ended in a round of its own).
 //
-// K stages are 128 elements (64 code bytes per operand row: a whole 64-byte request per
-// row).  Four stage buffers of 32 KB are all in flight while the matrix cores work from
-// registers: after the barrier that ends stage s the buffer of stage s is refilled with
-// stage s + 4 (of this tile or the next), so stages s+1 .. s+4 are in flight during stage s.
-// The scales come as whole 256-byte units of the MFMA-tiled layout (one 32-row panel x 8
-// blocks: two stages) into a ring of four 4 KB unit buffers.  Every fourth stage each wave
-// issues one 1 KB instruction (four panels of one unit, 16 bytes per lane): waves 0-3 the
-// stage's unit, waves 4-7 the next one (four instructions per unit where one 4-byte-per-lane
-// instruction per panel takes sixteen; measured 0.4-0.6% faster on the multi-round shapes).
+// K stages are 256 elements: 128 code bytes per operand row, so each DMA instruction moves
+// 8 whole 128-byte lines (a DMA probe on this chip: 54 B/clk per CU for whole lines against
+// 29 for 16 half lines of 64 bytes per instruction, whatever the bytes in flight; at the
+// matrix cores' full rate this tile consumes 33).  Two stage buffers of 64 KB and two 4 KB
+// scale units (the MFMA-tiled layout's 256-byte unit of a 32-row panel is one stage) fill
+// the LDS: during stage s the buffers hold stages s and s+1, and once every wave has read
+// stage s (a barrier before its last K-step, which also finds all of stage s+1 landed) its
+// buffer is refilled with stage s+2, of this tile or the next, between the last K-step's
+// MFMAs.  Each wave's DMA per stage: 8 code instructions (rows 64 v .. 64 v + 63 of the
+// tile, weights for waves 0-3) and two 4-byte-per-lane scale instructions (panels 2 (v % 4)
+// and 2 (v % 4) + 1 of its operand), the same count for every wave, so nothing in the
+// MFMA stream depends on the wave (a per-wave branch there spilled every register).
 //
-// LDS layout of a code buffer: tile rows 0..255 weights, 256..511 tokens, 64 bytes each; the
-// 16-byte chunk c of row r sits at slot c ^ ((r / 4) % 4).  gfx950's LDS serves a
-// ds_read_b128 16 lanes at a time from 64 banks (256 bytes): the 16 lanes reading rows
-// r..r+15 (r a multiple of 16) at one chunk then hit 16 distinct 16-byte bank groups (4
-// rows per bank row x 4 slots); measured conflict-free (the same rate as contiguous reads).
-// The DMA writes 64 lanes x 16 bytes contiguously (16 rows per instruction), lane l
-// fetching chunk (l % 4) ^ ((row / 4) % 4) of row l / 4.  Lane offsets are the same for
-// every tile; the tile's first row enters as the instruction's uniform offset, and rows past
-// the end of an operand read zeros (the buffer descriptor's size), which no stored output
-// uses.
+// LDS layout of a code buffer: tile rows 0..255 weights, 256..511 tokens, 128 bytes each;
+// the 16-byte chunk c of row r sits at slot c ^ ((r / 2) % 8), the conflict-free layout of
+// the tiled kernels above.  Lane offsets are the same for every tile; the tile's first row
+// enters as the instruction's uniform offset, and rows past the end of an operand read
+// zeros (the buffer descriptor's size), which no stored output uses.
 //
 // Waves: WO x WS, each owning (256/WO) x (256/WS) outputs as TM x TN 32 x 32 MFMA tiles (the
 // activation tile is the MFMA row operand: line-wide epilogue stores as in the tiled
 // kernels above).  Each K-step issues its MFMAs one at a time with the memory instructions
-// of the wave in between (the next K-step's fragments; after the stage's barrier, the DMA
-// of stage s+4 and the next stage's scales and fragments).
+// of the wave in between (the next K-step's fragments; in the last K-step the DMA of stage
+// s+2 and the next stage's scales and first fragments).
 namespace big {
 constexpr int BO = 256, BS = 256;
-constexpr int kRowB = 64;                        // code bytes per operand row per stage
+constexpr int kRowB = 128;                       // code bytes per operand row per stage
 constexpr int kRows = BO + BS;
-constexpr int kCodeBytes = kRows * kRowB;        // 32 KB
-constexpr int kPanels = kRows / 32;              // 16 scale panels
-constexpr int kUnitBytes = kPanels * 256;        // 4 KB: the scales of two stages
-constexpr int NB = 4;                            // code buffers (stages s+1..s+4 in flight)
-constexpr int NSC = 4;                           // scale unit buffers
+constexpr int kCodeBytes = kRows * kRowB;        // 64 KB
+constexpr int kUnitBytes = (kRows / 32) * 256;   // 4 KB: the scales of one stage
 }  // namespace big
 
 template <int WO_, int WS_, bool ROT_ = true, int GO_ = 4>
@@ -977,62 +976,49 @@ struct BigCfg {
     static constexpr bool kRotate = ROT_;        // K rotation of the tiles (see k_rotation)
     static constexpr int kGroupO = GO_;          // weight tiles per XCD sweep (see tile_origin)
     static constexpr int BO = big::BO, BS = big::BS;
-    static constexpr bool SW = true, TS = true;
     static constexpr int kWaves = WO * WS, kThreads = 64 * kWaves;
     static constexpr int TM = BO / WO / 32, TN = BS / WS / 32;
     static constexpr int kCodeDma = big::kCodeBytes / 1024 / kWaves;   // per wave per stage
-    // this wave's DMA instructions of stage t: its code share, and with every fourth stage
-    // one 1 KB instruction of scales
-    static constexpr int count(int t) { return kCodeDma + (t % 4 == 0 ? 1 : 0); }
-    // the wait in stage I (its index in a group of 8): stages I+2 and I+3 stay in flight
-    static constexpr int wait(int I) { return count(I + 2) + count(I + 3); }
-    // two units of 16 panels x 256 bytes per four stages: one 1 KB instruction per wave
-    static_assert(kCodeDma >= 1 && kWaves == 8 && 2 * big::kUnitBytes == kWaves * 1024, "split");
+    static constexpr int kDma = kCodeDma + 2;                           // with the two scale ones
+    static_assert(kWaves == 8 && kCodeDma == 8, "a wave streams 64 rows of one operand");
     static_assert(BO % (WO * 32) == 0 && BS % (WS * 32) == 0, "tiles");
-    static_assert(big::NB * big::kCodeBytes + big::NSC * big::kUnitBytes <= 160 * 1024, "LDS");
-    // a wave streams weight rows only or token rows only
-    static_assert((BO / 16) % kCodeDma == 0 && BO / 32 == 8, "weight waves");
+    static_assert(2 * big::kCodeBytes + 2 * big::kUnitBytes <= 160 * 1024, "LDS");
 };
 
 // This wave's DMA: its operand (weights or tokens), the lane offsets of its instructions
 // (the same for every tile), and the operand's bytes per row and per 32-row scale panel.
 struct BigPlan {
     __amdgpu_buffer_rsrc_t code, scale;
-    uint32_t code_off[8];                        // per DMA instruction
-    uint32_t scale_off;                          // the scale instruction
+    uint32_t code_off[8];                        // per code instruction
+    uint32_t scale_off[2];                       // per scale instruction
     uint32_t row_bytes, panel_bytes;             // 16 k, 32 k
-    int nst;                                     // stages per tile
-    bool weights, sweights;                      // code rows / scale panels of the weights
+    bool weights;
 };
 
 template <class C>
 __device__ __forceinline__ void big_plan(BigPlan& pl, const DmaArgs& p, int wave, int lane)
 {
-    const bool w = wave * C::kCodeDma * 16 < C::BO;
+    const bool w = wave < 4;                     // rows 64 wave .. 64 wave + 63 of the tile
     const int64_t rows = w ? p.out : p.S;
     const int tile0 = w ? 0 : C::BO;
     pl.weights = w;
     pl.code = buffer_rsrc(w ? p.wq : p.xq, rows * 16 * p.k);
-    // scale instruction of wave v: panels 4 ((v % 4) % 2) .. + 3 of the weights (v % 4 < 2) or
-    // of the tokens, lanes 16 j .. 16 j + 15 carrying panel + j, 16 bytes each
-    const bool sw = (wave & 3) < 2;
-    pl.sweights = sw;
-    pl.scale = buffer_rsrc(sw ? p.we : p.xe, (((sw ? p.out : p.S) + 31) / 32) * 32 * p.k);
+    pl.scale = buffer_rsrc(w ? p.we : p.xe, ((rows + 31) / 32) * 32 * p.k);
     pl.row_bytes = (uint32_t)(16 * p.k);
     pl.panel_bytes = (uint32_t)(32 * p.k);
-    pl.nst = (int)(p.k / 4);
 #pragma unroll
     for (int i = 0; i < C::kCodeDma; ++i) {
-        const int r = (wave * C::kCodeDma + i) * 16 + (lane >> 2) - tile0;   // operand row in tile
-        const int c = (lane & 3) ^ ((r >> 2) & 3);
+        const int r = (wave * C::kCodeDma + i) * 8 + (lane >> 3) - tile0;   // operand row in tile
+        const int c = (lane & 7) ^ ((r >> 1) & 7);
         pl.code_off[i] = (uint32_t)r * pl.row_bytes + 16u * (uint32_t)c;
     }
-    pl.scale_off = (uint32_t)(4 * (wave & 1) + (lane >> 4)) * pl.panel_bytes +
-                   16u * (uint32_t)(lane & 15);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+        pl.scale_off[j] = (uint32_t)(2 * (wave & 3) + j) * pl.panel_bytes + 4u * (uint32_t)lane;
 }
 
-// A tile as the DMA sees it: the uniform byte offsets of this wave's operand rows, and the
-// K rotation of the tile's stages (even).
+// A tile as the DMA sees it: the uniform byte offsets of this wave's operand rows and scale
+// panels, and the K rotation of the tile's stages.
 struct BigTile {
     uint32_t code_base, scale_base;
     int rot;
@@ -1042,39 +1028,30 @@ template <class C>
 __device__ __forceinline__ BigTile big_tile(const BigPlan& pl, int64_t o0, int64_t s0, int rot)
 {
     const uint32_t first = (uint32_t)(pl.weights ? o0 : s0);
-    const uint32_t sfirst = (uint32_t)(pl.sweights ? o0 : s0);
     return BigTile{(uint32_t)__builtin_amdgcn_readfirstlane((int)(first * pl.row_bytes)),
-                   (uint32_t)__builtin_amdgcn_readfirstlane((int)((sfirst / 32) * pl.panel_bytes)),
+                   (uint32_t)__builtin_amdgcn_readfirstlane((int)((first / 32) * pl.panel_bytes)),
                    __builtin_amdgcn_readfirstlane(rot)};
 }
 
-// The LDS of the big-tile kernel: four code buffers and four scale-unit buffers, each an
-// array of its own (the compiler orders an LDS read only after DMA into the same array).
+// The LDS of the big-tile kernel: two code buffers and two scale-unit buffers, each an array
+// of its own (the compiler orders an LDS read only after DMA into the same array).
 __shared__ __attribute__((aligned(16))) uint8_t big_c0[big::kCodeBytes];
 __shared__ __attribute__((aligned(16))) uint8_t big_c1[big::kCodeBytes];
-__shared__ __attribute__((aligned(16))) uint8_t big_c2[big::kCodeBytes];
-__shared__ __attribute__((aligned(16))) uint8_t big_c3[big::kCodeBytes];
 __shared__ __attribute__((aligned(16))) uint8_t big_u0[big::kUnitBytes];
 __shared__ __attribute__((aligned(16))) uint8_t big_u1[big::kUnitBytes];
-__shared__ __attribute__((aligned(16))) uint8_t big_u2[big::kUnitBytes];
-__shared__ __attribute__((aligned(16))) uint8_t big_u3[big::kUnitBytes];
 
 template <int I>
 __device__ __forceinline__ uint8_t* big_code()
 {
-    if constexpr (I % 4 == 0) return big_c0;
-    else if constexpr (I % 4 == 1) return big_c1;
-    else if constexpr (I % 4 == 2) return big_c2;
-    else return big_c3;
+    if constexpr (I % 2 == 0) return big_c0;
+    else return big_c1;
 }
 
 template <int I>
 __device__ __forceinline__ uint8_t* big_unit()
 {
-    if constexpr (I % 4 == 0) return big_u0;
-    else if constexpr (I % 4 == 1) return big_u1;
-    else if constexpr (I % 4 == 2) return big_u2;
-    else return big_u3;
+    if constexpr (I % 2 == 0) return big_u0;
+    else return big_u1;
 }
 
 // Calls f(std::integral_constant<int, i>) for i = 0 .. N-1 (unrolled, i a constant).
@@ -1089,46 +1066,30 @@ __device__ __forceinline__ void static_for(F&& f)
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// The DMA of one stage, I = its index in its group of 8 (code buffer I % 4; when I % 4 == 0
-// also the scales of stages I .. I+3: unit I/2 from waves 0-3, unit I/2 + 1 from waves 4-7):
-// this wave's instructions, scales first, one call per instruction d = 0 .. count-1, so that
+// Instruction D of this wave's DMA of one stage (physical stage ph of tile t) into buffer I:
+// D = 0, 1 its two scale panels, D = 2 .. 9 its code rows, one call per instruction so that
 // the caller can spread them between MFMAs.
-template <class C, int I>
-struct BigDma {
-    static constexpr int kScale = I % 4 == 0 ? 1 : 0;
-    static constexpr int kCount = C::count(I);
-    template <int D>
-    __device__ __forceinline__ static void issue(const BigPlan& pl, const BigTile& t, int ph,
-                                                 int wave)
-    {
+template <class C, int I, int D>
+__device__ __forceinline__ void big_dma(const BigPlan& pl, const BigTile& t, int ph, int wave)
+{
 #if defined(__HIP_DEVICE_COMPILE__)
-        // the wave's byte offset in the buffer, made opaque here so that the compiler forms
-        // each instruction's LDS address when it is issued instead of keeping one register per
-        // buffer and instruction alive across the loop (that ran out of scalar registers)
-        uint32_t woff = (uint32_t)wave;
-        asm volatile("" : "+s"(woff));
-        if constexpr (D < kScale) {
-            // waves 4-7 carry the next unit (stages ph + 2, ph + 3, wrapping with the K
-            // rotation); each wave's four panels land at panel (v % 4) * 4 of the unit
-            const int ph2 = ph + 2 < pl.nst ? ph + 2 : ph + 2 - pl.nst;
-            const uint32_t woff4 = (woff & 3u) * 1024u;
-            if (wave < 4)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    pl.scale, (lds_void_t*)(big_unit<I / 2>() + woff4), 16, pl.scale_off,
-                    (int)(t.scale_base + (uint32_t)(ph / 2) * 256u), 0, 0);
-            else
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    pl.scale, (lds_void_t*)(big_unit<I / 2 + 1>() + woff4), 16, pl.scale_off,
-                    (int)(t.scale_base + (uint32_t)(ph2 / 2) * 256u), 0, 0);
-        } else if constexpr (D < kCount) {
-            constexpr int c = D - kScale;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                pl.code, (lds_void_t*)(big_code<I>() + (woff * C::kCodeDma + c) * 1024), 16,
-                pl.code_off[c], (int)(t.code_base + (uint32_t)ph * big::kRowB), 0, 0);
-        }
-#endif
+    // the wave's byte offset in the buffer, made opaque here so that the compiler forms each
+    // instruction's LDS address when it is issued instead of keeping one register per buffer
+    // and instruction alive across the loop (that ran out of scalar registers)
+    uint32_t woff = (uint32_t)wave;
+    asm volatile("" : "+s"(woff));
+    if constexpr (D < 2) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            pl.scale, (lds_void_t*)(big_unit<I>() + (2u * woff + D) * 256u), 4, pl.scale_off[D],
+            (int)(t.scale_base + (uint32_t)ph * 256u), 0, 0);
+    } else {
+        constexpr int c = D - 2;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            pl.code, (lds_void_t*)(big_code<I>() + (woff * C::kCodeDma + c) * 1024), 16,
+            pl.code_off[c], (int)(t.code_base + (uint32_t)ph * big::kRowB), 0, 0);
     }
-};
+#endif
+}
 
 template <int TM, int TN>
 struct BigFrags {
@@ -1141,13 +1102,13 @@ struct BigScales {
     uint32_t w[TM], x[TN];
 };
 
-// Fragment P of K-step T in the order the MFMAs consume them: weight 0, tokens 0..TN-1,
-// weights 1..TM-1.
+// Fragment P of K-step T (blocks 2T, 2T + 1 of the stage) in the order the MFMAs consume
+// them: weight 0, tokens 0..TN-1, weights 1..TM-1.
 template <class C, int T, int P>
 __device__ __forceinline__ void big_frag_piece(BigFrags<C::TM, C::TN>& f, const uint8_t* buf,
                                                int wrow0, int xrow0, int lr, int lg)
 {
-    const uint32_t slot = 16u * (uint32_t)((2 * T + lg) ^ ((lr >> 2) & 3));
+    const uint32_t slot = 16u * (uint32_t)((2 * T + lg) ^ ((lr >> 1) & 7));
     if constexpr (P >= 1 && P <= C::TN) {
         constexpr int b = P - 1;
         f.b[b] = *reinterpret_cast<const uint4*>(buf + (C::BO + xrow0 + 32 * b + lr) * big::kRowB +
@@ -1159,7 +1120,7 @@ __device__ __forceinline__ void big_frag_piece(BigFrags<C::TM, C::TN>& f, const 
 }
 
 // Scale dword R of a unit buffer for this lane: weights 0..TM-1, then tokens 0..TN-1 (the
-// lane's dword of its row's 8 bytes: byte b selects the unit's K-step b).
+// lane's dword of its row's 8 bytes: byte T selects K-step T).
 template <class C, int R>
 __device__ __forceinline__ void big_scale_piece(BigScales<C::TM, C::TN>& sc, const uint8_t* u,
                                                 int wrow0, int xrow0, int lr, int lg)
@@ -1196,15 +1157,14 @@ struct BigWave {
     int wave, wrow0, xrow0, lr, lg;
 };
 
-// Stage s = 8 g + I of a tile (I a compile-time index: code buffer I % 4, unit buffer
-// (I / 2) % 4, scale bytes 2 (I % 2) and 2 (I % 2) + 1).  On entry f0 holds (or is loading)
-// K-step 0 of stage s and sc its unit's scales.  K-step 0 reads K-step 1's fragments in its
-// shadow.  K-step 1 takes, after its first MFMA, the wait for stage s+1 and the barrier (every
-// wave has then read all of stage s, and all of stage s+1 has landed), then issues the DMA
-// of the stage 4 ahead into stage s's buffer (`nt`, at physical stage `ph`: of this tile, the
-// next, or, past the last, a refetch into a buffer never read again so that every wait
-// counts the same) and reads the next stage's scales and K-step 0 fragments, all between its
-// MFMAs (after the last stage of all, reads of a buffer whose contents are not used).
+// Stage s (buffer I = s % 2).  On entry f0 holds (or is loading) K-step 0 of stage s and sc
+// its scales.  K-steps 0-2 read the next K-step's fragments in their shadow.  Then the wave
+// waits for its DMA of stage s+1 and its reads of stage s, and the barrier follows: all of
+// stage s+1 has landed and no wave reads buffer I again.  K-step 3 issues the DMA of stage
+// s+2 into buffer I (`nt`, physical stage `ph`: of this tile, the next, or, past the last,
+// a refetch into a buffer never read again) and reads stage s+1's scales and K-step 0
+// fragments, all between its MFMAs (after the last stage of all, reads of a buffer whose
+// contents are not used).
 template <class C, int I>
 __device__ __forceinline__ void big_stage(v16f (&acc)[C::TM][C::TN], const BigPlan& pl,
                                           const BigWave& wv, const BigTile& nt, int ph,
@@ -1212,46 +1172,46 @@ __device__ __forceinline__ void big_stage(v16f (&acc)[C::TM][C::TN], const BigPl
                                           BigFrags<C::TM, C::TN>& f1,
                                           BigScales<C::TM, C::TN>& sc)
 {
-    constexpr int kSel = 2 * (I & 1);
     constexpr int kPieces = C::TM + C::TN;
     constexpr int kSlots = C::TM * C::TN;
     static_assert(kPieces <= kSlots, "one fragment per MFMA slot");
-    big_kstep<C, kSel>(acc, f0, sc, [&](auto ic) {
+    static_assert(2 * kSlots >= C::kDma && 2 * (kSlots - 1) >= 2 * kPieces, "last K-step slots");
+    big_kstep<C, 0>(acc, f0, sc, [&](auto ic) {
         constexpr int i = decltype(ic)::value;
         if constexpr (i < kPieces)
             big_frag_piece<C, 1, i>(f1, big_code<I>(), wv.wrow0, wv.xrow0, wv.lr, wv.lg);
     });
-    BigScales<C::TM, C::TN> sn = sc;
-    constexpr int J = (I + 1) % 8;                       // index of stage s+1
-    constexpr bool kNewUnit = (J & 1) == 0;
-    using D = BigDma<C, (I + 4) % 8>;
-    constexpr int kReads = kPieces + (kNewUnit ? kPieces : 0);
-    static_assert(2 * (kSlots - 1) >= D::kCount, "DMA slots");
-    static_assert(2 * (kSlots - 1) >= kReads, "read slots");
-    big_kstep<C, kSel + 1>(acc, f1, sc, [&](auto ic) {
+    big_kstep<C, 1>(acc, f1, sc, [&](auto ic) {
         constexpr int i = decltype(ic)::value;
-        {
-            if constexpr (i == 0) {
-                __builtin_amdgcn_s_waitcnt(waitcnt_imm(C::wait(I), 0));
-                barrier_only();
+        if constexpr (i < kPieces)
+            big_frag_piece<C, 2, i>(f0, big_code<I>(), wv.wrow0, wv.xrow0, wv.lr, wv.lg);
+    });
+    big_kstep<C, 2>(acc, f0, sc, [&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i < kPieces)
+            big_frag_piece<C, 3, i>(f1, big_code<I>(), wv.wrow0, wv.xrow0, wv.lr, wv.lg);
+    });
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    barrier_only();
+    BigScales<C::TM, C::TN> sn = sc;
+    constexpr int J = 1 - I;
+    big_kstep<C, 3>(acc, f1, sc, [&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        // two DMA instructions per slot, then (from slot 1) two reads
+        static_for<2>([&](auto jc) {
+            constexpr int d = 2 * i + decltype(jc)::value;
+            if constexpr (d < C::kDma) big_dma<C, I, d>(pl, nt, ph, wv.wave);
+        });
+        static_for<2>([&](auto jc) {
+            constexpr int r = 2 * (i - 1) + decltype(jc)::value;
+            if constexpr (i >= 1 && r < 2 * kPieces) {
+                if constexpr (r < kPieces)
+                    big_scale_piece<C, r>(sn, big_unit<J>(), wv.wrow0, wv.xrow0, wv.lr, wv.lg);
+                else
+                    big_frag_piece<C, 0, r - kPieces>(f0, big_code<J>(), wv.wrow0, wv.xrow0,
+                                                      wv.lr, wv.lg);
             }
-            // slots 1.. : two DMA instructions and two reads per slot
-            static_for<2>([&](auto jc) {
-                constexpr int d = 2 * (i - 1) + decltype(jc)::value;
-                if constexpr (i >= 1) D::template issue<d>(pl, nt, ph, wv.wave);
-            });
-            static_for<2>([&](auto jc) {
-                constexpr int r = 2 * (i - 1) + decltype(jc)::value;
-                if constexpr (i >= 1 && r < kReads) {
-                    if constexpr (kNewUnit && r < kPieces)
-                        big_scale_piece<C, r>(sn, big_unit<J / 2>(), wv.wrow0, wv.xrow0, wv.lr,
-                                              wv.lg);
-                    else
-                        big_frag_piece<C, 0, kNewUnit ? r - kPieces : r>(
-                            f0, big_code<J>(), wv.wrow0, wv.xrow0, wv.lr, wv.lg);
-                }
-            });
-        }
+        });
     });
     sc = sn;
 }
@@ -1319,30 +1279,29 @@ gemm_big_kernel(DmaArgs p, float* __restrict__ y, int64_t tiles_o, int64_t tiles
     const BigWave wv{wave, (wave / C::WS) * (C::BO / C::WO), (wave % C::WS) * (C::BS / C::WS),
                      lane & 31, lane >> 5};
     const int64_t ntiles = tiles_o * tiles_s;
-    const int nst = (int)(p.k / 4);              // 128-element stages, a multiple of 8 (> 0)
+    const int nst = (int)(p.k / 8);              // 256-element stages, a multiple of 4 (> 0)
     const int64_t grid = gridDim.x;
     BigPlan pl;
     big_plan<C>(pl, p, wave, lane);
     auto tile_of = [&](int64_t t, int64_t& o0, int64_t& s0) {
         big_tile_origin<C::kGroupO>(t, tiles_o, tiles_s, o0, s0);
         return big_tile<C>(pl, o0, s0,
-                           C::kRotate ? 2 * (int)k_rotation(tiles_o, tiles_s, o0, s0, C::BO, C::BS,
-                                                            nst / 2)
+                           C::kRotate ? (int)k_rotation(tiles_o, tiles_s, o0, s0, C::BO, C::BS, nst)
                                       : 0);
     };
     int64_t t = blockIdx.x;                      // this workgroup's tiles: t, t + grid, ...
     int64_t o0, s0;
     BigTile cur = tile_of(t, o0, s0);
-    // the first tile's stages 0..3
-    static_for<4>([&](auto ic) {
+    // the first tile's stages 0 and 1
+    static_for<2>([&](auto ic) {
         constexpr int I = decltype(ic)::value;
         const int ph = I + cur.rot < nst ? I + cur.rot : I + cur.rot - nst;
-        static_for<BigDma<C, I>::kCount>([&](auto dc) {
-            BigDma<C, I>::template issue<decltype(dc)::value>(pl, cur, ph, wave);
+        static_for<C::kDma>([&](auto dc) {
+            big_dma<C, I, decltype(dc)::value>(pl, cur, ph, wave);
         });
     });
-    // stage 0: this wave's part once stages 1..3 remain in flight, then all of it
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(C::count(1) + C::count(2) + C::count(3), 0));
+    // stage 0: this wave's part once stage 1 remains in flight, then all of it
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(C::kDma, 0));
     barrier_only();
     BigFrags<C::TM, C::TN> f0, f1;
     BigScales<C::TM, C::TN> sc;
@@ -1364,26 +1323,21 @@ gemm_big_kernel(DmaArgs p, float* __restrict__ y, int64_t tiles_o, int64_t tiles
         const bool has_next = it + 1 < my_tiles;
         int64_t o1 = o0, s1 = s0;
         const BigTile nxt = has_next ? tile_of(t + grid, o1, s1) : cur;
-        // the DMA target of stage s is stage s + 4 of this tile (all but the last group's
-        // second half), else stage s + 4 - nst of the next tile, else (past the last tile)
-        // this tile's last stage again, into a buffer that is never read
+        // the DMA target of stage s is stage s + 2 of this tile (all but the last two
+        // stages), else stage s + 2 - nst of the next tile, else (past the last tile) this
+        // tile's last stage again, into a buffer that is never read
         int s = 0;
-        for (; s < nst - 8; s += 8) {
-            static_for<8>([&](auto ic) {
+        for (; s < nst - 2; s += 2) {
+            static_for<2>([&](auto ic) {
                 constexpr int I = decltype(ic)::value;
-                const int q = s + I + 4 + cur.rot;
+                const int q = s + I + 2 + cur.rot;
                 big_stage<C, I>(acc, pl, wv, cur, q >= nst ? q - nst : q, f0, f1, sc);
             });
         }
-        static_for<4>([&](auto ic) {
-            constexpr int I = decltype(ic)::value;
-            const int q = s + I + 4 + cur.rot;
-            big_stage<C, I>(acc, pl, wv, cur, q >= nst ? q - nst : q, f0, f1, sc);
-        });
         const int last = nst - 1 + cur.rot >= nst ? cur.rot - 1 : nst - 1 + cur.rot;
-        static_for<4>([&](auto ic) {
-            constexpr int I = 4 + decltype(ic)::value;
-            const int q = I - 4 + nxt.rot;
+        static_for<2>([&](auto ic) {
+            constexpr int I = decltype(ic)::value;
+            const int q = I + nxt.rot;
             big_stage<C, I>(acc, pl, wv, nxt, has_next ? (q >= nst ? q - nst : q) : last, f0, f1,
                             sc);
         });
@@ -1401,17 +1355,21 @@ gemm_big_kernel(DmaArgs p, float* __restrict__ y, int64_t tiles_o, int64_t tiles
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
 }
 
-// 256 x 256 tiles, 8 waves of 128 x 64 outputs each (the 4-wave 128 x 128 split measured
-// 1-9% slower on every shape tried)
+// 256 x 256 tiles, 8 waves of 128 x 64 outputs each (measured against 4 x 2 waves of
+// 64 x 128, 2 or 8 weight tiles per XCD sweep, four DMA instructions per MFMA slot and no K
+// rotation: each equal or slower)
 using CfgBig = BigCfg<2, 4>;
 
 // Whether the persistent big-tile kernel takes a GEMM: MFMA-tiled scales, fp32 output with no
-// residual, N a multiple of 1024 (whole groups of 8 stages), and at least two rounds of its
-// tiles.  Measured against the 256 x 128 producer/consumer kernel (graph-timed, rotated
-// buffers, best of two): S = 16384, N = 12288, out = 4096 (1024 tiles) 428 -> 418 us;
+// residual, N a multiple of 1024 (whole pairs of 256-element stages per tile, at least
+// four), and at least two rounds of its tiles.  Measured against the 256 x 128
+// producer/consumer kernel (graph-timed, rotated buffers, best of two), in its first form
+// with 128-element stages: S = 16384, N = 12288, out = 4096 (1024 tiles) 428 -> 418 us;
 // S = 16384, N = 4096 (1024 tiles) 192 -> 177 us; S = 2048, N = 4096, out = 24576 (768
 // tiles) 138 -> 133 us; with 128 tiles (q_proj, down_proj: half the CUs idle) 26 -> 40 us and
-// 58 -> 94 us, which is what the round count excludes.
+// 58 -> 94 us, which is what the round count excludes.  The 256-element stages (whole-line
+// DMA) against that form, same box, outputs bit-identical: 377 -> 365 us, 146 -> 140 us and
+// 122 -> 117 us on the three multi-round shapes.
 inline bool use_big(int64_t S, int64_t k, int64_t out, bool tiled, const uint16_t* res,
                     bool out_bf16)
 {
