@@ -1959,8 +1959,8 @@ gemm_skinny_kernel(DmaArgs p, float* __restrict__ y)
 // step in both operands, and four bf16 MFMAs cover it.  Tile 256 (out) x 128 (tokens), four
 // waves (2 x 2, each 4 x 2 MFMA tiles) at one wave per SIMD, so the 8-dword activation
 // fragments, their bf16 forms and the accumulators fit in registers; each wave
-// issues its quarter of the next stage's DMA between the MFMA rows of the current stage,
-// two stages in LDS, one barrier per stage.  A stage is 8
+// issues its quarter of the next stage's DMA between the MFMA rows of the current stage's
+// first K-step; two stages in LDS, one barrier per stage.  A stage is 8
 // blocks: 256 weight rows of 128 bytes, 128 activation rows of 256 bytes, then the scale
 // bytes (384 rows x 8; tiled: 12 panel units of 256 bytes).  Chunk c (16 bytes) of a weight
 // row r sits at slot c ^ ((r / 2) % 8), as in the W4A4 kernels; an activation row fills a
@@ -2137,7 +2137,11 @@ __device__ __forceinline__ void w4a8_first(W4A8Cvt& c, const W4A8Frags& f,
 // converted a group earlier, so the conversions fill the matrix core's shadow instead of
 // stopping it (graph-timed against converting each group right before its MFMAs: S=16384
 // N=12288 1355 -> 1334 us, S=2048 N=12288 181 -> 174, three other shapes within +-1.3%).
-// The DMA slots follow each weight tile.
+// The next stage's DMA is issued in K-step 0, its instructions spread over the slots that
+// follow each weight tile, so it has the stage's other three K-steps to land before the
+// wait that opens the next stage (spread over all four K-steps, the last requests went out
+// one weight tile before that wait: S=16384 N=12288 1286 -> 1242 us, N=4096 464 -> 450,
+// S=2048 N=12288 167 -> 163, outputs bit-identical).
 template <bool TS, int T, bool kNext>
 __device__ __forceinline__ void w4a8_mfma(v16f (&acc)[w4a8::TM][w4a8::TN], const W4A8Frags& f,
                                           const W4A8Cvt& cur, const W4A8Frags& fn, W4A8Cvt& nxt,
@@ -2145,7 +2149,6 @@ __device__ __forceinline__ void w4a8_mfma(v16f (&acc)[w4a8::TM][w4a8::TN], const
                                           const uint32_t (&xsc)[2][w4a8::TN],
                                           const W4A8Issue<TS>& dma)
 {
-    constexpr int kSlots = (w4a8::kDma + 3) / 4;   // DMA instructions per K-step
     using namespace w4a8;
     constexpr int kSel = TS ? T : 2 * (T & 1);
     constexpr int kWord = TS ? 0 : T >> 1;
@@ -2172,8 +2175,10 @@ __device__ __forceinline__ void w4a8_mfma(v16f (&acc)[w4a8::TM][w4a8::TN], const
             }
             __builtin_amdgcn_sched_barrier(0);
         });
+        if constexpr (T == 0) {
 #pragma unroll
-        for (int d = a * kSlots / TM; d < (a + 1) * kSlots / TM; ++d) dma(T * kSlots + d);
+            for (int d = a * kDma / TM; d < (a + 1) * kDma / TM; ++d) dma(d);
+        }
         __builtin_amdgcn_sched_barrier(0);
     });
 }
